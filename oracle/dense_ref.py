@@ -1,0 +1,82 @@
+"""Brute-force dense reference for tiny problems (torch CPU, float64).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE; used only to pin the C oracle.
+
+It shares no code with ``sta_oracle.c`` and reaches the same result by a
+different route:
+
+* the window of a query tile is found by ENUMERATION, not by a clamp
+  formula: among every placement [s, s+c) of a c-tile window that fits the
+  axis, take the one whose start is closest to the centred start
+  q + o - floor(w/2) (the projection of a point onto an interval is
+  unique, so there is exactly one);
+* the token mask is an explicit N x N boolean matrix built from token
+  coordinates;
+* attention itself is a library routine (``torch.nn.functional.
+  scaled_dot_product_attention`` with that mask), gradients come from
+  torch autograd, and LSE from ``torch.logsumexp`` over the masked scores.
+
+Source of the operator: "Fast Video Generation with Sliding Tile Attention"
+(abstract: attention restricted to local 3D windows instead of 3D full
+attention); window shifts as the stand-in for the deformable windows of
+"MegaSlide-DiT ..." (abstract, 3D-DSA).
+"""
+import itertools
+
+import numpy as np
+import torch
+
+
+def window_by_enumeration(n, w, q, o=0):
+    """Start and count of the allowed tile range on one axis."""
+    c = min(w, n)
+    centred = q + o - w // 2
+    best = None
+    for s in range(0, n - c + 1):
+        key = abs(s - centred)
+        if best is None or key < best[0]:
+            best = (key, s)
+    return best[1], c
+
+
+def token_mask(grid, tile, window, offsets=None):
+    """[N, N] bool: mask[i, j] is True when key token j may be attended by query token i."""
+    T_, H_, W_ = grid
+    nt = [g // t for g, t in zip(grid, tile)]
+    coords = np.array(list(itertools.product(range(T_), range(H_), range(W_))))  # raster order
+    tc = coords // np.array(tile)                                                  # tile coords
+    tid = (tc[:, 0] * nt[1] + tc[:, 1]) * nt[2] + tc[:, 2]
+    N = len(coords)
+    lo = np.zeros((N, 3), np.int64)
+    hi = np.zeros((N, 3), np.int64)
+    for i in range(N):
+        o = (0, 0, 0) if offsets is None else offsets[tid[i]]
+        for d in range(3):
+            s, c = window_by_enumeration(nt[d], window[d], int(tc[i, d]), int(o[d]))
+            lo[i, d], hi[i, d] = s, s + c
+    m = np.ones((N, N), bool)
+    for d in range(3):
+        m &= (tc[None, :, d] >= lo[:, None, d]) & (tc[None, :, d] < hi[:, None, d])
+    return m
+
+
+def attention(q, k, v, grid, tile, windows, offsets=None, scale=None, dout=None):
+    """q,k,v: float arrays [B,H,N,D] in raster order.  Returns float64 numpy
+    (o, lse) and, with dout given, also (dq, dk, dv)."""
+    q = torch.tensor(np.asarray(q), dtype=torch.float64)
+    k = torch.tensor(np.asarray(k), dtype=torch.float64)
+    v = torch.tensor(np.asarray(v), dtype=torch.float64)
+    B, H, N, D = q.shape
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    masks = torch.stack([torch.from_numpy(token_mask(grid, tile, windows[h], offsets)) for h in range(H)])
+    want_grad = dout is not None
+    for t in (q, k, v):
+        t.requires_grad_(want_grad)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=masks[None], scale=scale)
+    scores = torch.matmul(q, k.transpose(-1, -2)) * scale
+    lse = torch.logsumexp(scores.masked_fill(~masks[None], float("-inf")), dim=-1)
+    if not want_grad:
+        return o.detach().numpy(), lse.detach().numpy()
+    o.backward(torch.tensor(np.asarray(dout), dtype=torch.float64))
+    return (o.detach().numpy(), lse.detach().numpy(),
+            q.grad.numpy(), k.grad.numpy(), v.grad.numpy())

@@ -1,0 +1,113 @@
+"""Seeded synthetic inputs and the five workload shapes.
+
+This module holds no attention arithmetic: only geometry, random draws and
+the bf16 rounding of those draws.  The oracle, the HIP path, the smoke check
+and the benchmark all take their inputs from here, so both sides of every
+comparison see identical values.
+
+Workloads stand in for the pages' 5-second 720P video generation ("Fast
+Video Generation with Sliding Tile Attention", abstract): a (30,48,80) latent
+token grid, 24 heads of width 128.  Values are i.i.d. N(0,1), drawn with
+numpy's PCG64 from seed [1234 + cfg, stream], streams 0=Q 1=K 2=V 3=dO
+4=window offsets 5=per-head window choice, then rounded to bf16
+(round-to-nearest-even) for the bf16 workloads.
+"""
+import numpy as np
+
+STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_OFF, STREAM_WIN = range(6)
+
+# Window sizes (in tiles) that the per-head variant draws from.
+HEAD_WINDOW_CHOICES = ((3, 3, 3), (3, 3, 5), (5, 5, 5))
+
+CONFIGS = {
+    1: dict(name="tiny-fp32", B=1, H=2, D=64, dtype="f32", grid=(4, 8, 8), tile=(2, 4, 4),
+            window=(3, 3, 3), offsets=False, per_head=False, backward=False),
+    2: dict(name="mid-7680", B=1, H=24, D=128, dtype="bf16", grid=(8, 24, 40), tile=(4, 8, 8),
+            window=(3, 3, 3), offsets=False, per_head=False, backward=False),
+    3: dict(name="720p-115200", B=1, H=24, D=128, dtype="bf16", grid=(30, 48, 80), tile=(6, 8, 8),
+            window=(3, 3, 5), offsets=False, per_head=False, backward=False),
+    4: dict(name="720p-offsets-perhead", B=1, H=24, D=128, dtype="bf16", grid=(30, 48, 80),
+            tile=(6, 8, 8), window=None, offsets=True, per_head=True, backward=False),
+    5: dict(name="720p-train", B=1, H=24, D=128, dtype="bf16", grid=(30, 48, 80), tile=(6, 8, 8),
+            window=(3, 3, 5), offsets=False, per_head=False, backward=True),
+}
+
+
+def tiles_per_axis(grid, tile):
+    return tuple(g // t for g, t in zip(grid, tile))
+
+
+def num_tiles(grid, tile):
+    return int(np.prod(tiles_per_axis(grid, tile)))
+
+
+def rng(seed, stream):
+    return np.random.default_rng([int(seed), int(stream)])
+
+
+def round_bf16(x):
+    """float32 array -> float32 array holding the bf16 round-to-nearest-even
+    of each value (exactly representable in bf16)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def normal(shape, seed, stream, dtype):
+    x = rng(seed, stream).standard_normal(size=shape, dtype=np.float32)
+    return round_bf16(x) if dtype == "bf16" else x
+
+
+def windows_for(cfg, seed=None):
+    """[H,3] int32 window sizes (tiles) for a workload."""
+    c = CONFIGS[cfg] if isinstance(cfg, int) else cfg
+    if not c["per_head"]:
+        return np.tile(np.asarray(c["window"], np.int32), (c["H"], 1))
+    seed = 1234 + cfg if seed is None else seed
+    pick = rng(seed, STREAM_WIN).integers(0, len(HEAD_WINDOW_CHOICES), size=c["H"])
+    return np.asarray([HEAD_WINDOW_CHOICES[i] for i in pick], np.int32)
+
+
+def offsets_for(cfg, seed=None, lo=(-1, -2, -2), hi=(1, 2, 2)):
+    """[T,3] int32 per-query-tile window shifts (tiles), or None."""
+    c = CONFIGS[cfg] if isinstance(cfg, int) else cfg
+    if not c["offsets"]:
+        return None
+    seed = 1234 + cfg if seed is None else seed
+    T = num_tiles(c["grid"], c["tile"])
+    return rng(seed, STREAM_OFF).integers(lo, hi, endpoint=True, size=(T, 3)).astype(np.int32)
+
+
+def tensors(B, H, N, D, dtype, seed, with_dout=False):
+    """(q, k, v[, dout]) float32 numpy arrays [B,H,N,D] in raster token order."""
+    shape = (B, H, N, D)
+    out = [normal(shape, seed, s, dtype) for s in (STREAM_Q, STREAM_K, STREAM_V)]
+    if with_dout:
+        out.append(normal(shape, seed, STREAM_DO, dtype))
+    return tuple(out)
+
+
+def workload(cfg, heads=None):
+    """Everything one workload needs: dict with geometry, windows, offsets and
+    q, k, v (and dout for the training workload).  ``heads`` keeps only the
+    first few heads (same values as the full draw for those heads is NOT
+    guaranteed; it is a smaller workload of the same shape family)."""
+    c = dict(CONFIGS[cfg])
+    if heads is not None:
+        c["H"] = heads
+    seed = 1234 + cfg
+    N = int(np.prod(c["grid"]))
+    w = windows_for(cfg)[: c["H"]]
+    off = offsets_for(cfg)
+    ts = tensors(c["B"], c["H"], N, c["D"], c["dtype"], seed, with_dout=True)
+    c.update(N=N, windows=w, offsets=off, q=ts[0], k=ts[1], v=ts[2], dout=ts[3],
+             scale=1.0 / np.sqrt(c["D"]), seed=seed)
+    return c
+
+
+def counted_flops(kv_counts, B, L, D):
+    """Forward FLOP counted on unmasked tile pairs only: 4*B*L^2*D per pair
+    (QK^T and PV, 2 flop per multiply-add).  kv_counts: per (head, q-tile)."""
+    return 4.0 * B * float(np.sum(kv_counts)) * L * L * D

@@ -1,0 +1,53 @@
+"""Runs the oracle's pins against one oracle build and reports whether they
+all hold.  Used by test_oracle_mutants.py to show that deliberately altered
+copies of the oracle (planted mistakes, on the CPU only) are caught.
+
+    python -m tests.pin_runner /path/to/liboracle_variant.so   -> exit 0 if every pin holds
+"""
+import sys
+
+from oracle import oracle
+from tests import test_oracle_attention as A
+from tests import test_oracle_index as I
+from tests import test_oracle_perm as P
+from tests.conftest import read_golden
+
+
+def checks():
+    yield lambda: P.test_golden_small("perm_small.txt")
+    yield lambda: P.test_golden_small("perm_asym.txt")
+    yield lambda: P.test_bijection_and_tile_contiguity("asym")
+    for row in read_golden("window_axis.txt"):
+        yield (lambda r: lambda: I.test_window_axis_golden(r))(row)
+    yield lambda: I.test_attendee_counts_720p_golden()
+    yield lambda: I.test_tiny_fp32_workload_is_dense()
+    for case in range(4):
+        yield (lambda c: lambda: I.test_list_invariants(c))(case)
+        yield (lambda c: lambda: I.test_lists_match_enumerated_token_mask(c))(case)
+    yield lambda: I.test_interior_tiles_get_chebyshev_ball()
+    yield lambda: I.test_zero_offsets_equal_no_offsets_and_large_offsets_saturate()
+    yield lambda: A.test_constant_values_and_zero_queries()
+    yield lambda: A.test_whole_grid_window_is_full_attention()
+    yield lambda: A.test_unit_window_is_per_tile_attention()
+    for seed in (1, 2):
+        for off in (False, True):
+            yield (lambda s, o: lambda: A.test_forward_backward_match_torch_dense(s, o))(seed, off)
+    yield lambda: A.test_lse_bounds()
+    yield lambda: A.test_gradient_identities()
+    yield lambda: A.test_backward_matches_finite_differences()
+
+
+def main(path):
+    oracle.use(path)
+    for i, check in enumerate(checks()):
+        try:
+            check()
+        except (AssertionError, ValueError) as e:
+            print("pin %d failed: %s" % (i, str(e).splitlines()[0][:200] if str(e) else type(e).__name__))
+            return 1
+    print("all pins hold")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1]))
