@@ -1,0 +1,187 @@
+/*
+ * libsta -- sliding-tile attention (STA) for AMD Instinct MI355X (gfx950).
+ *
+ * The operator ("Fast Video Generation with Sliding Tile Attention",
+ * abstract): in a video diffusion transformer, 3D full attention over the
+ * (T,H,W) latent token grid is replaced by attention restricted to a local
+ * 3D window that slides with the query.  STA works at tile granularity: the
+ * grid is cut into (tt,th,tw) tiles, and every query tile attends to the
+ * key/value tiles in a window of tiles around it.  Two extensions:
+ *   - per-head window sizes;
+ *   - an optional integer shift of each query tile's window, standing in
+ *     for the motion-adaptive 3D Deformable Slide Attention (3D-DSA) of
+ *     "MegaSlide-DiT: Memory-Centric Adaptation and Deformable Local
+ *     Attention for Efficient Video Diffusion" (abstract).
+ *
+ * Window rule (the pages give none; this is the reading used throughout):
+ * on each axis with n tiles and window size w, the window holds
+ * c = min(w, n) tiles starting at clamp(q + o - floor(w/2), 0, n - c),
+ * where q is the query tile coordinate and o its shift.  Windows are moved
+ * inward at the borders, never cut, so every query tile of a head sees the
+ * same number of key tiles.
+ *
+ * Orders (raster = t slowest, w fastest):
+ *   raster token r = (t*H + h)*W + w;
+ *   tile id        = (t/tt * nh + h/th) * nw + w/tw,  n* = grid / tile;
+ *   tile order     = tile id * L + ((t%tt)*th + h%th)*tw + w%tw,
+ *                    L = tt*th*tw tokens per tile.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees, synchronises or prints.
+ *   - Work is enqueued on the given HIP stream (0 = the null stream) and
+ *     is asynchronous; device faults surface at the caller's next sync.
+ *   - Arguments are checked on the host before anything is launched: on
+ *     any error nothing is written.  STA_ERR_INVALID = malformed arguments;
+ *     STA_ERR_UNSUPPORTED = well-formed but not implemented (reason in
+ *     sta_last_error()); STA_ERR_HIP = a HIP launch error.
+ *   - Attention tensors are [B][H][N][D], D fastest, in TILE order
+ *     (sta_tile_reorder converts), 16-byte aligned, not aliasing each other.
+ *   - The index is shared by every batch item; window shifts are shared by
+ *     every head and batch item.
+ *   - Thread-safe: no mutable global state apart from a thread-local
+ *     error message.
+ */
+#ifndef LIBSTA_H
+#define LIBSTA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    STA_OK = 0,
+    STA_ERR_INVALID = 1,
+    STA_ERR_UNSUPPORTED = 2,
+    STA_ERR_HIP = 3
+} sta_status;
+
+typedef enum {
+    STA_BF16 = 0,   /* bf16 storage, fp32 accumulation (MFMA path)        */
+    STA_F32 = 1     /* fp32 storage and arithmetic (small shapes, checks) */
+} sta_dtype;
+
+typedef struct { int32_t t, h, w; } sta_dim3;
+
+/* Token grid and tile extents; every grid extent must be a positive
+ * multiple of the tile extent. */
+typedef struct { sta_dim3 grid; sta_dim3 tile; } sta_geom;
+
+/* Block-sparse index.  All four arrays are caller-owned DEVICE memory:
+ *   kv_idx [num_heads][num_tiles][max_kv]  key tiles of each query tile,
+ *                                          ascending tile id, padded -1
+ *   kv_cnt [num_heads][num_tiles]
+ *   q_idx  [num_heads][num_tiles][max_q]   query tiles whose window holds
+ *                                          each key tile, ascending, pad -1
+ *   q_cnt  [num_heads][num_tiles]
+ * Size max_kv / max_q with sta_index_dims.  q_idx/q_cnt are only needed by
+ * sta_bwd and may be NULL (with max_q = 0) for forward-only use. */
+typedef struct {
+    int32_t num_heads, num_tiles, max_kv, max_q;
+    int32_t *kv_idx, *kv_cnt;
+    int32_t *q_idx, *q_cnt;
+} sta_index;
+
+/* Name of a status code (static string). */
+const char *sta_status_str(sta_status s);
+
+/* Human-readable reason for the last non-OK status returned on the calling
+ * thread (static or thread-local storage; empty string if none). */
+const char *sta_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t sta_version(void);
+
+/*
+ * Host-only helper, launches nothing.  For H heads with window sizes
+ * windows_host[H] (tiles, each >= 1) returns
+ *   *max_kv: the largest list length of any query tile,
+ *            max_h prod_d min(w_hd, n_d);
+ *   *max_q : a safe capacity for the transposed lists: the exact maximum
+ *            when has_offsets == 0, else num_tiles (shifts can pile many
+ *            windows onto one key tile).
+ * Either output pointer may be NULL.
+ */
+sta_status sta_index_dims(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
+                          int32_t has_offsets, int32_t *max_kv, int32_t *max_q);
+
+/*
+ * Token permutation between raster order and tile order (the order the
+ * attention kernels read), for `outer` independent slabs of N rows of
+ * row_bytes bytes each (N = grid.t*grid.h*grid.w):
+ *   inverse == 0:  dst[o][tile_pos(r)] = src[o][r]     (raster -> tile)
+ *   inverse != 0:  dst[o][r] = src[o][tile_pos(r)]     (tile -> raster)
+ * A pure byte copy (exact for any dtype).  [B][H][N][D] bf16 tensors use
+ * outer = B*H, row_bytes = 2*D; [B][N][H][D] tensors use outer = B,
+ * row_bytes = 2*H*D; LSE [B][H][N] fp32 uses outer = B*H, row_bytes = 4.
+ * src and dst must not overlap.  Any alignment is accepted; 16-byte aligned
+ * pointers with row_bytes a multiple of 16 take the 16-byte path.
+ * Source of the operation: tiles of the token grid are the unit STA
+ * attends over ("Fast Video Generation with Sliding Tile Attention").
+ */
+sta_status sta_tile_reorder(const void *src, void *dst, int64_t outer, int64_t row_bytes,
+                            const sta_geom *g, int32_t inverse, hipStream_t stream);
+
+/*
+ * Builds the block-sparse index on the device.
+ *   windows_host [H]   window size (tiles) of each head, host memory;
+ *   offsets_dev        NULL, or DEVICE int32 [num_tiles][3] window shifts
+ *                      (dt,dh,dw) in tiles, one per query tile (tile id
+ *                      order), shared by all heads;
+ *   idx                caller-filled descriptor: num_heads == H,
+ *                      num_tiles == number of tiles, max_kv/max_q at least
+ *                      what sta_index_dims returns, device arrays
+ *                      allocated.  If q_idx is NULL only the forward lists
+ *                      are built.
+ * Deterministic: list order is ascending tile id, padding -1.
+ * Source: STA's tile windows ("Fast Video Generation with Sliding Tile
+ * Attention", abstract); shifted windows for 3D-DSA ("MegaSlide-DiT",
+ * abstract).
+ */
+sta_status sta_build_index(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
+                           const int32_t *offsets_dev, const sta_index *idx, hipStream_t stream);
+
+/*
+ * Fused forward.  For every (b, h) and query token i (tile order):
+ *   s_ij  = scale * <q_i, k_j>   for keys j in the tiles listed for tile(i)
+ *   lse_i = ln sum_j exp(s_ij)                                   (fp32)
+ *   o_i   = sum_j exp(s_ij - lse_i) v_j                          (dtype)
+ * q, k, v, o: [B][H][N][D] in tile order; lse: [B][H][N] fp32 in tile
+ * order.  D must be 64 or 128.  bf16 uses MFMA with fp32 accumulation; the
+ * probabilities are rounded to bf16 before the PV product.
+ * Source: attention restricted to the sliding 3D window ("Fast Video
+ * Generation with Sliding Tile Attention", abstract).
+ */
+sta_status sta_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
+                   const sta_geom *g, const sta_index *idx, hipStream_t stream);
+
+/*
+ * Backward of sta_fwd, given the upstream gradient dout and the forward's
+ * o and lse:
+ *   P_ij  = exp(s_ij - lse_i),  dP_ij = <dout_i, v_j>,
+ *   Delta_i = <dout_i, o_i>     (written to delta_ws, fp32 [B][H][N]),
+ *   dS_ij = P_ij (dP_ij - Delta_i),
+ *   dq_i  = scale * sum_j dS_ij k_j,
+ *   dk_j  = scale * sum_i dS_ij q_i,   dv_j = sum_i P_ij dout_i.
+ * All tensors [B][H][N][D] in tile order; dq, dk, dv are fully written
+ * (no accumulation into existing contents); no atomics, deterministic.
+ * Needs the transposed lists (idx->q_idx, idx->q_cnt).  delta_ws is a
+ * caller-owned device workspace of B*H*N floats.
+ * Source: the pages' system adapts a pre-trained DiT by full-parameter
+ * training through the local attention operator ("MegaSlide-DiT",
+ * abstract), which needs these gradients.
+ */
+sta_status sta_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dout, void *dq, void *dk, void *dv, float *delta_ws,
+                   int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
+                   const sta_geom *g, const sta_index *idx, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSTA_H */

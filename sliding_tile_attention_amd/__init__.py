@@ -1,0 +1,225 @@
+"""Python binding of libsta (sliding-tile attention for MI355X / gfx950).
+
+Thin ctypes layer over the C ABI in ``include/libsta.h``: the functions
+named ``sta_*`` take torch tensors (device memory) and marshal their data
+pointers, sizes and the current HIP stream; every step of the computation
+runs in the HIP kernels of ``libsta.so``.  There is no CPU fallback: if the
+library is missing, importing this package raises.
+
+Operator: "Fast Video Generation with Sliding Tile Attention" (abstract) --
+attention restricted to a window of tiles around each query tile of the
+(T,H,W) video token grid; optional per-query-tile window shifts stand in for
+the deformable windows (3D-DSA) of "MegaSlide-DiT" (abstract).
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsta.so")
+
+STA_OK, STA_ERR_INVALID, STA_ERR_UNSUPPORTED, STA_ERR_HIP = 0, 1, 2, 3
+STA_BF16, STA_F32 = 0, 1
+EXPORTS = ("sta_status_str", "sta_last_error", "sta_version", "sta_index_dims", "sta_tile_reorder",
+           "sta_build_index", "sta_fwd", "sta_bwd")
+
+
+class StaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (_STATUS_NAMES.get(status, status), message))
+        self.status = status
+
+
+_STATUS_NAMES = {0: "STA_OK", 1: "STA_ERR_INVALID", 2: "STA_ERR_UNSUPPORTED", 3: "STA_ERR_HIP"}
+
+
+class sta_dim3(ctypes.Structure):
+    _fields_ = [("t", ctypes.c_int32), ("h", ctypes.c_int32), ("w", ctypes.c_int32)]
+
+
+class sta_geom(ctypes.Structure):
+    _fields_ = [("grid", sta_dim3), ("tile", sta_dim3)]
+
+
+class sta_index(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("num_tiles", ctypes.c_int32),
+                ("max_kv", ctypes.c_int32), ("max_q", ctypes.c_int32),
+                ("kv_idx", ctypes.c_void_p), ("kv_cnt", ctypes.c_void_p),
+                ("q_idx", ctypes.c_void_p), ("q_cnt", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libsta.so is not built (expected at %s); run "
+                          "`python -m sliding_tile_attention_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    G, X = ctypes.POINTER(sta_geom), ctypes.POINTER(sta_index)
+    W = ctypes.POINTER(sta_dim3)
+    sig = {
+        "sta_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "sta_last_error": (ctypes.c_char_p, []),
+        "sta_version": (I32, []),
+        "sta_index_dims": (ctypes.c_int, [G, I32, W, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "sta_tile_reorder": (ctypes.c_int, [P, P, I64, I64, G, I32, P]),
+        "sta_build_index": (ctypes.c_int, [G, I32, W, P, X, P]),
+        "sta_fwd": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X, P]),
+        "sta_bwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status):
+    if status != STA_OK:
+        raise StaError(status, lib.sta_last_error().decode())
+
+
+@dataclass(frozen=True)
+class Geometry:
+    """Token grid (T,H,W) and tile (tt,th,tw) extents."""
+    grid: tuple
+    tile: tuple
+
+    def c(self):
+        return sta_geom(sta_dim3(*self.grid), sta_dim3(*self.tile))
+
+    @property
+    def tiles(self):
+        return tuple(g // t for g, t in zip(self.grid, self.tile))
+
+    @property
+    def num_tiles(self):
+        a, b, c = self.tiles
+        return a * b * c
+
+    @property
+    def tokens(self):
+        a, b, c = self.grid
+        return a * b * c
+
+    @property
+    def tile_tokens(self):
+        a, b, c = self.tile
+        return a * b * c
+
+
+def _windows(windows):
+    ws = [tuple(int(x) for x in w) for w in windows]
+    arr = (sta_dim3 * len(ws))(*[sta_dim3(*w) for w in ws])
+    return arr, len(ws)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+# ---------------------------------------------------------------- C ABI --
+
+def sta_index_dims(geom, windows, has_offsets):
+    """(max_kv, max_q) capacities for H = len(windows) heads."""
+    w, H = _windows(windows)
+    kv, q = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.sta_index_dims(ctypes.byref(geom.c()), H, w, int(bool(has_offsets)),
+                              ctypes.byref(kv), ctypes.byref(q)))
+    return kv.value, q.value
+
+
+def sta_tile_reorder(src, dst, outer, row_bytes, geom, inverse, stream=None):
+    _check(lib.sta_tile_reorder(_ptr(src), _ptr(dst), int(outer), int(row_bytes), ctypes.byref(geom.c()),
+                                int(bool(inverse)), _stream(stream)))
+
+
+def sta_build_index(geom, windows, offsets, index, stream=None):
+    """offsets: None or int32 device tensor [num_tiles, 3]; index: StaIndex."""
+    w, H = _windows(windows)
+    _check(lib.sta_build_index(ctypes.byref(geom.c()), H, w, _ptr(offsets), ctypes.byref(index.c()),
+                               _stream(stream)))
+
+
+def sta_fwd(q, k, v, o, lse, B, H, D, dtype, scale, geom, index, stream=None):
+    _check(lib.sta_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, D, dtype, float(scale),
+                       ctypes.byref(geom.c()), ctypes.byref(index.c()), _stream(stream)))
+
+
+def sta_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, scale, geom, index, stream=None):
+    _check(lib.sta_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                       _ptr(dv), _ptr(delta_ws), B, H, D, dtype, float(scale), ctypes.byref(geom.c()),
+                       ctypes.byref(index.c()), _stream(stream)))
+
+
+# ------------------------------------------------- allocation helpers --
+
+class StaIndex:
+    """Device buffers of a block-sparse index (allocated with torch)."""
+
+    def __init__(self, geom, windows, offsets=None, device="cuda", transposed=True, stream=None):
+        H, T = len(windows), geom.num_tiles
+        self.max_kv, max_q = sta_index_dims(geom, windows, offsets is not None)
+        self.max_q = max_q if transposed else 0
+        i32 = dict(dtype=torch.int32, device=device)
+        self.kv_idx = torch.empty((H, T, self.max_kv), **i32)
+        self.kv_cnt = torch.empty((H, T), **i32)
+        self.q_idx = torch.empty((H, T, self.max_q), **i32) if transposed else None
+        self.q_cnt = torch.empty((H, T), **i32) if transposed else None
+        self.num_heads, self.num_tiles = H, T
+        self.windows = [tuple(w) for w in windows]
+        sta_build_index(geom, windows, offsets, self, stream)
+
+    def c(self):
+        return sta_index(self.num_heads, self.num_tiles, self.max_kv, self.max_q,
+                         self.kv_idx.data_ptr(), self.kv_cnt.data_ptr(),
+                         self.q_idx.data_ptr() if self.q_idx is not None else None,
+                         self.q_cnt.data_ptr() if self.q_cnt is not None else None)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return STA_BF16
+    if t.dtype == torch.float32:
+        return STA_F32
+    raise TypeError("libsta supports bfloat16 and float32 tensors, got %s" % t.dtype)
+
+
+def tile_reorder(x, geom, inverse=False, out=None, stream=None):
+    """Permute the token axis of a contiguous [..., N, C] tensor between
+    raster and tile order; returns a new tensor (or writes `out`)."""
+    assert x.is_contiguous() and x.shape[-2] == geom.tokens
+    out = torch.empty_like(x) if out is None else out
+    row_bytes = x.shape[-1] * x.element_size()
+    outer = x.numel() // (geom.tokens * x.shape[-1])
+    sta_tile_reorder(x, out, outer, row_bytes, geom, inverse, stream)
+    return out
+
+
+def forward(q, k, v, geom, index, scale=None, stream=None):
+    """q, k, v [B,H,N,D] in tile order -> (o [B,H,N,D], lse [B,H,N] fp32)."""
+    B, H, N, D = q.shape
+    scale = D ** -0.5 if scale is None else scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    sta_fwd(q, k, v, o, lse, B, H, D, _dtype_code(q), scale, geom, index, stream)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, dout, geom, index, scale=None, stream=None):
+    """Gradients (dq, dk, dv) of forward(); all tensors in tile order."""
+    B, H, N, D = q.shape
+    scale = D ** -0.5 if scale is None else scale
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    sta_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, D, _dtype_code(q), scale, geom, index, stream)
+    return dq, dk, dv

@@ -1,0 +1,264 @@
+// C-ABI entry points of libsta: argument checks on the host, then dispatch
+// to the kernels.  Nothing is launched when a check fails.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace sta {
+
+static thread_local char g_err[512];
+
+sta_status fail(sta_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+int axis_max_attendees(int n, int w)
+{
+    int best = 0;
+    for (int k = 0; k < n; ++k) {
+        int cnt = 0;
+        for (int q = 0; q < n; ++q) {
+            int s, c;
+            axis_window(n, w, q, 0, s, c);
+            cnt += (k >= s && k < s + c);
+        }
+        best = cnt > best ? cnt : best;
+    }
+    return best;
+}
+
+// Largest token count / tile count the kernels index with 32-bit ints.
+static const int64_t kMaxTokens = (int64_t)1 << 30;
+static const int64_t kMaxTiles = (int64_t)1 << 20;
+
+static sta_status make_geo(const sta_geom *g, Geo &out)
+{
+    if (!g)
+        return fail(STA_ERR_INVALID, "geometry pointer is NULL");
+    const int gr[3] = {g->grid.t, g->grid.h, g->grid.w};
+    const int tl[3] = {g->tile.t, g->tile.h, g->tile.w};
+    for (int d = 0; d < 3; ++d) {
+        if (gr[d] <= 0 || tl[d] <= 0)
+            return fail(STA_ERR_INVALID, "grid and tile extents must be positive (axis %d: grid %d tile %d)",
+                        d, gr[d], tl[d]);
+        if (gr[d] % tl[d] != 0)
+            return fail(STA_ERR_INVALID, "grid extent %d is not a multiple of tile extent %d on axis %d",
+                        gr[d], tl[d], d);
+    }
+    int64_t N = (int64_t)gr[0] * gr[1] * gr[2];
+    int64_t T = (int64_t)(gr[0] / tl[0]) * (gr[1] / tl[1]) * (gr[2] / tl[2]);
+    if (N > kMaxTokens || T > kMaxTiles)
+        return fail(STA_ERR_UNSUPPORTED, "grid too large: %lld tokens, %lld tiles", (long long)N, (long long)T);
+    out.gt = gr[0]; out.gh = gr[1]; out.gw = gr[2];
+    out.tt = tl[0]; out.th = tl[1]; out.tw = tl[2];
+    out.nt = gr[0] / tl[0]; out.nh = gr[1] / tl[1]; out.nw = gr[2] / tl[2];
+    out.T = (int)T;
+    out.L = tl[0] * tl[1] * tl[2];
+    out.N = N;
+    return STA_OK;
+}
+
+static sta_status index_needs(const Geo &g, int H, const sta_dim3 *w, int has_offsets,
+                              int32_t &max_kv, int32_t &max_q)
+{
+    if (H <= 0)
+        return fail(STA_ERR_INVALID, "number of heads must be positive (got %d)", H);
+    if (!w)
+        return fail(STA_ERR_INVALID, "windows pointer is NULL");
+    int64_t kv = 0, qq = 0;
+    for (int h = 0; h < H; ++h) {
+        if (w[h].t < 1 || w[h].h < 1 || w[h].w < 1)
+            return fail(STA_ERR_INVALID, "window of head %d must be >= 1 on every axis (%d,%d,%d)",
+                        h, w[h].t, w[h].h, w[h].w);
+        int64_t c = (int64_t)(w[h].t < g.nt ? w[h].t : g.nt) * (w[h].h < g.nh ? w[h].h : g.nh) *
+                    (w[h].w < g.nw ? w[h].w : g.nw);
+        kv = c > kv ? c : kv;
+        if (!has_offsets) {
+            int64_t a = (int64_t)axis_max_attendees(g.nt, w[h].t) * axis_max_attendees(g.nh, w[h].h) *
+                        axis_max_attendees(g.nw, w[h].w);
+            qq = a > qq ? a : qq;
+        }
+    }
+    max_kv = (int32_t)kv;
+    max_q = has_offsets ? g.T : (int32_t)qq;
+    return STA_OK;
+}
+
+static sta_status check_index(const Geo &g, int H, const sta_index *idx, bool need_transposed)
+{
+    if (!idx)
+        return fail(STA_ERR_INVALID, "index pointer is NULL");
+    if (idx->num_heads != H)
+        return fail(STA_ERR_INVALID, "index has %d heads, call has %d", idx->num_heads, H);
+    if (idx->num_tiles != g.T)
+        return fail(STA_ERR_INVALID, "index has %d tiles, geometry has %d", idx->num_tiles, g.T);
+    if (idx->max_kv < 1 || idx->max_kv > g.T || !idx->kv_idx || !idx->kv_cnt)
+        return fail(STA_ERR_INVALID, "index forward lists are missing or max_kv=%d is out of range",
+                    idx->max_kv);
+    if (need_transposed && (idx->max_q < 1 || idx->max_q > g.T || !idx->q_idx || !idx->q_cnt))
+        return fail(STA_ERR_INVALID, "backward needs the transposed lists (q_idx, q_cnt, max_q=%d)",
+                    idx->max_q);
+    return STA_OK;
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static sta_status check_attn(const Geo &g, int B, int H, int D, sta_dtype dt, float scale)
+{
+    if (B <= 0 || H <= 0 || D <= 0)
+        return fail(STA_ERR_INVALID, "B, H and D must be positive (B=%d H=%d D=%d)", B, H, D);
+    if (dt != STA_BF16 && dt != STA_F32)
+        return fail(STA_ERR_INVALID, "unknown dtype %d", (int)dt);
+    if (!(scale > 0.0f) || !isfinite(scale))
+        return fail(STA_ERR_INVALID, "scale must be positive and finite");
+    if (D != 64 && D != 128)
+        return fail(STA_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", D);
+    if ((int64_t)B * H * g.N * D > ((int64_t)1 << 40))
+        return fail(STA_ERR_UNSUPPORTED, "tensor too large");
+    if (dt == STA_BF16 && g.L % 16 != 0)
+        return fail(STA_ERR_UNSUPPORTED, "bf16 path needs tokens per tile to be a multiple of 16 (L=%d)", g.L);
+    return STA_OK;
+}
+
+}  // namespace sta
+
+using namespace sta;
+
+extern "C" {
+
+const char *sta_status_str(sta_status s)
+{
+    switch (s) {
+    case STA_OK: return "STA_OK";
+    case STA_ERR_INVALID: return "STA_ERR_INVALID";
+    case STA_ERR_UNSUPPORTED: return "STA_ERR_UNSUPPORTED";
+    case STA_ERR_HIP: return "STA_ERR_HIP";
+    }
+    return "STA_ERR_UNKNOWN";
+}
+
+const char *sta_last_error(void) { return g_err; }
+
+int32_t sta_version(void) { return 10000; }
+
+sta_status sta_index_dims(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
+                          int32_t has_offsets, int32_t *max_kv, int32_t *max_q)
+{
+    Geo geo;
+    sta_status st = make_geo(g, geo);
+    if (st != STA_OK) return st;
+    int32_t kv, qq;
+    st = index_needs(geo, H, windows_host, has_offsets, kv, qq);
+    if (st != STA_OK) return st;
+    if (max_kv) *max_kv = kv;
+    if (max_q) *max_q = qq;
+    return STA_OK;
+}
+
+sta_status sta_tile_reorder(const void *src, void *dst, int64_t outer, int64_t row_bytes,
+                            const sta_geom *g, int32_t inverse, hipStream_t stream)
+{
+    Geo geo;
+    sta_status st = make_geo(g, geo);
+    if (st != STA_OK) return st;
+    if (!src || !dst)
+        return fail(STA_ERR_INVALID, "src and dst must be non-NULL");
+    if (outer <= 0 || row_bytes <= 0)
+        return fail(STA_ERR_INVALID, "outer and row_bytes must be positive");
+    int64_t bytes = outer * geo.N * row_bytes;
+    if (bytes / outer / geo.N != row_bytes || bytes > ((int64_t)1 << 42))
+        return fail(STA_ERR_UNSUPPORTED, "tensor too large");
+    const char *a = (const char *)src, *b = (const char *)dst;
+    if (a < b + bytes && b < a + bytes)
+        return fail(STA_ERR_INVALID, "src and dst overlap");
+    return launch_reorder(src, dst, outer, row_bytes, geo, inverse != 0, stream);
+}
+
+sta_status sta_build_index(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
+                           const int32_t *offsets_dev, const sta_index *idx, hipStream_t stream)
+{
+    Geo geo;
+    sta_status st = make_geo(g, geo);
+    if (st != STA_OK) return st;
+    int32_t kv, qq;
+    st = index_needs(geo, H, windows_host, offsets_dev != nullptr, kv, qq);
+    if (st != STA_OK) return st;
+    if (!idx)
+        return fail(STA_ERR_INVALID, "index pointer is NULL");
+    if (idx->num_heads != H || idx->num_tiles != geo.T)
+        return fail(STA_ERR_INVALID, "index descriptor is for %d heads x %d tiles, need %d x %d",
+                    idx->num_heads, idx->num_tiles, H, geo.T);
+    if (!idx->kv_idx || !idx->kv_cnt)
+        return fail(STA_ERR_INVALID, "kv_idx and kv_cnt must be allocated");
+    if (idx->max_kv < kv)
+        return fail(STA_ERR_INVALID, "max_kv=%d is below the %d this geometry needs", idx->max_kv, kv);
+    if (idx->q_idx || idx->q_cnt) {
+        if (!idx->q_idx || !idx->q_cnt)
+            return fail(STA_ERR_INVALID, "q_idx and q_cnt must both be given or both be NULL");
+        if (idx->max_q < qq)
+            return fail(STA_ERR_INVALID, "max_q=%d is below the %d this geometry needs", idx->max_q, qq);
+    }
+    int32_t wins[3 * 4096];
+    if (H > 4096)
+        return fail(STA_ERR_UNSUPPORTED, "more than 4096 heads");
+    for (int h = 0; h < H; ++h) {
+        wins[3 * h] = windows_host[h].t;
+        wins[3 * h + 1] = windows_host[h].h;
+        wins[3 * h + 2] = windows_host[h].w;
+    }
+    return launch_build_index(geo, H, wins, offsets_dev, *idx, stream);
+}
+
+sta_status sta_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
+                   const sta_geom *g, const sta_index *idx, hipStream_t stream)
+{
+    Geo geo;
+    sta_status st = make_geo(g, geo);
+    if (st != STA_OK) return st;
+    if ((st = check_attn(geo, B, H, D, dtype, scale)) != STA_OK) return st;
+    if ((st = check_index(geo, H, idx, false)) != STA_OK) return st;
+    if (!q || !k || !v || !o || !lse)
+        return fail(STA_ERR_INVALID, "q, k, v, o and lse must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return fail(STA_ERR_INVALID, "tensor pointers must be 16-byte aligned");
+    if (dtype == STA_F32)
+        return launch_fwd_f32((const float *)q, (const float *)k, (const float *)v, (float *)o, lse,
+                              B, H, D, scale, geo, *idx, stream);
+    return launch_fwd_bf16(q, k, v, o, lse, B, H, D, scale, geo, *idx, stream);
+}
+
+sta_status sta_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dout, void *dq, void *dk, void *dv, float *delta_ws,
+                   int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
+                   const sta_geom *g, const sta_index *idx, hipStream_t stream)
+{
+    Geo geo;
+    sta_status st = make_geo(g, geo);
+    if (st != STA_OK) return st;
+    if ((st = check_attn(geo, B, H, D, dtype, scale)) != STA_OK) return st;
+    if ((st = check_index(geo, H, idx, true)) != STA_OK) return st;
+    const void *ins[6] = {q, k, v, o, lse, dout};
+    void *outs[4] = {dq, dk, dv, delta_ws};
+    for (const void *p : ins)
+        if (!p || !aligned16(p))
+            return fail(STA_ERR_INVALID, "inputs must be non-NULL and 16-byte aligned");
+    for (void *p : outs)
+        if (!p || !aligned16(p))
+            return fail(STA_ERR_INVALID, "outputs must be non-NULL and 16-byte aligned");
+    if (dtype == STA_F32)
+        return launch_bwd_f32((const float *)q, (const float *)k, (const float *)v, (const float *)o, lse,
+                              (const float *)dout, (float *)dq, (float *)dk, (float *)dv, delta_ws,
+                              B, H, D, scale, geo, *idx, stream);
+    return launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, scale, geo, *idx, stream);
+}
+
+}  // extern "C"

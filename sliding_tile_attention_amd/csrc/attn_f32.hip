@@ -1,0 +1,198 @@
+// fp32 attention path: one thread per query row (forward, dQ) or key row
+// (dK/dV), walking the block-sparse lists.  Plain VALU code meant for small
+// shapes and for fp32 callers; the bf16 MFMA kernels carry the performance.
+#include "common.h"
+
+namespace sta {
+
+template <int D>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
+                                                      const float *__restrict__ V, float *__restrict__ O,
+                                                      float *__restrict__ LSE, const int32_t *__restrict__ kv_idx,
+                                                      const int32_t *__restrict__ kv_cnt, int max_kv, int B,
+                                                      int H, Geo g, float scale)
+{
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (int64_t)B * H * g.N) return;
+    const int64_t i = gid % g.N;
+    const int64_t bh = gid / g.N;
+    const int h = (int)(bh % H);
+    const int qt = (int)(i / g.L);
+    const float *kb = K + bh * g.N * D;
+    const float *vb = V + bh * g.N * D;
+    float q[D], acc[D];
+    for (int d = 0; d < D; ++d) {
+        q[d] = Q[gid * D + d];
+        acc[d] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+    const int cnt = kv_cnt[(int64_t)h * g.T + qt];
+    const int32_t *lst = kv_idx + ((int64_t)h * g.T + qt) * max_kv;
+    for (int e = 0; e < cnt; ++e) {
+        const int64_t j0 = (int64_t)lst[e] * g.L;
+        for (int jj = 0; jj < g.L; ++jj) {
+            const float *kr = kb + (j0 + jj) * D;
+            float s = 0.f;
+            for (int d = 0; d < D; ++d) s = fmaf(q[d], kr[d], s);
+            s *= scale;
+            const float mn = fmaxf(m, s);
+            const float alpha = expf(m - mn);   // m = -inf on the first key: alpha = 0
+            const float p = expf(s - mn);
+            l = l * alpha + p;
+            const float *vr = vb + (j0 + jj) * D;
+            for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vr[d], acc[d] * alpha);
+            m = mn;
+        }
+    }
+    const float inv = 1.f / l;
+    for (int d = 0; d < D; ++d) O[gid * D + d] = acc[d] * inv;
+    LSE[gid] = m + logf(l);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void delta_f32_kernel(const float *__restrict__ O, const float *__restrict__ dO,
+                                                        float *__restrict__ delta, int64_t rows)
+{
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    float s = 0.f;
+    for (int d = 0; d < D; ++d) s = fmaf(O[r * D + d], dO[r * D + d], s);
+    delta[r] = s;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void dq_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
+                                                     const float *__restrict__ V, const float *__restrict__ LSE,
+                                                     const float *__restrict__ dO, const float *__restrict__ delta,
+                                                     float *__restrict__ dQ, const int32_t *__restrict__ kv_idx,
+                                                     const int32_t *__restrict__ kv_cnt, int max_kv, int B, int H,
+                                                     Geo g, float scale)
+{
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (int64_t)B * H * g.N) return;
+    const int64_t i = gid % g.N;
+    const int64_t bh = gid / g.N;
+    const int h = (int)(bh % H);
+    const int qt = (int)(i / g.L);
+    const float *kb = K + bh * g.N * D;
+    const float *vb = V + bh * g.N * D;
+    float q[D], go[D], acc[D];
+    for (int d = 0; d < D; ++d) {
+        q[d] = Q[gid * D + d];
+        go[d] = dO[gid * D + d];
+        acc[d] = 0.f;
+    }
+    const float lse = LSE[gid], dl = delta[gid];
+    const int cnt = kv_cnt[(int64_t)h * g.T + qt];
+    const int32_t *lst = kv_idx + ((int64_t)h * g.T + qt) * max_kv;
+    for (int e = 0; e < cnt; ++e) {
+        const int64_t j0 = (int64_t)lst[e] * g.L;
+        for (int jj = 0; jj < g.L; ++jj) {
+            const float *kr = kb + (j0 + jj) * D;
+            const float *vr = vb + (j0 + jj) * D;
+            float s = 0.f, dp = 0.f;
+            for (int d = 0; d < D; ++d) {
+                s = fmaf(q[d], kr[d], s);
+                dp = fmaf(go[d], vr[d], dp);
+            }
+            const float p = expf(s * scale - lse);
+            const float ds = p * (dp - dl);
+            for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, kr[d], acc[d]);
+        }
+    }
+    for (int d = 0; d < D; ++d) dQ[gid * D + d] = acc[d] * scale;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
+                                                       const float *__restrict__ V, const float *__restrict__ LSE,
+                                                       const float *__restrict__ dO, const float *__restrict__ delta,
+                                                       float *__restrict__ dK, float *__restrict__ dV,
+                                                       const int32_t *__restrict__ q_idx,
+                                                       const int32_t *__restrict__ q_cnt, int max_q, int B, int H,
+                                                       Geo g, float scale)
+{
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (int64_t)B * H * g.N) return;
+    const int64_t j = gid % g.N;
+    const int64_t bh = gid / g.N;
+    const int h = (int)(bh % H);
+    const int kt = (int)(j / g.L);
+    const float *qb = Q + bh * g.N * D;
+    const float *ob = dO + bh * g.N * D;
+    const float *lb = LSE + bh * g.N;
+    const float *db = delta + bh * g.N;
+    float k[D], v[D], ak[D], av[D];
+    for (int d = 0; d < D; ++d) {
+        k[d] = K[gid * D + d];
+        v[d] = V[gid * D + d];
+        ak[d] = 0.f;
+        av[d] = 0.f;
+    }
+    const int cnt = q_cnt[(int64_t)h * g.T + kt];
+    const int32_t *lst = q_idx + ((int64_t)h * g.T + kt) * max_q;
+    for (int e = 0; e < cnt; ++e) {
+        const int64_t i0 = (int64_t)lst[e] * g.L;
+        for (int ii = 0; ii < g.L; ++ii) {
+            const float *qr = qb + (i0 + ii) * D;
+            const float *gr = ob + (i0 + ii) * D;
+            float s = 0.f, dp = 0.f;
+            for (int d = 0; d < D; ++d) {
+                s = fmaf(qr[d], k[d], s);
+                dp = fmaf(gr[d], v[d], dp);
+            }
+            const float p = expf(s * scale - lb[i0 + ii]);
+            const float ds = p * (dp - db[i0 + ii]);
+            for (int d = 0; d < D; ++d) {
+                av[d] = fmaf(p, gr[d], av[d]);
+                ak[d] = fmaf(ds, qr[d], ak[d]);
+            }
+        }
+    }
+    for (int d = 0; d < D; ++d) {
+        dK[gid * D + d] = ak[d] * scale;
+        dV[gid * D + d] = av[d];
+    }
+}
+
+static dim3 grid_for(int64_t threads) { return dim3((unsigned)((threads + 255) / 256)); }
+
+sta_status launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse, int B, int H,
+                          int D, float scale, const Geo &g, const sta_index &idx, hipStream_t s)
+{
+    const int64_t rows = (int64_t)B * H * g.N;
+    if (rows / 256 >= ((int64_t)1 << 31))
+        return fail(STA_ERR_UNSUPPORTED, "fp32 path: too many rows");
+    if (D == 64)
+        hipLaunchKernelGGL(fwd_f32_kernel<64>, grid_for(rows), dim3(256), 0, s, q, k, v, o, lse, idx.kv_idx,
+                           idx.kv_cnt, idx.max_kv, B, H, g, scale);
+    else
+        hipLaunchKernelGGL(fwd_f32_kernel<128>, grid_for(rows), dim3(256), 0, s, q, k, v, o, lse, idx.kv_idx,
+                           idx.kv_cnt, idx.max_kv, B, H, g, scale);
+    return check_launch();
+}
+
+sta_status launch_bwd_f32(const float *q, const float *k, const float *v, const float *o, const float *lse,
+                          const float *dout, float *dq, float *dk, float *dv, float *delta, int B, int H, int D,
+                          float scale, const Geo &g, const sta_index &idx, hipStream_t s)
+{
+    const int64_t rows = (int64_t)B * H * g.N;
+    if (rows / 256 >= ((int64_t)1 << 31))
+        return fail(STA_ERR_UNSUPPORTED, "fp32 path: too many rows");
+    if (D == 64) {
+        hipLaunchKernelGGL(delta_f32_kernel<64>, grid_for(rows), dim3(256), 0, s, o, dout, delta, rows);
+        hipLaunchKernelGGL(dq_f32_kernel<64>, grid_for(rows), dim3(256), 0, s, q, k, v, lse, dout, delta, dq,
+                           idx.kv_idx, idx.kv_cnt, idx.max_kv, B, H, g, scale);
+        hipLaunchKernelGGL(dkdv_f32_kernel<64>, grid_for(rows), dim3(256), 0, s, q, k, v, lse, dout, delta, dk,
+                           dv, idx.q_idx, idx.q_cnt, idx.max_q, B, H, g, scale);
+    } else {
+        hipLaunchKernelGGL(delta_f32_kernel<128>, grid_for(rows), dim3(256), 0, s, o, dout, delta, rows);
+        hipLaunchKernelGGL(dq_f32_kernel<128>, grid_for(rows), dim3(256), 0, s, q, k, v, lse, dout, delta, dq,
+                           idx.kv_idx, idx.kv_cnt, idx.max_kv, B, H, g, scale);
+        hipLaunchKernelGGL(dkdv_f32_kernel<128>, grid_for(rows), dim3(256), 0, s, q, k, v, lse, dout, delta, dk,
+                           dv, idx.q_idx, idx.q_cnt, idx.max_q, B, H, g, scale);
+    }
+    return check_launch();
+}
+
+}  // namespace sta

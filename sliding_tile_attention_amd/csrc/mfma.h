@@ -1,0 +1,68 @@
+// MFMA fragment conventions shared by the bf16 attention kernels (gfx950).
+//
+// v_mfma_f32_32x32x16_bf16 computes C[32x32] += A[32x16] * B[16x32].
+// Lane l (0..63) supplies row i = l%32 of A and column j = l%32 of B, each
+// as 8 bf16 values of the reduction index; lanes 0-31 and 32-63 supply the
+// two halves of the 16-long reduction.  Which physical k a value maps to
+// does not matter as long as A and B agree, so every kernel picks the
+// reduction order that makes its operand loads contiguous.
+// The result lane l, register r holds C[i][j] with
+//     j = l % 32,   i = 8*(r/4) + 4*(l/32) + r%4.
+//
+// Row permutation sigma: if the A rows fed to an MFMA are permuted by
+// sigma (swap bits 2 and 3 of the row index), the 16 result registers of
+// lane l hold rows 16*(r/8) + 8*(l/32) + r%8 -- i.e. registers 8k..8k+7
+// are 8 CONSECUTIVE rows, which is exactly the operand shape the next MFMA
+// needs when those rows become its reduction index.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace sta {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline int sigma32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Row of the result held by register r of lane l (unpermuted A rows).
+__device__ inline int mfma_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// Row held by register r of lane l when the A rows were permuted by sigma.
+__device__ inline int mfma_row_sigma(int lane, int r) { return 16 * (r >> 3) + 8 * (lane >> 5) + (r & 7); }
+
+__device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline bf16x8 zero8() { return __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u}); }
+
+__device__ inline bf16x8 ld8(const __bf16 *p) { return *(const bf16x8 *)p; }
+
+// Registers off..off+7 of an accumulator, rounded to bf16 (nearest even).
+__device__ inline bf16x8 cvt8(const f32x16 &s, int off)
+{
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (__bf16)s[off + i];
+    return r;
+}
+
+__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Packs element i of four 8-wide bf16 rows (as raw words) into 4 bf16
+// (row 0 in the low half of the first word): one column of a 4x8 block.
+__device__ inline u32x2 column4(const u32x4 &a, const u32x4 &b, const u32x4 &c, const u32x4 &d, int i)
+{
+    const int w = i >> 1;
+    if (i & 1)
+        return (u32x2){(a[w] >> 16) | (b[w] & 0xffff0000u), (c[w] >> 16) | (d[w] & 0xffff0000u)};
+    return (u32x2){(a[w] & 0xffffu) | (b[w] << 16), (c[w] & 0xffffu) | (d[w] << 16)};
+}
+
+}  // namespace sta

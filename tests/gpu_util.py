@@ -1,0 +1,94 @@
+"""Helpers for the GPU parity tests: device copies of the seeded inputs, the
+layer-level path through libsta (raster -> tile order -> kernels -> raster),
+and the numeric gates."""
+import sys
+
+import numpy as np
+import torch
+
+import sliding_tile_attention_amd as sta
+
+# Gates for bf16 outputs and gradients: max-abs error and relative L2 error.
+BF16_MAX_ABS = 2e-2
+BF16_REL_L2 = 1e-2
+# fp32 path: both sides compute in >= fp32 from the same fp32 inputs.
+F32_MAX_ABS = 1e-4
+
+
+def say(msg):
+    print("[gpu] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+def to_host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    max_abs = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    rel_l2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)) if got.size else 0.0
+    return max_abs, rel_l2
+
+
+def assert_close(got, ref, dtype, what=""):
+    max_abs, rel_l2 = errors(got, ref)
+    assert np.all(np.isfinite(got)), what + ": non-finite output"
+    if dtype == "bf16":
+        assert max_abs <= BF16_MAX_ABS and rel_l2 <= BF16_REL_L2, \
+            "%s: max-abs %.3e (gate %.0e), rel-L2 %.3e (gate %.0e)" % (what, max_abs, BF16_MAX_ABS, rel_l2,
+                                                                       BF16_REL_L2)
+    else:
+        assert max_abs <= F32_MAX_ABS, "%s: max-abs %.3e (gate %.0e)" % (what, max_abs, F32_MAX_ABS)
+    return max_abs, rel_l2
+
+
+class Layer:
+    """Device state of one attention layer: inputs reordered to tile order,
+    the index, and the outputs converted back to raster order."""
+
+    def __init__(self, grid, tile, windows, offsets, q, k, v, dtype, dout=None, transposed=True):
+        self.geom = sta.Geometry(tuple(grid), tuple(tile))
+        self.dtype = dtype
+        self.B, self.H, self.N, self.D = q.shape
+        self.windows = [tuple(int(x) for x in w) for w in windows]
+        self.off_dev = None if offsets is None else torch.from_numpy(np.ascontiguousarray(offsets, np.int32)).cuda()
+        self.index = sta.StaIndex(self.geom, self.windows, self.off_dev, transposed=transposed)
+        self.q, self.k, self.v = (sta.tile_reorder(to_dev(x, dtype), self.geom) for x in (q, k, v))
+        self.dout = None if dout is None else sta.tile_reorder(to_dev(dout, dtype), self.geom)
+
+    def forward(self, scale=None):
+        self.o, self.lse = sta.forward(self.q, self.k, self.v, self.geom, self.index, scale)
+        return (sta.tile_reorder(self.o, self.geom, inverse=True),
+                sta.tile_reorder(self.lse.unsqueeze(-1), self.geom, inverse=True).squeeze(-1))
+
+    def backward(self, scale=None):
+        dq, dk, dv = sta.backward(self.q, self.k, self.v, self.o, self.lse, self.dout, self.geom, self.index,
+                                  scale)
+        return tuple(sta.tile_reorder(x, self.geom, inverse=True) for x in (dq, dk, dv))
+
+
+def sample_rows(B, H, N, L, grid, tile, per_head_tiles, rows_per_tile, seed):
+    """Flat row ids (b*H + h)*N + raster_i covering the corner tiles and a few
+    seeded random tiles of every head."""
+    from oracle import oracle   # test infrastructure: only the parity checks use it
+    g = np.random.default_rng(seed)
+    n = [a // b for a, b in zip(grid, tile)]
+    T = int(np.prod(n))
+    corners = sorted({(a * n[1] + b) * n[2] + c for a in (0, n[0] - 1) for b in (0, n[1] - 1)
+                      for c in (0, n[2] - 1)})
+    inv = np.argsort(oracle.perm(grid, tile))   # tile-order slot -> raster token
+    rows = []
+    for b in range(B):
+        for h in range(H):
+            tiles = list(corners) + list(g.integers(0, T, size=per_head_tiles))
+            for t in tiles:
+                slots = g.choice(L, size=min(rows_per_tile, L), replace=False)
+                rows.extend(((b * H + h) * N + inv[t * L + slots]).tolist())
+    return np.unique(np.asarray(rows, np.int64))

@@ -8,10 +8,14 @@ comparison see identical values.
 Workloads stand in for the pages' 5-second 720P video generation ("Fast
 Video Generation with Sliding Tile Attention", abstract): a (30,48,80) latent
 token grid, 24 heads of width 128.  Values are i.i.d. N(0,1), drawn with
-numpy's PCG64 from seed [1234 + cfg, stream], streams 0=Q 1=K 2=V 3=dO
-4=window offsets 5=per-head window choice, then rounded to bf16
-(round-to-nearest-even) for the bf16 workloads.
+numpy's PCG64: tensors from seed [1234 + cfg, stream, b, h] per (batch, head)
+slab, streams 0=Q 1=K 2=V 3=dO; window offsets (stream 4) and the per-head
+window choice (stream 5) from seed [1234 + cfg, stream].  bf16 workloads
+round the draws to bf16 (round-to-nearest-even).
 """
+import concurrent.futures
+import os
+
 import numpy as np
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_OFF, STREAM_WIN = range(6)
@@ -49,15 +53,29 @@ def round_bf16(x):
     """float32 array -> float32 array holding the bf16 round-to-nearest-even
     of each value (exactly representable in bf16)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32)
+    assert np.all(np.isfinite(x[: min(x.size, 1 << 16)].reshape(-1)))
+    u = x.view(np.uint32)
+    # finite inputs stay below 0xFF800000, so the sum cannot wrap in 32 bits
+    r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def normal(shape, seed, stream, dtype):
-    x = rng(seed, stream).standard_normal(size=shape, dtype=np.float32)
-    return round_bf16(x) if dtype == "bf16" else x
+    """[B,H,N,D] i.i.d. N(0,1); slab (b,h) is drawn from PCG64 seeded with
+    [seed, stream, b, h], so the slabs can be generated in parallel."""
+    B, H = shape[0], shape[1]
+    out = np.empty(shape, np.float32)
+
+    def fill(bh):
+        b, h = divmod(bh, H)
+        g = np.random.default_rng([int(seed), int(stream), b, h])
+        x = g.standard_normal(size=shape[2:], dtype=np.float32)
+        out[b, h] = round_bf16(x) if dtype == "bf16" else x
+
+    with concurrent.futures.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(B * H)))
+    return out
 
 
 def windows_for(cfg, seed=None):
@@ -89,11 +107,11 @@ def tensors(B, H, N, D, dtype, seed, with_dout=False):
     return tuple(out)
 
 
-def workload(cfg, heads=None):
+def workload(cfg, heads=None, with_dout=None):
     """Everything one workload needs: dict with geometry, windows, offsets and
     q, k, v (and dout for the training workload).  ``heads`` keeps only the
-    first few heads (same values as the full draw for those heads is NOT
-    guaranteed; it is a smaller workload of the same shape family)."""
+    first few heads (their values equal those heads of the full draw).
+    dout is drawn for the training workload, or when with_dout is True."""
     c = dict(CONFIGS[cfg])
     if heads is not None:
         c["H"] = heads
@@ -101,8 +119,9 @@ def workload(cfg, heads=None):
     N = int(np.prod(c["grid"]))
     w = windows_for(cfg)[: c["H"]]
     off = offsets_for(cfg)
-    ts = tensors(c["B"], c["H"], N, c["D"], c["dtype"], seed, with_dout=True)
-    c.update(N=N, windows=w, offsets=off, q=ts[0], k=ts[1], v=ts[2], dout=ts[3],
+    want = c["backward"] if with_dout is None else with_dout
+    ts = tensors(c["B"], c["H"], N, c["D"], c["dtype"], seed, with_dout=want)
+    c.update(N=N, windows=w, offsets=off, q=ts[0], k=ts[1], v=ts[2], dout=ts[3] if want else None,
              scale=1.0 / np.sqrt(c["D"]), seed=seed)
     return c
 

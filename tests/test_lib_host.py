@@ -1,0 +1,181 @@
+"""Host-side tests of libsta (no GPU needed): the library loads, exports every
+entry point the header declares, sizes indices like the oracle, and rejects
+malformed calls before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import sliding_tile_attention_amd as sta
+from oracle import oracle
+from tests.inputs import CONFIGS, offsets_for, windows_for
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libsta.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sta_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(sta.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", sta.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT\s+(sta_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(sta.lib, name)
+
+
+def test_status_strings_and_version():
+    for code, name in ((0, "STA_OK"), (1, "STA_ERR_INVALID"), (2, "STA_ERR_UNSUPPORTED"), (3, "STA_ERR_HIP")):
+        assert sta.lib.sta_status_str(code).decode() == name
+    assert sta.lib.sta_version() >= 10000
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_index_dims_match_oracle(cfg):
+    c = CONFIGS[cfg]
+    geom = sta.Geometry(c["grid"], c["tile"])
+    w = windows_for(cfg)
+    off = offsets_for(cfg)
+    max_kv, max_q = sta.sta_index_dims(geom, w, off is not None)
+    kv_idx, kv_cnt, q_idx, q_cnt = oracle.index(c["grid"], c["tile"], w, off)
+    assert max_kv == kv_cnt.max()
+    if off is None:
+        assert max_q == q_cnt.max()          # exact without shifts
+    else:
+        assert max_q == geom.num_tiles and max_q >= q_cnt.max()
+
+
+def test_index_dims_random_geometries():
+    g = np.random.default_rng(3)
+    for _ in range(50):
+        n = g.integers(1, 9, size=3)
+        tile = g.integers(1, 3, size=3)
+        grid = tuple(int(a * b) for a, b in zip(n, tile))
+        w = g.integers(1, 10, size=(int(g.integers(1, 4)), 3))
+        _, kv_cnt, _, q_cnt = oracle.index(grid, tuple(int(x) for x in tile), w)
+        assert sta.sta_index_dims(sta.Geometry(grid, tuple(int(x) for x in tile)), w, False) == \
+            (kv_cnt.max(), q_cnt.max())
+
+
+# ---- argument checks: every call below must fail on the host -----------
+
+GEOM = sta.Geometry((4, 8, 8), (2, 4, 4))
+
+
+def _fake(n=1 << 16, align=0):
+    """A host buffer whose address stands in for a device pointer; the calls
+    below are rejected before anything could touch it."""
+    t = torch.empty(n + 64, dtype=torch.uint8)
+    off = (-t.data_ptr()) % 16 + align
+    return t[off:]
+
+
+def _expect(status, fn, *args):
+    with pytest.raises(sta.StaError) as e:
+        fn(*args)
+    assert e.value.status == status
+    assert sta.lib.sta_last_error().decode()
+
+
+class _FakeIndex:
+    def __init__(self, H=2, T=8, max_kv=8, max_q=8, transposed=True):
+        self.num_heads, self.num_tiles, self.max_kv, self.max_q = H, T, max_kv, max_q
+        self.buf = _fake()
+        self.transposed = transposed
+
+    def c(self):
+        p = self.buf.data_ptr()
+        return sta.sta_index(self.num_heads, self.num_tiles, self.max_kv, self.max_q, p, p,
+                             p if self.transposed else None, p if self.transposed else None)
+
+
+def test_reorder_rejects_bad_arguments():
+    a, b = _fake(), _fake()
+    _expect(sta.STA_ERR_INVALID, sta.sta_tile_reorder, a, b, 1, 4, sta.Geometry((5, 8, 8), (2, 4, 4)), 0, 0)
+    _expect(sta.STA_ERR_INVALID, sta.sta_tile_reorder, a, b, 1, 4, sta.Geometry((4, 8, 8), (0, 4, 4)), 0, 0)
+    _expect(sta.STA_ERR_INVALID, sta.sta_tile_reorder, None, b, 1, 4, GEOM, 0, 0)
+    _expect(sta.STA_ERR_INVALID, sta.sta_tile_reorder, a, b, 0, 4, GEOM, 0, 0)
+    _expect(sta.STA_ERR_INVALID, sta.sta_tile_reorder, a, b, 1, 0, GEOM, 0, 0)
+    _expect(sta.STA_ERR_INVALID, sta.sta_tile_reorder, a, a[16:], 1, 4, GEOM, 0, 0)   # overlap
+
+
+def test_build_index_rejects_bad_arguments():
+    w = [(3, 3, 3)] * 2
+    _expect(sta.STA_ERR_INVALID, sta.sta_build_index, GEOM, [(0, 3, 3), (3, 3, 3)], None, _FakeIndex(), 0)
+    _expect(sta.STA_ERR_INVALID, sta.sta_build_index, GEOM, w, None, _FakeIndex(H=3), 0)
+    _expect(sta.STA_ERR_INVALID, sta.sta_build_index, GEOM, w, None, _FakeIndex(T=9), 0)
+    _expect(sta.STA_ERR_INVALID, sta.sta_build_index, GEOM, w, None, _FakeIndex(max_kv=7), 0)
+    _expect(sta.STA_ERR_INVALID, sta.sta_build_index, GEOM, w, None, _FakeIndex(max_q=7), 0)
+    _expect(sta.STA_ERR_INVALID, sta.sta_build_index, sta.Geometry((4, 8, 9), (2, 4, 4)), w, None,
+            _FakeIndex(), 0)
+    # with shifts the transposed capacity must be the tile count
+    _expect(sta.STA_ERR_INVALID, sta.sta_build_index, sta.Geometry((6, 8, 8), (2, 4, 4)), w, _fake(),
+            _FakeIndex(T=12, max_kv=12, max_q=11), 0)
+
+
+def _fwd_args(**kw):
+    a = dict(q=_fake(), k=_fake(), v=_fake(), o=_fake(), lse=_fake(), B=1, H=2, D=64, dtype=sta.STA_BF16,
+             scale=0.125, geom=GEOM, index=_FakeIndex(), stream=0)
+    a.update(kw)
+    return a
+
+
+def test_fwd_rejects_bad_arguments():
+    f = lambda **kw: sta.sta_fwd(**_fwd_args(**kw))
+    bad = [
+        (sta.STA_ERR_INVALID, dict(q=None)),
+        (sta.STA_ERR_INVALID, dict(lse=None)),
+        (sta.STA_ERR_INVALID, dict(B=0)),
+        (sta.STA_ERR_INVALID, dict(H=3)),                       # index built for 2 heads
+        (sta.STA_ERR_INVALID, dict(scale=0.0)),
+        (sta.STA_ERR_INVALID, dict(scale=float("nan"))),
+        (sta.STA_ERR_INVALID, dict(dtype=7)),
+        (sta.STA_ERR_INVALID, dict(k=_fake(align=2))),           # misaligned
+        (sta.STA_ERR_INVALID, dict(index=_FakeIndex(T=9))),
+        (sta.STA_ERR_INVALID, dict(geom=sta.Geometry((4, 8, 7), (2, 4, 4)))),
+        (sta.STA_ERR_UNSUPPORTED, dict(D=96)),
+        (sta.STA_ERR_UNSUPPORTED, dict(geom=sta.Geometry((2, 3, 3), (2, 3, 1)),
+                                       index=_FakeIndex(T=3, max_kv=3, max_q=3))),  # L=6, bf16
+    ]
+    for status, kw in bad:
+        with pytest.raises(sta.StaError) as e:
+            f(**kw)
+        assert e.value.status == status, (kw, e.value)
+
+
+def test_bwd_rejects_bad_arguments():
+    def f(**kw):
+        a = _fwd_args()
+        a.update(dout=_fake(), dq=_fake(), dk=_fake(), dv=_fake(), delta_ws=_fake())
+        a.update(kw)
+        sta.sta_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
+                    a["delta_ws"], a["B"], a["H"], a["D"], a["dtype"], a["scale"], a["geom"], a["index"],
+                    a["stream"])
+    for status, kw in [(sta.STA_ERR_INVALID, dict(index=_FakeIndex(transposed=False))),
+                       (sta.STA_ERR_INVALID, dict(dout=None)),
+                       (sta.STA_ERR_INVALID, dict(delta_ws=None)),
+                       (sta.STA_ERR_INVALID, dict(dq=_fake(align=4))),
+                       (sta.STA_ERR_UNSUPPORTED, dict(D=32))]:
+        with pytest.raises(sta.StaError) as e:
+            f(**kw)
+        assert e.value.status == status, (kw, e.value)
+
+
+def test_index_dims_rejects_bad_arguments():
+    _expect(sta.STA_ERR_INVALID, sta.sta_index_dims, GEOM, [(1, 1, 0)], False)
+    _expect(sta.STA_ERR_INVALID, sta.sta_index_dims, sta.Geometry((3, 8, 8), (2, 4, 4)), [(1, 1, 1)], False)
+    g = sta.lib.sta_index_dims(ctypes.byref(GEOM.c()), 0, None, 0, None, None)
+    assert g == sta.STA_ERR_INVALID
