@@ -10,9 +10,10 @@
 //   tile of one (b, h); work items are ordered head-major and spread over the
 //   8 XCDs in contiguous ranges (xcd_remap) so that the workgroups sharing an
 //   XCD's L2 walk neighbouring windows of the same head.
-//   The key loop runs over (listed key tile, BN-key block) pairs.  K and V of
-//   the next block are fetched into registers while the current block is
-//   computed from LDS (double buffer, one barrier per block).
+//   The key loop runs over (listed key tile, BN-key block) pairs.  K and V
+//   blocks travel HBM -> LDS directly (global_load_lds, no staging
+//   registers) into a double buffer: the copy of block j+1 runs while block j
+//   is computed; one barrier per block.
 //
 // Per wave and 32-row query block (lane l owns query row l%32):
 //   S^T[BN x 32] = K_blk Q^T    (MFMA: A = K rows from LDS, B = Q in VGPRs)
@@ -20,12 +21,16 @@
 //   into one FMA; the running max is only moved when a block max exceeds it
 //   by more than 8 (2^8 headroom), which leaves the result exact and skips
 //   almost every rescale of the O accumulator;
-//   O^T[D x 32] += V^T_blk P^T  (MFMA: A = V^T rows from LDS, B = P in VGPRs)
+//   O^T[D x 32] += V^T_blk P^T  (MFMA: A = V^T via LDS transpose reads,
+//                                B = P in VGPRs)
 // K rows are fed permuted by sigma so that each lane's S^T registers hold 8
 // consecutive keys -- the B operand of the PV product without any shuffle.
-// V is stored transposed in LDS (D rows of BN keys), so the A operand of the
-// PV product is one 16-byte LDS read.  Rows of both LDS tiles are padded by
-// 16 bytes, which makes the 16-byte fragment reads bank-conflict free.
+//
+// LDS layout: K and V blocks are row-major [BN][D] with the 16-byte granules
+// of each row XOR-swizzled (granule c of row r stored at c ^ f(r)), which
+// keeps both read patterns bank-conflict free without padding:
+//   K (16-byte reads of 16 different rows):      f_K(r) = r mod (D/8)
+//   V (8-byte transpose reads of 4 rows x 32 B):  f_V(r) = 4*(r mod 4)
 #include "common.h"
 #include "mfma.h"
 
@@ -34,38 +39,41 @@ namespace sta {
 template <int D, int NW, int QB, int BN>
 struct FwdCfg {
     static constexpr int THREADS = NW * 64;
-    static constexpr int M = NW * QB * 32;    // query rows per workgroup
-    static constexpr int KS = D / 16;          // reduction steps of QK^T
-    static constexpr int KB = BN / 32;         // 32-key sub-blocks
-    static constexpr int DB = D / 32;          // 32-wide column blocks of O^T
-    static constexpr int KP = D + 8;           // LDS row pitch of K (bf16)
-    static constexpr int VP = BN + 8;          // LDS row pitch of V^T (bf16)
-    static constexpr int KE = BN * KP;
-    static constexpr int VE = D * VP;
-    static constexpr int STAGE = KE + VE;      // one buffer, bf16 elements
-    static constexpr int KCH = BN * D / 8;     // 16-byte chunks of a K block
-    static constexpr int VCH = (BN / 4) * (D / 8);  // 4-key x 8-column chunks of V
-    static constexpr int KPT = (KCH + THREADS - 1) / THREADS;
-    static constexpr int VPT = (VCH + THREADS - 1) / THREADS;
+    static constexpr int M = NW * QB * 32;     // query rows per workgroup
+    static constexpr int KS = D / 16;           // reduction steps of QK^T
+    static constexpr int KB = BN / 32;          // 32-key sub-blocks
+    static constexpr int DB = D / 32;           // 32-wide column blocks of O^T
+    static constexpr int GR = D / 8;            // 16-byte granules per row
+    static constexpr int BLK = BN * D;          // bf16 elements of one K (or V) block
+    static constexpr int STAGE = 2 * BLK;       // K + V
+    static constexpr int WAVE_ELEMS = 512;      // one wave-wide 16-byte copy = 1 KB
+    static constexpr int COPIES = BLK / (THREADS * 8);   // copies per thread per block
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+    static_assert(BLK % (THREADS * 8) == 0, "block must split evenly over the workgroup");
 };
 
+template <int GR>
+__device__ inline int swz_k(int r) { return r & (GR - 1); }
+template <int GR>
+__device__ inline int swz_v(int r) { return ((r & 3) << 2) & (GR - 1); }
+
 template <int D, int NW, int QB, int BN>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     __bf16 *__restrict__ O, float *__restrict__ LSE, const int32_t *__restrict__ kv_idx,
     const int32_t *__restrict__ kv_cnt, int max_kv, int H, Geo g, int rblocks, int total,
     float scale_log2)
 {
     using C = FwdCfg<D, NW, QB, BN>;
-    __shared__ __attribute__((aligned(16))) __bf16 smem[2 * C::STAGE];
+    __shared__ __attribute__((aligned(1024))) __bf16 smem[2 * C::STAGE];
 
     const int work = xcd_remap(blockIdx.x, total);
     const int rb = work % rblocks;
     const int qt = (work / rblocks) % g.T;
     const int bh = work / (rblocks * g.T);
     const int h = bh % H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, grp = lane >> 5;
     const int L = g.L;
     const int64_t base = (int64_t)bh * g.N * D;
@@ -98,65 +106,64 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
     const int nkb = (L + BN - 1) / BN;
     const int nblk = cnt * nkb;
 
-    u32x4 kreg[C::KPT];
-    u32x4 vreg[C::VPT][4];
-
-    auto gload = [&](int blk) {
+    // Issue the asynchronous copy of key block `blk` into LDS buffer `buf`.
+    // Rows past the tile end (ragged last block) re-read the last valid row;
+    // their scores are masked, so their contents never matter.
+    auto gload = [&](int blk, int buf) {
         const int e = blk / nkb;
         const int k0 = (blk - e * nkb) * BN;
-        const int valid = L - k0 < BN ? L - k0 : BN;
-        const int64_t kbase = base + ((int64_t)lst[e] * L + k0) * D;
-#pragma unroll
-        for (int i = 0; i < C::KPT; ++i) {
-            const int c = tid + i * C::THREADS;
-            const int row = c / (D / 8), col = c % (D / 8);
-            const bool ok = c < C::KCH && row < valid;
-            kreg[i] = ok ? *(const u32x4 *)(K + kbase + (int64_t)row * D + col * 8) : (u32x4){0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int i = 0; i < C::VPT; ++i) {
-            const int c = tid + i * C::THREADS;
-            const int kg = c % (BN / 4), dg = c / (BN / 4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = kg * 4 + r;
-                const bool ok = c < C::VCH && key < valid;
-                vreg[i][r] = ok ? *(const u32x4 *)(V + kbase + (int64_t)key * D + dg * 8) : (u32x4){0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto swrite = [&](int buf) {
+        const int last = (L - k0 < BN ? L - k0 : BN) - 1;
+        const __bf16 *kb = K + base + ((int64_t)lst[e] * L + k0) * D;
+        const __bf16 *vb = V + base + ((int64_t)lst[e] * L + k0) * D;
         __bf16 *Ks = smem + buf * C::STAGE;
-        __bf16 *Vs = Ks + C::KE;
+        __bf16 *Vs = Ks + C::BLK;
 #pragma unroll
-        for (int i = 0; i < C::KPT; ++i) {
-            const int c = tid + i * C::THREADS;
-            if (c < C::KCH) *(u32x4 *)(Ks + (c / (D / 8)) * C::KP + (c % (D / 8)) * 8) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < C::VPT; ++i) {
-            const int c = tid + i * C::THREADS;
-            if (c < C::VCH) {
-                const int kg = c % (BN / 4), dg = c / (BN / 4);
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    *(u32x2 *)(Vs + (dg * 8 + j) * C::VP + kg * 4) =
-                        column4(vreg[i][0], vreg[i][1], vreg[i][2], vreg[i][3], j);
-            }
+        for (int i = 0; i < C::COPIES; ++i) {
+            const int chunk = (i * NW + wave) * 64 + lane;   // 16-byte granule slot in the block
+            const int r = chunk / C::GR, pg = chunk % C::GR;
+            const int rr = r < last ? r : last;
+            const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
+            g2lds16(kb + rr * D + (pg ^ swz_k<C::GR>(r)) * 8, Ks + lds_off);
+            g2lds16(vb + rr * D + (pg ^ swz_v<C::GR>(r)) * 8, Vs + lds_off);
         }
     };
 
-    if (nblk > 0) {
-        gload(0);
-        swrite(0);
-    }
-    __syncthreads();
+    // Per-lane LDS offsets that do not depend on the block.
+    const int arow = sigma32(l32);                  // K row this lane feeds to the S^T MFMA
+    int koff[C::KB][C::KS];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const int r = kb * 32 + arow;
+            koff[kb][ks] = r * D + ((2 * ks + grp) ^ swz_k<C::GR>(r)) * 8;
+        }
+    // Transpose reads of V: lane s = 4j + c of a 16-lane group reads row
+    // (key0 + j), columns d0 + 4c .. +3.
+    const int s16 = lane & 15, grp16 = lane >> 4;
+    const int vj = s16 >> 2, vc = s16 & 3;
+    int voff[C::DB][C::KB][2][2];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int r = kb * 32 + kk * 16 + 8 * grp + 4 * hh + vj;
+                    const int col = db * 32 + 16 * (grp16 & 1) + 4 * vc;
+                    voff[db][kb][kk][hh] = r * D + (((col >> 3) ^ swz_v<C::GR>(r)) << 3) + (col & 7);
+                }
 
-    const int arow = sigma32(l32);   // K row this lane feeds to the S^T MFMA
+    if (nblk > 0) gload(0, 0);
+
     for (int blk = 0; blk < nblk; ++blk) {
-        if (blk + 1 < nblk) gload(blk + 1);
+        __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of block blk have landed
+        __syncthreads();                   // ... and everyone's; buffer (blk+1)&1 is free
+        if (blk + 1 < nblk) gload(blk + 1, (blk + 1) & 1);
         const __bf16 *Ks = smem + (blk & 1) * C::STAGE;
-        const __bf16 *Vs = Ks + C::KE;
+        const __bf16 *Vs = Ks + C::BLK;
         const int k0 = (blk % nkb) * BN;
         const int valid = L - k0 < BN ? L - k0 : BN;
 
@@ -169,7 +176,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
                 for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-                const bf16x8 a = ld8(Ks + (kb * 32 + arow) * C::KP + ks * 16 + grp * 8);
+                const bf16x8 a = ld8(Ks + koff[kb][ks]);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(a, qf[qb][ks], s[qb][kb]);
             }
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
             for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-            mx = fmaxf(mx, xor32(mx)) * scale_log2;
+            mx = max_pair32(mx) * scale_log2;
             if (__any(mx > m_i[qb] + 8.f)) {
                 const float mn = fmaxf(m_i[qb], mx);
                 const float alpha = __builtin_amdgcn_exp2f(m_i[qb] - mn);
@@ -223,19 +230,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(
             for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 a = ld8(Vs + (db * 32 + l32) * C::VP + kb * 32 + kk * 16 + grp * 8);
+                    const bf16x8 a = cat8(ld_tr4(Vs + voff[db][kb][kk][0]), ld_tr4(Vs + voff[db][kb][kk][1]));
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a, pf[qb][kb][kk], acc[qb][db]);
                 }
-
-        if (blk + 1 < nblk) swrite((blk + 1) & 1);
-        __syncthreads();
     }
 
     // Epilogue: lanes l and l^32 hold the two halves of row l%32's sum.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const float lt = l_i[qb] + xor32(l_i[qb]);
+        const float lt = sum_pair32(l_i[qb]);
         const float inv = 1.f / lt;
         const int row = wrow0 + qb * 32 + l32;
         if (row < L) {
@@ -271,11 +275,23 @@ static sta_status run_fwd(const void *q, const void *k, const void *v, void *o, 
     return check_launch();
 }
 
+// Tile shape: waves per workgroup, 32-row query blocks per wave, keys per
+// LDS block.  Overridable at compile time for tuning sweeps.
+#ifndef STA_FWD_NW
+#define STA_FWD_NW 4
+#endif
+#ifndef STA_FWD_QB
+#define STA_FWD_QB 1
+#endif
+#ifndef STA_FWD_BN
+#define STA_FWD_BN 64
+#endif
+
 sta_status launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                            int D, float scale, const Geo &g, const sta_index &idx, hipStream_t s)
 {
-    if (D == 128) return run_fwd<128, 4, 1, 64>(q, k, v, o, lse, B, H, scale, g, idx, s);
-    return run_fwd<64, 4, 1, 64>(q, k, v, o, lse, B, H, scale, g, idx, s);
+    if (D == 128) return run_fwd<128, STA_FWD_NW, STA_FWD_QB, STA_FWD_BN>(q, k, v, o, lse, B, H, scale, g, idx, s);
+    return run_fwd<64, STA_FWD_NW, STA_FWD_QB, STA_FWD_BN>(q, k, v, o, lse, B, H, scale, g, idx, s);
 }
 
 }  // namespace sta

@@ -55,6 +55,43 @@ __device__ inline bf16x8 cvt8(const f32x16 &s, int off)
 
 __device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// max / sum of x over lanes l and l^32 (v_permlane32_swap: each lane gets
+// its own value and its partner's, in some order).
+__device__ inline float max_pair32(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_pair32(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element (i%4) of the 8-byte chunks addressed by lanes
+// 4j + i/4 of its group, j = 0..3.  If lane s = 4j + c of a group points at
+// row (r0 + j), columns (c0 + 4c .. c0 + 4c + 3) of a row-major bf16 matrix,
+// lane i of the group receives rows r0..r0+3 of column c0 + i.
+__device__ inline bf16x4 ld_tr4(const __bf16 *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
+}
+
+__device__ inline bf16x8 cat8(bf16x4 a, bf16x4 b)
+{
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Asynchronous 16-byte global -> LDS copy: lane l's 16 bytes land at
+// lds_base + 16*l (lds_base must be the same for the whole wave).
+__device__ inline void g2lds16(const void *src, void *lds_base)
+{
+    __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
 // Packs element i of four 8-wide bf16 rows (as raw words) into 4 bf16
 // (row 0 in the low half of the first word): one column of a 4x8 block.
 __device__ inline u32x2 column4(const u32x4 &a, const u32x4 &b, const u32x4 &c, const u32x4 &d, int i)
