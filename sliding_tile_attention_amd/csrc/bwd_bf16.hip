@@ -1,13 +1,416 @@
-// Sliding-tile attention backward, bf16 (placeholder until the MFMA kernels land).
+// Sliding-tile attention backward, bf16 in / fp32 accumulate, gfx950.
+//
+// Gradients of the tile-masked softmax attention of the forward pass, for
+// full-parameter training through the local attention operator
+// ("MegaSlide-DiT: Memory-Centric Adaptation and Deformable Local Attention
+// for Efficient Video Diffusion", abstract):
+//   P = exp(s - lse),  dP = dO V^T,  Delta = rowsum(dO o O),
+//   dS = P o (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+// Three kernels, no atomics, deterministic:
+//   1. bwd_pre: Delta_i = <dO_i, O_i> (fp32), one pass over O and dO.
+//   2. dq: query-stationary, walks each query tile's key-tile list (same
+//      schedule as the forward) and accumulates dQ in registers.
+//   3. dkdv: key-stationary, walks each key tile's TRANSPOSED list (the query
+//      tiles whose window holds it) and accumulates dK and dV in registers.
+// S and dP are recomputed in both 2 and 3.
+//
+// MFMA orientation (see mfma.h for the fragment conventions):
+//   dq:   S^T = K Q^T, dP^T = V dO^T      (A = K / V rows from LDS, B = Q / dO
+//                                          in VGPRs; lane owns a query row)
+//         dQ^T += K^T dS^T                 (A = K^T by LDS transpose reads)
+//   dkdv: S = Q K^T, dP = dO V^T          (A = Q / dO rows from LDS, B = K / V
+//                                          in VGPRs; lane owns a key row)
+//         dV += P^T dO, dK += dS^T Q       (B = dO / Q by LDS transpose reads)
+// LDS tiles are row-major with 16-byte granules XOR-swizzled by
+// f(r) = 4*(r mod 4) ^ ((r / 4) mod 4), which keeps both the 16-byte row
+// reads (16 distinct rows per 16 lanes) and the transpose reads (4 rows x
+// 32 bytes per 16 lanes) free of bank conflicts.
+#include <type_traits>
+
 #include "common.h"
+#include "mfma.h"
 
 namespace sta {
 
-sta_status launch_bwd_bf16(const void *, const void *, const void *, const void *, const float *, const void *,
-                           void *, void *, void *, float *, int, int, int, float, const Geo &, const sta_index &,
-                           hipStream_t)
+template <int GR>
+__device__ inline int swz_u(int r) { return ((((r & 3) << 2) ^ ((r >> 2) & 3))) & (GR - 1); }
+
+// ---------------------------------------------------------------------------
+// 1. Delta = rowsum(dO * O).  16 lanes per row (16 bytes each for D=128).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16 *__restrict__ O, const __bf16 *__restrict__ dO,
+                                                      float *__restrict__ delta, int64_t rows)
 {
-    return fail(STA_ERR_UNSUPPORTED, "bf16 backward not built yet");
+    constexpr int LPR = D / 8;                 // lanes per row
+    const int64_t row = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / LPR;
+    const int part = threadIdx.x % LPR;
+    float s = 0.f;
+    if (row < rows) {
+        const bf16x8 a = ld8(O + row * D + part * 8);
+        const bf16x8 b = ld8(dO + row * D + part * 8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = fmaf((float)a[i], (float)b[i], s);
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, LPR);
+    if (row < rows && part == 0) delta[row] = s;
+}
+
+// Asynchronous copy of `rows` rows (row-major, D bf16 each) starting at src
+// into a swizzled LDS tile; rows >= valid re-read row valid-1 (callers mask
+// them).  Every thread of the workgroup takes part.
+template <int D, int THREADS, int ROWS>
+__device__ inline void copy_rows(const __bf16 *src, __bf16 *lds, int valid, int tid)
+{
+    constexpr int GR = D / 8;
+    constexpr int COPIES = ROWS * D / (THREADS * 8);
+    static_assert(ROWS * D % (THREADS * 8) == 0, "tile must split evenly");
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < COPIES; ++i) {
+        const int slot = (i * (THREADS / 64) + wave) * 64 + lane;
+        const int r = slot / GR, pg = slot % GR;
+        const int rr = r < valid ? r : valid - 1;
+        g2lds16(src + rr * D + (pg ^ swz_u<GR>(r)) * 8, lds + (i * (THREADS / 64) + wave) * 512);
+    }
+}
+
+// Element offset of logical (row r, column c) in a swizzled LDS tile.
+template <int D>
+__device__ inline int lds_at(int r, int c)
+{
+    return r * D + (((c >> 3) ^ swz_u<D / 8>(r)) << 3) + (c & 7);
+}
+
+// ---------------------------------------------------------------------------
+// 2. dQ (query-stationary).
+// ---------------------------------------------------------------------------
+template <int D, int NW, int BN>
+__global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
+    const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
+    const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
+    __bf16 *__restrict__ dQ, const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt, int max_kv,
+    int H, Geo g, int rblocks, int total, float scale_log2, float scale)
+{
+    constexpr int THREADS = NW * 64, M = NW * 32, KS = D / 16, KB = BN / 32, DB = D / 32;
+    constexpr int BLK = BN * D, STAGE = 2 * BLK;
+    __shared__ __attribute__((aligned(1024))) __bf16 smem[2 * STAGE];
+
+    const int work = xcd_remap(blockIdx.x, total);
+    const int rb = work % rblocks;
+    const int qt = (work / rblocks) % g.T;
+    const int bh = work / (rblocks * g.T);
+    const int h = bh % H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, grp = lane >> 5;
+    const int L = g.L;
+    const int64_t base = (int64_t)bh * g.N * D;
+    const int row = rb * M + wave * 32 + l32;        // query row (inside the tile) of this lane
+    const bool row_ok = row < L;
+    const int64_t grow = (int64_t)qt * L + (row_ok ? row : L - 1);
+
+    bf16x8 qf[KS], of[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = ld8(Q + base + grow * D + ks * 16 + grp * 8);
+        of[ks] = ld8(dO + base + grow * D + ks * 16 + grp * 8);
+    }
+    const float nlse2 = -LSE[(int64_t)bh * g.N + grow] * 1.4426950408889634f;
+    const float dlt = Delta[(int64_t)bh * g.N + grow];
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+    const int cnt = kv_cnt[(int64_t)h * g.T + qt];
+    const int32_t *lst = kv_idx + ((int64_t)h * g.T + qt) * max_kv;
+    const int nkb = (L + BN - 1) / BN;
+    const int nblk = cnt * nkb;
+
+    const int arow = sigma32(l32);
+    int kofs[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kofs[ks] = lds_at<D>(arow, 16 * ks + 8 * grp);
+    const int vj = (lane & 15) >> 2, vc = lane & 3;
+    // (the swizzle of row r depends on r mod 16, so each half has its own offset)
+    int tofs[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            tofs[db][hh] = lds_at<D>(8 * grp + 4 * hh + vj, db * 32 + 16 * ((lane >> 4) & 1) + 4 * vc);
+
+    auto gload = [&](int blk, int buf) {
+        const int e = blk / nkb;
+        const int k0 = (blk - e * nkb) * BN;
+        const int valid = L - k0 < BN ? L - k0 : BN;
+        const int64_t row0 = (int64_t)lst[e] * L + k0;
+        copy_rows<D, THREADS, BN>(K + base + row0 * D, smem + buf * STAGE, valid, tid);
+        copy_rows<D, THREADS, BN>(V + base + row0 * D, smem + buf * STAGE + BLK, valid, tid);
+    };
+
+    auto step = [&](auto bufc, int blk) {
+        constexpr int BUF = decltype(bufc)::value;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (blk + 1 < nblk) gload(blk + 1, 1 - BUF);
+        const __bf16 *Ks = smem + BUF * STAGE;
+        const __bf16 *Vs = Ks + BLK;
+        const int k0 = (blk % nkb) * BN;
+        const int valid = L - k0 < BN ? L - k0 : BN;
+
+        f32x16 s[KB], dp[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { s[kb][r] = 0.f; dp[kb][r] = 0.f; }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                s[kb] = mfma32(ld8(Ks + kb * 32 * D + kofs[ks]), qf[ks], s[kb]);
+                dp[kb] = mfma32(ld8(Vs + kb * 32 * D + kofs[ks]), of[ks], dp[kb]);
+            }
+        }
+        bf16x8 dsf[KB][2];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                bf16x8 v;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 8 * hf + i;
+                    float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, nlse2));
+                    if (valid < BN && kb * 32 + mfma_row_sigma(lane, r) >= valid) p = 0.f;
+                    v[i] = (__bf16)(p * (dp[kb][r] - dlt));
+                }
+                dsf[kb][hf] = v;
+            }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const __bf16 *kp = Ks + (kb * 32 + kk * 16) * D;
+                    acc[db] = mfma32(cat8(ld_tr4(kp + tofs[db][0]), ld_tr4(kp + tofs[db][1])), dsf[kb][kk], acc[db]);
+                }
+    };
+
+    if (nblk > 0) gload(0, 0);
+    for (int blk = 0; blk < nblk; blk += 2) {
+        step(std::integral_constant<int, 0>{}, blk);
+        if (blk + 1 < nblk) step(std::integral_constant<int, 1>{}, blk + 1);
+    }
+
+    if (row_ok) {
+        __bf16 *op = dQ + base + ((int64_t)qt * L + row) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 v;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v[t] = (__bf16)(acc[db][4 * j + t] * scale);
+                *(bf16x4 *)(op + db * 32 + 8 * j + 4 * grp) = v;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dK, dV (key-stationary, over the transposed lists).
+// ---------------------------------------------------------------------------
+template <int D, int NW, int BQ>
+__global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
+    const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
+    const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
+    __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, const int32_t *__restrict__ q_idx,
+    const int32_t *__restrict__ q_cnt, int max_q, int H, Geo g, int rblocks, int total, float scale_log2,
+    float scale)
+{
+    constexpr int THREADS = NW * 64, M = NW * 32, KS = D / 16, SB = BQ / 32, DB = D / 32;
+    constexpr int BLK = BQ * D;
+    constexpr int STAGE = 2 * BLK + 2 * BQ * 2;    // Q, dO (bf16) + LSE, Delta (fp32 as 2 bf16 slots each)
+    static_assert(BQ == 64, "LSE/Delta staging assumes one 64-lane dword copy per array");
+    __shared__ __attribute__((aligned(1024))) __bf16 smem[2 * STAGE];
+
+    const int work = xcd_remap(blockIdx.x, total);
+    const int rb = work % rblocks;
+    const int kt = (work / rblocks) % g.T;
+    const int bh = work / (rblocks * g.T);
+    const int h = bh % H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, grp = lane >> 5;
+    const int L = g.L;
+    const int64_t base = (int64_t)bh * g.N * D;
+    const int64_t sbase = (int64_t)bh * g.N;
+    const int krow0 = rb * M + wave * 32;            // first key row (inside the tile) of this wave
+    const int krow = krow0 + l32;
+    const int64_t gk = (int64_t)kt * L + (krow < L ? krow : L - 1);
+
+    bf16x8 kf[KS], vf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        kf[ks] = ld8(K + base + gk * D + ks * 16 + grp * 8);
+        vf[ks] = ld8(V + base + gk * D + ks * 16 + grp * 8);
+    }
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
+
+    const int cnt = q_cnt[(int64_t)h * g.T + kt];
+    const int32_t *lst = q_idx + ((int64_t)h * g.T + kt) * max_q;
+    const int nqb = (L + BQ - 1) / BQ;
+    const int nblk = cnt * nqb;
+
+    const int arow = sigma32(l32);
+    int aofs[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) aofs[ks] = lds_at<D>(arow, 16 * ks + 8 * grp);
+    const int vj = (lane & 15) >> 2, vc = lane & 3;
+    // (the swizzle of row r depends on r mod 16, so each half has its own offset)
+    int tofs[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            tofs[db][hh] = lds_at<D>(8 * grp + 4 * hh + vj, db * 32 + 16 * ((lane >> 4) & 1) + 4 * vc);
+
+    auto gload = [&](int blk, int buf) {
+        const int e = blk / nqb;
+        const int q0 = (blk - e * nqb) * BQ;
+        const int valid = L - q0 < BQ ? L - q0 : BQ;
+        const int64_t row0 = (int64_t)lst[e] * L + q0;
+        __bf16 *st = smem + buf * STAGE;
+        copy_rows<D, THREADS, BQ>(Q + base + row0 * D, st, valid, tid);
+        copy_rows<D, THREADS, BQ>(dO + base + row0 * D, st + BLK, valid, tid);
+        if (wave == 0) {
+            const int rr = lane < valid ? lane : valid - 1;
+            __builtin_amdgcn_global_load_lds((const void *)(LSE + sbase + row0 + rr),
+                                             (__attribute__((address_space(3))) void *)(st + 2 * BLK), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(Delta + sbase + row0 + rr),
+                                             (__attribute__((address_space(3))) void *)(st + 2 * BLK + 2 * BQ), 4,
+                                             0, 0);
+        }
+    };
+
+    auto step = [&](auto bufc, int blk) {
+        constexpr int BUF = decltype(bufc)::value;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (blk + 1 < nblk) gload(blk + 1, 1 - BUF);
+        const __bf16 *Qs = smem + BUF * STAGE;
+        const __bf16 *Os = Qs + BLK;
+        const float *Ls = (const float *)(Qs + 2 * BLK);
+        const float *Dl = Ls + BQ;
+        const int q0 = (blk % nqb) * BQ;
+        const int valid = L - q0 < BQ ? L - q0 : BQ;
+
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+            f32x16 s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                s = mfma32(ld8(Qs + sb * 32 * D + aofs[ks]), kf[ks], s);
+                dp = mfma32(ld8(Os + sb * 32 * D + aofs[ks]), vf[ks], dp);
+            }
+            // registers 8kk..8kk+7 hold query rows sb*32 + 16kk + 8grp + 0..7
+            bf16x8 pf[2], dsf[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int qr = sb * 32 + 16 * kk + 8 * grp;
+                const f32x4 l0 = *(const f32x4 *)(Ls + qr), l1 = *(const f32x4 *)(Ls + qr + 4);
+                const f32x4 d0 = *(const f32x4 *)(Dl + qr), d1 = *(const f32x4 *)(Dl + qr + 4);
+                bf16x8 pv, dv8;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float lse = i < 4 ? l0[i] : l1[i - 4];
+                    const float dl = i < 4 ? d0[i] : d1[i - 4];
+                    float p = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + i], scale_log2, -lse * 1.4426950408889634f));
+                    if (valid < BQ && qr + i >= valid) p = 0.f;
+                    pv[i] = (__bf16)p;
+                    dv8[i] = (__bf16)(p * (dp[8 * kk + i] - dl));
+                }
+                pf[kk] = pv;
+                dsf[kk] = dv8;
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int off = (sb * 32 + kk * 16) * D;
+                    dv[db] = mfma32(pf[kk], cat8(ld_tr4(Os + off + tofs[db][0]), ld_tr4(Os + off + tofs[db][1])), dv[db]);
+                    dk[db] = mfma32(dsf[kk], cat8(ld_tr4(Qs + off + tofs[db][0]), ld_tr4(Qs + off + tofs[db][1])), dk[db]);
+                }
+        }
+    };
+
+    if (nblk > 0) gload(0, 0);
+    for (int blk = 0; blk < nblk; blk += 2) {
+        step(std::integral_constant<int, 0>{}, blk);
+        if (blk + 1 < nblk) step(std::integral_constant<int, 1>{}, blk + 1);
+    }
+
+    // lane holds column d = 32*db + l%32 of key rows 8*(r/4) + 4*grp + r%4.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int kr = krow0 + mfma_row(lane, r);
+        if (kr < L) {
+            const int64_t o = base + ((int64_t)kt * L + kr) * D + l32;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                dK[o + db * 32] = (__bf16)(dk[db][r] * scale);
+                dV[o + db * 32] = (__bf16)dv[db][r];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+
+template <int D>
+static sta_status run_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                          const void *dout, void *dq, void *dk, void *dv, float *delta, int B, int H, float scale,
+                          const Geo &g, const sta_index &idx, hipStream_t s)
+{
+    constexpr int NW = 4, BN = 64, BQ = 64, M = NW * 32;
+    const int64_t rows = (int64_t)B * H * g.N;
+    const int rblocks = (g.L + M - 1) / M;
+    const int64_t total = (int64_t)B * H * g.T * rblocks;
+    if (total >= ((int64_t)1 << 31) || rows * (D / 8) / 256 >= ((int64_t)1 << 31))
+        return fail(STA_ERR_UNSUPPORTED, "too many work items");
+    const float scale_log2 = scale * 1.4426950408889634f;
+    const __bf16 *Q = (const __bf16 *)q, *K = (const __bf16 *)k, *V = (const __bf16 *)v;
+    const __bf16 *O = (const __bf16 *)o, *dO = (const __bf16 *)dout;
+
+    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, s, O, dO,
+                       delta, rows);
+    sta_status st = check_launch();
+    if (st != STA_OK) return st;
+    hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
+                       (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q, H, g,
+                       rblocks, (int)total, scale_log2, scale);
+    if ((st = check_launch()) != STA_OK) return st;
+    hipLaunchKernelGGL((dq_kernel<D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
+                       (const float *)delta, (__bf16 *)dq, idx.kv_idx, idx.kv_cnt, idx.max_kv, H, g, rblocks,
+                       (int)total, scale_log2, scale);
+    return check_launch();
+}
+
+sta_status launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                           const void *dout, void *dq, void *dk, void *dv, float *delta, int B, int H, int D,
+                           float scale, const Geo &g, const sta_index &idx, hipStream_t s)
+{
+    if (D == 128) return run_bwd<128>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, scale, g, idx, s);
+    return run_bwd<64>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, scale, g, idx, s);
 }
 
 }  // namespace sta

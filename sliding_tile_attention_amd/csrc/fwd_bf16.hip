@@ -31,6 +31,8 @@
 // keeps both read patterns bank-conflict free without padding:
 //   K (16-byte reads of 16 different rows):      f_K(r) = r mod (D/8)
 //   V (8-byte transpose reads of 4 rows x 32 B):  f_V(r) = 4*(r mod 4)
+#include <type_traits>
+
 #include "common.h"
 #include "mfma.h"
 
@@ -57,8 +59,12 @@ __device__ inline int swz_k(int r) { return r & (GR - 1); }
 template <int GR>
 __device__ inline int swz_v(int r) { return ((r & 3) << 2) & (GR - 1); }
 
+#ifndef STA_FWD_MINB
+#define STA_FWD_MINB 2
+#endif
+
 template <int D, int NW, int QB, int BN>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     __bf16 *__restrict__ O, float *__restrict__ LSE, const int32_t *__restrict__ kv_idx,
     const int32_t *__restrict__ kv_cnt, int max_kv, int H, Geo g, int rblocks, int total,
@@ -106,63 +112,75 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(
     const int nkb = (L + BN - 1) / BN;
     const int nblk = cnt * nkb;
 
+    // ---- per-lane offsets (bf16 elements), fixed for the whole kernel ----
+    // Copies: wave-wide copy i of a block fills granule slots
+    // (i*NW + wave)*64 + lane, i.e. row r = slot / GR, physical granule slot % GR,
+    // which must receive logical granule (slot % GR) ^ f(r) of row r.
+    int gk[C::COPIES], gv[C::COPIES];
+#pragma unroll
+    for (int i = 0; i < C::COPIES; ++i) {
+        const int slot = (i * NW + wave) * 64 + lane;
+        const int r = slot / C::GR, pg = slot % C::GR;
+        gk[i] = r * D + (pg ^ swz_k<C::GR>(r)) * 8;
+        gv[i] = r * D + (pg ^ swz_v<C::GR>(r)) * 8;
+    }
+    // S^T operand: lane feeds K row sigma(l%32) of each 32-key sub-block;
+    // the swizzle of that row does not depend on the sub-block.
+    const int arow = sigma32(l32);
+    int kofs[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) kofs[ks] = arow * D + ((2 * ks + grp) ^ swz_k<C::GR>(arow)) * 8;
+    // PV operand by transpose reads: lane s = 4j + c of a 16-lane group reads
+    // row 8*grp + 4*half + j (+ sub-block rows), columns db*32 + 16*((lane>>4)&1) + 4c.
+    const int vj = (lane & 15) >> 2, vc = lane & 3;
+    int vofs[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+        const int r = 8 * grp + vj;
+        const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * vc;
+        vofs[db] = r * D + (((col >> 3) ^ swz_v<C::GR>(r)) << 3) + (col & 7);
+    }
+
     // Issue the asynchronous copy of key block `blk` into LDS buffer `buf`.
-    // Rows past the tile end (ragged last block) re-read the last valid row;
-    // their scores are masked, so their contents never matter.
+    // In a ragged last block, rows past the tile end re-read the last valid
+    // row; their scores are masked, so their contents never matter.
     auto gload = [&](int blk, int buf) {
         const int e = blk / nkb;
         const int k0 = (blk - e * nkb) * BN;
-        const int last = (L - k0 < BN ? L - k0 : BN) - 1;
-        const __bf16 *kb = K + base + ((int64_t)lst[e] * L + k0) * D;
-        const __bf16 *vb = V + base + ((int64_t)lst[e] * L + k0) * D;
+        const int valid = L - k0 < BN ? L - k0 : BN;
+        const int64_t row0 = (int64_t)lst[e] * L + k0;
+        const __bf16 *kb = K + base + row0 * D;
+        const __bf16 *vb = V + base + row0 * D;
         __bf16 *Ks = smem + buf * C::STAGE;
         __bf16 *Vs = Ks + C::BLK;
+        if (valid == BN) {
 #pragma unroll
-        for (int i = 0; i < C::COPIES; ++i) {
-            const int chunk = (i * NW + wave) * 64 + lane;   // 16-byte granule slot in the block
-            const int r = chunk / C::GR, pg = chunk % C::GR;
-            const int rr = r < last ? r : last;
-            const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
-            g2lds16(kb + rr * D + (pg ^ swz_k<C::GR>(r)) * 8, Ks + lds_off);
-            g2lds16(vb + rr * D + (pg ^ swz_v<C::GR>(r)) * 8, Vs + lds_off);
+            for (int i = 0; i < C::COPIES; ++i) {
+                const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
+                g2lds16(kb + gk[i], Ks + lds_off);
+                g2lds16(vb + gv[i], Vs + lds_off);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::COPIES; ++i) {
+                const int slot = (i * NW + wave) * 64 + lane;
+                const int r = slot / C::GR, pg = slot % C::GR;
+                const int rr = r < valid - 1 ? r : valid - 1;
+                const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
+                g2lds16(kb + rr * D + (pg ^ swz_k<C::GR>(r)) * 8, Ks + lds_off);
+                g2lds16(vb + rr * D + (pg ^ swz_v<C::GR>(r)) * 8, Vs + lds_off);
+            }
         }
     };
 
-    // Per-lane LDS offsets that do not depend on the block.
-    const int arow = sigma32(l32);                  // K row this lane feeds to the S^T MFMA
-    int koff[C::KB][C::KS];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            const int r = kb * 32 + arow;
-            koff[kb][ks] = r * D + ((2 * ks + grp) ^ swz_k<C::GR>(r)) * 8;
-        }
-    // Transpose reads of V: lane s = 4j + c of a 16-lane group reads row
-    // (key0 + j), columns d0 + 4c .. +3.
-    const int s16 = lane & 15, grp16 = lane >> 4;
-    const int vj = s16 >> 2, vc = s16 & 3;
-    int voff[C::DB][C::KB][2][2];
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int r = kb * 32 + kk * 16 + 8 * grp + 4 * hh + vj;
-                    const int col = db * 32 + 16 * (grp16 & 1) + 4 * vc;
-                    voff[db][kb][kk][hh] = r * D + (((col >> 3) ^ swz_v<C::GR>(r)) << 3) + (col & 7);
-                }
-
-    if (nblk > 0) gload(0, 0);
-
-    for (int blk = 0; blk < nblk; ++blk) {
+    // One key block from LDS buffer BUF (a compile-time constant, so every
+    // LDS address below is a per-lane register plus an immediate).
+    auto step = [&](auto bufc, int blk) {
+        constexpr int BUF = decltype(bufc)::value;
         __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of block blk have landed
-        __syncthreads();                   // ... and everyone's; buffer (blk+1)&1 is free
-        if (blk + 1 < nblk) gload(blk + 1, (blk + 1) & 1);
-        const __bf16 *Ks = smem + (blk & 1) * C::STAGE;
+        __syncthreads();                   // ... and everyone's; the other buffer is free
+        if (blk + 1 < nblk) gload(blk + 1, 1 - BUF);
+        const __bf16 *Ks = smem + BUF * C::STAGE;
         const __bf16 *Vs = Ks + C::BLK;
         const int k0 = (blk % nkb) * BN;
         const int valid = L - k0 < BN ? L - k0 : BN;
@@ -176,12 +194,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(
                 for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < C::KS; ++ks) {
-                const bf16x8 a = ld8(Ks + koff[kb][ks]);
+                const bf16x8 a = ld8(Ks + kb * 32 * D + kofs[ks]);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(a, qf[qb][ks], s[qb][kb]);
             }
         }
 
+        // Probabilities, rounded to bf16 (the PV operand), and their sum.
+        // Exponents use the running max m_i; a block whose partial sum stays
+        // below 2^8 cannot overflow and is accepted as is.  Otherwise (first
+        // block, or scores that jumped) the true max is taken, O and l are
+        // rescaled, and the block is recomputed.
         bf16x8 pf[QB][C::KB][2];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -192,13 +215,30 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(
                     for (int r = 0; r < 16; ++r)
                         if (kb * 32 + mfma_row_sigma(lane, r) >= valid) s[qb][kb][r] = -INFINITY;
             }
-            float mx = -INFINITY;
+            auto probs = [&]() {
+                const float mneg = -m_i[qb];
+                float ls = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
+                for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-            mx = max_pair32(mx) * scale_log2;
-            if (__any(mx > m_i[qb] + 8.f)) {
+                    for (int hf = 0; hf < 2; ++hf) {
+                        bf16x8 v;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            v[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[qb][kb][8 * hf + i], scale_log2, mneg));
+                        pf[qb][kb][hf] = v;
+                        ls = sum8(v, ls);
+                    }
+                return ls;
+            };
+            float ls = probs();
+            if (__any(!(ls < 256.f))) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+                mx = max_pair32(mx) * scale_log2;
                 const float mn = fmaxf(m_i[qb], mx);
                 const float alpha = __builtin_amdgcn_exp2f(m_i[qb] - mn);
                 m_i[qb] = mn;
@@ -207,19 +247,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(
                 for (int db = 0; db < C::DB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
-            }
-            const float mneg = -m_i[qb];
-            float ls = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], scale_log2, mneg));
-                    s[qb][kb][r] = p;
-                    ls += p;
-                }
-                pf[qb][kb][0] = cvt8(s[qb][kb], 0);
-                pf[qb][kb][1] = cvt8(s[qb][kb], 8);
+                ls = probs();
             }
             l_i[qb] += ls;
         }
@@ -230,10 +258,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(
             for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 a = cat8(ld_tr4(Vs + voff[db][kb][kk][0]), ld_tr4(Vs + voff[db][kb][kk][1]));
+                    const __bf16 *vp = Vs + (kb * 32 + kk * 16) * D + vofs[db];
+                    const bf16x8 a = cat8(ld_tr4(vp), ld_tr4(vp + 4 * D));
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a, pf[qb][kb][kk], acc[qb][db]);
                 }
+    };
+
+    if (nblk > 0) gload(0, 0);
+    for (int blk = 0; blk < nblk; blk += 2) {
+        step(std::integral_constant<int, 0>{}, blk);
+        if (blk + 1 < nblk) step(std::integral_constant<int, 1>{}, blk + 1);
     }
 
     // Epilogue: lanes l and l^32 hold the two halves of row l%32's sum.

@@ -85,6 +85,19 @@ __device__ inline bf16x8 cat8(bf16x4 a, bf16x4 b)
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Sum of the 8 bf16 values of v, accumulated in fp32 onto acc (v_dot2 with 1s).
+__device__ inline float sum8(bf16x8 v, float acc)
+{
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+    return acc;
+}
+
 // Asynchronous 16-byte global -> LDS copy: lane l's 16 bytes land at
 // lds_base + 16*l (lds_base must be the same for the whole wave).
 __device__ inline void g2lds16(const void *src, void *lds_base)

@@ -13,6 +13,11 @@ BF16_MAX_ABS = 2e-2
 BF16_REL_L2 = 1e-2
 # fp32 path: both sides compute in >= fp32 from the same fp32 inputs.
 F32_MAX_ABS = 1e-4
+# LSE of the bf16 path: the kernel sums the probabilities after rounding
+# them to bf16 (the same values the PV product uses).  A sum of positive
+# terms each carrying relative error <= 2^-9 has relative error <= 2^-9, so
+# |dLSE| <= ln(1 + 2^-9) = 1.95e-3; 2.5e-3 leaves room for fp32 rounding.
+BF16_LSE_MAX_ABS = 2.5e-3
 
 
 def say(msg):
@@ -35,6 +40,13 @@ def errors(got, ref):
     max_abs = float(np.max(np.abs(got - ref))) if got.size else 0.0
     rel_l2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)) if got.size else 0.0
     return max_abs, rel_l2
+
+
+def assert_lse(got, ref, dtype, what="LSE"):
+    err = float(np.max(np.abs(np.asarray(got, np.float64) - ref))) if np.size(ref) else 0.0
+    gate = BF16_LSE_MAX_ABS if dtype == "bf16" else F32_MAX_ABS
+    assert err <= gate, "%s: max-abs %.3e (gate %.1e)" % (what, err, gate)
+    return err
 
 
 def assert_close(got, ref, dtype, what=""):

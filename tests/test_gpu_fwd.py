@@ -5,7 +5,7 @@ import pytest
 import torch
 
 from oracle import oracle
-from tests.gpu_util import Layer, assert_close, sample_rows, say, to_host
+from tests.gpu_util import Layer, assert_close, assert_lse, sample_rows, say, to_host
 from tests.inputs import CONFIGS, offsets_for, tensors, windows_for, workload
 
 pytestmark = pytest.mark.gpu
@@ -40,7 +40,7 @@ def test_fwd_bf16_small_full(case):
     torch.cuda.synchronize()
     ro, rl = oracle.fwd(q, k, v, grid, tile, windows, off)
     assert_close(to_host(o), ro, "bf16", name + " O")
-    assert np.max(np.abs(to_host(lse) - rl)) < 1e-3
+    assert_lse(to_host(lse), rl, "bf16")
 
 
 def test_fwd_f32_tiny_workload():
@@ -83,7 +83,7 @@ def test_fwd_mid_workload():
     rows = np.unique(np.concatenate([full, samp]))
     ro, rl = oracle.fwd(w["q"], w["k"], w["v"], w["grid"], w["tile"], w["windows"], rows=rows)
     assert_close(o.reshape(-1, D)[rows], ro, "bf16", "O")
-    assert np.max(np.abs(lse.reshape(-1)[rows] - rl)) < 1e-3
+    assert_lse(lse.reshape(-1)[rows], rl, "bf16")
 
 
 @pytest.mark.parametrize("cfg", [3, 4])
@@ -100,5 +100,5 @@ def test_fwd_720p_sampled(cfg):
     ro, rl = oracle.fwd(w["q"], w["k"], w["v"], w["grid"], w["tile"], w["windows"], w["offsets"], rows=rows)
     o = o.reshape(-1, D)[torch.from_numpy(rows).cuda()]
     assert_close(to_host(o), ro, "bf16", "O")
-    assert np.max(np.abs(to_host(lse.reshape(-1)[torch.from_numpy(rows).cuda()]) - rl)) < 1e-3
+    assert_lse(to_host(lse.reshape(-1)[torch.from_numpy(rows).cuda()]), rl, "bf16")
     assert torch.isfinite(layer.o).all()
