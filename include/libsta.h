@@ -180,6 +180,27 @@ sta_status sta_bwd(const void *q, const void *k, const void *v, const void *o, c
                    int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
                    const sta_geom *g, const sta_index *idx, hipStream_t stream);
 
+/* Stages of the backward, for sta_bwd_parts. */
+typedef enum {
+    STA_BWD_DELTA = 1,   /* delta_ws = rowsum(dout o o)                     */
+    STA_BWD_DKDV = 2,    /* dk, dv   (reads delta_ws)                        */
+    STA_BWD_DQ = 4,      /* dq       (reads delta_ws)                        */
+    STA_BWD_ALL = 7
+} sta_bwd_part;
+
+/*
+ * sta_bwd restricted to the stages in `parts` (a mask of sta_bwd_part),
+ * run in the order DELTA, DKDV, DQ.  sta_bwd == sta_bwd_parts(..., STA_BWD_ALL).
+ * Outputs of stages not requested may be NULL and are not touched; a stage
+ * that reads delta_ws expects it to hold the DELTA stage's result for the
+ * same o and dout.  Lets a caller skip dq (queries that need no gradient) or
+ * dk/dv, or time the stages one by one.  Same arguments and errors as sta_bwd.
+ */
+sta_status sta_bwd_parts(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                         const void *dout, void *dq, void *dk, void *dv, float *delta_ws,
+                         int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
+                         const sta_geom *g, const sta_index *idx, int32_t parts, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

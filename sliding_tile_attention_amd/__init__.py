@@ -22,8 +22,9 @@ LIB_PATH = os.path.join(_HERE, "libsta.so")
 
 STA_OK, STA_ERR_INVALID, STA_ERR_UNSUPPORTED, STA_ERR_HIP = 0, 1, 2, 3
 STA_BF16, STA_F32 = 0, 1
+STA_BWD_DELTA, STA_BWD_DKDV, STA_BWD_DQ, STA_BWD_ALL = 1, 2, 4, 7
 EXPORTS = ("sta_status_str", "sta_last_error", "sta_version", "sta_index_dims", "sta_tile_reorder",
-           "sta_build_index", "sta_fwd", "sta_bwd")
+           "sta_build_index", "sta_fwd", "sta_bwd", "sta_bwd_parts")
 
 
 class StaError(RuntimeError):
@@ -53,7 +54,7 @@ class sta_index(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libsta.so is not built (expected at %s); run "
-                          "`python -m sliding_tile_attention_amd.build`" % LIB_PATH)
+                          "`python sliding_tile_attention_amd/build.py`" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     G, X = ctypes.POINTER(sta_geom), ctypes.POINTER(sta_index)
@@ -67,6 +68,8 @@ def _load():
         "sta_build_index": (ctypes.c_int, [G, I32, W, P, X, P]),
         "sta_fwd": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X, P]),
         "sta_bwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X, P]),
+        "sta_bwd_parts": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X,
+                                         I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -159,6 +162,13 @@ def sta_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, scale, 
     _check(lib.sta_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                        _ptr(dv), _ptr(delta_ws), B, H, D, dtype, float(scale), ctypes.byref(geom.c()),
                        ctypes.byref(index.c()), _stream(stream)))
+
+
+def sta_bwd_parts(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, scale, geom, index, parts,
+                  stream=None):
+    _check(lib.sta_bwd_parts(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                             _ptr(dv), _ptr(delta_ws), B, H, D, dtype, float(scale), ctypes.byref(geom.c()),
+                             ctypes.byref(index.c()), int(parts), _stream(stream)))
 
 
 # ------------------------------------------------- allocation helpers --

@@ -1,6 +1,9 @@
 """Builds libsta.so (all HIP sources, gfx950) in place, next to this file.
 
-    python -m sliding_tile_attention_amd.build [--force]
+    python sliding_tile_attention_amd/build.py [--force]
+
+Run as a script (not as a module of the package): importing the package
+loads libsta.so, which is what this builds.
 """
 import concurrent.futures
 import os

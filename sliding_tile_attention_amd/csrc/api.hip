@@ -236,29 +236,44 @@ sta_status sta_fwd(const void *q, const void *k, const void *v, void *o, float *
     return launch_fwd_bf16(q, k, v, o, lse, B, H, D, scale, geo, *idx, stream);
 }
 
-sta_status sta_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
-                   const void *dout, void *dq, void *dk, void *dv, float *delta_ws,
-                   int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
-                   const sta_geom *g, const sta_index *idx, hipStream_t stream)
+sta_status sta_bwd_parts(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                         const void *dout, void *dq, void *dk, void *dv, float *delta_ws,
+                         int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
+                         const sta_geom *g, const sta_index *idx, int32_t parts, hipStream_t stream)
 {
     Geo geo;
     sta_status st = make_geo(g, geo);
     if (st != STA_OK) return st;
     if ((st = check_attn(geo, B, H, D, dtype, scale)) != STA_OK) return st;
-    if ((st = check_index(geo, H, idx, true)) != STA_OK) return st;
-    const void *ins[6] = {q, k, v, o, lse, dout};
-    void *outs[4] = {dq, dk, dv, delta_ws};
-    for (const void *p : ins)
-        if (!p || !aligned16(p))
+    if (parts < 1 || parts > STA_BWD_ALL)
+        return fail(STA_ERR_INVALID, "parts must be a non-empty mask of STA_BWD_DELTA|DKDV|DQ (got %d)", parts);
+    if ((st = check_index(geo, H, idx, (parts & STA_BWD_DKDV) != 0)) != STA_OK) return st;
+    const bool need_do = true, need_o = (parts & STA_BWD_DELTA) != 0;
+    const bool need_qkv = (parts & (STA_BWD_DKDV | STA_BWD_DQ)) != 0;
+    struct { const void *p; bool need; } ins[] = {{q, need_qkv}, {k, need_qkv}, {v, need_qkv}, {o, need_o},
+                                                  {lse, need_qkv}, {dout, need_do}, {delta_ws, true}};
+    for (auto &a : ins)
+        if (a.need && (!a.p || !aligned16(a.p)))
             return fail(STA_ERR_INVALID, "inputs must be non-NULL and 16-byte aligned");
-    for (void *p : outs)
-        if (!p || !aligned16(p))
+    struct { void *p; bool need; } outs[] = {{dq, (parts & STA_BWD_DQ) != 0}, {dk, (parts & STA_BWD_DKDV) != 0},
+                                             {dv, (parts & STA_BWD_DKDV) != 0}};
+    for (auto &a : outs)
+        if (a.need && (!a.p || !aligned16(a.p)))
             return fail(STA_ERR_INVALID, "outputs must be non-NULL and 16-byte aligned");
     if (dtype == STA_F32)
         return launch_bwd_f32((const float *)q, (const float *)k, (const float *)v, (const float *)o, lse,
                               (const float *)dout, (float *)dq, (float *)dk, (float *)dv, delta_ws,
-                              B, H, D, scale, geo, *idx, stream);
-    return launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, scale, geo, *idx, stream);
+                              B, H, D, scale, geo, *idx, parts, stream);
+    return launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, scale, geo, *idx, parts, stream);
+}
+
+sta_status sta_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dout, void *dq, void *dk, void *dv, float *delta_ws,
+                   int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
+                   const sta_geom *g, const sta_index *idx, hipStream_t stream)
+{
+    return sta_bwd_parts(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, scale, g, idx,
+                         STA_BWD_ALL, stream);
 }
 
 }  // extern "C"

@@ -174,23 +174,31 @@ sta_status launch_fwd_f32(const float *q, const float *k, const float *v, float 
 
 sta_status launch_bwd_f32(const float *q, const float *k, const float *v, const float *o, const float *lse,
                           const float *dout, float *dq, float *dk, float *dv, float *delta, int B, int H, int D,
-                          float scale, const Geo &g, const sta_index &idx, hipStream_t s)
+                          float scale, const Geo &g, const sta_index &idx, int parts, hipStream_t s)
 {
     const int64_t rows = (int64_t)B * H * g.N;
     if (rows / 256 >= ((int64_t)1 << 31))
         return fail(STA_ERR_UNSUPPORTED, "fp32 path: too many rows");
-    if (D == 64) {
-        hipLaunchKernelGGL(delta_f32_kernel<64>, grid_for(rows), dim3(256), 0, s, o, dout, delta, rows);
-        hipLaunchKernelGGL(dq_f32_kernel<64>, grid_for(rows), dim3(256), 0, s, q, k, v, lse, dout, delta, dq,
-                           idx.kv_idx, idx.kv_cnt, idx.max_kv, B, H, g, scale);
-        hipLaunchKernelGGL(dkdv_f32_kernel<64>, grid_for(rows), dim3(256), 0, s, q, k, v, lse, dout, delta, dk,
-                           dv, idx.q_idx, idx.q_cnt, idx.max_q, B, H, g, scale);
-    } else {
-        hipLaunchKernelGGL(delta_f32_kernel<128>, grid_for(rows), dim3(256), 0, s, o, dout, delta, rows);
-        hipLaunchKernelGGL(dq_f32_kernel<128>, grid_for(rows), dim3(256), 0, s, q, k, v, lse, dout, delta, dq,
-                           idx.kv_idx, idx.kv_cnt, idx.max_kv, B, H, g, scale);
-        hipLaunchKernelGGL(dkdv_f32_kernel<128>, grid_for(rows), dim3(256), 0, s, q, k, v, lse, dout, delta, dk,
-                           dv, idx.q_idx, idx.q_cnt, idx.max_q, B, H, g, scale);
+    const dim3 grid = grid_for(rows), blk(256);
+    if (parts & STA_BWD_DELTA) {
+        if (D == 64) hipLaunchKernelGGL(delta_f32_kernel<64>, grid, blk, 0, s, o, dout, delta, rows);
+        else hipLaunchKernelGGL(delta_f32_kernel<128>, grid, blk, 0, s, o, dout, delta, rows);
+    }
+    if (parts & STA_BWD_DKDV) {
+        if (D == 64)
+            hipLaunchKernelGGL(dkdv_f32_kernel<64>, grid, blk, 0, s, q, k, v, lse, dout, delta, dk, dv, idx.q_idx,
+                               idx.q_cnt, idx.max_q, B, H, g, scale);
+        else
+            hipLaunchKernelGGL(dkdv_f32_kernel<128>, grid, blk, 0, s, q, k, v, lse, dout, delta, dk, dv, idx.q_idx,
+                               idx.q_cnt, idx.max_q, B, H, g, scale);
+    }
+    if (parts & STA_BWD_DQ) {
+        if (D == 64)
+            hipLaunchKernelGGL(dq_f32_kernel<64>, grid, blk, 0, s, q, k, v, lse, dout, delta, dq, idx.kv_idx,
+                               idx.kv_cnt, idx.max_kv, B, H, g, scale);
+        else
+            hipLaunchKernelGGL(dq_f32_kernel<128>, grid, blk, 0, s, q, k, v, lse, dout, delta, dq, idx.kv_idx,
+                               idx.kv_cnt, idx.max_kv, B, H, g, scale);
     }
     return check_launch();
 }

@@ -379,7 +379,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 template <int D>
 static sta_status run_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
                           const void *dout, void *dq, void *dk, void *dv, float *delta, int B, int H, float scale,
-                          const Geo &g, const sta_index &idx, hipStream_t s)
+                          const Geo &g, const sta_index &idx, int parts, hipStream_t s)
 {
     constexpr int NW = 4, BN = 64, BQ = 64, M = NW * 32;
     const int64_t rows = (int64_t)B * H * g.N;
@@ -391,26 +391,33 @@ static sta_status run_bwd(const void *q, const void *k, const void *v, const voi
     const __bf16 *Q = (const __bf16 *)q, *K = (const __bf16 *)k, *V = (const __bf16 *)v;
     const __bf16 *O = (const __bf16 *)o, *dO = (const __bf16 *)dout;
 
-    hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, s, O, dO,
-                       delta, rows);
-    sta_status st = check_launch();
-    if (st != STA_OK) return st;
-    hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
-                       (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q, H, g,
-                       rblocks, (int)total, scale_log2, scale);
-    if ((st = check_launch()) != STA_OK) return st;
-    hipLaunchKernelGGL((dq_kernel<D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
-                       (const float *)delta, (__bf16 *)dq, idx.kv_idx, idx.kv_cnt, idx.max_kv, H, g, rblocks,
-                       (int)total, scale_log2, scale);
-    return check_launch();
+    sta_status st = STA_OK;
+    if (parts & STA_BWD_DELTA) {
+        hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, s, O, dO,
+                           delta, rows);
+        if ((st = check_launch()) != STA_OK) return st;
+    }
+    if (parts & STA_BWD_DKDV) {
+        hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
+                           (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q, H, g,
+                           rblocks, (int)total, scale_log2, scale);
+        if ((st = check_launch()) != STA_OK) return st;
+    }
+    if (parts & STA_BWD_DQ) {
+        hipLaunchKernelGGL((dq_kernel<D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
+                           (const float *)delta, (__bf16 *)dq, idx.kv_idx, idx.kv_cnt, idx.max_kv, H, g, rblocks,
+                           (int)total, scale_log2, scale);
+        if ((st = check_launch()) != STA_OK) return st;
+    }
+    return st;
 }
 
 sta_status launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,
                            const void *dout, void *dq, void *dk, void *dv, float *delta, int B, int H, int D,
-                           float scale, const Geo &g, const sta_index &idx, hipStream_t s)
+                           float scale, const Geo &g, const sta_index &idx, int parts, hipStream_t s)
 {
-    if (D == 128) return run_bwd<128>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, scale, g, idx, s);
-    return run_bwd<64>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, scale, g, idx, s);
+    if (D == 128) return run_bwd<128>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, scale, g, idx, parts, s);
+    return run_bwd<64>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, scale, g, idx, parts, s);
 }
 
 }  // namespace sta

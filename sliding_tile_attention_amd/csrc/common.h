@@ -48,7 +48,7 @@ sta_status launch_fwd_f32(const float *q, const float *k, const float *v, float 
 sta_status launch_bwd_f32(const float *q, const float *k, const float *v, const float *o,
                           const float *lse, const float *dout, float *dq, float *dk, float *dv,
                           float *delta, int B, int H, int D, float scale, const Geo &g,
-                          const sta_index &idx, hipStream_t s);
+                          const sta_index &idx, int parts, hipStream_t s);
 
 sta_status launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                            int B, int H, int D, float scale, const Geo &g, const sta_index &idx,
@@ -56,7 +56,7 @@ sta_status launch_fwd_bf16(const void *q, const void *k, const void *v, void *o,
 sta_status launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
                            const float *lse, const void *dout, void *dq, void *dk, void *dv,
                            float *delta, int B, int H, int D, float scale, const Geo &g,
-                           const sta_index &idx, hipStream_t s);
+                           const sta_index &idx, int parts, hipStream_t s);
 
 inline sta_status check_launch()
 {
