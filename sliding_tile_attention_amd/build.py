@@ -19,6 +19,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "reorder.hip", "index.hip", "attn_f32.hip", "fwd_bf16.hip", "bwd_bf16.hip"]
 HEADERS = ["common.h", "mfma.h"]
+# Per-source extra compiler flags (none at present).
+EXTRA = {}
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -38,7 +40,7 @@ def _compile(src, force):
     deps = [s] + [os.path.join(CSRC, h) for h in HEADERS] + [os.path.join(ROOT, "include", "libsta.h")]
     if not force and os.path.exists(o) and os.path.getmtime(o) >= _newest(deps):
         return o
-    cmd = [HIPCC] + FLAGS + ["-c", s, "-o", o]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", s, "-o", o]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

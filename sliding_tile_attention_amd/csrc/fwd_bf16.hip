@@ -49,9 +49,10 @@ struct FwdCfg {
     static constexpr int BLK = BN * D;          // bf16 elements of one K (or V) block
     static constexpr int STAGE = 2 * BLK;       // K + V
     static constexpr int WAVE_ELEMS = 512;      // one wave-wide 16-byte copy = 1 KB
-    static constexpr int COPIES = BLK / (THREADS * 8);   // copies per thread per block
+    static constexpr int GRANULES = BLK / 8;    // 16-byte granules of one K (or V) block
+    static constexpr int COPIES = (GRANULES + THREADS - 1) / THREADS;   // copies per thread per block
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-    static_assert(BLK % (THREADS * 8) == 0, "block must split evenly over the workgroup");
+    static_assert(GRANULES % 64 == 0, "a block is a whole number of wave-wide copies");
 };
 
 template <int GR>
@@ -124,6 +125,9 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         gk[i] = r * D + (pg ^ swz_k<C::GR>(r)) * 8;
         gv[i] = r * D + (pg ^ swz_v<C::GR>(r)) * 8;
     }
+    // A copy slot past the block (workgroups whose thread count does not
+    // divide the block) is skipped; the test is uniform per wave.
+    auto copy_live = [&](int i) { return C::GRANULES % C::THREADS == 0 || (i * NW + wave) * 64 < C::GRANULES; };
     // S^T operand: lane feeds K row sigma(l%32) of each 32-key sub-block;
     // the swizzle of that row does not depend on the sub-block.
     const int arow = sigma32(l32);
@@ -156,6 +160,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         if (valid == BN) {
 #pragma unroll
             for (int i = 0; i < C::COPIES; ++i) {
+                if (!copy_live(i)) continue;
                 const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
                 g2lds16(kb + gk[i], Ks + lds_off);
                 g2lds16(vb + gv[i], Vs + lds_off);
@@ -163,6 +168,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         } else {
 #pragma unroll
             for (int i = 0; i < C::COPIES; ++i) {
+                if (!copy_live(i)) continue;
                 const int slot = (i * NW + wave) * 64 + lane;
                 const int r = slot / C::GR, pg = slot % C::GR;
                 const int rr = r < valid - 1 ? r : valid - 1;

@@ -98,6 +98,15 @@ __device__ inline float sum8(bf16x8 v, float acc)
     return acc;
 }
 
+// Wait until at most N vector-memory operations of this wave are in flight
+// (lgkm and export counters untouched).
+template <int N>
+__device__ inline void wait_vmem()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Asynchronous 16-byte global -> LDS copy: lane l's 16 bytes land at
 // lds_base + 16*l (lds_base must be the same for the whole wave).
 __device__ inline void g2lds16(const void *src, void *lds_base)
