@@ -161,7 +161,7 @@ sta_status launch_fwd_f32(const float *q, const float *k, const float *v, float 
                           int D, float scale, const Geo &g, const sta_index &idx, hipStream_t s)
 {
     const int64_t rows = (int64_t)B * H * g.N;
-    if (rows / 256 >= ((int64_t)1 << 31))
+    if (!grid_fits((rows + 255) / 256, 256))
         return fail(STA_ERR_UNSUPPORTED, "fp32 path: too many rows");
     if (D == 64)
         hipLaunchKernelGGL(fwd_f32_kernel<64>, grid_for(rows), dim3(256), 0, s, q, k, v, o, lse, idx.kv_idx,
@@ -177,7 +177,7 @@ sta_status launch_bwd_f32(const float *q, const float *k, const float *v, const 
                           float scale, const Geo &g, const sta_index &idx, int parts, hipStream_t s)
 {
     const int64_t rows = (int64_t)B * H * g.N;
-    if (rows / 256 >= ((int64_t)1 << 31))
+    if (!grid_fits((rows + 255) / 256, 256))
         return fail(STA_ERR_UNSUPPORTED, "fp32 path: too many rows");
     const dim3 grid = grid_for(rows), blk(256);
     if (parts & STA_BWD_DELTA) {

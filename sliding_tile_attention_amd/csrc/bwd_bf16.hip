@@ -233,8 +233,9 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 {
     constexpr int THREADS = NW * 64, M = NW * 32, KS = D / 16, SB = BQ / 32, DB = D / 32;
     constexpr int BLK = BQ * D;
-    constexpr int STAGE = 2 * BLK + 2 * BQ * 2;    // Q, dO (bf16) + LSE, Delta (fp32 as 2 bf16 slots each)
-    static_assert(BQ == 64, "LSE/Delta staging assumes one 64-lane dword copy per array");
+    constexpr int SROWS = BQ > 64 ? BQ : 64;        // LSE / Delta slots (one 64-lane dword copy each)
+    constexpr int STAGE = 2 * BLK + 2 * SROWS * 2;  // Q, dO (bf16) + LSE, Delta (fp32 as 2 bf16 slots each)
+    static_assert(BQ <= 64 && BQ % 32 == 0, "query block of 32 or 64 rows");
     __shared__ __attribute__((aligned(1024))) __bf16 smem[2 * STAGE];
 
     const int work = xcd_remap(blockIdx.x, total);
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
             __builtin_amdgcn_global_load_lds((const void *)(LSE + sbase + row0 + rr),
                                              (__attribute__((address_space(3))) void *)(st + 2 * BLK), 4, 0, 0);
             __builtin_amdgcn_global_load_lds((const void *)(Delta + sbase + row0 + rr),
-                                             (__attribute__((address_space(3))) void *)(st + 2 * BLK + 2 * BQ), 4,
+                                             (__attribute__((address_space(3))) void *)(st + 2 * BLK + 2 * SROWS), 4,
                                              0, 0);
         }
     };
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
         const __bf16 *Qs = smem + BUF * STAGE;
         const __bf16 *Os = Qs + BLK;
         const float *Ls = (const float *)(Qs + 2 * BLK);
-        const float *Dl = Ls + BQ;
+        const float *Dl = Ls + SROWS;
         const int q0 = (blk % nqb) * BQ;
         const int valid = L - q0 < BQ ? L - q0 : BQ;
 
@@ -376,16 +377,28 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 
 // ---------------------------------------------------------------------------
 
+// Tile shapes (overridable at compile time for tuning sweeps): waves per
+// workgroup, keys per block in dQ, query rows per block in dK/dV.
+#ifndef STA_BWD_NW
+#define STA_BWD_NW 4
+#endif
+#ifndef STA_BWD_BN
+#define STA_BWD_BN 64
+#endif
+#ifndef STA_BWD_BQ
+#define STA_BWD_BQ 64
+#endif
+
 template <int D>
 static sta_status run_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
                           const void *dout, void *dq, void *dk, void *dv, float *delta, int B, int H, float scale,
                           const Geo &g, const sta_index &idx, int parts, hipStream_t s)
 {
-    constexpr int NW = 4, BN = 64, BQ = 64, M = NW * 32;
+    constexpr int NW = STA_BWD_NW, BN = STA_BWD_BN, BQ = STA_BWD_BQ, M = NW * 32;
     const int64_t rows = (int64_t)B * H * g.N;
     const int rblocks = (g.L + M - 1) / M;
     const int64_t total = (int64_t)B * H * g.T * rblocks;
-    if (total >= ((int64_t)1 << 31) || rows * (D / 8) / 256 >= ((int64_t)1 << 31))
+    if (!grid_fits(total, NW * 64) || !grid_fits((rows * (D / 8) + 255) / 256, 256))
         return fail(STA_ERR_UNSUPPORTED, "too many work items");
     const float scale_log2 = scale * 1.4426950408889634f;
     const __bf16 *Q = (const __bf16 *)q, *K = (const __bf16 *)k, *V = (const __bf16 *)v;

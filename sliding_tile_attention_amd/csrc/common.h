@@ -58,6 +58,19 @@ sta_status launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
                            float *delta, int B, int H, int D, float scale, const Geo &g,
                            const sta_index &idx, int parts, hipStream_t s);
 
+// Stream-ordered device workspace (per-device pool that keeps freed memory
+// for reuse); the buffer may be used by work queued on `s` until the
+// matching workspace_free on the same stream.
+sta_status workspace_alloc(void **p, size_t bytes, hipStream_t s);
+sta_status workspace_free(void *p, hipStream_t s);
+
+// A 1-D launch of `blocks` workgroups of `threads` must keep the total
+// work-item count of the grid dimension below 2^32.
+inline bool grid_fits(int64_t blocks, int threads)
+{
+    return blocks >= 0 && blocks * (int64_t)threads < ((int64_t)1 << 32);
+}
+
 inline sta_status check_launch()
 {
     hipError_t e = hipGetLastError();

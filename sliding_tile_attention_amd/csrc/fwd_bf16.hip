@@ -5,12 +5,22 @@
 // mask is tile-granular, so a workgroup that owns rows of one query tile
 // walks that tile's key-tile list and never masks inside a tile.
 //
+// Two launches:
+//   1. vt_kernel: V^T of every tile, [b,h,tile][D][Lp] with the key axis
+//      padded with zeros to Lp (a multiple of the key block), into a
+//      stream-ordered workspace.  Every V tile is read by ~45 query tiles'
+//      workgroups, so transposing it once lets the PV product fetch its
+//      operand with full-width LDS reads instead of transposing reads,
+//      which move half the bytes per LDS instruction -- the LDS port, not
+//      the matrix cores, is what bounds this kernel.
+//   2. fwd_bf16_kernel, below.
+//
 // Work decomposition
 //   workgroup = NW waves = M = NW*QB*32 consecutive query rows of one query
 //   tile of one (b, h); work items are ordered head-major and spread over the
 //   8 XCDs in contiguous ranges (xcd_remap) so that the workgroups sharing an
 //   XCD's L2 walk neighbouring windows of the same head.
-//   The key loop runs over (listed key tile, BN-key block) pairs.  K and V
+//   The key loop runs over (listed key tile, BN-key block) pairs.  K and V^T
 //   blocks travel HBM -> LDS directly (global_load_lds, no staging
 //   registers) into a double buffer: the copy of block j+1 runs while block j
 //   is computed; one barrier per block.
@@ -21,16 +31,14 @@
 //   into one FMA; the running max is only moved when a block max exceeds it
 //   by more than 8 (2^8 headroom), which leaves the result exact and skips
 //   almost every rescale of the O accumulator;
-//   O^T[D x 32] += V^T_blk P^T  (MFMA: A = V^T via LDS transpose reads,
-//                                B = P in VGPRs)
+//   O^T[D x 32] += V^T_blk P^T  (MFMA: A = V^T rows from LDS, B = P in VGPRs)
 // K rows are fed permuted by sigma so that each lane's S^T registers hold 8
 // consecutive keys -- the B operand of the PV product without any shuffle.
 //
-// LDS layout: K and V blocks are row-major [BN][D] with the 16-byte granules
-// of each row XOR-swizzled (granule c of row r stored at c ^ f(r)), which
-// keeps both read patterns bank-conflict free without padding:
-//   K (16-byte reads of 16 different rows):      f_K(r) = r mod (D/8)
-//   V (8-byte transpose reads of 4 rows x 32 B):  f_V(r) = 4*(r mod 4)
+// LDS layout: the K block is row-major [BN][D], the V^T block [D][BN]; the
+// 16-byte granules of each row are XOR-swizzled (granule c of row r stored
+// at c ^ f(r)) so that 16 lanes reading 16 consecutive rows at one logical
+// granule touch 16 distinct 16-byte bank groups -- conflict free, no padding.
 #include <type_traits>
 
 #include "common.h"
@@ -45,30 +53,75 @@ struct FwdCfg {
     static constexpr int KS = D / 16;           // reduction steps of QK^T
     static constexpr int KB = BN / 32;          // 32-key sub-blocks
     static constexpr int DB = D / 32;           // 32-wide column blocks of O^T
-    static constexpr int GR = D / 8;            // 16-byte granules per row
-    static constexpr int BLK = BN * D;          // bf16 elements of one K (or V) block
-    static constexpr int STAGE = 2 * BLK;       // K + V
+    static constexpr int GR = D / 8;            // 16-byte granules per K row
+    static constexpr int GV = BN / 8;           // 16-byte granules per V^T row
+    static constexpr int BLK = BN * D;          // bf16 elements of one K (or V^T) block
+    static constexpr int STAGE = 2 * BLK;       // K + V^T
     static constexpr int WAVE_ELEMS = 512;      // one wave-wide 16-byte copy = 1 KB
-    static constexpr int GRANULES = BLK / 8;    // 16-byte granules of one K (or V) block
+    static constexpr int GRANULES = BLK / 8;    // 16-byte granules of one block
     static constexpr int COPIES = (GRANULES + THREADS - 1) / THREADS;   // copies per thread per block
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
     static_assert(GRANULES % 64 == 0, "a block is a whole number of wave-wide copies");
 };
 
-template <int GR>
-__device__ inline int swz_k(int r) { return r & (GR - 1); }
-template <int GR>
-__device__ inline int swz_v(int r) { return ((r & 3) << 2) & (GR - 1); }
+// Swizzle of a row of G 16-byte granules: rows r = 0..15 read at one logical
+// granule land in 16 distinct 16-byte slots of a 256-byte bank line.
+template <int G>
+__device__ inline int swz_row(int r)
+{
+    if constexpr (G >= 16) return r & 15;
+    else return (r / (16 / G)) & (G - 1);
+}
 
 #ifndef STA_FWD_MINB
-#define STA_FWD_MINB 2
+#define STA_FWD_MINB 3
 #endif
+
+// Key padding of the V^T workspace (a multiple of every key block size).
+constexpr int kVtPad = 64;
+
+template <int D>
+__global__ __launch_bounds__(256) void vt_kernel(const __bf16 *__restrict__ V, __bf16 *__restrict__ VT, int L,
+                                                 int Lp, int chunks)
+{
+    // one workgroup per 64-key chunk of one (b, h, tile)
+    __shared__ uint32_t tile[64][D / 2 + 1];   // 64 keys x D values as bf16 pairs; odd stride: no conflicts
+    const int c = (int)(blockIdx.x % (unsigned)chunks);
+    const int64_t bt = blockIdx.x / (unsigned)chunks;
+    const int k0 = c * 64;
+    const __bf16 *src = V + (bt * L + k0) * D;
+    constexpr int RG = D / 8;                 // 16-byte granules per V row
+    for (int i = threadIdx.x; i < 64 * RG; i += 256) {
+        const int r = i / RG, gc = i % RG;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (k0 + r < L) v = __builtin_nontemporal_load((const u32x4 *)(src + (int64_t)r * D + gc * 8));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) tile[r][gc * 4 + t] = v[t];
+    }
+    __syncthreads();
+    // unit u: column pair p (rows 2p, 2p+1 of V^T), key group kg (8 keys)
+    __bf16 *dst = VT + bt * D * Lp + k0;
+    for (int u = threadIdx.x; u < (D / 2) * 8; u += 256) {
+        const int p = u / 8, kg = u % 8;
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = tile[kg * 8 + j][p];
+        u32x4 lo, hi;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            lo[t] = (w[2 * t] & 0xffffu) | (w[2 * t + 1] << 16);
+            hi[t] = (w[2 * t] >> 16) | (w[2 * t + 1] & 0xffff0000u);
+        }
+        __builtin_nontemporal_store(lo, (u32x4 *)(dst + (int64_t)(2 * p) * Lp + kg * 8));
+        __builtin_nontemporal_store(hi, (u32x4 *)(dst + (int64_t)(2 * p + 1) * Lp + kg * 8));
+    }
+}
 
 template <int D, int NW, int QB, int BN>
 __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
-    const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
+    const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ VT,
     __bf16 *__restrict__ O, float *__restrict__ LSE, const int32_t *__restrict__ kv_idx,
-    const int32_t *__restrict__ kv_cnt, int max_kv, int H, Geo g, int rblocks, int total,
+    const int32_t *__restrict__ kv_cnt, int max_kv, int H, Geo g, int Lp, int rblocks, int total,
     float scale_log2)
 {
     using C = FwdCfg<D, NW, QB, BN>;
@@ -84,6 +137,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     const int l32 = lane & 31, grp = lane >> 5;
     const int L = g.L;
     const int64_t base = (int64_t)bh * g.N * D;
+    const int64_t vt_base = (int64_t)bh * g.T * D * Lp;
     const int wrow0 = rb * C::M + wave * QB * 32;   // first row of this wave inside the tile
 
     // Q fragments: B operand of S^T = K Q^T, lane = query row, 8 columns.
@@ -115,15 +169,16 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
 
     // ---- per-lane offsets (bf16 elements), fixed for the whole kernel ----
     // Copies: wave-wide copy i of a block fills granule slots
-    // (i*NW + wave)*64 + lane, i.e. row r = slot / GR, physical granule slot % GR,
-    // which must receive logical granule (slot % GR) ^ f(r) of row r.
+    // (i*NW + wave)*64 + lane, i.e. row r = slot / (granules per row) and
+    // physical granule p, which must receive logical granule p ^ f(r).
     int gk[C::COPIES], gv[C::COPIES];
 #pragma unroll
     for (int i = 0; i < C::COPIES; ++i) {
         const int slot = (i * NW + wave) * 64 + lane;
         const int r = slot / C::GR, pg = slot % C::GR;
-        gk[i] = r * D + (pg ^ swz_k<C::GR>(r)) * 8;
-        gv[i] = r * D + (pg ^ swz_v<C::GR>(r)) * 8;
+        gk[i] = r * D + (pg ^ swz_row<C::GR>(r)) * 8;
+        const int rv = slot / C::GV, pv = slot % C::GV;
+        gv[i] = rv * Lp + (pv ^ swz_row<C::GV>(rv)) * 8;
     }
     // A copy slot past the block (workgroups whose thread count does not
     // divide the block) is skipped; the test is uniform per wave.
@@ -133,28 +188,28 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     const int arow = sigma32(l32);
     int kofs[C::KS];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) kofs[ks] = arow * D + ((2 * ks + grp) ^ swz_k<C::GR>(arow)) * 8;
-    // PV operand by transpose reads: lane s = 4j + c of a 16-lane group reads
-    // row 8*grp + 4*half + j (+ sub-block rows), columns db*32 + 16*((lane>>4)&1) + 4c.
-    const int vj = (lane & 15) >> 2, vc = lane & 3;
-    int vofs[C::DB];
+    for (int ks = 0; ks < C::KS; ++ks) kofs[ks] = arow * D + ((2 * ks + grp) ^ swz_row<C::GR>(arow)) * 8;
+    // PV operand: lane feeds V^T row d = db*32 + l%32, keys kb*32 + kk*16 +
+    // 8*grp .. +7, i.e. logical granule 4kb + 2kk + grp of that row; the
+    // swizzle depends only on l%32.
+    int vofs[C::KB][2];
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-        const int r = 8 * grp + vj;
-        const int col = db * 32 + 16 * ((lane >> 4) & 1) + 4 * vc;
-        vofs[db] = r * D + (((col >> 3) ^ swz_v<C::GR>(r)) << 3) + (col & 7);
-    }
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            vofs[kb][kk] = l32 * BN + (((4 * kb + 2 * kk + grp) ^ swz_row<C::GV>(l32)) << 3);
 
     // Issue the asynchronous copy of key block `blk` into LDS buffer `buf`.
-    // In a ragged last block, rows past the tile end re-read the last valid
-    // row; their scores are masked, so their contents never matter.
+    // In a ragged last block, K rows past the tile end re-read the last
+    // valid row (their scores are masked, so their contents never matter);
+    // V^T keys past the tile end are the workspace's zero padding.
     auto gload = [&](int blk, int buf) {
         const int e = blk / nkb;
         const int k0 = (blk - e * nkb) * BN;
         const int valid = L - k0 < BN ? L - k0 : BN;
-        const int64_t row0 = (int64_t)lst[e] * L + k0;
-        const __bf16 *kb = K + base + row0 * D;
-        const __bf16 *vb = V + base + row0 * D;
+        const int tk = lst[e];
+        const __bf16 *kb = K + base + ((int64_t)tk * L + k0) * D;
+        const __bf16 *vb = VT + vt_base + (int64_t)tk * D * Lp + k0;
         __bf16 *Ks = smem + buf * C::STAGE;
         __bf16 *Vs = Ks + C::BLK;
         if (valid == BN) {
@@ -173,8 +228,8 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
                 const int r = slot / C::GR, pg = slot % C::GR;
                 const int rr = r < valid - 1 ? r : valid - 1;
                 const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
-                g2lds16(kb + rr * D + (pg ^ swz_k<C::GR>(r)) * 8, Ks + lds_off);
-                g2lds16(vb + rr * D + (pg ^ swz_v<C::GR>(r)) * 8, Vs + lds_off);
+                g2lds16(kb + rr * D + (pg ^ swz_row<C::GR>(r)) * 8, Ks + lds_off);
+                g2lds16(vb + gv[i], Vs + lds_off);
             }
         }
     };
@@ -264,8 +319,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
             for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const __bf16 *vp = Vs + (kb * 32 + kk * 16) * D + vofs[db];
-                    const bf16x8 a = cat8(ld_tr4(vp), ld_tr4(vp + 4 * D));
+                    const bf16x8 a = ld8(Vs + db * 32 * BN + vofs[kb][kk]);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a, pf[qb][kb][kk], acc[qb][db]);
                 }
@@ -300,20 +354,33 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     }
 }
 
+// V^T workspace + transpose, then the attention kernel.
 template <int D, int NW, int QB, int BN>
 static sta_status run_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                           float scale, const Geo &g, const sta_index &idx, hipStream_t s)
 {
     using C = FwdCfg<D, NW, QB, BN>;
+    static_assert(kVtPad % BN == 0, "V^T padding must be a multiple of the key block");
     const int rblocks = (g.L + C::M - 1) / C::M;
     const int64_t total = (int64_t)B * H * g.T * rblocks;
-    if (total >= ((int64_t)1 << 31))
+    const int chunks = (g.L + kVtPad - 1) / kVtPad;
+    const int Lp = chunks * kVtPad;
+    const int64_t vt_blocks = (int64_t)B * H * g.T * chunks;
+    if (!grid_fits(total, C::THREADS) || !grid_fits(vt_blocks, 256))
         return fail(STA_ERR_UNSUPPORTED, "too many work items");
+    const size_t vt_bytes = (size_t)B * H * g.T * D * Lp * sizeof(__bf16);
+    void *vt = nullptr;
+    sta_status st = workspace_alloc(&vt, vt_bytes, s);
+    if (st != STA_OK) return st;
+    hipLaunchKernelGGL(vt_kernel<D>, dim3((unsigned)vt_blocks), dim3(256), 0, s, (const __bf16 *)v, (__bf16 *)vt,
+                       g.L, Lp, chunks);
     const float scale_log2 = scale * 1.4426950408889634f;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BN>), dim3((unsigned)total), dim3(C::THREADS), 0, s,
-                       (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (__bf16 *)o, lse, idx.kv_idx,
-                       idx.kv_cnt, idx.max_kv, H, g, rblocks, (int)total, scale_log2);
-    return check_launch();
+                       (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)vt, (__bf16 *)o, lse, idx.kv_idx,
+                       idx.kv_cnt, idx.max_kv, H, g, Lp, rblocks, (int)total, scale_log2);
+    st = check_launch();
+    const sta_status fs = workspace_free(vt, s);
+    return st != STA_OK ? st : fs;
 }
 
 // Tile shape: waves per workgroup, 32-row query blocks per wave, keys per
@@ -325,7 +392,7 @@ static sta_status run_fwd(const void *q, const void *k, const void *v, void *o, 
 #define STA_FWD_QB 1
 #endif
 #ifndef STA_FWD_BN
-#define STA_FWD_BN 64
+#define STA_FWD_BN 32
 #endif
 
 sta_status launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,

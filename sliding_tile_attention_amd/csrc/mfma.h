@@ -107,11 +107,53 @@ __device__ inline void wait_vmem()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until at most n vector-memory operations are in flight, n a runtime
+// multiple of STEP no larger than MAXN (dispatched to constant waits).
+template <int MAXN, int STEP>
+__device__ inline void wait_vmem_le(int n)
+{
+    if constexpr (MAXN <= 0) {
+        wait_vmem<0>();
+    } else {
+        if (n >= MAXN) wait_vmem<MAXN>();
+        else wait_vmem_le<MAXN - STEP, STEP>(n);
+    }
+}
+
+// Workgroup barrier without the release fence of __syncthreads() (which
+// waits for every outstanding memory operation, LDS copies in flight
+// included).  Callers make the LDS data they hand over visible themselves:
+// LDS reads are complete once their results are used, and asynchronous
+// global -> LDS copies are waited for with wait_vmem.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ inline void barrier_nofence()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Asynchronous 16-byte global -> LDS copy: lane l's 16 bytes land at
 // lds_base + 16*l (lds_base must be the same for the whole wave).
 __device__ inline void g2lds16(const void *src, void *lds_base)
 {
     __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+// Buffer descriptor over `bytes` bytes from `base` (raw addressing: loads at
+// offsets >= bytes return zero).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+// Asynchronous 16-byte buffer -> LDS copy: lane l's 16 bytes at descriptor
+// offset voffset land at lds_base + 16*l (lds_base wave-uniform).  The
+// per-lane offset is a plain register that can stay loop-invariant.
+__device__ inline void b2lds16(__amdgpu_buffer_rsrc_t r, int voffset, void *lds_base)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, voffset, 0, 0,
+                                             0);
 }
 
 // Packs element i of four 8-wide bf16 rows (as raw words) into 4 bf16
