@@ -171,14 +171,14 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     // Copies: wave-wide copy i of a block fills granule slots
     // (i*NW + wave)*64 + lane, i.e. row r = slot / (granules per row) and
     // physical granule p, which must receive logical granule p ^ f(r).
-    int gk[C::COPIES], gv[C::COPIES];
+    int gk[C::COPIES], gv[C::COPIES];     // byte offsets inside a K block / V^T tile
 #pragma unroll
     for (int i = 0; i < C::COPIES; ++i) {
         const int slot = (i * NW + wave) * 64 + lane;
         const int r = slot / C::GR, pg = slot % C::GR;
-        gk[i] = r * D + (pg ^ swz_row<C::GR>(r)) * 8;
+        gk[i] = (r * D + (pg ^ swz_row<C::GR>(r)) * 8) * 2;
         const int rv = slot / C::GV, pv = slot % C::GV;
-        gv[i] = rv * Lp + (pv ^ swz_row<C::GV>(rv)) * 8;
+        gv[i] = (rv * Lp + (pv ^ swz_row<C::GV>(rv)) * 8) * 2;
     }
     // A copy slot past the block (workgroups whose thread count does not
     // divide the block) is skipped; the test is uniform per wave.
@@ -199,40 +199,38 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         for (int kk = 0; kk < 2; ++kk)
             vofs[kb][kk] = l32 * BN + (((4 * kb + 2 * kk + grp) ^ swz_row<C::GV>(l32)) << 3);
 
-    // Issue the asynchronous copy of key block `blk` into LDS buffer `buf`.
-    // In a ragged last block, K rows past the tile end re-read the last
-    // valid row (their scores are masked, so their contents never matter);
-    // V^T keys past the tile end are the workspace's zero padding.
-    auto gload = [&](int blk, int buf) {
-        const int e = blk / nkb;
-        const int k0 = (blk - e * nkb) * BN;
-        const int valid = L - k0 < BN ? L - k0 : BN;
-        const int tk = lst[e];
-        const __bf16 *kb = K + base + ((int64_t)tk * L + k0) * D;
-        const __bf16 *vb = VT + vt_base + (int64_t)tk * D * Lp + k0;
+    // The key-block stream is walked with counters (no divisions): the
+    // copy stream is one block ahead of the compute stream; the next tile
+    // id of the list is prefetched when a tile is entered.
+    int c_e = 0, c_k0 = 0;                               // next block to copy
+    int c_tile = cnt > 0 ? lst[0] : 0;
+    int n_tile = cnt > 1 ? lst[1] : 0;
+    // Issue the asynchronous copy of the next block into LDS buffer `buf`
+    // through buffer descriptors over that block: K rows past a ragged
+    // tile end read as zero (their scores are masked), V^T keys past it are
+    // the workspace's zero padding.
+    auto gload = [&](int buf) {
+        const int valid = L - c_k0 < BN ? L - c_k0 : BN;
+        const auto rk = make_rsrc(K + base + ((int64_t)c_tile * L + c_k0) * D, valid * D * 2);
+        const auto rv = make_rsrc(VT + vt_base + (int64_t)c_tile * D * Lp + c_k0, (D * Lp - c_k0) * 2);
         __bf16 *Ks = smem + buf * C::STAGE;
         __bf16 *Vs = Ks + C::BLK;
-        if (valid == BN) {
 #pragma unroll
-            for (int i = 0; i < C::COPIES; ++i) {
-                if (!copy_live(i)) continue;
-                const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
-                g2lds16(kb + gk[i], Ks + lds_off);
-                g2lds16(vb + gv[i], Vs + lds_off);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < C::COPIES; ++i) {
-                if (!copy_live(i)) continue;
-                const int slot = (i * NW + wave) * 64 + lane;
-                const int r = slot / C::GR, pg = slot % C::GR;
-                const int rr = r < valid - 1 ? r : valid - 1;
-                const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
-                g2lds16(kb + rr * D + (pg ^ swz_row<C::GR>(r)) * 8, Ks + lds_off);
-                g2lds16(vb + gv[i], Vs + lds_off);
-            }
+        for (int i = 0; i < C::COPIES; ++i) {
+            if (!copy_live(i)) continue;
+            const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
+            b2lds16(rk, gk[i], Ks + lds_off);
+            b2lds16(rv, gv[i], Vs + lds_off);
+        }
+        c_k0 += BN;
+        if (c_k0 >= L) {
+            c_k0 = 0;
+            ++c_e;
+            c_tile = n_tile;
+            n_tile = c_e + 1 < cnt ? lst[c_e + 1] : 0;
         }
     };
+    int s_k0 = 0;                                        // key offset of the block computed next
 
     // One key block from LDS buffer BUF (a compile-time constant, so every
     // LDS address below is a per-lane register plus an immediate).
@@ -240,11 +238,11 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         constexpr int BUF = decltype(bufc)::value;
         __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of block blk have landed
         __syncthreads();                   // ... and everyone's; the other buffer is free
-        if (blk + 1 < nblk) gload(blk + 1, 1 - BUF);
+        if (blk + 1 < nblk) gload(1 - BUF);
         const __bf16 *Ks = smem + BUF * C::STAGE;
         const __bf16 *Vs = Ks + C::BLK;
-        const int k0 = (blk % nkb) * BN;
-        const int valid = L - k0 < BN ? L - k0 : BN;
+        const int valid = L - s_k0 < BN ? L - s_k0 : BN;
+        s_k0 = s_k0 + BN >= L ? 0 : s_k0 + BN;
 
         f32x16 s[QB][C::KB];
 #pragma unroll
@@ -325,7 +323,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
                 }
     };
 
-    if (nblk > 0) gload(0, 0);
+    if (nblk > 0) gload(0);
     for (int blk = 0; blk < nblk; blk += 2) {
         step(std::integral_constant<int, 0>{}, blk);
         if (blk + 1 < nblk) step(std::integral_constant<int, 1>{}, blk + 1);
