@@ -21,6 +21,12 @@
 //   dkdv: S = Q K^T, dP = dO V^T          (A = Q / dO rows from LDS, B = K / V
 //                                          in VGPRs; lane owns a key row)
 //         dV += P^T dO, dK += dS^T Q       (B = dO / Q by LDS transpose reads)
+// The key (dQ) or query (dK/dV) blocks of a list are walked with counters
+// and copied HBM -> LDS through buffer descriptors whose per-lane offsets
+// are loop-invariant; rows past a ragged tile end read as zero.  No mask is
+// needed for them: in dQ a zero key row adds dS*0 to dQ (and its P, dS stay
+// finite); in dK/dV a zero query row has zero Q and dO, so it adds nothing
+// to dK = dS^T Q or dV = P^T dO.
 // LDS tiles are row-major with 16-byte granules XOR-swizzled by
 // f(r) = 4*(r mod 4) ^ ((r / 4) mod 4), which keeps both the 16-byte row
 // reads (16 distinct rows per 16 lanes) and the transpose reads (4 rows x
@@ -57,22 +63,68 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16 *__restrict__
     if (row < rows && part == 0) delta[row] = s;
 }
 
-// Asynchronous copy of `rows` rows (row-major, D bf16 each) starting at src
-// into a swizzled LDS tile; rows >= valid re-read row valid-1 (callers mask
-// them).  Every thread of the workgroup takes part.
+// Byte offsets (inside a row-major tile of D-wide bf16 rows) of the
+// 16-byte granules that copy i of thread tid moves into a swizzled LDS tile:
+// wave-wide copy i fills LDS granule slots (i*W + wave)*64 + lane, i.e. row
+// r = slot / GR, physical granule p, which receives logical granule
+// p ^ f(r).  Loop-invariant: computed once per kernel.
 template <int D, int THREADS, int ROWS>
-__device__ inline void copy_rows(const __bf16 *src, __bf16 *lds, int valid, int tid)
-{
-    constexpr int GR = D / 8;
-    constexpr int COPIES = ROWS * D / (THREADS * 8);
+struct RowCopy {
+    static constexpr int GR = D / 8;
+    static constexpr int W = THREADS / 64;
+    static constexpr int COPIES = ROWS * D / (THREADS * 8);
+    static constexpr int ROWS_PER_COPY = W * 64 / GR;
+    // the swizzle repeats every 16 rows: when a copy spans a multiple of
+    // that, copy i is copy 0 shifted by i*ROWS_PER_COPY rows
+    static constexpr bool SHIFT = ROWS_PER_COPY % 16 == 0;
     static_assert(ROWS * D % (THREADS * 8) == 0, "tile must split evenly");
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    int off[SHIFT ? 1 : COPIES];
+    __device__ explicit RowCopy(int tid)
+    {
+        const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-    for (int i = 0; i < COPIES; ++i) {
-        const int slot = (i * (THREADS / 64) + wave) * 64 + lane;
-        const int r = slot / GR, pg = slot % GR;
-        const int rr = r < valid ? r : valid - 1;
-        g2lds16(src + rr * D + (pg ^ swz_u<GR>(r)) * 8, lds + (i * (THREADS / 64) + wave) * 512);
+        for (int i = 0; i < (SHIFT ? 1 : COPIES); ++i) {
+            const int slot = (i * W + wave) * 64 + lane;
+            const int r = slot / GR, pg = slot % GR;
+            off[i] = (r * D + (pg ^ swz_u<GR>(r)) * 8) * 2;
+        }
+    }
+    // Asynchronous copy of `valid` rows from src into the LDS tile; rows
+    // past `valid` (a ragged tile end) read as zero.  Every thread of the
+    // workgroup takes part.
+    __device__ void copy(const __bf16 *src, int valid, __bf16 *lds, int wave) const
+    {
+        const auto rs = make_rsrc(src, valid * D * 2);
+#pragma unroll
+        for (int i = 0; i < COPIES; ++i) {
+            if constexpr (SHIFT)
+                b2lds16(rs, off[0], lds + (i * W + wave) * 512, i * ROWS_PER_COPY * D * 2);
+            else
+                b2lds16(rs, off[i], lds + (i * W + wave) * 512);
+        }
+    }
+};
+
+// Position in a key- or query-tile list walked block by block (no
+// divisions); the next tile id is prefetched when a tile is entered.
+struct ListWalk {
+    int e, r0, tile, next;
+};
+__device__ inline void walk_init(ListWalk &w, const int32_t *lst, int cnt)
+{
+    w.e = 0;
+    w.r0 = 0;
+    w.tile = cnt > 0 ? lst[0] : 0;
+    w.next = cnt > 1 ? lst[1] : 0;
+}
+__device__ inline void walk_next(ListWalk &w, const int32_t *lst, int cnt, int step, int L)
+{
+    w.r0 += step;
+    if (w.r0 >= L) {
+        w.r0 = 0;
+        ++w.e;
+        w.tile = w.next;
+        w.next = w.e + 1 < cnt ? lst[w.e + 1] : 0;
     }
 }
 
@@ -144,24 +196,24 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
         for (int hh = 0; hh < 2; ++hh)
             tofs[db][hh] = lds_at<D>(8 * grp + 4 * hh + vj, db * 32 + 16 * ((lane >> 4) & 1) + 4 * vc);
 
-    auto gload = [&](int blk, int buf) {
-        const int e = blk / nkb;
-        const int k0 = (blk - e * nkb) * BN;
-        const int valid = L - k0 < BN ? L - k0 : BN;
-        const int64_t row0 = (int64_t)lst[e] * L + k0;
-        copy_rows<D, THREADS, BN>(K + base + row0 * D, smem + buf * STAGE, valid, tid);
-        copy_rows<D, THREADS, BN>(V + base + row0 * D, smem + buf * STAGE + BLK, valid, tid);
+    const RowCopy<D, THREADS, BN> rc(tid);
+    ListWalk cw;                                    // next key block to copy
+    walk_init(cw, lst, cnt);
+    auto gload = [&](int buf) {
+        const int valid = L - cw.r0 < BN ? L - cw.r0 : BN;
+        const int64_t row0 = (int64_t)cw.tile * L + cw.r0;
+        rc.copy(K + base + row0 * D, valid, smem + buf * STAGE, wave);
+        rc.copy(V + base + row0 * D, valid, smem + buf * STAGE + BLK, wave);
+        walk_next(cw, lst, cnt, BN, L);
     };
 
     auto step = [&](auto bufc, int blk) {
         constexpr int BUF = decltype(bufc)::value;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (blk + 1 < nblk) gload(blk + 1, 1 - BUF);
+        if (blk + 1 < nblk) gload(1 - BUF);
         const __bf16 *Ks = smem + BUF * STAGE;
         const __bf16 *Vs = Ks + BLK;
-        const int k0 = (blk % nkb) * BN;
-        const int valid = L - k0 < BN ? L - k0 : BN;
 
         f32x16 s[KB], dp[KB];
 #pragma unroll
@@ -183,8 +235,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int r = 8 * hf + i;
-                    float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, nlse2));
-                    if (valid < BN && kb * 32 + mfma_row_sigma(lane, r) >= valid) p = 0.f;
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, nlse2));
                     v[i] = (__bf16)(p * (dp[kb][r] - dlt));
                 }
                 dsf[kb][hf] = v;
@@ -200,7 +251,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
                 }
     };
 
-    if (nblk > 0) gload(0, 0);
+    if (nblk > 0) gload(0);
     for (int blk = 0; blk < nblk; blk += 2) {
         step(std::integral_constant<int, 0>{}, blk);
         if (blk + 1 < nblk) step(std::integral_constant<int, 1>{}, blk + 1);
@@ -283,35 +334,35 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
         for (int hh = 0; hh < 2; ++hh)
             tofs[db][hh] = lds_at<D>(8 * grp + 4 * hh + vj, db * 32 + 16 * ((lane >> 4) & 1) + 4 * vc);
 
-    auto gload = [&](int blk, int buf) {
-        const int e = blk / nqb;
-        const int q0 = (blk - e * nqb) * BQ;
-        const int valid = L - q0 < BQ ? L - q0 : BQ;
-        const int64_t row0 = (int64_t)lst[e] * L + q0;
+    const RowCopy<D, THREADS, BQ> rc(tid);
+    ListWalk cw;                                    // next query block to copy
+    walk_init(cw, lst, cnt);
+    auto gload = [&](int buf) {
+        const int valid = L - cw.r0 < BQ ? L - cw.r0 : BQ;
+        const int64_t row0 = (int64_t)cw.tile * L + cw.r0;
         __bf16 *st = smem + buf * STAGE;
-        copy_rows<D, THREADS, BQ>(Q + base + row0 * D, st, valid, tid);
-        copy_rows<D, THREADS, BQ>(dO + base + row0 * D, st + BLK, valid, tid);
-        if (wave == 0) {
-            const int rr = lane < valid ? lane : valid - 1;
-            __builtin_amdgcn_global_load_lds((const void *)(LSE + sbase + row0 + rr),
-                                             (__attribute__((address_space(3))) void *)(st + 2 * BLK), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(Delta + sbase + row0 + rr),
-                                             (__attribute__((address_space(3))) void *)(st + 2 * BLK + 2 * SROWS), 4,
-                                             0, 0);
+        rc.copy(Q + base + row0 * D, valid, st, wave);
+        rc.copy(dO + base + row0 * D, valid, st + BLK, wave);
+        if (wave == 0) {                            // LSE and Delta of the block's rows (zero past the end)
+            const auto rl = make_rsrc(LSE + sbase + row0, valid * 4);
+            const auto rd = make_rsrc(Delta + sbase + row0, valid * 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void *)(st + 2 * BLK), 4,
+                                                     lane * 4, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rd, (__attribute__((address_space(3))) void *)(st + 2 * BLK + 2 * SROWS), 4, lane * 4, 0, 0, 0);
         }
+        walk_next(cw, lst, cnt, BQ, L);
     };
 
     auto step = [&](auto bufc, int blk) {
         constexpr int BUF = decltype(bufc)::value;
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (blk + 1 < nblk) gload(blk + 1, 1 - BUF);
+        if (blk + 1 < nblk) gload(1 - BUF);
         const __bf16 *Qs = smem + BUF * STAGE;
         const __bf16 *Os = Qs + BLK;
         const float *Ls = (const float *)(Qs + 2 * BLK);
         const float *Dl = Ls + SROWS;
-        const int q0 = (blk % nqb) * BQ;
-        const int valid = L - q0 < BQ ? L - q0 : BQ;
 
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) {
@@ -335,8 +386,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
                 for (int i = 0; i < 8; ++i) {
                     const float lse = i < 4 ? l0[i] : l1[i - 4];
                     const float dl = i < 4 ? d0[i] : d1[i - 4];
-                    float p = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + i], scale_log2, -lse * 1.4426950408889634f));
-                    if (valid < BQ && qr + i >= valid) p = 0.f;
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + i], scale_log2, -lse * 1.4426950408889634f));
                     pv[i] = (__bf16)p;
                     dv8[i] = (__bf16)(p * (dp[8 * kk + i] - dl));
                 }
@@ -354,7 +404,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
         }
     };
 
-    if (nblk > 0) gload(0, 0);
+    if (nblk > 0) gload(0);
     for (int blk = 0; blk < nblk; blk += 2) {
         step(std::integral_constant<int, 0>{}, blk);
         if (blk + 1 < nblk) step(std::integral_constant<int, 1>{}, blk + 1);
@@ -386,7 +436,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 #define STA_BWD_BN 64
 #endif
 #ifndef STA_BWD_BQ
-#define STA_BWD_BQ 64
+#define STA_BWD_BQ 32
 #endif
 
 template <int D>

@@ -148,12 +148,13 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes)
 }
 
 // Asynchronous 16-byte buffer -> LDS copy: lane l's 16 bytes at descriptor
-// offset voffset land at lds_base + 16*l (lds_base wave-uniform).  The
-// per-lane offset is a plain register that can stay loop-invariant.
-__device__ inline void b2lds16(__amdgpu_buffer_rsrc_t r, int voffset, void *lds_base)
+// offset voffset + soffset land at lds_base + 16*l (lds_base and soffset
+// wave-uniform).  The per-lane offset is a plain register that can stay
+// loop-invariant.
+__device__ inline void b2lds16(__amdgpu_buffer_rsrc_t r, int voffset, void *lds_base, int soffset = 0)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, voffset, 0, 0,
-                                             0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, voffset,
+                                             soffset, 0, 0);
 }
 
 // Packs element i of four 8-wide bf16 rows (as raw words) into 4 bf16
