@@ -17,6 +17,17 @@ backward 2.5x that, as the operator's "linear in sequence length" work.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 Prints ONE JSON line.
+
+HBM traffic of the attention kernels (roofline "traffic") comes from two
+rocprofv3 counter passes over this benchmark (FETCH_SIZE, then WRITE_SIZE),
+summarised into profiles/traffic.json by
+
+    python bench.py --write-traffic FETCH_CSV WRITE_CSV
+
+Each counter is scaled by what it reads for the raster->tile reorder kernel of
+the same step, a plain permutation copy whose bytes are known (every byte of
+its input read once and written once).  The summary records a digest of the
+kernel sources; when they change, "traffic" is reported as null.
 """
 import argparse
 import hashlib
@@ -34,7 +45,6 @@ METRIC = "effective attention TFLOP/s (unmasked tile pairs) + ms/layer, 115200-t
 PEAK_BF16_TFLOPS = 2516.6        # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 WORKLOAD = 5                     # the training workload of tests/inputs.py
-KEY_TILE_45 = 72                 # tile (1,1,2): exactly 45 query tiles attend it (the mean)
 
 
 def parse():
@@ -43,9 +53,20 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=320,
+    ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="query rows and key rows of the oracle sample (CPU baseline)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 --pmc counter_collection.csv files into profiles/traffic.json")
     return ap.parse_args()
+
+
+# Kernel name fragments (as rocprofv3 reports them) -> benchmark names, and
+# the sources each kernel is built from.
+KERNELS = {"fwd_bf16_kernel": "fwd", "dkdv_kernel": "bwd_dkdv", "dq_kernel": "bwd_dq"}
+KERNEL_SOURCES = {"fwd": ["fwd_bf16.hip", "mfma.h", "common.h"],
+                  "bwd_dkdv": ["bwd_bf16.hip", "mfma.h", "common.h"],
+                  "bwd_dq": ["bwd_bf16.hip", "mfma.h", "common.h"]}
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_sources_digest(names):
@@ -56,47 +77,96 @@ def kernel_sources_digest(names):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, per_launch_flop_digest):
+def measured_traffic(kernel):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        with open(path) as f:
+        with open(TRAFFIC_JSON) as f:
             rec = json.load(f).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_digest") != per_launch_flop_digest:
+    if not rec or rec.get("source_digest") != kernel_sources_digest(KERNEL_SOURCES[kernel]):
         return None
     return rec.get("bytes_per_launch")
+
+
+def write_traffic(fetch_csv, write_csv):
+    """profiles/traffic.json from the FETCH_SIZE and WRITE_SIZE passes (KiB
+    per dispatch), calibrated on the reorder kernel (a permutation copy)."""
+    import csv
+    import collections
+    from tests.inputs import CONFIGS
+
+    c = CONFIGS[WORKLOAD]
+    n = int(np.prod(c["grid"]))
+    copy_bytes = c["B"] * c["H"] * n * c["D"] * 2          # one reorder launch reads and writes this
+    means = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = collections.defaultdict(list)
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                key = "reorder" if "reorder_kernel" in name else next(
+                    (v for k, v in KERNELS.items() if k in name), None)
+                if key:
+                    vals[key].append(float(row["Counter_Value"]) * 1024.0)
+        means[counter] = {k: float(np.mean(v)) for k, v in vals.items()}
+    cal = {ctr: copy_bytes / means[ctr]["reorder"] for ctr in means}
+    out = {"_calibration": {"kernel": "reorder_kernel (raster <-> tile order copy)", "bytes_per_launch": copy_bytes,
+                            "FETCH_SIZE_bytes": means["FETCH_SIZE"]["reorder"],
+                            "WRITE_SIZE_bytes": means["WRITE_SIZE"]["reorder"],
+                            "fetch_factor": cal["FETCH_SIZE"], "write_factor": cal["WRITE_SIZE"]}}
+    for key in KERNELS.values():
+        fb = means["FETCH_SIZE"][key] * cal["FETCH_SIZE"]
+        wb = means["WRITE_SIZE"][key] * cal["WRITE_SIZE"]
+        out[key] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
+                    "source_digest": kernel_sources_digest(KERNEL_SOURCES[key])}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def cpu_baseline(w, rows):
     """The plain CPU oracle on a bounded sample of the same workload: forward
     and dQ for `rows` query rows plus dK/dV for `rows` key rows of head 0,
-    counted as `rows` rows of the training step."""
+    counted as `rows` rows of the training step.  Query rows are the first
+    rows (tile order) of the first query tiles; key rows those of the first
+    key tiles that exactly 45 query tiles attend, so every sampled row meets
+    45 tiles of keys (or queries), as the average row of the workload does."""
     from oracle import oracle    # test infrastructure: only this leg of the benchmark uses it
     B, H, N, D = w["q"].shape
     L = int(np.prod(w["tile"]))
+    oracle.load()
     inv = np.argsort(oracle.perm(w["grid"], w["tile"]))       # tile-order slot -> raster token
-    g = np.random.default_rng(7)
-    qrows = np.sort(inv[g.choice(L, rows, replace=False)])                      # query tile 0
-    krows = np.sort(inv[KEY_TILE_45 * L + g.choice(L, rows, replace=False)])    # 45 query tiles attend it
+    T = N // L
+    _, _, _, q_cnt = oracle.index(w["grid"], w["tile"], w["windows"][:1], None, T, T)[:4]
+    q_cnt = np.asarray(q_cnt)[0]
+    ktiles = np.flatnonzero(q_cnt == 45)
+    nt = -(-rows // L)
+    qslots = (np.arange(nt)[:, None] * L + np.arange(L)[None, :]).ravel()[:rows]
+    kslots = (ktiles[:nt, None] * L + np.arange(L)[None, :]).ravel()[:rows]
+    qrows, krows = np.sort(inv[qslots]), np.sort(inv[kslots])
     keys_per_row = 45 * L
     flop = rows * 3.5 * 4.0 * keys_per_row * D
-    oracle.load()
     t0 = time.perf_counter()
     oracle.fwd(w["q"], w["k"], w["v"], w["grid"], w["tile"], w["windows"], rows=qrows)
     oracle.bwd(w["q"], w["k"], w["v"], w["dout"], w["grid"], w["tile"], w["windows"], qrows=qrows, krows=krows)
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": "head 0: forward + dQ for %d query rows of query tile 0 and dK/dV for %d key rows of key "
-                      "tile %d (45 query tiles attend it), counted as %d training rows of 17280 keys each; "
-                      "%.1f s wall" % (rows, rows, KEY_TILE_45, rows, dt)}
+            "sample": "head 0: forward + dQ for %d query rows (query tiles 0..%d) and dK/dV for %d key rows (key "
+                      "tiles attended by 45 query tiles), counted as %d training rows of %d keys each; %.1f s wall"
+                      % (rows, nt - 1, rows, rows, keys_per_row, dt)}
 
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the sliding-tile attention path here has no multi-GPU "
               "mode (--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -180,10 +250,9 @@ def main():
     alg = {"fwd": fwd_flop, "bwd_dkdv": 2.0 * fwd_flop, "bwd_dq": 0.5 * fwd_flop}
     dominant = max(alg, key=lambda n: per[n])
     achieved = alg[dominant] / (per[dominant] * 1e-3) / 1e12
-    digest = kernel_sources_digest(["fwd_bf16.hip" if dominant == "fwd" else "bwd_bf16.hip", "mfma.h"])
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "kernel": dominant,
-                "traffic": measured_traffic(dominant, digest)}
+                "traffic": measured_traffic(dominant)}
 
     tensor_bytes = B * H * N * D * 2
     reorder_gbs = 3 * 2 * tensor_bytes / (per["reorder_qkv"] * 1e-3) / 1e9

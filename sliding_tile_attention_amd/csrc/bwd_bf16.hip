@@ -6,6 +6,8 @@
 // for Efficient Video Diffusion", abstract):
 //   P = exp(s - lse),  dP = dO V^T,  Delta = rowsum(dO o O),
 //   dS = P o (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+// P enters the products rounded to bf16; dK/dV also form dS from that
+// rounded P (dQ from the fp32 one).
 // Three kernels, no atomics, deterministic:
 //   1. bwd_pre: Delta_i = <dO_i, O_i> (fp32), one pass over O and dO.
 //   2. dq: query-stationary, walks each query tile's key-tile list (same
@@ -105,6 +107,33 @@ struct RowCopy {
     }
 };
 
+// NBUF-slot ring of LDS stages: block b lives in slot b mod NBUF and is
+// copied NBUF-1 blocks ahead.  At block blk a wave waits until its copies of
+// blk have landed (those of the NBUF-2 later blocks, PER copies each, may
+// still be in flight), then a fence-free barrier makes every wave's copies
+// visible and tells all waves that the slot of block blk-1 is free.
+template <int NBUF, int PER>
+__device__ inline void ring_wait(int blk, int nblk)
+{
+    static_assert(NBUF == 2 || NBUF == 3, "ring depth");
+    if constexpr (NBUF == 3) {
+        if (blk + 1 < nblk) wait_vmem<PER>();
+        else wait_vmem<0>();
+    } else {
+        wait_vmem<0>();
+    }
+    barrier_nofence();
+}
+
+template <int I, int N, typename F>
+__device__ inline void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
 // Position in a key- or query-tile list walked block by block (no
 // divisions); the next tile id is prefetched when a tile is entered.
 struct ListWalk {
@@ -128,7 +157,9 @@ __device__ inline void walk_next(ListWalk &w, const int32_t *lst, int cnt, int s
     }
 }
 
-// Element offset of logical (row r, column c) in a swizzled LDS tile.
+// Element offset of logical (row r, column c) in a swizzled LDS tile.  For
+// a column c + 8m whose extra granule bits m are disjoint from those of
+// c >> 3, the offset is lds_at(r, c) ^ (8m).
 template <int D>
 __device__ inline int lds_at(int r, int c)
 {
@@ -138,7 +169,7 @@ __device__ inline int lds_at(int r, int c)
 // ---------------------------------------------------------------------------
 // 2. dQ (query-stationary).
 // ---------------------------------------------------------------------------
-template <int D, int NW, int BN>
+template <int D, int NW, int BN, int NBUF>
 __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
@@ -147,7 +178,15 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
 {
     constexpr int THREADS = NW * 64, M = NW * 32, KS = D / 16, KB = BN / 32, DB = D / 32;
     constexpr int BLK = BN * D, STAGE = 2 * BLK;
-    __shared__ __attribute__((aligned(1024))) __bf16 smem[2 * STAGE];
+    // one array per ring slot: the compiler then sees that LDS reads of one
+    // slot never alias the copies in flight into another
+    __shared__ __attribute__((aligned(1024))) __bf16 slot0[STAGE], slot1[STAGE], slot2[NBUF > 2 ? STAGE : 1];
+    auto stage = [&](auto bc) -> __bf16 * {
+        constexpr int b = decltype(bc)::value;
+        if constexpr (b == 0) return slot0;
+        else if constexpr (b == 1) return slot1;
+        else return slot2;
+    };
 
     const int work = xcd_remap(blockIdx.x, total);
     const int rb = work % rblocks;
@@ -171,6 +210,9 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
     }
     const float nlse2 = -LSE[(int64_t)bh * g.N + grow] * 1.4426950408889634f;
     const float dlt = Delta[(int64_t)bh * g.N + grow];
+    // Q, dO, LSE, Delta complete before the first copy (later waits leave
+    // copies in flight, which would otherwise guard every use of them).
+    wait_vmem<0>();
 
     f32x16 acc[DB];
 #pragma unroll
@@ -183,36 +225,32 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
     const int nkb = (L + BN - 1) / BN;
     const int nblk = cnt * nkb;
 
-    const int arow = sigma32(l32);
-    int kofs[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kofs[ks] = lds_at<D>(arow, 16 * ks + 8 * grp);
+    // LDS offsets: a row's swizzle only XORs granule bits, and the granule
+    // bits that vary with the step (ks) or column block (db) sit above the
+    // lane's own, so every offset is one per-lane base XOR a constant.
+    const int kbase = lds_at<D>(sigma32(l32), 8 * grp);            // step ks: ^ 16*ks
     const int vj = (lane & 15) >> 2, vc = lane & 3;
-    // (the swizzle of row r depends on r mod 16, so each half has its own offset)
-    int tofs[DB][2];
+    // (the swizzle of row r depends on r mod 16, so each half has its own base)
+    int tbase[2];                                                   // column block db: ^ 32*db
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            tofs[db][hh] = lds_at<D>(8 * grp + 4 * hh + vj, db * 32 + 16 * ((lane >> 4) & 1) + 4 * vc);
+    for (int hh = 0; hh < 2; ++hh) tbase[hh] = lds_at<D>(8 * grp + 4 * hh + vj, 16 * ((lane >> 4) & 1) + 4 * vc);
 
     const RowCopy<D, THREADS, BN> rc(tid);
     ListWalk cw;                                    // next key block to copy
     walk_init(cw, lst, cnt);
-    auto gload = [&](int buf) {
+    auto gload = [&](auto bc) {
         const int valid = L - cw.r0 < BN ? L - cw.r0 : BN;
         const int64_t row0 = (int64_t)cw.tile * L + cw.r0;
-        rc.copy(K + base + row0 * D, valid, smem + buf * STAGE, wave);
-        rc.copy(V + base + row0 * D, valid, smem + buf * STAGE + BLK, wave);
+        rc.copy(K + base + row0 * D, valid, stage(bc), wave);
+        rc.copy(V + base + row0 * D, valid, stage(bc) + BLK, wave);
         walk_next(cw, lst, cnt, BN, L);
     };
 
     auto step = [&](auto bufc, int blk) {
         constexpr int BUF = decltype(bufc)::value;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (blk + 1 < nblk) gload(1 - BUF);
-        const __bf16 *Ks = smem + BUF * STAGE;
+        ring_wait<NBUF, 2 * decltype(rc)::COPIES>(blk, nblk);
+        if (blk + NBUF - 1 < nblk) gload(std::integral_constant<int, (BUF + NBUF - 1) % NBUF>{});
+        const __bf16 *Ks = stage(bufc);
         const __bf16 *Vs = Ks + BLK;
 
         f32x16 s[KB], dp[KB];
@@ -222,8 +260,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
             for (int r = 0; r < 16; ++r) { s[kb][r] = 0.f; dp[kb][r] = 0.f; }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                s[kb] = mfma32(ld8(Ks + kb * 32 * D + kofs[ks]), qf[ks], s[kb]);
-                dp[kb] = mfma32(ld8(Vs + kb * 32 * D + kofs[ks]), of[ks], dp[kb]);
+                s[kb] = mfma32(ld8(Ks + kb * 32 * D + (kbase ^ (16 * ks))), qf[ks], s[kb]);
+                dp[kb] = mfma32(ld8(Vs + kb * 32 * D + (kbase ^ (16 * ks))), of[ks], dp[kb]);
             }
         }
         bf16x8 dsf[KB][2];
@@ -247,15 +285,18 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     const __bf16 *kp = Ks + (kb * 32 + kk * 16) * D;
-                    acc[db] = mfma32(cat8(ld_tr4(kp + tofs[db][0]), ld_tr4(kp + tofs[db][1])), dsf[kb][kk], acc[db]);
+                    acc[db] = mfma32(cat8(ld_tr4(kp + (tbase[0] ^ (32 * db))), ld_tr4(kp + (tbase[1] ^ (32 * db)))),
+                                     dsf[kb][kk], acc[db]);
                 }
     };
 
-    if (nblk > 0) gload(0);
-    for (int blk = 0; blk < nblk; blk += 2) {
-        step(std::integral_constant<int, 0>{}, blk);
-        if (blk + 1 < nblk) step(std::integral_constant<int, 1>{}, blk + 1);
-    }
+    static_for<0, NBUF - 1>([&](auto bc) {
+        if ((int)decltype(bc)::value < nblk) gload(bc);
+    });
+    for (int blk = 0; blk < nblk; blk += NBUF)
+        static_for<0, NBUF>([&](auto bc) {
+            if (blk + (int)decltype(bc)::value < nblk) step(bc, blk + (int)decltype(bc)::value);
+        });
 
     if (row_ok) {
         __bf16 *op = dQ + base + ((int64_t)qt * L + row) * D;
@@ -274,7 +315,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
 // ---------------------------------------------------------------------------
 // 3. dK, dV (key-stationary, over the transposed lists).
 // ---------------------------------------------------------------------------
-template <int D, int NW, int BQ>
+template <int D, int NW, int BQ, int NBUF>
 __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
@@ -287,7 +328,13 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     constexpr int SROWS = BQ > 64 ? BQ : 64;        // LSE / Delta slots (one 64-lane dword copy each)
     constexpr int STAGE = 2 * BLK + 2 * SROWS * 2;  // Q, dO (bf16) + LSE, Delta (fp32 as 2 bf16 slots each)
     static_assert(BQ <= 64 && BQ % 32 == 0, "query block of 32 or 64 rows");
-    __shared__ __attribute__((aligned(1024))) __bf16 smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) __bf16 slot0[STAGE], slot1[STAGE], slot2[NBUF > 2 ? STAGE : 1];
+    auto stage = [&](auto bc) -> __bf16 * {
+        constexpr int b = decltype(bc)::value;
+        if constexpr (b == 0) return slot0;
+        else if constexpr (b == 1) return slot1;
+        else return slot2;
+    };
 
     const int work = xcd_remap(blockIdx.x, total);
     const int rb = work % rblocks;
@@ -310,6 +357,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
         kf[ks] = ld8(K + base + gk * D + ks * 16 + grp * 8);
         vf[ks] = ld8(V + base + gk * D + ks * 16 + grp * 8);
     }
+    wait_vmem<0>();          // K, V complete before the first copy (see dq_kernel)
     f32x16 dk[DB], dv[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -321,26 +369,23 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     const int nqb = (L + BQ - 1) / BQ;
     const int nblk = cnt * nqb;
 
-    const int arow = sigma32(l32);
-    int aofs[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) aofs[ks] = lds_at<D>(arow, 16 * ks + 8 * grp);
+    // LDS offsets: a row's swizzle only XORs granule bits, and the granule
+    // bits that vary with the step (ks) or column block (db) sit above the
+    // lane's own, so every offset is one per-lane base XOR a constant.
+    const int kbase = lds_at<D>(sigma32(l32), 8 * grp);            // step ks: ^ 16*ks
     const int vj = (lane & 15) >> 2, vc = lane & 3;
-    // (the swizzle of row r depends on r mod 16, so each half has its own offset)
-    int tofs[DB][2];
+    // (the swizzle of row r depends on r mod 16, so each half has its own base)
+    int tbase[2];                                                   // column block db: ^ 32*db
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-            tofs[db][hh] = lds_at<D>(8 * grp + 4 * hh + vj, db * 32 + 16 * ((lane >> 4) & 1) + 4 * vc);
+    for (int hh = 0; hh < 2; ++hh) tbase[hh] = lds_at<D>(8 * grp + 4 * hh + vj, 16 * ((lane >> 4) & 1) + 4 * vc);
 
     const RowCopy<D, THREADS, BQ> rc(tid);
     ListWalk cw;                                    // next query block to copy
     walk_init(cw, lst, cnt);
-    auto gload = [&](int buf) {
+    auto gload = [&](auto bc) {
         const int valid = L - cw.r0 < BQ ? L - cw.r0 : BQ;
         const int64_t row0 = (int64_t)cw.tile * L + cw.r0;
-        __bf16 *st = smem + buf * STAGE;
+        __bf16 *st = stage(bc);
         rc.copy(Q + base + row0 * D, valid, st, wave);
         rc.copy(dO + base + row0 * D, valid, st + BLK, wave);
         if (wave == 0) {                            // LSE and Delta of the block's rows (zero past the end)
@@ -356,41 +401,58 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 
     auto step = [&](auto bufc, int blk) {
         constexpr int BUF = decltype(bufc)::value;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (blk + 1 < nblk) gload(1 - BUF);
-        const __bf16 *Qs = smem + BUF * STAGE;
+        if (wave == 0)
+            ring_wait<NBUF, 2 * decltype(rc)::COPIES + 2>(blk, nblk);
+        else
+            ring_wait<NBUF, 2 * decltype(rc)::COPIES>(blk, nblk);
+        if (blk + NBUF - 1 < nblk) gload(std::integral_constant<int, (BUF + NBUF - 1) % NBUF>{});
+        // keep the per-step offsets (base ^ constant) from being hoisted
+        // into registers of their own for the whole loop
+        int kb_ = kbase, tb0 = tbase[0], tb1 = tbase[1];
+        asm volatile("" : "+v"(kb_), "+v"(tb0), "+v"(tb1));
+        const __bf16 *Qs = stage(bufc);
         const __bf16 *Os = Qs + BLK;
         const float *Ls = (const float *)(Qs + 2 * BLK);
         const float *Dl = Ls + SROWS;
 
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) {
-            f32x16 s, dp;
+            // S, then P (rounded to bf16: the dV operand), then dP and
+            // dS = P (dP - Delta) from the same rounded P, so that S and dP
+            // are never live together.
+            // Registers 8kk..8kk+7 hold query rows sb*32 + 16kk + 8grp + 0..7.
+            f32x16 acc;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s = mfma32(ld8(Qs + sb * 32 * D + aofs[ks]), kf[ks], s);
-                dp = mfma32(ld8(Os + sb * 32 * D + aofs[ks]), vf[ks], dp);
-            }
-            // registers 8kk..8kk+7 hold query rows sb*32 + 16kk + 8grp + 0..7
+            for (int ks = 0; ks < KS; ++ks) acc = mfma32(ld8(Qs + sb * 32 * D + (kb_ ^ (16 * ks))), kf[ks], acc);
             bf16x8 pf[2], dsf[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const int qr = sb * 32 + 16 * kk + 8 * grp;
                 const f32x4 l0 = *(const f32x4 *)(Ls + qr), l1 = *(const f32x4 *)(Ls + qr + 4);
-                const f32x4 d0 = *(const f32x4 *)(Dl + qr), d1 = *(const f32x4 *)(Dl + qr + 4);
-                bf16x8 pv, dv8;
+                bf16x8 pv;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float lse = i < 4 ? l0[i] : l1[i - 4];
-                    const float dl = i < 4 ? d0[i] : d1[i - 4];
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + i], scale_log2, -lse * 1.4426950408889634f));
-                    pv[i] = (__bf16)p;
-                    dv8[i] = (__bf16)(p * (dp[8 * kk + i] - dl));
+                    pv[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc[8 * kk + i], scale_log2, -lse * 1.4426950408889634f));
                 }
                 pf[kk] = pv;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc = mfma32(ld8(Os + sb * 32 * D + (kb_ ^ (16 * ks))), vf[ks], acc);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int qr = sb * 32 + 16 * kk + 8 * grp;
+                const f32x4 d0 = *(const f32x4 *)(Dl + qr), d1 = *(const f32x4 *)(Dl + qr + 4);
+                bf16x8 dv8;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float dl = i < 4 ? d0[i] : d1[i - 4];
+                    dv8[i] = (__bf16)((float)pf[kk][i] * (acc[8 * kk + i] - dl));
+                }
                 dsf[kk] = dv8;
             }
 #pragma unroll
@@ -398,17 +460,20 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     const int off = (sb * 32 + kk * 16) * D;
-                    dv[db] = mfma32(pf[kk], cat8(ld_tr4(Os + off + tofs[db][0]), ld_tr4(Os + off + tofs[db][1])), dv[db]);
-                    dk[db] = mfma32(dsf[kk], cat8(ld_tr4(Qs + off + tofs[db][0]), ld_tr4(Qs + off + tofs[db][1])), dk[db]);
+                    const int t0 = tb0 ^ (32 * db), t1 = tb1 ^ (32 * db);
+                    dv[db] = mfma32(pf[kk], cat8(ld_tr4(Os + off + t0), ld_tr4(Os + off + t1)), dv[db]);
+                    dk[db] = mfma32(dsf[kk], cat8(ld_tr4(Qs + off + t0), ld_tr4(Qs + off + t1)), dk[db]);
                 }
         }
     };
 
-    if (nblk > 0) gload(0);
-    for (int blk = 0; blk < nblk; blk += 2) {
-        step(std::integral_constant<int, 0>{}, blk);
-        if (blk + 1 < nblk) step(std::integral_constant<int, 1>{}, blk + 1);
-    }
+    static_for<0, NBUF - 1>([&](auto bc) {
+        if ((int)decltype(bc)::value < nblk) gload(bc);
+    });
+    for (int blk = 0; blk < nblk; blk += NBUF)
+        static_for<0, NBUF>([&](auto bc) {
+            if (blk + (int)decltype(bc)::value < nblk) step(bc, blk + (int)decltype(bc)::value);
+        });
 
     // lane holds column d = 32*db + l%32 of key rows 8*(r/4) + 4*grp + r%4.
 #pragma unroll
@@ -428,12 +493,16 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 // ---------------------------------------------------------------------------
 
 // Tile shapes (overridable at compile time for tuning sweeps): waves per
-// workgroup, keys per block in dQ, query rows per block in dK/dV.
+// workgroup, keys per block in dQ, query rows per block in dK/dV, LDS ring
+// depth.
 #ifndef STA_BWD_NW
 #define STA_BWD_NW 4
 #endif
+#ifndef STA_BWD_NBUF
+#define STA_BWD_NBUF 2
+#endif
 #ifndef STA_BWD_BN
-#define STA_BWD_BN 64
+#define STA_BWD_BN 32
 #endif
 #ifndef STA_BWD_BQ
 #define STA_BWD_BQ 32
@@ -461,13 +530,13 @@ static sta_status run_bwd(const void *q, const void *k, const void *v, const voi
         if ((st = check_launch()) != STA_OK) return st;
     }
     if (parts & STA_BWD_DKDV) {
-        hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
+        hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ, STA_BWD_NBUF>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
                            (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q, H, g,
                            rblocks, (int)total, scale_log2, scale);
         if ((st = check_launch()) != STA_OK) return st;
     }
     if (parts & STA_BWD_DQ) {
-        hipLaunchKernelGGL((dq_kernel<D, NW, BN>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
+        hipLaunchKernelGGL((dq_kernel<D, NW, BN, STA_BWD_NBUF>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
                            (const float *)delta, (__bf16 *)dq, idx.kv_idx, idx.kv_cnt, idx.max_kv, H, g, rblocks,
                            (int)total, scale_log2, scale);
         if ((st = check_launch()) != STA_OK) return st;
