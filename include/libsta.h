@@ -27,8 +27,9 @@
  *                    L = tt*th*tw tokens per tile.
  *
  * Conventions for every call:
- *   - All tensor pointers are DEVICE pointers owned by the caller; the
- *     library never allocates, frees, synchronises or prints.
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never synchronises or prints; the only memory it obtains is
+ *     the stream-ordered workspace of the bf16 forward (see sta_fwd).
  *   - Work is enqueued on the given HIP stream (0 = the null stream) and
  *     is asynchronous; device faults surface at the caller's next sync.
  *   - Arguments are checked on the host before anything is launched: on
@@ -152,6 +153,14 @@ sta_status sta_build_index(const sta_geom *g, int32_t H, const sta_dim3 *windows
  * q, k, v, o: [B][H][N][D] in tile order; lse: [B][H][N] fp32 in tile
  * order.  D must be 64 or 128.  bf16 uses MFMA with fp32 accumulation; the
  * probabilities are rounded to bf16 before the PV product.
+ * Workspace (bf16 only): the call first writes V transposed per tile,
+ * B*H*num_tiles*D*Lp*2 bytes with Lp = L rounded up to a multiple of 64,
+ * into memory taken from a per-device pool on `stream` and given back on
+ * `stream` after the attention kernel (hipMallocFromPoolAsync /
+ * hipFreeAsync).  The pool keeps freed memory for reuse, so repeated calls
+ * of one shape reach the driver only once; it holds at most the largest
+ * concurrently used workspaces until the process ends.  A failed
+ * allocation returns STA_ERR_HIP before anything is launched.
  * Source: attention restricted to the sliding 3D window ("Fast Video
  * Generation with Sliding Tile Attention", abstract).
  */
