@@ -158,8 +158,39 @@ def cpu_baseline(w, rows):
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": "head 0: forward + dQ for %d query rows (query tiles 0..%d) and dK/dV for %d key rows (key "
-                      "tiles attended by 45 query tiles), counted as %d training rows of %d keys each; %.1f s wall"
-                      % (rows, nt - 1, rows, rows, keys_per_row, dt)}
+                      "tiles attended by 45 query tiles), counted as %d training rows of %d keys each; %.1f s wall "
+                      "on %s" % (rows, nt - 1, rows, rows, keys_per_row, dt, cpu_model())}
+
+
+def gemm_ceiling(torch, dev, n=8192, reps=10):
+    """Attainable dense bf16 rate on this GPU: a large square torch.matmul
+    (hipBLASLt), as a measured ceiling beside the published peak."""
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(2):
+        torch.matmul(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return {"value": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s",
+            "what": "bf16 %dx%dx%d torch.matmul (hipBLASLt), mean of %d" % (n, n, n, reps)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -252,7 +283,8 @@ def main():
     achieved = alg[dominant] / (per[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "kernel": dominant,
-                "traffic": measured_traffic(dominant)}
+                "traffic": measured_traffic(dominant),
+                "measured_gemm_ceiling": gemm_ceiling(torch, dev)}
 
     tensor_bytes = B * H * N * D * 2
     reorder_gbs = 3 * 2 * tensor_bytes / (per["reorder_qkv"] * 1e-3) / 1e9

@@ -102,3 +102,34 @@ def test_fwd_720p_sampled(cfg):
     assert_close(to_host(o), ro, "bf16", "O")
     assert_lse(to_host(lse.reshape(-1)[torch.from_numpy(rows).cuda()]), rl, "bf16")
     assert torch.isfinite(layer.o).all()
+
+
+def test_fwd_workspace_reuse_and_streams():
+    """The bf16 forward takes its V^T workspace from a stream-ordered pool:
+    interleaved calls of two shapes (the pool hands memory back and forth),
+    and a call on a second stream, must give bit-identical results to the
+    first call of each shape (the kernels are deterministic), and that first
+    call matches the oracle."""
+    say("fwd bf16 workspace reuse / streams")
+    shapes = [((4, 8, 12), (2, 4, 4), 1, 2, 128, [(3, 3, 3), (1, 3, 3)]),
+              ((6, 8, 8), (3, 4, 4), 2, 1, 128, [(3, 3, 3)])]
+    layers, firsts = [], []
+    for i, (grid, tile, B, H, D, windows) in enumerate(shapes):
+        q, k, v = tensors(B, H, int(np.prod(grid)), D, "bf16", 300 + i)
+        layer = Layer(grid, tile, windows, None, q, k, v, "bf16")
+        o, lse = layer.forward()
+        torch.cuda.synchronize()
+        ro, rl = oracle.fwd(q, k, v, grid, tile, windows)
+        assert_close(to_host(o), ro, "bf16", "first call O")
+        layers.append(layer)
+        firsts.append((o.clone(), lse.clone()))
+    for rep in range(3):
+        for layer, (o0, l0) in zip(layers, firsts):
+            o, lse = layer.forward()
+            assert torch.equal(o, o0) and torch.equal(lse, l0), "repeat %d differs" % rep
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        outs = [layer.forward() for layer in layers]
+    side.synchronize()
+    for (o, lse), (o0, l0) in zip(outs, firsts):
+        assert torch.equal(o, o0) and torch.equal(lse, l0), "second stream differs"
