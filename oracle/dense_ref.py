@@ -9,7 +9,9 @@ different route:
   formula: among every placement [s, s+c) of a c-tile window that fits the
   axis, take the one whose start is closest to the centred start
   q + o - floor(w/2) (the projection of a point onto an interval is
-  unique, so there is exactly one);
+  unique, so there is exactly one); under the truncating border rule, the
+  centre is the grid tile nearest to q + o and the window is the set of
+  tiles within -floor(w/2) .. w-1-floor(w/2) of it;
 * the token mask is an explicit N x N boolean matrix built from token
   coordinates;
 * attention itself is a library routine (``torch.nn.functional.
@@ -39,8 +41,18 @@ def window_by_enumeration(n, w, q, o=0):
     return best[1], c
 
 
-def token_mask(grid, tile, window, offsets=None):
-    """[N, N] bool: mask[i, j] is True when key token j may be attended by query token i."""
+def window_truncated_by_enumeration(n, w, q, o=0):
+    """Start and count under the truncating border rule, by enumeration:
+    the centre is the grid tile nearest to q + o, and the window is every
+    tile k of the axis with -floor(w/2) <= k - centre <= w - 1 - floor(w/2)."""
+    centre = min(range(n), key=lambda c: abs(c - (q + o)))
+    members = [k for k in range(n) if -(w // 2) <= k - centre <= w - 1 - w // 2]
+    return members[0], len(members)
+
+
+def token_mask(grid, tile, window, offsets=None, border="shift"):
+    """[N, N] bool: mask[i, j] is True when key token j may be attended by
+    query token i.  offsets: None or [T, 3] (one shift per query tile)."""
     T_, H_, W_ = grid
     nt = [g // t for g, t in zip(grid, tile)]
     coords = np.array(list(itertools.product(range(T_), range(H_), range(W_))))  # raster order
@@ -52,7 +64,8 @@ def token_mask(grid, tile, window, offsets=None):
     for i in range(N):
         o = (0, 0, 0) if offsets is None else offsets[tid[i]]
         for d in range(3):
-            s, c = window_by_enumeration(nt[d], window[d], int(tc[i, d]), int(o[d]))
+            rule = window_truncated_by_enumeration if border == "truncate" else window_by_enumeration
+            s, c = rule(nt[d], window[d], int(tc[i, d]), int(o[d]))
             lo[i, d], hi[i, d] = s, s + c
     m = np.ones((N, N), bool)
     for d in range(3):
@@ -60,15 +73,19 @@ def token_mask(grid, tile, window, offsets=None):
     return m
 
 
-def attention(q, k, v, grid, tile, windows, offsets=None, scale=None, dout=None):
-    """q,k,v: float arrays [B,H,N,D] in raster order.  Returns float64 numpy
+def attention(q, k, v, grid, tile, windows, offsets=None, scale=None, dout=None, border="shift"):
+    """q,k,v: float arrays [B,H,N,D] in raster order.  offsets: None, [T, 3]
+    (shared by heads) or [H, T, 3] (one set per head).  Returns float64 numpy
     (o, lse) and, with dout given, also (dq, dk, dv)."""
     q = torch.tensor(np.asarray(q), dtype=torch.float64)
     k = torch.tensor(np.asarray(k), dtype=torch.float64)
     v = torch.tensor(np.asarray(v), dtype=torch.float64)
     B, H, N, D = q.shape
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
-    masks = torch.stack([torch.from_numpy(token_mask(grid, tile, windows[h], offsets)) for h in range(H)])
+    per_head = offsets is not None and np.asarray(offsets).ndim == 3
+    masks = torch.stack([torch.from_numpy(token_mask(grid, tile, windows[h],
+                                                     np.asarray(offsets)[h] if per_head else offsets, border))
+                         for h in range(H)])
     want_grad = dout is not None
     for t in (q, k, v):
         t.requires_grad_(want_grad)

@@ -8,6 +8,11 @@ All tensors here are numpy arrays in RASTER token order (t slowest, w
 fastest), shaped [B, H, N, D]; floating inputs are float32 and outputs are
 float64.  Row ids passed to ``fwd``/``bwd`` are flat ``(b*H + h)*N + i``
 with ``i`` a raster token index.
+
+Window options (the 3D-DSA variants): ``border="truncate"`` selects the
+truncating border rule instead of the inward shift, and ``offsets`` may be
+[T, 3] (one shift per query tile, shared by heads) or [H, T, 3] (one per
+head and query tile).
 """
 import ctypes
 import os
@@ -45,13 +50,13 @@ def load(path=None):
     f64p = ctypes.POINTER(ctypes.c_double)
     lib.oracle_perm.argtypes = [i32p, i32p, i64p]
     lib.oracle_perm.restype = ctypes.c_int
-    lib.oracle_index.argtypes = [i32p, i32p, ctypes.c_int, i32p, i32p,
+    lib.oracle_index.argtypes = [i32p, i32p, ctypes.c_int, i32p, i32p, ctypes.c_int,
                                  ctypes.c_int, i32p, i32p, ctypes.c_int, i32p, i32p]
     lib.oracle_index.restype = ctypes.c_int
-    lib.oracle_fwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, i32p, i32p, i32p,
+    lib.oracle_fwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, i32p, i32p, i32p, ctypes.c_int,
                                ctypes.c_double, f32p, f32p, f32p, ctypes.c_int64, i64p, f64p, f64p]
     lib.oracle_fwd.restype = ctypes.c_int
-    lib.oracle_bwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, i32p, i32p, i32p,
+    lib.oracle_bwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, i32p, i32p, i32p, ctypes.c_int,
                                ctypes.c_double, f32p, f32p, f32p, f32p,
                                ctypes.c_int64, i64p, f64p, ctypes.c_int64, i64p, f64p, f64p]
     lib.oracle_bwd.restype = ctypes.c_int
@@ -91,6 +96,24 @@ def tiles_per_axis(grid, tile):
     return tuple(g // t for g, t in zip(grid, tile))
 
 
+_TRUNCATE, _HEAD_OFFS = 1, 2
+
+
+def _window_opts(offsets, H, T, border):
+    """(offsets as a contiguous int32 array or None, flags)."""
+    if border not in ("shift", "truncate"):
+        raise ValueError("border must be 'shift' or 'truncate'")
+    flags = _TRUNCATE if border == "truncate" else 0
+    if offsets is None:
+        return None, flags
+    off = _i32(offsets)
+    if off.ndim == 3:
+        if off.shape != (H, T, 3):
+            raise ValueError("per-head offsets must be [H, T, 3]")
+        return off, flags | _HEAD_OFFS
+    return off.reshape(T, 3), flags
+
+
 def perm(grid, tile):
     """perm[r] = tile-contiguous position of raster token r."""
     lib = _load()
@@ -102,7 +125,7 @@ def perm(grid, tile):
     return out
 
 
-def index(grid, tile, windows, offsets=None, max_kv=None, max_q=None):
+def index(grid, tile, windows, offsets=None, max_kv=None, max_q=None, border="shift"):
     """Block-sparse lists: (kv_idx [H,T,max_kv], kv_cnt [H,T], q_idx [H,T,max_q], q_cnt [H,T])."""
     lib = _load()
     windows = _i32(windows).reshape(-1, 3)
@@ -114,9 +137,9 @@ def index(grid, tile, windows, offsets=None, max_kv=None, max_q=None):
     kv_cnt = np.empty((H, T), np.int32)
     q_idx = np.empty((H, T, max_q), np.int32)
     q_cnt = np.empty((H, T), np.int32)
-    off = None if offsets is None else _i32(offsets).reshape(T, 3)
+    off, flags = _window_opts(offsets, H, T, border)
     ok = lib.oracle_index(_ptr(_i32(grid), ctypes.c_int32), _ptr(_i32(tile), ctypes.c_int32), H,
-                          _ptr(windows, ctypes.c_int32), _ptr(off, ctypes.c_int32),
+                          _ptr(windows, ctypes.c_int32), _ptr(off, ctypes.c_int32), flags,
                           max_kv, _ptr(kv_idx, ctypes.c_int32), _ptr(kv_cnt, ctypes.c_int32),
                           max_q, _ptr(q_idx, ctypes.c_int32), _ptr(q_cnt, ctypes.c_int32))
     if not ok:
@@ -130,7 +153,7 @@ def _rows(rows, total):
     return np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
 
 
-def fwd(q, k, v, grid, tile, windows, offsets=None, scale=None, rows=None):
+def fwd(q, k, v, grid, tile, windows, offsets=None, scale=None, rows=None, border="shift"):
     """Forward rows: returns (o [n_rows, D], lse [n_rows]) in float64.
     With rows=None every row is computed and o is reshaped to [B,H,N,D]."""
     lib = _load()
@@ -140,12 +163,12 @@ def fwd(q, k, v, grid, tile, windows, offsets=None, scale=None, rows=None):
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     windows = _i32(windows).reshape(H, 3)
     T = int(np.prod(tiles_per_axis(grid, tile)))
-    off = None if offsets is None else _i32(offsets).reshape(T, 3)
+    off, flags = _window_opts(offsets, H, T, border)
     r = _rows(rows, B * H * N)
     o = np.empty((len(r), D), np.float64)
     lse = np.empty(len(r), np.float64)
     ok = lib.oracle_fwd(B, H, D, _ptr(_i32(grid), ctypes.c_int32), _ptr(_i32(tile), ctypes.c_int32),
-                        _ptr(windows, ctypes.c_int32), _ptr(off, ctypes.c_int32), scale,
+                        _ptr(windows, ctypes.c_int32), _ptr(off, ctypes.c_int32), flags, scale,
                         _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
                         len(r), _ptr(r, ctypes.c_int64), _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
     if not ok:
@@ -155,7 +178,7 @@ def fwd(q, k, v, grid, tile, windows, offsets=None, scale=None, rows=None):
     return o, lse
 
 
-def bwd(q, k, v, dout, grid, tile, windows, offsets=None, scale=None, qrows=None, krows=None):
+def bwd(q, k, v, dout, grid, tile, windows, offsets=None, scale=None, qrows=None, krows=None, border="shift"):
     """Backward rows: returns (dq [n_q, D], dk [n_k, D], dv [n_k, D]) in float64.
     With qrows=None and krows=None everything is computed, shaped [B,H,N,D]."""
     lib = _load()
@@ -164,7 +187,7 @@ def bwd(q, k, v, dout, grid, tile, windows, offsets=None, scale=None, qrows=None
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     windows = _i32(windows).reshape(H, 3)
     T = int(np.prod(tiles_per_axis(grid, tile)))
-    off = None if offsets is None else _i32(offsets).reshape(T, 3)
+    off, flags = _window_opts(offsets, H, T, border)
     full = qrows is None and krows is None
     qr = _rows(qrows, B * H * N) if (qrows is not None or full) else np.zeros(0, np.int64)
     kr = _rows(krows, B * H * N) if (krows is not None or full) else np.zeros(0, np.int64)
@@ -172,7 +195,7 @@ def bwd(q, k, v, dout, grid, tile, windows, offsets=None, scale=None, qrows=None
     dk = np.empty((len(kr), D), np.float64)
     dv = np.empty((len(kr), D), np.float64)
     ok = lib.oracle_bwd(B, H, D, _ptr(_i32(grid), ctypes.c_int32), _ptr(_i32(tile), ctypes.c_int32),
-                        _ptr(windows, ctypes.c_int32), _ptr(off, ctypes.c_int32), scale,
+                        _ptr(windows, ctypes.c_int32), _ptr(off, ctypes.c_int32), flags, scale,
                         _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
                         _ptr(dout, ctypes.c_float),
                         len(qr), _ptr(qr, ctypes.c_int64), _ptr(dq, ctypes.c_double),

@@ -28,6 +28,15 @@
  *   R3 window start = q + o - floor(w/2) before clamping (even w leans low).
  *   R4 offsets are integer tile units, one (dt,dh,dw) per query tile, shared
  *      by all heads and batch items, added before clamping.
+ *   Options (the `flags` argument of the entry points), for the NEXT-ranked
+ *   3D-DSA variants (motion-adaptive windows are not pinned by the pages):
+ *   ORACLE_TRUNCATE  border rule instead of R1: per axis the shifted centre
+ *                    q + o is clamped into [0, n-1] and the window
+ *                    [centre - floor(w/2), centre - floor(w/2) + w - 1] is
+ *                    cut at the grid border (so it always holds the clamped
+ *                    centre and is never empty).
+ *   ORACLE_HEAD_OFFS offsets are [H][T][3], one shift per head and query tile
+ *                    (batch items still share them).
  *   R6 raster order everywhere: t slowest, w fastest (tokens, tiles and the
  *      position inside a tile).
  *   R8 softmax scale is an argument (1/sqrt(D) in every workload).
@@ -40,6 +49,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+#define ORACLE_TRUNCATE 1
+#define ORACLE_HEAD_OFFS 2
 
 /* ------------------------------------------------------------------ */
 /* Geometry                                                            */
@@ -59,19 +71,39 @@ static int tiles_per_axis(const int grid[3], const int tile[3], int n[3])
 
 /* The window of query tile qc (tile coordinates) for window size win and
  * optional offset off: per axis the start s and count c of the allowed
- * tile range [s, s+c).  Readings R1-R4. */
+ * tile range [s, s+c).  Readings R1-R4, or the truncating border rule. */
 static void window_of(const int n[3], const int win[3], const int qc[3],
-                      const int *off, int s[3], int c[3])
+                      const int *off, int truncate, int s[3], int c[3])
 {
     for (int d = 0; d < 3; ++d) {
-        int cnt = win[d] < n[d] ? win[d] : n[d];     /* R2 */
         int o = off ? off[d] : 0;                    /* R4 */
-        int start = qc[d] + o - win[d] / 2;          /* R3 */
-        if (start < 0) start = 0;                    /* R1 */
-        if (start > n[d] - cnt) start = n[d] - cnt;  /* R1 */
-        s[d] = start;
-        c[d] = cnt;
+        if (truncate) {
+            int centre = qc[d] + o;
+            if (centre < 0) centre = 0;
+            if (centre > n[d] - 1) centre = n[d] - 1;
+            int lo = centre - win[d] / 2;
+            int hi = lo + win[d] - 1;
+            if (lo < 0) lo = 0;
+            if (hi > n[d] - 1) hi = n[d] - 1;
+            s[d] = lo;
+            c[d] = hi - lo + 1;
+        } else {
+            int cnt = win[d] < n[d] ? win[d] : n[d];     /* R2 */
+            int start = qc[d] + o - win[d] / 2;          /* R3 */
+            if (start < 0) start = 0;                    /* R1 */
+            if (start > n[d] - cnt) start = n[d] - cnt;  /* R1 */
+            s[d] = start;
+            c[d] = cnt;
+        }
     }
+}
+
+/* Offset triple of query tile q under head h (or NULL). */
+static const int *offset_of(const int *offsets, int flags, int h, int T, int q)
+{
+    if (!offsets)
+        return NULL;
+    return offsets + 3 * ((int64_t)((flags & ORACLE_HEAD_OFFS) ? h * T : 0) + q);
 }
 
 static void tile_coords(int id, const int n[3], int tc[3])
@@ -133,10 +165,10 @@ int oracle_perm(const int grid[3], const int tile[3], int64_t *perm)
  * the transposed lists: for every key tile k, the ascending query tiles q
  * whose window holds k (q_idx[h][k][0..q_cnt), padded -1 to max_q).
  * Brute force over all (q, k) pairs.  Returns 0 if a list would not fit or
- * the geometry is invalid, else 1.  windows: [H][3]; offsets: [T][3] or
- * NULL. */
+ * the geometry is invalid, else 1.  windows: [H][3]; offsets: [T][3] (or
+ * [H][T][3] with ORACLE_HEAD_OFFS) or NULL. */
 int oracle_index(const int grid[3], const int tile[3], int H,
-                 const int *windows, const int *offsets,
+                 const int *windows, const int *offsets, int flags,
                  int max_kv, int32_t *kv_idx, int32_t *kv_cnt,
                  int max_q, int32_t *q_idx, int32_t *q_cnt)
 {
@@ -149,7 +181,7 @@ int oracle_index(const int grid[3], const int tile[3], int H,
         for (int q = 0; q < T; ++q) {
             int qc[3], s[3], c[3], cnt = 0;
             tile_coords(q, n, qc);
-            window_of(n, win, qc, offsets ? offsets + 3 * q : NULL, s, c);
+            window_of(n, win, qc, offset_of(offsets, flags, h, T, q), flags & ORACLE_TRUNCATE, s, c);
             int32_t *row = kv_idx + ((int64_t)h * T + q) * max_kv;
             for (int j = 0; j < max_kv; ++j) row[j] = -1;
             for (int k = 0; k < T; ++k) {
@@ -170,7 +202,7 @@ int oracle_index(const int grid[3], const int tile[3], int H,
             for (int q = 0; q < T; ++q) {
                 int qc[3], s[3], c[3];
                 tile_coords(q, n, qc);
-                window_of(n, win, qc, offsets ? offsets + 3 * q : NULL, s, c);
+                window_of(n, win, qc, offset_of(offsets, flags, h, T, q), flags & ORACLE_TRUNCATE, s, c);
                 if (tile_in_window(kc, s, c)) {
                     if (cnt >= max_q) return 0;
                     row[cnt++] = q;
@@ -192,12 +224,13 @@ typedef struct {
     int64_t N;
     const float *q, *k, *v, *dout;   /* [B][H][N][D], raster token order */
     const int *windows, *offsets;
+    int flags;
     double scale;
 } problem;
 
 static int make_problem(problem *p, int B, int H, int D, const int grid[3],
                         const int tile[3], const int *windows, const int *offsets,
-                        double scale, const float *q, const float *k,
+                        int flags, double scale, const float *q, const float *k,
                         const float *v, const float *dout)
 {
     if (B <= 0 || H <= 0 || D <= 0 || !tiles_per_axis(grid, tile, p->n))
@@ -208,6 +241,7 @@ static int make_problem(problem *p, int B, int H, int D, const int grid[3],
     p->N = (int64_t)grid[0] * grid[1] * grid[2];
     p->q = q; p->k = k; p->v = v; p->dout = dout;
     p->windows = windows; p->offsets = offsets;
+    p->flags = flags;
     p->scale = scale;
     return 1;
 }
@@ -225,8 +259,9 @@ static int allowed(const problem *p, int h, int64_t i, int64_t j)
     token_tile(i, p->grid, p->tile, qc);
     token_tile(j, p->grid, p->tile, kc);
     int qid = (qc[0] * p->n[1] + qc[1]) * p->n[2] + qc[2];
-    window_of(p->n, p->windows + 3 * h, qc,
-              p->offsets ? p->offsets + 3 * qid : NULL, s, c);
+    int T = p->n[0] * p->n[1] * p->n[2];
+    window_of(p->n, p->windows + 3 * h, qc, offset_of(p->offsets, p->flags, h, T, qid),
+              p->flags & ORACLE_TRUNCATE, s, c);
     return tile_in_window(kc, s, c);
 }
 
@@ -280,12 +315,12 @@ static void split_row_id(const problem *p, int64_t id, int *b, int *h, int64_t *
  * Returns 0 on invalid arguments, else 1.
  */
 int oracle_fwd(int B, int H, int D, const int grid[3], const int tile[3],
-               const int *windows, const int *offsets, double scale,
+               const int *windows, const int *offsets, int flags, double scale,
                const float *q, const float *k, const float *v,
                int64_t n_rows, const int64_t *rows, double *o, double *lse)
 {
     problem p;
-    if (!make_problem(&p, B, H, D, grid, tile, windows, offsets, scale, q, k, v, NULL))
+    if (!make_problem(&p, B, H, D, grid, tile, windows, offsets, flags, scale, q, k, v, NULL))
         return 0;
     int ok = 1;
 #pragma omp parallel
@@ -349,13 +384,13 @@ static int64_t row_stats(const problem *p, int b, int h, int64_t i,
  * Returns 0 on invalid arguments or allocation failure, else 1.
  */
 int oracle_bwd(int B, int H, int D, const int grid[3], const int tile[3],
-               const int *windows, const int *offsets, double scale,
+               const int *windows, const int *offsets, int flags, double scale,
                const float *q, const float *k, const float *v, const float *dout,
                int64_t n_q, const int64_t *qrows, double *dq,
                int64_t n_k, const int64_t *krows, double *dk, double *dv)
 {
     problem p;
-    if (!make_problem(&p, B, H, D, grid, tile, windows, offsets, scale, q, k, v, dout))
+    if (!make_problem(&p, B, H, D, grid, tile, windows, offsets, flags, scale, q, k, v, dout))
         return 0;
     int ok = 1;
 

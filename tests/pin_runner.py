@@ -10,6 +10,7 @@ from oracle import oracle
 from tests import test_oracle_attention as A
 from tests import test_oracle_index as I
 from tests import test_oracle_perm as P
+from tests import test_oracle_window_options as W
 from tests.conftest import read_golden
 
 
@@ -35,6 +36,16 @@ def checks():
     yield lambda: A.test_lse_bounds()
     yield lambda: A.test_gradient_identities()
     yield lambda: A.test_backward_matches_finite_differences()
+    for row in read_golden("window_axis_truncate.txt"):
+        yield (lambda r: lambda: W.test_truncate_axis_golden(r))(row)
+    for case in range(len(W.CASES)):
+        yield (lambda c: lambda: W.test_truncate_lists_match_enumeration_and_transpose(c))(case)
+    yield lambda: W.test_truncate_holds_clamped_centre_and_never_exceeds_window()
+    yield lambda: W.test_truncate_interior_equals_shift_and_border_is_smaller()
+    yield lambda: W.test_truncate_mirror_symmetry_and_wide_window()
+    for border in ("shift", "truncate"):
+        yield (lambda b: lambda: W.test_head_offsets_reduce_to_shared_and_single_head(b))(border)
+        yield (lambda b: lambda: W.test_attention_options_match_torch_dense(b))(border)
 
 
 def main(path):

@@ -42,6 +42,11 @@ MUTANTS = {
     "dq-uses-v": ("const float *kj = row_of(&p, p.k, b, h, js[a]);",
                   "const float *kj = row_of(&p, p.v, b, h, js[a]);"),
     "delta-drops-p": ("dl += exp(ss[a] - L) * dot(", "dl += dot("),
+    "truncate-window-end-off-by-one": ("int hi = lo + win[d] - 1;", "int hi = lo + win[d];"),
+    "truncate-centre-not-clamped-high": ("if (centre > n[d] - 1) centre = n[d] - 1;", ""),
+    "truncate-centre-not-clamped-low": ("if (centre < 0) centre = 0;", ""),
+    "head-offsets-ignore-head-stride": ("((flags & ORACLE_HEAD_OFFS) ? h * T : 0)",
+                                        "((flags & ORACLE_HEAD_OFFS) ? h : 0)"),
 }
 
 
