@@ -96,6 +96,25 @@ const char *sta_last_error(void);
 /* Library version, major*10000 + minor*100 + patch. */
 int32_t sta_version(void);
 
+/* Border rule of a query tile's key-tile window, per axis. */
+typedef enum {
+    /* The window keeps its size min(w, n) and its start q + o - floor(w/2)
+     * is moved inside [0, n - size]: every query tile of a head sees the
+     * same number of key tiles (the default). */
+    STA_BORDER_SHIFT = 0,
+    /* The shifted centre q + o is clamped into [0, n-1] and the window
+     * [centre - floor(w/2), centre - floor(w/2) + w - 1] is cut at the grid
+     * border: windows at the border are smaller, never empty. */
+    STA_BORDER_TRUNCATE = 1
+} sta_border;
+
+/* Options of the index.  A NULL pointer means all fields 0 (the defaults). */
+typedef struct {
+    int32_t border;            /* an sta_border value */
+    int32_t per_head_offsets;  /* 0: offsets are [num_tiles][3], shared by the
+                                  heads; 1: [H][num_tiles][3], one set per head */
+} sta_index_opts;
+
 /*
  * Host-only helper, launches nothing.  For H heads with window sizes
  * windows_host[H] (tiles, each >= 1) returns
@@ -108,6 +127,13 @@ int32_t sta_version(void);
  */
 sta_status sta_index_dims(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
                           int32_t has_offsets, int32_t *max_kv, int32_t *max_q);
+
+/* sta_index_dims for an index built with options (opts may be NULL).  With
+ * STA_BORDER_TRUNCATE and no offsets, *max_q = max_h prod_d min(w_hd, n_d).
+ * STA_ERR_INVALID for an unknown border value. */
+sta_status sta_index_dims_ex(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
+                             int32_t has_offsets, const sta_index_opts *opts, int32_t *max_kv,
+                             int32_t *max_q);
 
 /*
  * Token permutation between raster order and tile order (the order the
@@ -144,6 +170,22 @@ sta_status sta_tile_reorder(const void *src, void *dst, int64_t outer, int64_t r
  */
 sta_status sta_build_index(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
                            const int32_t *offsets_dev, const sta_index *idx, hipStream_t stream);
+
+/*
+ * sta_build_index with options (opts may be NULL = sta_build_index):
+ *   opts->border            STA_BORDER_SHIFT or STA_BORDER_TRUNCATE;
+ *   opts->per_head_offsets  1: offsets_dev is DEVICE int32 [H][num_tiles][3],
+ *                           one shift triple per head and query tile.
+ * Size the lists with sta_index_dims_ex and the same options.  Attention
+ * calls read the lists as built; with truncated windows the list lengths
+ * differ between query tiles.
+ * Source: motion-adaptive local windows of 3D-DSA ("MegaSlide-DiT",
+ * abstract); the pages give no rule for them, so both options are
+ * readings and the shifts are inputs.
+ */
+sta_status sta_build_index_ex(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
+                              const int32_t *offsets_dev, const sta_index_opts *opts, const sta_index *idx,
+                              hipStream_t stream);
 
 /*
  * Fused forward.  For every (b, h) and query token i (tile order):

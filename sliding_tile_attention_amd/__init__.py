@@ -23,8 +23,9 @@ LIB_PATH = os.path.join(_HERE, "libsta.so")
 STA_OK, STA_ERR_INVALID, STA_ERR_UNSUPPORTED, STA_ERR_HIP = 0, 1, 2, 3
 STA_BF16, STA_F32 = 0, 1
 STA_BWD_DELTA, STA_BWD_DKDV, STA_BWD_DQ, STA_BWD_ALL = 1, 2, 4, 7
-EXPORTS = ("sta_status_str", "sta_last_error", "sta_version", "sta_index_dims", "sta_tile_reorder",
-           "sta_build_index", "sta_fwd", "sta_bwd", "sta_bwd_parts")
+STA_BORDER_SHIFT, STA_BORDER_TRUNCATE = 0, 1
+EXPORTS = ("sta_status_str", "sta_last_error", "sta_version", "sta_index_dims", "sta_index_dims_ex",
+           "sta_tile_reorder", "sta_build_index", "sta_build_index_ex", "sta_fwd", "sta_bwd", "sta_bwd_parts")
 
 
 class StaError(RuntimeError):
@@ -44,6 +45,10 @@ class sta_geom(ctypes.Structure):
     _fields_ = [("grid", sta_dim3), ("tile", sta_dim3)]
 
 
+class sta_index_opts(ctypes.Structure):
+    _fields_ = [("border", ctypes.c_int32), ("per_head_offsets", ctypes.c_int32)]
+
+
 class sta_index(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("num_tiles", ctypes.c_int32),
                 ("max_kv", ctypes.c_int32), ("max_q", ctypes.c_int32),
@@ -57,15 +62,17 @@ def _load():
                           "`python sliding_tile_attention_amd/build.py`" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
-    G, X = ctypes.POINTER(sta_geom), ctypes.POINTER(sta_index)
+    G, X, OP = ctypes.POINTER(sta_geom), ctypes.POINTER(sta_index), ctypes.POINTER(sta_index_opts)
     W = ctypes.POINTER(sta_dim3)
     sig = {
         "sta_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "sta_last_error": (ctypes.c_char_p, []),
         "sta_version": (I32, []),
         "sta_index_dims": (ctypes.c_int, [G, I32, W, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+        "sta_index_dims_ex": (ctypes.c_int, [G, I32, W, I32, OP, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "sta_tile_reorder": (ctypes.c_int, [P, P, I64, I64, G, I32, P]),
         "sta_build_index": (ctypes.c_int, [G, I32, W, P, X, P]),
+        "sta_build_index_ex": (ctypes.c_int, [G, I32, W, P, OP, X, P]),
         "sta_fwd": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X, P]),
         "sta_bwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X, P]),
         "sta_bwd_parts": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X,
@@ -132,12 +139,28 @@ def _stream(stream):
 
 # ---------------------------------------------------------------- C ABI --
 
+def _opts(border, per_head_offsets):
+    if border not in ("shift", "truncate"):
+        raise ValueError("border must be 'shift' or 'truncate'")
+    return sta_index_opts(STA_BORDER_TRUNCATE if border == "truncate" else STA_BORDER_SHIFT,
+                          int(bool(per_head_offsets)))
+
+
 def sta_index_dims(geom, windows, has_offsets):
     """(max_kv, max_q) capacities for H = len(windows) heads."""
     w, H = _windows(windows)
     kv, q = ctypes.c_int32(), ctypes.c_int32()
     _check(lib.sta_index_dims(ctypes.byref(geom.c()), H, w, int(bool(has_offsets)),
                               ctypes.byref(kv), ctypes.byref(q)))
+    return kv.value, q.value
+
+
+def sta_index_dims_ex(geom, windows, has_offsets, border="shift", per_head_offsets=False):
+    w, H = _windows(windows)
+    kv, q = ctypes.c_int32(), ctypes.c_int32()
+    opts = _opts(border, per_head_offsets)
+    _check(lib.sta_index_dims_ex(ctypes.byref(geom.c()), H, w, int(bool(has_offsets)), ctypes.byref(opts),
+                                 ctypes.byref(kv), ctypes.byref(q)))
     return kv.value, q.value
 
 
@@ -151,6 +174,15 @@ def sta_build_index(geom, windows, offsets, index, stream=None):
     w, H = _windows(windows)
     _check(lib.sta_build_index(ctypes.byref(geom.c()), H, w, _ptr(offsets), ctypes.byref(index.c()),
                                _stream(stream)))
+
+
+def sta_build_index_ex(geom, windows, offsets, index, border="shift", per_head_offsets=False, stream=None):
+    """offsets: None, or int32 device tensor [num_tiles, 3] ([H, num_tiles, 3]
+    with per_head_offsets); border: 'shift' or 'truncate'."""
+    w, H = _windows(windows)
+    opts = _opts(border, per_head_offsets)
+    _check(lib.sta_build_index_ex(ctypes.byref(geom.c()), H, w, _ptr(offsets), ctypes.byref(opts),
+                                  ctypes.byref(index.c()), _stream(stream)))
 
 
 def sta_fwd(q, k, v, o, lse, B, H, D, dtype, scale, geom, index, stream=None):
@@ -174,11 +206,14 @@ def sta_bwd_parts(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, s
 # ------------------------------------------------- allocation helpers --
 
 class StaIndex:
-    """Device buffers of a block-sparse index (allocated with torch)."""
+    """Device buffers of a block-sparse index (allocated with torch).
+    offsets: None, an int32 device tensor [num_tiles, 3] shared by the heads,
+    or [H, num_tiles, 3] (one set per head); border: 'shift' or 'truncate'."""
 
-    def __init__(self, geom, windows, offsets=None, device="cuda", transposed=True, stream=None):
+    def __init__(self, geom, windows, offsets=None, device="cuda", transposed=True, stream=None, border="shift"):
         H, T = len(windows), geom.num_tiles
-        self.max_kv, max_q = sta_index_dims(geom, windows, offsets is not None)
+        per_head = offsets is not None and offsets.dim() == 3
+        self.max_kv, max_q = sta_index_dims_ex(geom, windows, offsets is not None, border, per_head)
         self.max_q = max_q if transposed else 0
         i32 = dict(dtype=torch.int32, device=device)
         self.kv_idx = torch.empty((H, T, self.max_kv), **i32)
@@ -187,7 +222,8 @@ class StaIndex:
         self.q_cnt = torch.empty((H, T), **i32) if transposed else None
         self.num_heads, self.num_tiles = H, T
         self.windows = [tuple(w) for w in windows]
-        sta_build_index(geom, windows, offsets, self, stream)
+        self.border = border
+        sta_build_index_ex(geom, windows, offsets, self, border, per_head, stream)
 
     def c(self):
         return sta_index(self.num_heads, self.num_tiles, self.max_kv, self.max_q,

@@ -66,7 +66,7 @@ static sta_status make_geo(const sta_geom *g, Geo &out)
     return STA_OK;
 }
 
-static sta_status index_needs(const Geo &g, int H, const sta_dim3 *w, int has_offsets,
+static sta_status index_needs(const Geo &g, int H, const sta_dim3 *w, int has_offsets, bool truncate,
                               int32_t &max_kv, int32_t &max_q)
 {
     if (H <= 0)
@@ -82,13 +82,29 @@ static sta_status index_needs(const Geo &g, int H, const sta_dim3 *w, int has_of
                     (w[h].w < g.nw ? w[h].w : g.nw);
         kv = c > kv ? c : kv;
         if (!has_offsets) {
-            int64_t a = (int64_t)axis_max_attendees(g.nt, w[h].t) * axis_max_attendees(g.nh, w[h].h) *
-                        axis_max_attendees(g.nw, w[h].w);
+            // truncated windows: a key tile lies in the windows of at most
+            // min(w, n) query tiles per axis (their centres are within w)
+            int64_t a = truncate ? c
+                                 : (int64_t)axis_max_attendees(g.nt, w[h].t) * axis_max_attendees(g.nh, w[h].h) *
+                                       axis_max_attendees(g.nw, w[h].w);
             qq = a > qq ? a : qq;
         }
     }
     max_kv = (int32_t)kv;
     max_q = has_offsets ? g.T : (int32_t)qq;
+    return STA_OK;
+}
+
+static sta_status index_options(const sta_index_opts *opts, bool &truncate, bool &per_head)
+{
+    truncate = per_head = false;
+    if (!opts) return STA_OK;
+    if (opts->border != STA_BORDER_SHIFT && opts->border != STA_BORDER_TRUNCATE)
+        return fail(STA_ERR_INVALID, "unknown border rule %d", opts->border);
+    if (opts->per_head_offsets != 0 && opts->per_head_offsets != 1)
+        return fail(STA_ERR_INVALID, "per_head_offsets must be 0 or 1 (got %d)", opts->per_head_offsets);
+    truncate = opts->border == STA_BORDER_TRUNCATE;
+    per_head = opts->per_head_offsets == 1;
     return STA_OK;
 }
 
@@ -147,16 +163,25 @@ const char *sta_status_str(sta_status s)
 
 const char *sta_last_error(void) { return g_err; }
 
-int32_t sta_version(void) { return 10000; }
+int32_t sta_version(void) { return 10100; }
 
 sta_status sta_index_dims(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
                           int32_t has_offsets, int32_t *max_kv, int32_t *max_q)
 {
+    return sta_index_dims_ex(g, H, windows_host, has_offsets, nullptr, max_kv, max_q);
+}
+
+sta_status sta_index_dims_ex(const sta_geom *g, int32_t H, const sta_dim3 *windows_host, int32_t has_offsets,
+                             const sta_index_opts *opts, int32_t *max_kv, int32_t *max_q)
+{
     Geo geo;
     sta_status st = make_geo(g, geo);
     if (st != STA_OK) return st;
+    bool truncate, per_head;
+    st = index_options(opts, truncate, per_head);
+    if (st != STA_OK) return st;
     int32_t kv, qq;
-    st = index_needs(geo, H, windows_host, has_offsets, kv, qq);
+    st = index_needs(geo, H, windows_host, has_offsets, truncate, kv, qq);
     if (st != STA_OK) return st;
     if (max_kv) *max_kv = kv;
     if (max_q) *max_q = qq;
@@ -185,11 +210,21 @@ sta_status sta_tile_reorder(const void *src, void *dst, int64_t outer, int64_t r
 sta_status sta_build_index(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
                            const int32_t *offsets_dev, const sta_index *idx, hipStream_t stream)
 {
+    return sta_build_index_ex(g, H, windows_host, offsets_dev, nullptr, idx, stream);
+}
+
+sta_status sta_build_index_ex(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
+                              const int32_t *offsets_dev, const sta_index_opts *opts, const sta_index *idx,
+                              hipStream_t stream)
+{
     Geo geo;
     sta_status st = make_geo(g, geo);
     if (st != STA_OK) return st;
+    bool truncate, per_head;
+    st = index_options(opts, truncate, per_head);
+    if (st != STA_OK) return st;
     int32_t kv, qq;
-    st = index_needs(geo, H, windows_host, offsets_dev != nullptr, kv, qq);
+    st = index_needs(geo, H, windows_host, offsets_dev != nullptr, truncate, kv, qq);
     if (st != STA_OK) return st;
     if (!idx)
         return fail(STA_ERR_INVALID, "index pointer is NULL");
@@ -214,7 +249,7 @@ sta_status sta_build_index(const sta_geom *g, int32_t H, const sta_dim3 *windows
         wins[3 * h + 1] = windows_host[h].h;
         wins[3 * h + 2] = windows_host[h].w;
     }
-    return launch_build_index(geo, H, wins, offsets_dev, *idx, stream);
+    return launch_build_index(geo, H, wins, offsets_dev, per_head, truncate, *idx, stream);
 }
 
 sta_status sta_fwd(const void *q, const void *k, const void *v, void *o, float *lse,

@@ -28,6 +28,20 @@ __host__ __device__ inline void axis_window(int n, int w, int q, int o, int &s, 
     s = s > n - c ? n - c : s;
 }
 
+// Truncating border rule: the shifted centre is clamped into the grid and
+// the window [centre - w/2, centre - w/2 + w - 1] is cut at the border.
+__host__ __device__ inline void axis_window_truncated(int n, int w, int q, int o, int &s, int &c)
+{
+    int centre = q + o;
+    centre = centre < 0 ? 0 : centre;
+    centre = centre > n - 1 ? n - 1 : centre;
+    int lo = centre - w / 2, hi = lo + w - 1;
+    lo = lo < 0 ? 0 : lo;
+    hi = hi > n - 1 ? n - 1 : hi;
+    s = lo;
+    c = hi - lo + 1;
+}
+
 // Error reporting: records a thread-local message and returns the status.
 sta_status fail(sta_status s, const char *fmt, ...);
 
@@ -38,9 +52,9 @@ int axis_max_attendees(int n, int w);
 sta_status launch_reorder(const void *src, void *dst, int64_t outer, int64_t row_bytes,
                           const Geo &g, bool inverse, hipStream_t s);
 
-// windows: [H][3] host array
+// windows: [H][3] host array; offsets: [T][3], or [H][T][3] when per_head
 sta_status launch_build_index(const Geo &g, int H, const int32_t *windows, const int32_t *offsets,
-                              const sta_index &idx, hipStream_t s);
+                              bool per_head, bool truncate, const sta_index &idx, hipStream_t s);
 
 sta_status launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                           int B, int H, int D, float scale, const Geo &g, const sta_index &idx,

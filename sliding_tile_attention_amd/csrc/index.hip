@@ -1,8 +1,9 @@
 // Block-sparse index builder.
 //
 // Forward lists: one thread per (head, query tile).  The window is a product
-// of three axis ranges, so walking t, then h, then w inside it emits tile ids
-// in ascending order with no sorting.
+// of three axis ranges (shifted inward, or truncated at the border), so
+// walking t, then h, then w inside it emits tile ids in ascending order with
+// no sorting.  Shifts are shared by the heads or given per head.
 // Transposed lists: one thread per (head, key tile), scanning every query
 // tile in ascending order and testing its (possibly shifted) window.  No
 // atomics, so both list sets are deterministic.
@@ -16,28 +17,40 @@ struct Windows {
     int w[kHeadsPerLaunch][3];
 };
 
-__device__ inline void tile_window(const Geo &g, const int *win, const int32_t *offsets, int q,
+// Window of query tile q; `offsets` already points at this head's shifts.
+__device__ inline void tile_window(const Geo &g, const int *win, const int32_t *offsets, bool truncate, int q,
                                    int s[3], int c[3])
 {
     const int qt = q / (g.nh * g.nw), qh = (q / g.nw) % g.nh, qw = q % g.nw;
     const int o0 = offsets ? offsets[3 * q + 0] : 0;
     const int o1 = offsets ? offsets[3 * q + 1] : 0;
     const int o2 = offsets ? offsets[3 * q + 2] : 0;
-    axis_window(g.nt, win[0], qt, o0, s[0], c[0]);
-    axis_window(g.nh, win[1], qh, o1, s[1], c[1]);
-    axis_window(g.nw, win[2], qw, o2, s[2], c[2]);
+    if (truncate) {
+        axis_window_truncated(g.nt, win[0], qt, o0, s[0], c[0]);
+        axis_window_truncated(g.nh, win[1], qh, o1, s[1], c[1]);
+        axis_window_truncated(g.nw, win[2], qw, o2, s[2], c[2]);
+    } else {
+        axis_window(g.nt, win[0], qt, o0, s[0], c[0]);
+        axis_window(g.nh, win[1], qh, o1, s[1], c[1]);
+        axis_window(g.nw, win[2], qw, o2, s[2], c[2]);
+    }
+}
+
+__device__ inline const int32_t *head_offsets(const int32_t *offsets, bool per_head, int h, int T)
+{
+    return offsets && per_head ? offsets + (int64_t)h * T * 3 : offsets;
 }
 
 __global__ __launch_bounds__(256) void index_fwd_kernel(Geo g, int h0, int nheads, Windows wins,
-                                                        const int32_t *__restrict__ offsets,
-                                                        int32_t *__restrict__ kv_idx,
+                                                        const int32_t *__restrict__ offsets, bool per_head,
+                                                        bool truncate, int32_t *__restrict__ kv_idx,
                                                         int32_t *__restrict__ kv_cnt, int max_kv)
 {
     const int gid = blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= nheads * g.T) return;
     const int hl = gid / g.T, q = gid % g.T, h = h0 + hl;
     int s[3], c[3];
-    tile_window(g, wins.w[hl], offsets, q, s, c);
+    tile_window(g, wins.w[hl], head_offsets(offsets, per_head, h, g.T), truncate, q, s, c);
     int32_t *row = kv_idx + ((int64_t)h * g.T + q) * max_kv;
     int n = 0;
     for (int a = s[0]; a < s[0] + c[0]; ++a)
@@ -49,19 +62,20 @@ __global__ __launch_bounds__(256) void index_fwd_kernel(Geo g, int h0, int nhead
 }
 
 __global__ __launch_bounds__(256) void index_bwd_kernel(Geo g, int h0, int nheads, Windows wins,
-                                                        const int32_t *__restrict__ offsets,
-                                                        int32_t *__restrict__ q_idx,
+                                                        const int32_t *__restrict__ offsets, bool per_head,
+                                                        bool truncate, int32_t *__restrict__ q_idx,
                                                         int32_t *__restrict__ q_cnt, int max_q)
 {
     const int gid = blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= nheads * g.T) return;
     const int hl = gid / g.T, k = gid % g.T, h = h0 + hl;
+    const int32_t *hoff = head_offsets(offsets, per_head, h, g.T);
     const int kt = k / (g.nh * g.nw), kh = (k / g.nw) % g.nh, kw = k % g.nw;
     int32_t *row = q_idx + ((int64_t)h * g.T + k) * max_q;
     int n = 0;
     for (int q = 0; q < g.T; ++q) {
         int s[3], c[3];
-        tile_window(g, wins.w[hl], offsets, q, s, c);
+        tile_window(g, wins.w[hl], hoff, truncate, q, s, c);
         const bool in = kt >= s[0] && kt < s[0] + c[0] && kh >= s[1] && kh < s[1] + c[1] &&
                         kw >= s[2] && kw < s[2] + c[2];
         if (in && n < max_q) row[n++] = q;
@@ -71,7 +85,7 @@ __global__ __launch_bounds__(256) void index_bwd_kernel(Geo g, int h0, int nhead
 }
 
 sta_status launch_build_index(const Geo &g, int H, const int32_t *windows, const int32_t *offsets,
-                              const sta_index &idx, hipStream_t s)
+                              bool per_head, bool truncate, const sta_index &idx, hipStream_t s)
 {
     for (int h0 = 0; h0 < H; h0 += kHeadsPerLaunch) {
         const int nh = H - h0 < kHeadsPerLaunch ? H - h0 : kHeadsPerLaunch;
@@ -81,13 +95,13 @@ sta_status launch_build_index(const Geo &g, int H, const int32_t *windows, const
                 w.w[i][d] = i < nh ? windows[3 * (h0 + i) + d] : 1;
         const int threads = nh * g.T;
         const dim3 grid((threads + 255) / 256);
-        hipLaunchKernelGGL(index_fwd_kernel, grid, dim3(256), 0, s, g, h0, nh, w, offsets, idx.kv_idx,
-                           idx.kv_cnt, idx.max_kv);
+        hipLaunchKernelGGL(index_fwd_kernel, grid, dim3(256), 0, s, g, h0, nh, w, offsets, per_head, truncate,
+                           idx.kv_idx, idx.kv_cnt, idx.max_kv);
         sta_status st = check_launch();
         if (st != STA_OK) return st;
         if (idx.q_idx) {
-            hipLaunchKernelGGL(index_bwd_kernel, grid, dim3(256), 0, s, g, h0, nh, w, offsets, idx.q_idx,
-                               idx.q_cnt, idx.max_q);
+            hipLaunchKernelGGL(index_bwd_kernel, grid, dim3(256), 0, s, g, h0, nh, w, offsets, per_head,
+                               truncate, idx.q_idx, idx.q_cnt, idx.max_q);
             if ((st = check_launch()) != STA_OK) return st;
         }
     }

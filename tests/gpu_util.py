@@ -65,13 +65,13 @@ class Layer:
     """Device state of one attention layer: inputs reordered to tile order,
     the index, and the outputs converted back to raster order."""
 
-    def __init__(self, grid, tile, windows, offsets, q, k, v, dtype, dout=None, transposed=True):
+    def __init__(self, grid, tile, windows, offsets, q, k, v, dtype, dout=None, transposed=True, border="shift"):
         self.geom = sta.Geometry(tuple(grid), tuple(tile))
         self.dtype = dtype
         self.B, self.H, self.N, self.D = q.shape
         self.windows = [tuple(int(x) for x in w) for w in windows]
         self.off_dev = None if offsets is None else torch.from_numpy(np.ascontiguousarray(offsets, np.int32)).cuda()
-        self.index = sta.StaIndex(self.geom, self.windows, self.off_dev, transposed=transposed)
+        self.index = sta.StaIndex(self.geom, self.windows, self.off_dev, transposed=transposed, border=border)
         self.q, self.k, self.v = (sta.tile_reorder(to_dev(x, dtype), self.geom) for x in (q, k, v))
         self.dout = None if dout is None else sta.tile_reorder(to_dev(dout, dtype), self.geom)
 

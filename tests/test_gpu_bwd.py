@@ -121,3 +121,44 @@ def test_bwd_720p_training_sampled():
     assert (sdk.abs() / scale_k).max().item() < 1e-2
     for t in (dq, dk, dv):
         assert torch.isfinite(t).all()
+
+
+@pytest.mark.parametrize("case", __import__("tests.test_gpu_fwd", fromlist=["OPTION_CASES"]).OPTION_CASES,
+                         ids=lambda c: c[0])
+def test_bwd_bf16_window_options(case):
+    """Backward with truncated windows (transposed lists of unequal length)
+    and per-head shifts."""
+    from tests.test_gpu_fwd import option_offsets
+    name, grid, tile, B, H, D, windows, border, kind = case
+    say("bwd bf16 options " + name)
+    T = int(np.prod([a // b for a, b in zip(grid, tile)]))
+    off = option_offsets(kind, H, T, 9)
+    N = int(np.prod(grid))
+    q, k, v, do = tensors(B, H, N, D, "bf16", 93, with_dout=True)
+    layer = Layer(grid, tile, windows, off, q, k, v, "bf16", dout=do, border=border)
+    layer.forward()
+    dq, dk, dv = layer.backward()
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.bwd(q, k, v, do, grid, tile, windows, off, border=border)
+    assert_close(to_host(dq), rq, "bf16", name + " dQ")
+    assert_close(to_host(dk), rk, "bf16", name + " dK")
+    assert_close(to_host(dv), rv, "bf16", name + " dV")
+
+
+def test_f32_window_options():
+    """fp32 path with truncated windows and per-head shifts (forward and backward)."""
+    grid, tile, windows = (4, 8, 12), (2, 4, 4), [(3, 3, 3), (1, 3, 5)]
+    B, H, D = 1, 2, 64
+    T = int(np.prod([a // b for a, b in zip(grid, tile)]))
+    off = np.random.default_rng(12).integers(-2, 2, endpoint=True, size=(H, T, 3)).astype(np.int32)
+    N = int(np.prod(grid))
+    q, k, v, do = tensors(B, H, N, D, "f32", 95, with_dout=True)
+    say("f32 window options")
+    layer = Layer(grid, tile, windows, off, q, k, v, "f32", dout=do, border="truncate")
+    o, _ = layer.forward()
+    dq, dk, dv = layer.backward()
+    torch.cuda.synchronize()
+    ro, _ = oracle.fwd(q, k, v, grid, tile, windows, off, border="truncate")
+    rq, rk, rv = oracle.bwd(q, k, v, do, grid, tile, windows, off, border="truncate")
+    for name, got, ref in (("O", o, ro), ("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        assert_close(to_host(got), ref, "f32", name)

@@ -133,3 +133,37 @@ def test_fwd_workspace_reuse_and_streams():
     side.synchronize()
     for (o, lse), (o0, l0) in zip(outs, firsts):
         assert torch.equal(o, o0) and torch.equal(lse, l0), "second stream differs"
+
+
+OPTION_CASES = [
+    # name, grid, tile, B, H, D, windows, border, offsets kind (None / "shared" / "head")
+    ("trunc-L32-D128", (4, 8, 12), (2, 4, 4), 1, 3, 128, [(3, 3, 3), (1, 3, 3), (5, 5, 5)], "truncate", None),
+    ("trunc-headoff-L48-D64", (6, 8, 16), (3, 4, 4), 2, 2, 64, [(1, 3, 3), (3, 3, 5)], "truncate", "head"),
+    ("shift-headoff-L128-D128", (4, 16, 24), (2, 8, 8), 1, 2, 128, [(3, 3, 3), (1, 1, 3)], "shift", "head"),
+    ("trunc-shared-L384-D128", (12, 16, 24), (6, 8, 8), 1, 2, 128, [(3, 3, 3), (1, 3, 3)], "truncate", "shared"),
+]
+
+
+def option_offsets(kind, H, T, seed):
+    g = np.random.default_rng(seed)
+    if kind is None:
+        return None
+    shape = (T, 3) if kind == "shared" else (H, T, 3)
+    return g.integers([-1, -2, -2], [1, 2, 2], endpoint=True, size=shape).astype(np.int32)
+
+
+@pytest.mark.parametrize("case", OPTION_CASES, ids=lambda c: c[0])
+def test_fwd_bf16_window_options(case):
+    """Truncated windows (lists of unequal length) and per-head shifts."""
+    name, grid, tile, B, H, D, windows, border, kind = case
+    say("fwd bf16 options " + name)
+    T = int(np.prod([a // b for a, b in zip(grid, tile)]))
+    off = option_offsets(kind, H, T, 9)
+    N = int(np.prod(grid))
+    q, k, v = tensors(B, H, N, D, "bf16", 91)
+    layer = Layer(grid, tile, windows, off, q, k, v, "bf16", border=border)
+    o, lse = layer.forward()
+    torch.cuda.synchronize()
+    ro, rl = oracle.fwd(q, k, v, grid, tile, windows, off, border=border)
+    assert_close(to_host(o), ro, "bf16", name + " O")
+    assert_lse(to_host(lse), rl, "bf16")

@@ -47,12 +47,12 @@ def test_reorder_bit_exact_and_round_trip(case):
     assert torch.equal(back.cpu(), src_h)
 
 
-def _check_index(grid, tile, windows, offsets):
+def _check_index(grid, tile, windows, offsets, border="shift"):
     geom = sta.Geometry(grid, tile)
     off = None if offsets is None else torch.from_numpy(np.ascontiguousarray(offsets, np.int32)).cuda()
-    idx = sta.StaIndex(geom, windows, off)
+    idx = sta.StaIndex(geom, windows, off, border=border)
     torch.cuda.synchronize()
-    ref = oracle.index(grid, tile, windows, offsets, max_kv=idx.max_kv, max_q=idx.max_q)
+    ref = oracle.index(grid, tile, windows, offsets, max_kv=idx.max_kv, max_q=idx.max_q, border=border)
     got = [x.cpu().numpy() for x in (idx.kv_idx, idx.kv_cnt, idx.q_idx, idx.q_cnt)]
     for name, a, b in zip(("kv_idx", "kv_cnt", "q_idx", "q_cnt"), got, ref):
         assert np.array_equal(a, b), name
@@ -88,3 +88,34 @@ def test_index_forward_only():
     ref = oracle.index(c["grid"], c["tile"], windows_for(2), None, max_kv=idx.max_kv)
     assert np.array_equal(idx.kv_idx.cpu().numpy(), ref[0])
     assert np.array_equal(idx.kv_cnt.cpu().numpy(), ref[1])
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_index_options_random_geometries(seed):
+    """Truncated windows and per-head shifts (the 3D-DSA index options):
+    every list bit-exact against the oracle."""
+    g = np.random.default_rng(2000 + seed)
+    n = g.integers(1, 9, size=3)
+    tile = tuple(int(x) for x in g.integers(1, 4, size=3))
+    grid = tuple(int(a * b) for a, b in zip(n, tile))
+    H = int(g.integers(1, 5))
+    T = int(np.prod(n))
+    windows = g.integers(1, 10, size=(H, 3))
+    border = "truncate" if seed % 3 else "shift"
+    kind = seed % 4
+    offsets = (None if kind == 0 else
+               g.integers(-4, 5, size=(T, 3)).astype(np.int32) if kind == 1 else
+               g.integers(-4, 5, size=(H, T, 3)).astype(np.int32))
+    say("index options seed %d grid %s tile %s H %d border %s offsets %s" %
+        (seed, grid, tile, H, border, None if offsets is None else offsets.shape))
+    _check_index(grid, tile, windows, offsets, border)
+
+
+def test_index_options_720p_shape():
+    """Per-head windows, per-head shifts and truncation at the 720P tile grid."""
+    c = CONFIGS[4]
+    H = 24
+    g = np.random.default_rng(77)
+    offsets = g.integers([-1, -2, -2], [1, 2, 2], endpoint=True, size=(H, 300, 3)).astype(np.int32)
+    say("index options 720p")
+    _check_index(c["grid"], c["tile"], windows_for(4), offsets, "truncate")

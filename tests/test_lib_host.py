@@ -179,3 +179,35 @@ def test_index_dims_rejects_bad_arguments():
     _expect(sta.STA_ERR_INVALID, sta.sta_index_dims, sta.Geometry((3, 8, 8), (2, 4, 4)), [(1, 1, 1)], False)
     g = sta.lib.sta_index_dims(ctypes.byref(GEOM.c()), 0, None, 0, None, None)
     assert g == sta.STA_ERR_INVALID
+
+
+def test_index_dims_ex_match_oracle_with_options():
+    """Truncated windows without shifts: the capacities are exact (the
+    central tile of every axis has the full window and the most attendees)."""
+    g = np.random.default_rng(4)
+    for _ in range(40):
+        n = g.integers(1, 9, size=3)
+        tile = tuple(int(x) for x in g.integers(1, 3, size=3))
+        grid = tuple(int(a * b) for a, b in zip(n, tile))
+        w = g.integers(1, 10, size=(int(g.integers(1, 4)), 3))
+        _, kv_cnt, _, q_cnt = oracle.index(grid, tile, w, border="truncate")
+        geom = sta.Geometry(grid, tile)
+        assert sta.sta_index_dims_ex(geom, w, False, "truncate") == (kv_cnt.max(), q_cnt.max())
+        assert sta.sta_index_dims_ex(geom, w, False, "shift") == sta.sta_index_dims(geom, w, False)
+        T = int(np.prod(n))
+        assert sta.sta_index_dims_ex(geom, w, True, "truncate", True)[1] == T
+
+
+def test_index_options_reject_bad_values():
+    w = (sta.sta_dim3 * 1)(sta.sta_dim3(3, 3, 3))
+    kv, q = ctypes.c_int32(), ctypes.c_int32()
+    for border, per_head in ((2, 0), (-1, 0), (0, 2)):
+        opts = sta.sta_index_opts(border, per_head)
+        st = sta.lib.sta_index_dims_ex(ctypes.byref(GEOM.c()), 1, w, 0, ctypes.byref(opts), ctypes.byref(kv),
+                                       ctypes.byref(q))
+        assert st == sta.STA_ERR_INVALID and sta.lib.sta_last_error().decode()
+        st = sta.lib.sta_build_index_ex(ctypes.byref(GEOM.c()), 1, w, None, ctypes.byref(opts),
+                                        ctypes.byref(_FakeIndex(H=1).c()), None)
+        assert st == sta.STA_ERR_INVALID
+    with pytest.raises(ValueError):
+        sta.sta_index_dims_ex(GEOM, [(3, 3, 3)], False, "wrap")
