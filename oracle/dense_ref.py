@@ -73,18 +73,30 @@ def token_mask(grid, tile, window, offsets=None, border="shift"):
     return m
 
 
-def attention(q, k, v, grid, tile, windows, offsets=None, scale=None, dout=None, border="shift"):
-    """q,k,v: float arrays [B,H,N,D] in raster order.  offsets: None, [T, 3]
-    (shared by heads) or [H, T, 3] (one set per head).  Returns float64 numpy
-    (o, lse) and, with dout given, also (dq, dk, dv)."""
+def joint_mask(video_mask, n_text):
+    """Token-type-aware mask of a joint sequence: video tokens (in the order
+    of video_mask) followed by n_text text tokens; text rows and text
+    columns are fully allowed."""
+    nv = video_mask.shape[0]
+    m = np.ones((nv + n_text, nv + n_text), bool)
+    m[:nv, :nv] = video_mask
+    return m
+
+
+def attention(q, k, v, grid, tile, windows, offsets=None, scale=None, dout=None, border="shift", n_text=0):
+    """q,k,v: float arrays [B,H,N,D] in raster order (N = grid tokens +
+    n_text, text tokens last).  offsets: None, [T, 3] (shared by heads) or
+    [H, T, 3] (one set per head).  Returns float64 numpy (o, lse) and, with
+    dout given, also (dq, dk, dv)."""
     q = torch.tensor(np.asarray(q), dtype=torch.float64)
     k = torch.tensor(np.asarray(k), dtype=torch.float64)
     v = torch.tensor(np.asarray(v), dtype=torch.float64)
     B, H, N, D = q.shape
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     per_head = offsets is not None and np.asarray(offsets).ndim == 3
-    masks = torch.stack([torch.from_numpy(token_mask(grid, tile, windows[h],
-                                                     np.asarray(offsets)[h] if per_head else offsets, border))
+    masks = torch.stack([torch.from_numpy(joint_mask(token_mask(grid, tile, windows[h],
+                                                                np.asarray(offsets)[h] if per_head else offsets,
+                                                                border), n_text))
                          for h in range(H)])
     want_grad = dout is not None
     for t in (q, k, v):

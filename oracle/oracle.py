@@ -9,6 +9,10 @@ fastest), shaped [B, H, N, D]; floating inputs are float32 and outputs are
 float64.  Row ids passed to ``fwd``/``bwd`` are flat ``(b*H + h)*N + i``
 with ``i`` a raster token index.
 
+Joint text + video sequences: ``n_text`` text tokens follow the grid's
+video tokens in every [B, H, N, D] tensor (N = grid tokens + n_text); text
+queries attend every key and every query attends the text keys.
+
 Window options (the 3D-DSA variants): ``border="truncate"`` selects the
 truncating border rule instead of the inward shift, and ``offsets`` may be
 [T, 3] (one shift per query tile, shared by heads) or [H, T, 3] (one per
@@ -54,10 +58,10 @@ def load(path=None):
                                  ctypes.c_int, i32p, i32p, ctypes.c_int, i32p, i32p]
     lib.oracle_index.restype = ctypes.c_int
     lib.oracle_fwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, i32p, i32p, i32p, ctypes.c_int,
-                               ctypes.c_double, f32p, f32p, f32p, ctypes.c_int64, i64p, f64p, f64p]
+                               ctypes.c_int, ctypes.c_double, f32p, f32p, f32p, ctypes.c_int64, i64p, f64p, f64p]
     lib.oracle_fwd.restype = ctypes.c_int
     lib.oracle_bwd.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, i32p, i32p, i32p, ctypes.c_int,
-                               ctypes.c_double, f32p, f32p, f32p, f32p,
+                               ctypes.c_int, ctypes.c_double, f32p, f32p, f32p, f32p,
                                ctypes.c_int64, i64p, f64p, ctypes.c_int64, i64p, f64p, f64p]
     lib.oracle_bwd.restype = ctypes.c_int
     if path is None:
@@ -153,13 +157,13 @@ def _rows(rows, total):
     return np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
 
 
-def fwd(q, k, v, grid, tile, windows, offsets=None, scale=None, rows=None, border="shift"):
+def fwd(q, k, v, grid, tile, windows, offsets=None, scale=None, rows=None, border="shift", n_text=0):
     """Forward rows: returns (o [n_rows, D], lse [n_rows]) in float64.
     With rows=None every row is computed and o is reshaped to [B,H,N,D]."""
     lib = _load()
     q, k, v = _f32(q), _f32(k), _f32(v)
     B, H, N, D = q.shape
-    assert k.shape == q.shape and v.shape == q.shape and N == int(np.prod(grid))
+    assert k.shape == q.shape and v.shape == q.shape and N == int(np.prod(grid)) + n_text
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     windows = _i32(windows).reshape(H, 3)
     T = int(np.prod(tiles_per_axis(grid, tile)))
@@ -168,7 +172,7 @@ def fwd(q, k, v, grid, tile, windows, offsets=None, scale=None, rows=None, borde
     o = np.empty((len(r), D), np.float64)
     lse = np.empty(len(r), np.float64)
     ok = lib.oracle_fwd(B, H, D, _ptr(_i32(grid), ctypes.c_int32), _ptr(_i32(tile), ctypes.c_int32),
-                        _ptr(windows, ctypes.c_int32), _ptr(off, ctypes.c_int32), flags, scale,
+                        _ptr(windows, ctypes.c_int32), _ptr(off, ctypes.c_int32), flags, int(n_text), scale,
                         _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
                         len(r), _ptr(r, ctypes.c_int64), _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
     if not ok:
@@ -178,12 +182,14 @@ def fwd(q, k, v, grid, tile, windows, offsets=None, scale=None, rows=None, borde
     return o, lse
 
 
-def bwd(q, k, v, dout, grid, tile, windows, offsets=None, scale=None, qrows=None, krows=None, border="shift"):
+def bwd(q, k, v, dout, grid, tile, windows, offsets=None, scale=None, qrows=None, krows=None, border="shift",
+        n_text=0):
     """Backward rows: returns (dq [n_q, D], dk [n_k, D], dv [n_k, D]) in float64.
     With qrows=None and krows=None everything is computed, shaped [B,H,N,D]."""
     lib = _load()
     q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
     B, H, N, D = q.shape
+    assert N == int(np.prod(grid)) + n_text
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     windows = _i32(windows).reshape(H, 3)
     T = int(np.prod(tiles_per_axis(grid, tile)))
@@ -195,7 +201,7 @@ def bwd(q, k, v, dout, grid, tile, windows, offsets=None, scale=None, qrows=None
     dk = np.empty((len(kr), D), np.float64)
     dv = np.empty((len(kr), D), np.float64)
     ok = lib.oracle_bwd(B, H, D, _ptr(_i32(grid), ctypes.c_int32), _ptr(_i32(tile), ctypes.c_int32),
-                        _ptr(windows, ctypes.c_int32), _ptr(off, ctypes.c_int32), flags, scale,
+                        _ptr(windows, ctypes.c_int32), _ptr(off, ctypes.c_int32), flags, int(n_text), scale,
                         _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
                         _ptr(dout, ctypes.c_float),
                         len(qr), _ptr(qr, ctypes.c_int64), _ptr(dq, ctypes.c_double),

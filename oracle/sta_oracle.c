@@ -37,6 +37,11 @@
  *                    centre and is never empty).
  *   ORACLE_HEAD_OFFS offsets are [H][T][3], one shift per head and query tile
  *                    (batch items still share them).
+ *   Joint text + video sequences (token-type-aware masking, MOD-DiT README
+ *   mirror, "Token-Type-Aware Masking"): the attention entry points take
+ *   n_text >= 0 text tokens stored after the grid's video tokens; a text
+ *   query attends every key and every query attends every text key, while
+ *   video-video pairs keep the window rule.
  *   R6 raster order everywhere: t slowest, w fastest (tokens, tiles and the
  *      position inside a tile).
  *   R8 softmax scale is an argument (1/sqrt(D) in every workload).
@@ -221,7 +226,9 @@ int oracle_index(const int grid[3], const int tile[3], int H,
 typedef struct {
     int B, H, D;
     int grid[3], tile[3], n[3];
-    int64_t N;
+    int64_t N;                       /* rows per (b, h): Nv video + ntext text tokens */
+    int64_t Nv;
+    int ntext;
     const float *q, *k, *v, *dout;   /* [B][H][N][D], raster token order */
     const int *windows, *offsets;
     int flags;
@@ -230,15 +237,17 @@ typedef struct {
 
 static int make_problem(problem *p, int B, int H, int D, const int grid[3],
                         const int tile[3], const int *windows, const int *offsets,
-                        int flags, double scale, const float *q, const float *k,
+                        int flags, int ntext, double scale, const float *q, const float *k,
                         const float *v, const float *dout)
 {
-    if (B <= 0 || H <= 0 || D <= 0 || !tiles_per_axis(grid, tile, p->n))
+    if (B <= 0 || H <= 0 || D <= 0 || ntext < 0 || !tiles_per_axis(grid, tile, p->n))
         return 0;
     p->B = B; p->H = H; p->D = D;
     memcpy(p->grid, grid, sizeof p->grid);
     memcpy(p->tile, tile, sizeof p->tile);
-    p->N = (int64_t)grid[0] * grid[1] * grid[2];
+    p->Nv = (int64_t)grid[0] * grid[1] * grid[2];
+    p->ntext = ntext;
+    p->N = p->Nv + ntext;
     p->q = q; p->k = k; p->v = v; p->dout = dout;
     p->windows = windows; p->offsets = offsets;
     p->flags = flags;
@@ -251,10 +260,13 @@ static const float *row_of(const problem *p, const float *x, int b, int h, int64
     return x + (((int64_t)b * p->H + h) * p->N + i) * p->D;
 }
 
-/* Is key token j allowed for query token i under head h?  The mask is
- * M_h[i,j] = [tile(j) lies in the window of tile(i)]. */
+/* Is key token j allowed for query token i under head h?  A text token
+ * (index >= Nv) on either side makes the pair allowed; between video tokens
+ * the mask is M_h[i,j] = [tile(j) lies in the window of tile(i)]. */
 static int allowed(const problem *p, int h, int64_t i, int64_t j)
 {
+    if (i >= p->Nv || j >= p->Nv)
+        return 1;
     int qc[3], kc[3], s[3], c[3];
     token_tile(i, p->grid, p->tile, qc);
     token_tile(j, p->grid, p->tile, kc);
@@ -315,12 +327,12 @@ static void split_row_id(const problem *p, int64_t id, int *b, int *h, int64_t *
  * Returns 0 on invalid arguments, else 1.
  */
 int oracle_fwd(int B, int H, int D, const int grid[3], const int tile[3],
-               const int *windows, const int *offsets, int flags, double scale,
+               const int *windows, const int *offsets, int flags, int ntext, double scale,
                const float *q, const float *k, const float *v,
                int64_t n_rows, const int64_t *rows, double *o, double *lse)
 {
     problem p;
-    if (!make_problem(&p, B, H, D, grid, tile, windows, offsets, flags, scale, q, k, v, NULL))
+    if (!make_problem(&p, B, H, D, grid, tile, windows, offsets, flags, ntext, scale, q, k, v, NULL))
         return 0;
     int ok = 1;
 #pragma omp parallel
@@ -384,13 +396,13 @@ static int64_t row_stats(const problem *p, int b, int h, int64_t i,
  * Returns 0 on invalid arguments or allocation failure, else 1.
  */
 int oracle_bwd(int B, int H, int D, const int grid[3], const int tile[3],
-               const int *windows, const int *offsets, int flags, double scale,
+               const int *windows, const int *offsets, int flags, int ntext, double scale,
                const float *q, const float *k, const float *v, const float *dout,
                int64_t n_q, const int64_t *qrows, double *dq,
                int64_t n_k, const int64_t *krows, double *dk, double *dv)
 {
     problem p;
-    if (!make_problem(&p, B, H, D, grid, tile, windows, offsets, flags, scale, q, k, v, dout))
+    if (!make_problem(&p, B, H, D, grid, tile, windows, offsets, flags, ntext, scale, q, k, v, dout))
         return 0;
     int ok = 1;
 

@@ -9,6 +9,7 @@ import sys
 from oracle import oracle
 from tests import test_oracle_attention as A
 from tests import test_oracle_index as I
+from tests import test_oracle_joint_text as J
 from tests import test_oracle_perm as P
 from tests import test_oracle_window_options as W
 from tests.conftest import read_golden
@@ -46,6 +47,13 @@ def checks():
     for border in ("shift", "truncate"):
         yield (lambda b: lambda: W.test_head_offsets_reduce_to_shared_and_single_head(b))(border)
         yield (lambda b: lambda: W.test_attention_options_match_torch_dense(b))(border)
+        for nt in (1, 7):
+            yield (lambda b, n: lambda: J.test_joint_matches_torch_dense(b, n))(border, nt)
+    yield lambda: J.test_text_rows_are_unmasked_attention()
+    yield lambda: J.test_video_rows_merge_window_and_text_keys()
+    yield lambda: J.test_whole_grid_window_with_text_is_full_attention()
+    yield lambda: J.test_zero_text_tokens_equal_video_only()
+    yield lambda: J.test_text_permutation_equivariance()
 
 
 def main(path):

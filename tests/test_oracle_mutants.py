@@ -47,6 +47,10 @@ MUTANTS = {
     "truncate-centre-not-clamped-low": ("if (centre < 0) centre = 0;", ""),
     "head-offsets-ignore-head-stride": ("((flags & ORACLE_HEAD_OFFS) ? h * T : 0)",
                                         "((flags & ORACLE_HEAD_OFFS) ? h : 0)"),
+    "text-keys-hidden-from-video": ("if (i >= p->Nv || j >= p->Nv)\n        return 1;",
+                                    "if (i >= p->Nv)\n        return 1;\n    if (j >= p->Nv)\n        return 0;"),
+    "text-queries-see-text-only": ("if (i >= p->Nv || j >= p->Nv)\n        return 1;",
+                                   "if (j >= p->Nv)\n        return 1;\n    if (i >= p->Nv)\n        return 0;"),
 }
 
 
