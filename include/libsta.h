@@ -12,6 +12,10 @@
  *     for the motion-adaptive 3D Deformable Slide Attention (3D-DSA) of
  *     "MegaSlide-DiT: Memory-Centric Adaptation and Deformable Local
  *     Attention for Efficient Video Diffusion" (abstract).
+ * Joint text + video sequences (the *_ex attention calls): text tokens
+ * follow the video tokens; a pair with a text token on either side is
+ * always attended (token-type-aware masking, MOD-DiT README mirror,
+ * "Token-Type-Aware Masking").
  *
  * Window rule (the pages give none; this is the reading used throughout):
  * on each axis with n tiles and window size w, the window holds
@@ -251,6 +255,55 @@ sta_status sta_bwd_parts(const void *q, const void *k, const void *v, const void
                          const void *dout, void *dq, void *dk, void *dv, float *delta_ws,
                          int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
                          const sta_geom *g, const sta_index *idx, int32_t parts, hipStream_t stream);
+
+/* Options of the attention calls.  A NULL pointer means all fields 0. */
+typedef struct {
+    /* Text tokens appended after the N video tokens of every (b, h) slab
+     * (>= 0).  Attention tensors become [B][H][N + n_text][D] (lse and
+     * delta_ws [B][H][N + n_text]): rows 0..N-1 are the video tokens in tile
+     * order, rows N.. the text tokens in the caller's order.  A text query
+     * attends every key, every query attends every text key, and video
+     * pairs keep the tile window.  The index is that of the video grid. */
+    int32_t n_text;
+} sta_attn_opts;
+
+/*
+ * sta_tile_reorder over slabs of N + opts->n_text rows: the first N rows
+ * are permuted as by sta_tile_reorder, the text rows after them are copied
+ * to the same place.  opts may be NULL (= sta_tile_reorder).  STA_ERR_INVALID
+ * for n_text < 0.
+ */
+sta_status sta_tile_reorder_ex(const void *src, void *dst, int64_t outer, int64_t row_bytes,
+                               const sta_geom *g, int32_t inverse, const sta_attn_opts *opts,
+                               hipStream_t stream);
+
+/*
+ * sta_fwd with options (opts may be NULL = sta_fwd).  With opts->n_text = M
+ * > 0, for query row i of a slab of N + M rows the keys j are: for i < N
+ * (video) the rows of the tiles listed for tile(i) and the text rows N..;
+ * for i >= N (text) every row.  Formulas, dtypes and errors as sta_fwd; the
+ * bf16 workspace grows to B*H*(num_tiles + ceil(M/L))*D*Lp*2 bytes.
+ * STA_ERR_INVALID for n_text < 0; STA_ERR_UNSUPPORTED when N + n_text
+ * exceeds 2^30 rows.
+ * Source: token-type-aware masking of joint text-video attention (MOD-DiT
+ * README, "Token-Type-Aware Masking") over STA's tile windows.
+ */
+sta_status sta_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
+                      const sta_geom *g, const sta_index *idx, const sta_attn_opts *opts,
+                      hipStream_t stream);
+
+/*
+ * sta_bwd_parts with options (opts may be NULL = sta_bwd_parts): the
+ * gradients of sta_fwd_ex with the same opts, key set as there.  delta_ws
+ * holds B*H*(N + n_text) floats.  Errors as sta_bwd_parts and sta_fwd_ex.
+ * Source: as sta_fwd_ex and sta_bwd.
+ */
+sta_status sta_bwd_ex(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                      const void *dout, void *dq, void *dk, void *dv, float *delta_ws,
+                      int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
+                      const sta_geom *g, const sta_index *idx, int32_t parts, const sta_attn_opts *opts,
+                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,9 @@ library is missing, importing this package raises.
 Operator: "Fast Video Generation with Sliding Tile Attention" (abstract) --
 attention restricted to a window of tiles around each query tile of the
 (T,H,W) video token grid; optional per-query-tile window shifts stand in for
-the deformable windows (3D-DSA) of "MegaSlide-DiT" (abstract).
+the deformable windows (3D-DSA) of "MegaSlide-DiT" (abstract).  Joint text +
+video sequences (``n_text`` text tokens after the video tokens) follow the
+token-type-aware masking of the MOD-DiT README ("Token-Type-Aware Masking").
 """
 import ctypes
 import os
@@ -25,7 +27,8 @@ STA_BF16, STA_F32 = 0, 1
 STA_BWD_DELTA, STA_BWD_DKDV, STA_BWD_DQ, STA_BWD_ALL = 1, 2, 4, 7
 STA_BORDER_SHIFT, STA_BORDER_TRUNCATE = 0, 1
 EXPORTS = ("sta_status_str", "sta_last_error", "sta_version", "sta_index_dims", "sta_index_dims_ex",
-           "sta_tile_reorder", "sta_build_index", "sta_build_index_ex", "sta_fwd", "sta_bwd", "sta_bwd_parts")
+           "sta_tile_reorder", "sta_tile_reorder_ex", "sta_build_index", "sta_build_index_ex", "sta_fwd",
+           "sta_fwd_ex", "sta_bwd", "sta_bwd_parts", "sta_bwd_ex")
 
 
 class StaError(RuntimeError):
@@ -49,6 +52,10 @@ class sta_index_opts(ctypes.Structure):
     _fields_ = [("border", ctypes.c_int32), ("per_head_offsets", ctypes.c_int32)]
 
 
+class sta_attn_opts(ctypes.Structure):
+    _fields_ = [("n_text", ctypes.c_int32)]
+
+
 class sta_index(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("num_tiles", ctypes.c_int32),
                 ("max_kv", ctypes.c_int32), ("max_q", ctypes.c_int32),
@@ -63,6 +70,7 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     G, X, OP = ctypes.POINTER(sta_geom), ctypes.POINTER(sta_index), ctypes.POINTER(sta_index_opts)
+    AO = ctypes.POINTER(sta_attn_opts)
     W = ctypes.POINTER(sta_dim3)
     sig = {
         "sta_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -71,12 +79,16 @@ def _load():
         "sta_index_dims": (ctypes.c_int, [G, I32, W, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "sta_index_dims_ex": (ctypes.c_int, [G, I32, W, I32, OP, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
         "sta_tile_reorder": (ctypes.c_int, [P, P, I64, I64, G, I32, P]),
+        "sta_tile_reorder_ex": (ctypes.c_int, [P, P, I64, I64, G, I32, AO, P]),
         "sta_build_index": (ctypes.c_int, [G, I32, W, P, X, P]),
         "sta_build_index_ex": (ctypes.c_int, [G, I32, W, P, OP, X, P]),
         "sta_fwd": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X, P]),
+        "sta_fwd_ex": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X, AO, P]),
         "sta_bwd": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X, P]),
         "sta_bwd_parts": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X,
                                          I32, P]),
+        "sta_bwd_ex": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X,
+                                      I32, AO, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -169,6 +181,12 @@ def sta_tile_reorder(src, dst, outer, row_bytes, geom, inverse, stream=None):
                                 int(bool(inverse)), _stream(stream)))
 
 
+def sta_tile_reorder_ex(src, dst, outer, row_bytes, geom, inverse, n_text=0, stream=None):
+    opts = sta_attn_opts(int(n_text))
+    _check(lib.sta_tile_reorder_ex(_ptr(src), _ptr(dst), int(outer), int(row_bytes), ctypes.byref(geom.c()),
+                                   int(bool(inverse)), ctypes.byref(opts), _stream(stream)))
+
+
 def sta_build_index(geom, windows, offsets, index, stream=None):
     """offsets: None or int32 device tensor [num_tiles, 3]; index: StaIndex."""
     w, H = _windows(windows)
@@ -190,6 +208,12 @@ def sta_fwd(q, k, v, o, lse, B, H, D, dtype, scale, geom, index, stream=None):
                        ctypes.byref(geom.c()), ctypes.byref(index.c()), _stream(stream)))
 
 
+def sta_fwd_ex(q, k, v, o, lse, B, H, D, dtype, scale, geom, index, n_text=0, stream=None):
+    opts = sta_attn_opts(int(n_text))
+    _check(lib.sta_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, D, dtype, float(scale),
+                          ctypes.byref(geom.c()), ctypes.byref(index.c()), ctypes.byref(opts), _stream(stream)))
+
+
 def sta_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, scale, geom, index, stream=None):
     _check(lib.sta_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                        _ptr(dv), _ptr(delta_ws), B, H, D, dtype, float(scale), ctypes.byref(geom.c()),
@@ -201,6 +225,14 @@ def sta_bwd_parts(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, s
     _check(lib.sta_bwd_parts(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                              _ptr(dv), _ptr(delta_ws), B, H, D, dtype, float(scale), ctypes.byref(geom.c()),
                              ctypes.byref(index.c()), int(parts), _stream(stream)))
+
+
+def sta_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, scale, geom, index, parts,
+               n_text=0, stream=None):
+    opts = sta_attn_opts(int(n_text))
+    _check(lib.sta_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                          _ptr(dv), _ptr(delta_ws), B, H, D, dtype, float(scale), ctypes.byref(geom.c()),
+                          ctypes.byref(index.c()), int(parts), ctypes.byref(opts), _stream(stream)))
 
 
 # ------------------------------------------------- allocation helpers --
@@ -240,32 +272,38 @@ def _dtype_code(t):
     raise TypeError("libsta supports bfloat16 and float32 tensors, got %s" % t.dtype)
 
 
-def tile_reorder(x, geom, inverse=False, out=None, stream=None):
-    """Permute the token axis of a contiguous [..., N, C] tensor between
-    raster and tile order; returns a new tensor (or writes `out`)."""
-    assert x.is_contiguous() and x.shape[-2] == geom.tokens
+def tile_reorder(x, geom, inverse=False, out=None, stream=None, n_text=0):
+    """Permute the token axis of a contiguous [..., N + n_text, C] tensor
+    between raster and tile order (the n_text text rows after the grid's
+    tokens stay in place); returns a new tensor (or writes `out`)."""
+    S = geom.tokens + n_text
+    assert x.is_contiguous() and x.shape[-2] == S
     out = torch.empty_like(x) if out is None else out
     row_bytes = x.shape[-1] * x.element_size()
-    outer = x.numel() // (geom.tokens * x.shape[-1])
-    sta_tile_reorder(x, out, outer, row_bytes, geom, inverse, stream)
+    outer = x.numel() // (S * x.shape[-1])
+    sta_tile_reorder_ex(x, out, outer, row_bytes, geom, inverse, n_text, stream)
     return out
 
 
-def forward(q, k, v, geom, index, scale=None, stream=None):
-    """q, k, v [B,H,N,D] in tile order -> (o [B,H,N,D], lse [B,H,N] fp32)."""
-    B, H, N, D = q.shape
+def forward(q, k, v, geom, index, scale=None, stream=None, n_text=0):
+    """q, k, v [B,H,N+n_text,D] (video rows in tile order, then the text
+    rows) -> (o [B,H,N+n_text,D], lse [B,H,N+n_text] fp32)."""
+    B, H, S, D = q.shape
+    assert S == geom.tokens + n_text
     scale = D ** -0.5 if scale is None else scale
     o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    sta_fwd(q, k, v, o, lse, B, H, D, _dtype_code(q), scale, geom, index, stream)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    sta_fwd_ex(q, k, v, o, lse, B, H, D, _dtype_code(q), scale, geom, index, n_text, stream)
     return o, lse
 
 
-def backward(q, k, v, o, lse, dout, geom, index, scale=None, stream=None):
-    """Gradients (dq, dk, dv) of forward(); all tensors in tile order."""
-    B, H, N, D = q.shape
+def backward(q, k, v, o, lse, dout, geom, index, scale=None, stream=None, n_text=0):
+    """Gradients (dq, dk, dv) of forward(); same layout as forward()."""
+    B, H, S, D = q.shape
+    assert S == geom.tokens + n_text
     scale = D ** -0.5 if scale is None else scale
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    sta_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, D, _dtype_code(q), scale, geom, index, stream)
+    delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    sta_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, D, _dtype_code(q), scale, geom, index,
+               STA_BWD_ALL, n_text, stream)
     return dq, dk, dv

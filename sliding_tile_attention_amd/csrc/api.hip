@@ -63,6 +63,26 @@ static sta_status make_geo(const sta_geom *g, Geo &out)
     out.T = (int)T;
     out.L = tl[0] * tl[1] * tl[2];
     out.N = N;
+    out.text = 0;
+    out.Tt = 0;
+    out.TT = out.T;
+    out.S = N;
+    return STA_OK;
+}
+
+// Appends the text tokens of the attention options to a geometry.
+static sta_status add_text(Geo &g, const sta_attn_opts *opts)
+{
+    if (!opts || opts->n_text == 0) return STA_OK;
+    if (opts->n_text < 0)
+        return fail(STA_ERR_INVALID, "n_text must be >= 0 (got %d)", opts->n_text);
+    if (g.N + opts->n_text > kMaxTokens)
+        return fail(STA_ERR_UNSUPPORTED, "too many tokens: %lld video + %d text",
+                    (long long)g.N, opts->n_text);
+    g.text = opts->n_text;
+    g.Tt = (g.text + g.L - 1) / g.L;
+    g.TT = g.T + g.Tt;
+    g.S = g.N + g.text;
     return STA_OK;
 }
 
@@ -137,7 +157,7 @@ static sta_status check_attn(const Geo &g, int B, int H, int D, sta_dtype dt, fl
         return fail(STA_ERR_INVALID, "scale must be positive and finite");
     if (D != 64 && D != 128)
         return fail(STA_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", D);
-    if ((int64_t)B * H * g.N * D > ((int64_t)1 << 40))
+    if ((int64_t)B * H * g.S * D > ((int64_t)1 << 40))
         return fail(STA_ERR_UNSUPPORTED, "tensor too large");
     if (dt == STA_BF16 && g.L % 16 != 0)
         return fail(STA_ERR_UNSUPPORTED, "bf16 path needs tokens per tile to be a multiple of 16 (L=%d)", g.L);
@@ -163,7 +183,7 @@ const char *sta_status_str(sta_status s)
 
 const char *sta_last_error(void) { return g_err; }
 
-int32_t sta_version(void) { return 10100; }
+int32_t sta_version(void) { return 10200; }
 
 sta_status sta_index_dims(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
                           int32_t has_offsets, int32_t *max_kv, int32_t *max_q)
@@ -191,15 +211,25 @@ sta_status sta_index_dims_ex(const sta_geom *g, int32_t H, const sta_dim3 *windo
 sta_status sta_tile_reorder(const void *src, void *dst, int64_t outer, int64_t row_bytes,
                             const sta_geom *g, int32_t inverse, hipStream_t stream)
 {
+    return sta_tile_reorder_ex(src, dst, outer, row_bytes, g, inverse, nullptr, stream);
+}
+
+sta_status sta_tile_reorder_ex(const void *src, void *dst, int64_t outer, int64_t row_bytes,
+                               const sta_geom *g, int32_t inverse, const sta_attn_opts *opts,
+                               hipStream_t stream)
+{
     Geo geo;
     sta_status st = make_geo(g, geo);
     if (st != STA_OK) return st;
+    if ((st = add_text(geo, opts)) != STA_OK) return st;
     if (!src || !dst)
         return fail(STA_ERR_INVALID, "src and dst must be non-NULL");
     if (outer <= 0 || row_bytes <= 0)
         return fail(STA_ERR_INVALID, "outer and row_bytes must be positive");
-    int64_t bytes = outer * geo.N * row_bytes;
-    if (bytes / outer / geo.N != row_bytes || bytes > ((int64_t)1 << 42))
+    if (outer > ((int64_t)1 << 42) || row_bytes > ((int64_t)1 << 42))
+        return fail(STA_ERR_UNSUPPORTED, "tensor too large");
+    int64_t bytes = outer * geo.S * row_bytes;
+    if (bytes / outer / geo.S != row_bytes || bytes > ((int64_t)1 << 42))
         return fail(STA_ERR_UNSUPPORTED, "tensor too large");
     const char *a = (const char *)src, *b = (const char *)dst;
     if (a < b + bytes && b < a + bytes)
@@ -256,9 +286,18 @@ sta_status sta_fwd(const void *q, const void *k, const void *v, void *o, float *
                    int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
                    const sta_geom *g, const sta_index *idx, hipStream_t stream)
 {
+    return sta_fwd_ex(q, k, v, o, lse, B, H, D, dtype, scale, g, idx, nullptr, stream);
+}
+
+sta_status sta_fwd_ex(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
+                      const sta_geom *g, const sta_index *idx, const sta_attn_opts *opts,
+                      hipStream_t stream)
+{
     Geo geo;
     sta_status st = make_geo(g, geo);
     if (st != STA_OK) return st;
+    if ((st = add_text(geo, opts)) != STA_OK) return st;
     if ((st = check_attn(geo, B, H, D, dtype, scale)) != STA_OK) return st;
     if ((st = check_index(geo, H, idx, false)) != STA_OK) return st;
     if (!q || !k || !v || !o || !lse)
@@ -276,9 +315,20 @@ sta_status sta_bwd_parts(const void *q, const void *k, const void *v, const void
                          int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
                          const sta_geom *g, const sta_index *idx, int32_t parts, hipStream_t stream)
 {
+    return sta_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, scale, g, idx, parts, nullptr,
+                      stream);
+}
+
+sta_status sta_bwd_ex(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                      const void *dout, void *dq, void *dk, void *dv, float *delta_ws,
+                      int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
+                      const sta_geom *g, const sta_index *idx, int32_t parts, const sta_attn_opts *opts,
+                      hipStream_t stream)
+{
     Geo geo;
     sta_status st = make_geo(g, geo);
     if (st != STA_OK) return st;
+    if ((st = add_text(geo, opts)) != STA_OK) return st;
     if ((st = check_attn(geo, B, H, D, dtype, scale)) != STA_OK) return st;
     if (parts < 1 || parts > STA_BWD_ALL)
         return fail(STA_ERR_INVALID, "parts must be a non-empty mask of STA_BWD_DELTA|DKDV|DQ (got %d)", parts);

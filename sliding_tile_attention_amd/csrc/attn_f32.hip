@@ -5,6 +5,27 @@
 
 namespace sta {
 
+// Calls f(r) for every partner row r of row i of a slab: for a video row
+// the rows of its listed tiles, then the text rows; for a text row every
+// row (MOD-DiT README, "Token-Type-Aware Masking").
+template <typename F>
+__device__ inline void for_partners(int64_t i, int h, const Geo &g, const int32_t *idx, const int32_t *cnt_,
+                                    int max_e, F &&f)
+{
+    if (i >= g.N) {
+        for (int64_t r = 0; r < g.S; ++r) f(r);
+        return;
+    }
+    const int t = (int)(i / g.L);
+    const int cnt = cnt_[(int64_t)h * g.T + t];
+    const int32_t *lst = idx + ((int64_t)h * g.T + t) * max_e;
+    for (int e = 0; e < cnt; ++e) {
+        const int64_t r0 = (int64_t)lst[e] * g.L;
+        for (int rr = 0; rr < g.L; ++rr) f(r0 + rr);
+    }
+    for (int64_t r = g.N; r < g.S; ++r) f(r);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float *__restrict__ Q, const float *__restrict__ K,
                                                       const float *__restrict__ V, float *__restrict__ O,
@@ -13,37 +34,31 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float *__restrict__ 
                                                       int H, Geo g, float scale)
 {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= (int64_t)B * H * g.N) return;
-    const int64_t i = gid % g.N;
-    const int64_t bh = gid / g.N;
+    if (gid >= (int64_t)B * H * g.S) return;
+    const int64_t i = gid % g.S;
+    const int64_t bh = gid / g.S;
     const int h = (int)(bh % H);
-    const int qt = (int)(i / g.L);
-    const float *kb = K + bh * g.N * D;
-    const float *vb = V + bh * g.N * D;
+    const float *kb = K + bh * g.S * D;
+    const float *vb = V + bh * g.S * D;
     float q[D], acc[D];
     for (int d = 0; d < D; ++d) {
         q[d] = Q[gid * D + d];
         acc[d] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
-    const int cnt = kv_cnt[(int64_t)h * g.T + qt];
-    const int32_t *lst = kv_idx + ((int64_t)h * g.T + qt) * max_kv;
-    for (int e = 0; e < cnt; ++e) {
-        const int64_t j0 = (int64_t)lst[e] * g.L;
-        for (int jj = 0; jj < g.L; ++jj) {
-            const float *kr = kb + (j0 + jj) * D;
-            float s = 0.f;
-            for (int d = 0; d < D; ++d) s = fmaf(q[d], kr[d], s);
-            s *= scale;
-            const float mn = fmaxf(m, s);
-            const float alpha = expf(m - mn);   // m = -inf on the first key: alpha = 0
-            const float p = expf(s - mn);
-            l = l * alpha + p;
-            const float *vr = vb + (j0 + jj) * D;
-            for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vr[d], acc[d] * alpha);
-            m = mn;
-        }
-    }
+    for_partners(i, h, g, kv_idx, kv_cnt, max_kv, [&](int64_t j) {
+        const float *kr = kb + j * D;
+        float s = 0.f;
+        for (int d = 0; d < D; ++d) s = fmaf(q[d], kr[d], s);
+        s *= scale;
+        const float mn = fmaxf(m, s);
+        const float alpha = expf(m - mn);   // m = -inf on the first key: alpha = 0
+        const float p = expf(s - mn);
+        l = l * alpha + p;
+        const float *vr = vb + j * D;
+        for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vr[d], acc[d] * alpha);
+        m = mn;
+    });
     const float inv = 1.f / l;
     for (int d = 0; d < D; ++d) O[gid * D + d] = acc[d] * inv;
     LSE[gid] = m + logf(l);
@@ -69,13 +84,12 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float *__restrict__ Q
                                                      Geo g, float scale)
 {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= (int64_t)B * H * g.N) return;
-    const int64_t i = gid % g.N;
-    const int64_t bh = gid / g.N;
+    if (gid >= (int64_t)B * H * g.S) return;
+    const int64_t i = gid % g.S;
+    const int64_t bh = gid / g.S;
     const int h = (int)(bh % H);
-    const int qt = (int)(i / g.L);
-    const float *kb = K + bh * g.N * D;
-    const float *vb = V + bh * g.N * D;
+    const float *kb = K + bh * g.S * D;
+    const float *vb = V + bh * g.S * D;
     float q[D], go[D], acc[D];
     for (int d = 0; d < D; ++d) {
         q[d] = Q[gid * D + d];
@@ -83,23 +97,18 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float *__restrict__ Q
         acc[d] = 0.f;
     }
     const float lse = LSE[gid], dl = delta[gid];
-    const int cnt = kv_cnt[(int64_t)h * g.T + qt];
-    const int32_t *lst = kv_idx + ((int64_t)h * g.T + qt) * max_kv;
-    for (int e = 0; e < cnt; ++e) {
-        const int64_t j0 = (int64_t)lst[e] * g.L;
-        for (int jj = 0; jj < g.L; ++jj) {
-            const float *kr = kb + (j0 + jj) * D;
-            const float *vr = vb + (j0 + jj) * D;
-            float s = 0.f, dp = 0.f;
-            for (int d = 0; d < D; ++d) {
-                s = fmaf(q[d], kr[d], s);
-                dp = fmaf(go[d], vr[d], dp);
-            }
-            const float p = expf(s * scale - lse);
-            const float ds = p * (dp - dl);
-            for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, kr[d], acc[d]);
+    for_partners(i, h, g, kv_idx, kv_cnt, max_kv, [&](int64_t j) {
+        const float *kr = kb + j * D;
+        const float *vr = vb + j * D;
+        float s = 0.f, dp = 0.f;
+        for (int d = 0; d < D; ++d) {
+            s = fmaf(q[d], kr[d], s);
+            dp = fmaf(go[d], vr[d], dp);
         }
-    }
+        const float p = expf(s * scale - lse);
+        const float ds = p * (dp - dl);
+        for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, kr[d], acc[d]);
+    });
     for (int d = 0; d < D; ++d) dQ[gid * D + d] = acc[d] * scale;
 }
 
@@ -113,15 +122,14 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float *__restrict__
                                                        Geo g, float scale)
 {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= (int64_t)B * H * g.N) return;
-    const int64_t j = gid % g.N;
-    const int64_t bh = gid / g.N;
+    if (gid >= (int64_t)B * H * g.S) return;
+    const int64_t j = gid % g.S;
+    const int64_t bh = gid / g.S;
     const int h = (int)(bh % H);
-    const int kt = (int)(j / g.L);
-    const float *qb = Q + bh * g.N * D;
-    const float *ob = dO + bh * g.N * D;
-    const float *lb = LSE + bh * g.N;
-    const float *db = delta + bh * g.N;
+    const float *qb = Q + bh * g.S * D;
+    const float *ob = dO + bh * g.S * D;
+    const float *lb = LSE + bh * g.S;
+    const float *db = delta + bh * g.S;
     float k[D], v[D], ak[D], av[D];
     for (int d = 0; d < D; ++d) {
         k[d] = K[gid * D + d];
@@ -129,26 +137,21 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float *__restrict__
         ak[d] = 0.f;
         av[d] = 0.f;
     }
-    const int cnt = q_cnt[(int64_t)h * g.T + kt];
-    const int32_t *lst = q_idx + ((int64_t)h * g.T + kt) * max_q;
-    for (int e = 0; e < cnt; ++e) {
-        const int64_t i0 = (int64_t)lst[e] * g.L;
-        for (int ii = 0; ii < g.L; ++ii) {
-            const float *qr = qb + (i0 + ii) * D;
-            const float *gr = ob + (i0 + ii) * D;
-            float s = 0.f, dp = 0.f;
-            for (int d = 0; d < D; ++d) {
-                s = fmaf(qr[d], k[d], s);
-                dp = fmaf(gr[d], v[d], dp);
-            }
-            const float p = expf(s * scale - lb[i0 + ii]);
-            const float ds = p * (dp - db[i0 + ii]);
-            for (int d = 0; d < D; ++d) {
-                av[d] = fmaf(p, gr[d], av[d]);
-                ak[d] = fmaf(ds, qr[d], ak[d]);
-            }
+    for_partners(j, h, g, q_idx, q_cnt, max_q, [&](int64_t i) {
+        const float *qr = qb + i * D;
+        const float *gr = ob + i * D;
+        float s = 0.f, dp = 0.f;
+        for (int d = 0; d < D; ++d) {
+            s = fmaf(qr[d], k[d], s);
+            dp = fmaf(gr[d], v[d], dp);
         }
-    }
+        const float p = expf(s * scale - lb[i]);
+        const float ds = p * (dp - db[i]);
+        for (int d = 0; d < D; ++d) {
+            av[d] = fmaf(p, gr[d], av[d]);
+            ak[d] = fmaf(ds, qr[d], ak[d]);
+        }
+    });
     for (int d = 0; d < D; ++d) {
         dK[gid * D + d] = ak[d] * scale;
         dV[gid * D + d] = av[d];
@@ -160,7 +163,7 @@ static dim3 grid_for(int64_t threads) { return dim3((unsigned)((threads + 255) /
 sta_status launch_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse, int B, int H,
                           int D, float scale, const Geo &g, const sta_index &idx, hipStream_t s)
 {
-    const int64_t rows = (int64_t)B * H * g.N;
+    const int64_t rows = (int64_t)B * H * g.S;
     if (!grid_fits((rows + 255) / 256, 256))
         return fail(STA_ERR_UNSUPPORTED, "fp32 path: too many rows");
     if (D == 64)
@@ -176,7 +179,7 @@ sta_status launch_bwd_f32(const float *q, const float *k, const float *v, const 
                           const float *dout, float *dq, float *dk, float *dv, float *delta, int B, int H, int D,
                           float scale, const Geo &g, const sta_index &idx, int parts, hipStream_t s)
 {
-    const int64_t rows = (int64_t)B * H * g.N;
+    const int64_t rows = (int64_t)B * H * g.S;
     if (!grid_fits((rows + 255) / 256, 256))
         return fail(STA_ERR_UNSUPPORTED, "fp32 path: too many rows");
     const dim3 grid = grid_for(rows), blk(256);

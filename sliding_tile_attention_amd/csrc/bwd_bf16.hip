@@ -15,6 +15,10 @@
 //   3. dkdv: key-stationary, walks each key tile's TRANSPOSED list (the query
 //      tiles whose window holds it) and accumulates dK and dV in registers.
 // S and dP are recomputed in both 2 and 3.
+// Joint text + video sequences (MOD-DiT README, "Token-Type-Aware
+// Masking"): both walks continue past their list into the text
+// pseudo-tiles, and a text pseudo-tile walks every video tile first (every
+// query attends the text keys; a text query attends every key).
 //
 // MFMA orientation (see mfma.h for the fragment conventions):
 //   dq:   S^T = K Q^T, dP^T = V dO^T      (A = K / V rows from LDS, B = Q / dO
@@ -134,26 +138,29 @@ __device__ inline void static_for(F &&f)
     }
 }
 
-// Position in a key- or query-tile list walked block by block (no
-// divisions); the next tile id is prefetched when a tile is entered.
+// Position in a walk over the tiles of a key- or query-tile list and then
+// the text pseudo-tiles, block by block (no divisions); the next tile id is
+// prefetched when a tile is entered.
 struct ListWalk {
-    int e, r0, tile, next;
+    int e, r0, tile, len, next;
 };
-__device__ inline void walk_init(ListWalk &w, const int32_t *lst, int cnt)
+__device__ inline void walk_init(ListWalk &w, const int32_t *lst, int cnt, const Geo &g)
 {
     w.e = 0;
     w.r0 = 0;
-    w.tile = cnt > 0 ? lst[0] : 0;
-    w.next = cnt > 1 ? lst[1] : 0;
+    w.tile = entry_tile(lst, cnt, g.T, 0);
+    w.len = tile_rows(g, w.tile);
+    w.next = entry_tile(lst, cnt, g.T, 1);
 }
-__device__ inline void walk_next(ListWalk &w, const int32_t *lst, int cnt, int step, int L)
+__device__ inline void walk_next(ListWalk &w, const int32_t *lst, int cnt, int step, const Geo &g)
 {
     w.r0 += step;
-    if (w.r0 >= L) {
+    if (w.r0 >= w.len) {
         w.r0 = 0;
         ++w.e;
         w.tile = w.next;
-        w.next = w.e + 1 < cnt ? lst[w.e + 1] : 0;
+        w.len = tile_rows(g, w.tile);
+        w.next = entry_tile(lst, cnt, g.T, w.e + 1);
     }
 }
 
@@ -188,19 +195,19 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
         else return slot2;
     };
 
-    const int work = xcd_remap(blockIdx.x, total);
-    const int rb = work % rblocks;
-    const int qt = (work / rblocks) % g.T;
-    const int bh = work / (rblocks * g.T);
+    int bh, qt, rb;
+    decode_item(xcd_remap(blockIdx.x, total), rblocks, g, bh, qt, rb);
+    const int qlen = tile_rows(g, qt);               // query rows of this tile
+    if (rb * M >= qlen) return;                      // row block past a ragged text pseudo-tile
     const int h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, grp = lane >> 5;
     const int L = g.L;
-    const int64_t base = (int64_t)bh * g.N * D;
+    const int64_t base = (int64_t)bh * g.S * D;
     const int row = rb * M + wave * 32 + l32;        // query row (inside the tile) of this lane
-    const bool row_ok = row < L;
-    const int64_t grow = (int64_t)qt * L + (row_ok ? row : L - 1);
+    const bool row_ok = row < qlen;
+    const int64_t grow = (int64_t)qt * L + (row_ok ? row : qlen - 1);
 
     bf16x8 qf[KS], of[KS];
 #pragma unroll
@@ -208,8 +215,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
         qf[ks] = ld8(Q + base + grow * D + ks * 16 + grp * 8);
         of[ks] = ld8(dO + base + grow * D + ks * 16 + grp * 8);
     }
-    const float nlse2 = -LSE[(int64_t)bh * g.N + grow] * 1.4426950408889634f;
-    const float dlt = Delta[(int64_t)bh * g.N + grow];
+    const float nlse2 = -LSE[(int64_t)bh * g.S + grow] * 1.4426950408889634f;
+    const float dlt = Delta[(int64_t)bh * g.S + grow];
     // Q, dO, LSE, Delta complete before the first copy (later waits leave
     // copies in flight, which would otherwise guard every use of them).
     wait_vmem<0>();
@@ -220,10 +227,11 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    const int cnt = kv_cnt[(int64_t)h * g.T + qt];
-    const int32_t *lst = kv_idx + ((int64_t)h * g.T + qt) * max_kv;
-    const int nkb = (L + BN - 1) / BN;
-    const int nblk = cnt * nkb;
+    // key tiles: the window's list, or every video tile for a text query
+    const bool video_q = qt < g.T;
+    const int cnt = video_q ? kv_cnt[(int64_t)h * g.T + qt] : g.T;
+    const int32_t *lst = video_q ? kv_idx + ((int64_t)h * g.T + qt) * max_kv : nullptr;
+    const int nblk = walk_blocks(g, cnt, BN);
 
     // LDS offsets: a row's swizzle only XORs granule bits, and the granule
     // bits that vary with the step (ks) or column block (db) sit above the
@@ -237,13 +245,13 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
 
     const RowCopy<D, THREADS, BN> rc(tid);
     ListWalk cw;                                    // next key block to copy
-    walk_init(cw, lst, cnt);
+    walk_init(cw, lst, cnt, g);
     auto gload = [&](auto bc) {
-        const int valid = L - cw.r0 < BN ? L - cw.r0 : BN;
+        const int valid = cw.len - cw.r0 < BN ? cw.len - cw.r0 : BN;
         const int64_t row0 = (int64_t)cw.tile * L + cw.r0;
         rc.copy(K + base + row0 * D, valid, stage(bc), wave);
         rc.copy(V + base + row0 * D, valid, stage(bc) + BLK, wave);
-        walk_next(cw, lst, cnt, BN, L);
+        walk_next(cw, lst, cnt, BN, g);
     };
 
     auto step = [&](auto bufc, int blk) {
@@ -336,20 +344,20 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
         else return slot2;
     };
 
-    const int work = xcd_remap(blockIdx.x, total);
-    const int rb = work % rblocks;
-    const int kt = (work / rblocks) % g.T;
-    const int bh = work / (rblocks * g.T);
+    int bh, kt, rb;
+    decode_item(xcd_remap(blockIdx.x, total), rblocks, g, bh, kt, rb);
+    const int klen = tile_rows(g, kt);               // key rows of this tile
+    if (rb * M >= klen) return;                      // row block past a ragged text pseudo-tile
     const int h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, grp = lane >> 5;
     const int L = g.L;
-    const int64_t base = (int64_t)bh * g.N * D;
-    const int64_t sbase = (int64_t)bh * g.N;
+    const int64_t base = (int64_t)bh * g.S * D;
+    const int64_t sbase = (int64_t)bh * g.S;
     const int krow0 = rb * M + wave * 32;            // first key row (inside the tile) of this wave
     const int krow = krow0 + l32;
-    const int64_t gk = (int64_t)kt * L + (krow < L ? krow : L - 1);
+    const int64_t gk = (int64_t)kt * L + (krow < klen ? krow : klen - 1);
 
     bf16x8 kf[KS], vf[KS];
 #pragma unroll
@@ -364,10 +372,11 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
 
-    const int cnt = q_cnt[(int64_t)h * g.T + kt];
-    const int32_t *lst = q_idx + ((int64_t)h * g.T + kt) * max_q;
-    const int nqb = (L + BQ - 1) / BQ;
-    const int nblk = cnt * nqb;
+    // query tiles: the transposed list, or every video tile for a text key
+    const bool video_k = kt < g.T;
+    const int cnt = video_k ? q_cnt[(int64_t)h * g.T + kt] : g.T;
+    const int32_t *lst = video_k ? q_idx + ((int64_t)h * g.T + kt) * max_q : nullptr;
+    const int nblk = walk_blocks(g, cnt, BQ);
 
     // LDS offsets: a row's swizzle only XORs granule bits, and the granule
     // bits that vary with the step (ks) or column block (db) sit above the
@@ -381,9 +390,9 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 
     const RowCopy<D, THREADS, BQ> rc(tid);
     ListWalk cw;                                    // next query block to copy
-    walk_init(cw, lst, cnt);
+    walk_init(cw, lst, cnt, g);
     auto gload = [&](auto bc) {
-        const int valid = L - cw.r0 < BQ ? L - cw.r0 : BQ;
+        const int valid = cw.len - cw.r0 < BQ ? cw.len - cw.r0 : BQ;
         const int64_t row0 = (int64_t)cw.tile * L + cw.r0;
         __bf16 *st = stage(bc);
         rc.copy(Q + base + row0 * D, valid, st, wave);
@@ -396,7 +405,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rd, (__attribute__((address_space(3))) void *)(st + 2 * BLK + 2 * SROWS), 4, lane * 4, 0, 0, 0);
         }
-        walk_next(cw, lst, cnt, BQ, L);
+        walk_next(cw, lst, cnt, BQ, g);
     };
 
     auto step = [&](auto bufc, int blk) {
@@ -479,7 +488,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int kr = krow0 + mfma_row(lane, r);
-        if (kr < L) {
+        if (kr < klen) {
             const int64_t o = base + ((int64_t)kt * L + kr) * D + l32;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
@@ -514,9 +523,9 @@ static sta_status run_bwd(const void *q, const void *k, const void *v, const voi
                           const Geo &g, const sta_index &idx, int parts, hipStream_t s)
 {
     constexpr int NW = STA_BWD_NW, BN = STA_BWD_BN, BQ = STA_BWD_BQ, M = NW * 32;
-    const int64_t rows = (int64_t)B * H * g.N;
+    const int64_t rows = (int64_t)B * H * g.S;
     const int rblocks = (g.L + M - 1) / M;
-    const int64_t total = (int64_t)B * H * g.T * rblocks;
+    const int64_t total = (int64_t)B * H * g.TT * rblocks;
     if (!grid_fits(total, NW * 64) || !grid_fits((rows * (D / 8) + 255) / 256, 256))
         return fail(STA_ERR_UNSUPPORTED, "too many work items");
     const float scale_log2 = scale * 1.4426950408889634f;

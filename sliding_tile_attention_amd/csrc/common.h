@@ -10,14 +10,63 @@ namespace sta {
 
 // Geometry in the form the kernels use.  tile order: tile id * L + in-tile
 // raster index; tile id raster over (nt, nh, nw).
+// Joint text + video sequences: `text` text tokens follow the N video
+// tokens of every (b, h) slab (S = N + text rows).  The kernels walk them as
+// Tt text pseudo-tiles T .. T+Tt-1 of L rows each (the last one ragged), so
+// that pseudo-tile t starts at slab row t * L like a video tile.
 struct Geo {
     int gt, gh, gw;   // token grid
     int tt, th, tw;   // tile extents
     int nt, nh, nw;   // tiles per axis
     int T;            // number of tiles
     int L;            // tokens per tile
-    int64_t N;        // tokens
+    int64_t N;        // video tokens
+    int text;         // text tokens after the video tokens
+    int Tt;           // text pseudo-tiles, ceil(text / L)
+    int TT;           // T + Tt
+    int64_t S;        // rows per (b, h) slab, N + text
 };
+
+// Rows of tile t: L for a video tile, the text rows it holds for a text
+// pseudo-tile.
+__host__ __device__ inline int tile_rows(const Geo &g, int t)
+{
+    if (t < g.T) return g.L;
+    const int r = g.text - (t - g.T) * g.L;
+    return r < g.L ? r : g.L;
+}
+
+// Tile of entry e of a walk: the cnt tiles of a list (lst, or every video
+// tile in order when lst is null), then the text pseudo-tiles.  Token-type-
+// aware masking (MOD-DiT README, "Token-Type-Aware Masking"): every query
+// attends the text keys, and a text query attends every key.
+__host__ __device__ inline int entry_tile(const int32_t *lst, int cnt, int T, int e)
+{
+    return e < cnt ? (lst ? lst[e] : e) : T + (e - cnt);
+}
+
+// Blocks of `step` rows in a walk over cnt video tiles and every text
+// pseudo-tile.
+__host__ __device__ inline int walk_blocks(const Geo &g, int cnt, int step)
+{
+    const int per = (g.L + step - 1) / step;
+    if (g.Tt == 0) return cnt * per;
+    const int last = g.text - (g.Tt - 1) * g.L;
+    return cnt * per + (g.Tt - 1) * per + (last + step - 1) / step;
+}
+
+// Work item of a query- (or key-) stationary kernel: rblocks row blocks of
+// every tile of every (b, h); per (b, h) the text pseudo-tiles come first,
+// since their walks over every tile are the longest.
+__device__ inline void decode_item(int work, int rblocks, const Geo &g, int &bh, int &tile, int &rb)
+{
+    const int per = g.TT * rblocks;
+    bh = work / per;
+    const int it = work - bh * per;
+    const int t = it / rblocks;
+    rb = it - t * rblocks;
+    tile = t < g.Tt ? g.T + t : t - g.Tt;
+}
 
 // Window start and count on one axis (window rule of the library header).
 __host__ __device__ inline void axis_window(int n, int w, int q, int o, int &s, int &c)
@@ -49,6 +98,7 @@ sta_status fail(sta_status s, const char *fmt, ...);
 int axis_max_attendees(int n, int w);
 
 // ---- launchers (one per source file) ----
+// text rows after the grid's tokens of every slab are copied unchanged
 sta_status launch_reorder(const void *src, void *dst, int64_t outer, int64_t row_bytes,
                           const Geo &g, bool inverse, hipStream_t s);
 

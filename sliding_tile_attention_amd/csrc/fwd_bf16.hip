@@ -6,14 +6,20 @@
 // walks that tile's key-tile list and never masks inside a tile.
 //
 // Two launches:
-//   1. vt_kernel: V^T of every tile, [b,h,tile][D][Lp] with the key axis
-//      padded with zeros to Lp (a multiple of the key block), into a
-//      stream-ordered workspace.  Every V tile is read by ~45 query tiles'
+//   1. vt_kernel: V^T of every tile (and text pseudo-tile), [b,h,tile][D][Lp]
+//      with the key axis padded with zeros to Lp (a multiple of the key
+//      block), into a stream-ordered workspace.  Every V tile is read by ~45 query tiles'
 //      workgroups, so transposing it once lets the PV product fetch its
 //      operand with full-width LDS reads instead of transposing reads,
 //      which move half the bytes per LDS instruction -- the LDS port, not
 //      the matrix cores, is what bounds this kernel.
 //   2. fwd_bf16_kernel, below.
+//
+// Joint text + video sequences (MOD-DiT README, "Token-Type-Aware
+// Masking"): after its listed tiles a video query tile walks the text
+// pseudo-tiles; a text pseudo-tile's queries walk every video tile and then
+// the text.  Key rows past a pseudo-tile's ragged end are masked like
+// those past any block end.
 //
 // Work decomposition
 //   workgroup = NW waves = M = NW*QB*32 consecutive query rows of one query
@@ -81,15 +87,18 @@ __device__ inline int swz_row(int r)
 constexpr int kVtPad = 64;
 
 template <int D>
-__global__ __launch_bounds__(256) void vt_kernel(const __bf16 *__restrict__ V, __bf16 *__restrict__ VT, int L,
+__global__ __launch_bounds__(256) void vt_kernel(const __bf16 *__restrict__ V, __bf16 *__restrict__ VT, Geo g,
                                                  int Lp, int chunks)
 {
     // one workgroup per 64-key chunk of one (b, h, tile)
     __shared__ uint32_t tile[64][D / 2 + 1];   // 64 keys x D values as bf16 pairs; odd stride: no conflicts
     const int c = (int)(blockIdx.x % (unsigned)chunks);
     const int64_t bt = blockIdx.x / (unsigned)chunks;
+    const int64_t bh = bt / g.TT;
+    const int t = (int)(bt - bh * g.TT);
+    const int L = tile_rows(g, t);
     const int k0 = c * 64;
-    const __bf16 *src = V + (bt * L + k0) * D;
+    const __bf16 *src = V + (bh * g.S + (int64_t)t * g.L + k0) * D;
     constexpr int RG = D / 8;                 // 16-byte granules per V row
     for (int i = threadIdx.x; i < 64 * RG; i += 256) {
         const int r = i / RG, gc = i % RG;
@@ -127,17 +136,17 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     using C = FwdCfg<D, NW, QB, BN>;
     __shared__ __attribute__((aligned(1024))) __bf16 smem[2 * C::STAGE];
 
-    const int work = xcd_remap(blockIdx.x, total);
-    const int rb = work % rblocks;
-    const int qt = (work / rblocks) % g.T;
-    const int bh = work / (rblocks * g.T);
+    int bh, qt, rb;
+    decode_item(xcd_remap(blockIdx.x, total), rblocks, g, bh, qt, rb);
+    const int qlen = tile_rows(g, qt);               // query rows of this tile
+    if (rb * C::M >= qlen) return;                   // row block past a ragged text pseudo-tile
     const int h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, grp = lane >> 5;
     const int L = g.L;
-    const int64_t base = (int64_t)bh * g.N * D;
-    const int64_t vt_base = (int64_t)bh * g.T * D * Lp;
+    const int64_t base = (int64_t)bh * g.S * D;
+    const int64_t vt_base = (int64_t)bh * g.TT * D * Lp;
     const int wrow0 = rb * C::M + wave * QB * 32;   // first row of this wave inside the tile
 
     // Q fragments: B operand of S^T = K Q^T, lane = query row, 8 columns.
@@ -147,7 +156,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         const int row = wrow0 + qb * 32 + l32;
         const __bf16 *p = Q + base + ((int64_t)qt * L + row) * D + grp * 8;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) qf[qb][ks] = row < L ? ld8(p + ks * 16) : zero8();
+        for (int ks = 0; ks < C::KS; ++ks) qf[qb][ks] = row < qlen ? ld8(p + ks * 16) : zero8();
     }
 
     f32x16 acc[QB][C::DB];
@@ -162,10 +171,11 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
             for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.f;
     }
 
-    const int cnt = kv_cnt[(int64_t)h * g.T + qt];
-    const int32_t *lst = kv_idx + ((int64_t)h * g.T + qt) * max_kv;
-    const int nkb = (L + BN - 1) / BN;
-    const int nblk = cnt * nkb;
+    // key tiles: the window's list, or every video tile for a text query
+    const bool video_q = qt < g.T;
+    const int cnt = video_q ? kv_cnt[(int64_t)h * g.T + qt] : g.T;
+    const int32_t *lst = video_q ? kv_idx + ((int64_t)h * g.T + qt) * max_kv : nullptr;
+    const int nblk = walk_blocks(g, cnt, BN);
 
     // ---- per-lane offsets (bf16 elements), fixed for the whole kernel ----
     // Copies: wave-wide copy i of a block fills granule slots
@@ -203,14 +213,15 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     // copy stream is one block ahead of the compute stream; the next tile
     // id of the list is prefetched when a tile is entered.
     int c_e = 0, c_k0 = 0;                               // next block to copy
-    int c_tile = cnt > 0 ? lst[0] : 0;
-    int n_tile = cnt > 1 ? lst[1] : 0;
+    int c_tile = entry_tile(lst, cnt, g.T, 0);
+    int c_len = tile_rows(g, c_tile);
+    int n_tile = entry_tile(lst, cnt, g.T, 1);
     // Issue the asynchronous copy of the next block into LDS buffer `buf`
     // through buffer descriptors over that block: K rows past a ragged
     // tile end read as zero (their scores are masked), V^T keys past it are
     // the workspace's zero padding.
     auto gload = [&](int buf) {
-        const int valid = L - c_k0 < BN ? L - c_k0 : BN;
+        const int valid = c_len - c_k0 < BN ? c_len - c_k0 : BN;
         const auto rk = make_rsrc(K + base + ((int64_t)c_tile * L + c_k0) * D, valid * D * 2);
         const auto rv = make_rsrc(VT + vt_base + (int64_t)c_tile * D * Lp + c_k0, (D * Lp - c_k0) * 2);
         __bf16 *Ks = smem + buf * C::STAGE;
@@ -223,14 +234,16 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
             b2lds16(rv, gv[i], Vs + lds_off);
         }
         c_k0 += BN;
-        if (c_k0 >= L) {
+        if (c_k0 >= c_len) {
             c_k0 = 0;
             ++c_e;
             c_tile = n_tile;
-            n_tile = c_e + 1 < cnt ? lst[c_e + 1] : 0;
+            c_len = tile_rows(g, c_tile);
+            n_tile = entry_tile(lst, cnt, g.T, c_e + 1);
         }
     };
-    int s_k0 = 0;                                        // key offset of the block computed next
+    int s_e = 0, s_k0 = 0;                               // entry and key offset of the block computed next
+    int s_len = tile_rows(g, entry_tile(lst, cnt, g.T, 0));
 
     // One key block from LDS buffer BUF (a compile-time constant, so every
     // LDS address below is a per-lane register plus an immediate).
@@ -241,8 +254,13 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         if (blk + 1 < nblk) gload(1 - BUF);
         const __bf16 *Ks = smem + BUF * C::STAGE;
         const __bf16 *Vs = Ks + C::BLK;
-        const int valid = L - s_k0 < BN ? L - s_k0 : BN;
-        s_k0 = s_k0 + BN >= L ? 0 : s_k0 + BN;
+        const int valid = s_len - s_k0 < BN ? s_len - s_k0 : BN;
+        s_k0 += BN;
+        if (s_k0 >= s_len) {       // entry lengths: L for listed tiles, then the text pseudo-tiles'
+            s_k0 = 0;
+            ++s_e;
+            s_len = s_e < cnt ? L : tile_rows(g, g.T + (s_e - cnt));
+        }
 
         f32x16 s[QB][C::KB];
 #pragma unroll
@@ -335,7 +353,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         const float lt = sum_pair32(l_i[qb]);
         const float inv = 1.f / lt;
         const int row = wrow0 + qb * 32 + l32;
-        if (row < L) {
+        if (row < qlen) {
             __bf16 *op = O + base + ((int64_t)qt * L + row) * D;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
@@ -347,7 +365,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
                     *(bf16x4 *)(op + db * 32 + 8 * j + 4 * grp) = v;
                 }
             if (grp == 0)
-                LSE[(int64_t)bh * g.N + (int64_t)qt * L + row] = (m_i[qb] + __log2f(lt)) * 0.69314718055994531f;
+                LSE[(int64_t)bh * g.S + (int64_t)qt * L + row] = (m_i[qb] + __log2f(lt)) * 0.69314718055994531f;
         }
     }
 }
@@ -360,18 +378,18 @@ static sta_status run_fwd(const void *q, const void *k, const void *v, void *o, 
     using C = FwdCfg<D, NW, QB, BN>;
     static_assert(kVtPad % BN == 0, "V^T padding must be a multiple of the key block");
     const int rblocks = (g.L + C::M - 1) / C::M;
-    const int64_t total = (int64_t)B * H * g.T * rblocks;
+    const int64_t total = (int64_t)B * H * g.TT * rblocks;
     const int chunks = (g.L + kVtPad - 1) / kVtPad;
     const int Lp = chunks * kVtPad;
-    const int64_t vt_blocks = (int64_t)B * H * g.T * chunks;
+    const int64_t vt_blocks = (int64_t)B * H * g.TT * chunks;
     if (!grid_fits(total, C::THREADS) || !grid_fits(vt_blocks, 256))
         return fail(STA_ERR_UNSUPPORTED, "too many work items");
-    const size_t vt_bytes = (size_t)B * H * g.T * D * Lp * sizeof(__bf16);
+    const size_t vt_bytes = (size_t)B * H * g.TT * D * Lp * sizeof(__bf16);
     void *vt = nullptr;
     sta_status st = workspace_alloc(&vt, vt_bytes, s);
     if (st != STA_OK) return st;
     hipLaunchKernelGGL(vt_kernel<D>, dim3((unsigned)vt_blocks), dim3(256), 0, s, (const __bf16 *)v, (__bf16 *)vt,
-                       g.L, Lp, chunks);
+                       g, Lp, chunks);
     const float scale_log2 = scale * 1.4426950408889634f;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BN>), dim3((unsigned)total), dim3(C::THREADS), 0, s,
                        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)vt, (__bf16 *)o, lse, idx.kv_idx,

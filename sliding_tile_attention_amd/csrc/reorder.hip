@@ -5,6 +5,7 @@
 // thread owns one vector-sized chunk of one run and walks it through all
 // `outer` slabs, so the index arithmetic is paid once per chunk position
 // and every wave reads and writes contiguous, fully coalesced memory.
+// Text rows that follow the grid's tokens in a slab are copied in place.
 #include "common.h"
 
 namespace sta {
@@ -12,21 +13,28 @@ namespace sta {
 template <typename V>
 __global__ __launch_bounds__(256) void reorder_kernel(const V *__restrict__ src, V *__restrict__ dst,
                                                       int64_t outer, int64_t slab, int64_t row_vec,
-                                                      int64_t run_vec, int64_t chunks, Geo g, int inverse)
+                                                      int64_t run_vec, int64_t chunks, int64_t text_chunks, Geo g,
+                                                      int inverse)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < chunks; gid += stride) {
-        const int64_t u = gid / run_vec;     // run index, raster order of (t, h, w-tile)
-        const int64_t c = gid - u * run_vec; // chunk inside the run
-        const int jw = (int)(u % g.nw);
-        const int64_t th_ = u / g.nw;
-        const int h = (int)(th_ % g.gh);
-        const int t = (int)(th_ / g.gh);
-        const int64_t raster = ((int64_t)t * g.gh + h) * g.gw + (int64_t)jw * g.tw;
-        const int64_t tile_id = ((int64_t)(t / g.tt) * g.nh + h / g.th) * g.nw + jw;
-        const int64_t tiled = tile_id * g.L + ((int64_t)(t % g.tt) * g.th + h % g.th) * g.tw;
-        const int64_t s0 = (inverse ? tiled : raster) * row_vec + c;
-        const int64_t d0 = (inverse ? raster : tiled) * row_vec + c;
+    for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < chunks + text_chunks;
+         gid += stride) {
+        int64_t s0, d0;
+        if (gid < chunks) {
+            const int64_t u = gid / run_vec;     // run index, raster order of (t, h, w-tile)
+            const int64_t c = gid - u * run_vec; // chunk inside the run
+            const int jw = (int)(u % g.nw);
+            const int64_t th_ = u / g.nw;
+            const int h = (int)(th_ % g.gh);
+            const int t = (int)(th_ / g.gh);
+            const int64_t raster = ((int64_t)t * g.gh + h) * g.gw + (int64_t)jw * g.tw;
+            const int64_t tile_id = ((int64_t)(t / g.tt) * g.nh + h / g.th) * g.nw + jw;
+            const int64_t tiled = tile_id * g.L + ((int64_t)(t % g.tt) * g.th + h % g.th) * g.tw;
+            s0 = (inverse ? tiled : raster) * row_vec + c;
+            d0 = (inverse ? raster : tiled) * row_vec + c;
+        } else {                                 // text rows keep their place
+            s0 = d0 = g.N * row_vec + (gid - chunks);
+        }
         int64_t o = 0;
         for (; o + 4 <= outer; o += 4) {
             V a0 = __builtin_nontemporal_load(src + s0 + (o + 0) * slab);
@@ -55,11 +63,12 @@ static sta_status run(const void *src, void *dst, int64_t outer, int64_t row_byt
     const int64_t row_vec = row_bytes / vb;      // units per token row
     const int64_t run_vec = g.tw * row_vec;      // units per run of tw tokens
     const int64_t chunks = (g.N / g.tw) * run_vec;
-    const int64_t slab = g.N * row_vec;
-    int64_t blocks = (chunks + 255) / 256;
+    const int64_t text_chunks = (int64_t)g.text * row_vec;
+    const int64_t slab = g.S * row_vec;
+    int64_t blocks = (chunks + text_chunks + 255) / 256;
     if (blocks > (1 << 20)) blocks = 1 << 20;    // grid-stride loop covers the rest
     hipLaunchKernelGGL(reorder_kernel<V>, dim3((unsigned)blocks), dim3(256), 0, s, (const V *)src, (V *)dst,
-                       outer, slab, row_vec, run_vec, chunks, g, inverse ? 1 : 0);
+                       outer, slab, row_vec, run_vec, chunks, text_chunks, g, inverse ? 1 : 0);
     return check_launch();
 }
 

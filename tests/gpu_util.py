@@ -63,27 +63,36 @@ def assert_close(got, ref, dtype, what=""):
 
 class Layer:
     """Device state of one attention layer: inputs reordered to tile order,
-    the index, and the outputs converted back to raster order."""
+    the index, and the outputs converted back to raster order.  With n_text
+    > 0 the token axis holds the grid's tokens and then n_text text tokens,
+    which stay in place."""
 
-    def __init__(self, grid, tile, windows, offsets, q, k, v, dtype, dout=None, transposed=True, border="shift"):
+    def __init__(self, grid, tile, windows, offsets, q, k, v, dtype, dout=None, transposed=True, border="shift",
+                 n_text=0):
         self.geom = sta.Geometry(tuple(grid), tuple(tile))
         self.dtype = dtype
+        self.n_text = n_text
         self.B, self.H, self.N, self.D = q.shape
         self.windows = [tuple(int(x) for x in w) for w in windows]
         self.off_dev = None if offsets is None else torch.from_numpy(np.ascontiguousarray(offsets, np.int32)).cuda()
         self.index = sta.StaIndex(self.geom, self.windows, self.off_dev, transposed=transposed, border=border)
-        self.q, self.k, self.v = (sta.tile_reorder(to_dev(x, dtype), self.geom) for x in (q, k, v))
-        self.dout = None if dout is None else sta.tile_reorder(to_dev(dout, dtype), self.geom)
+        self.q, self.k, self.v = (self._tiled(to_dev(x, dtype)) for x in (q, k, v))
+        self.dout = None if dout is None else self._tiled(to_dev(dout, dtype))
+
+    def _tiled(self, x):
+        return sta.tile_reorder(x, self.geom, n_text=self.n_text)
+
+    def _raster(self, x):
+        return sta.tile_reorder(x, self.geom, inverse=True, n_text=self.n_text)
 
     def forward(self, scale=None):
-        self.o, self.lse = sta.forward(self.q, self.k, self.v, self.geom, self.index, scale)
-        return (sta.tile_reorder(self.o, self.geom, inverse=True),
-                sta.tile_reorder(self.lse.unsqueeze(-1), self.geom, inverse=True).squeeze(-1))
+        self.o, self.lse = sta.forward(self.q, self.k, self.v, self.geom, self.index, scale, n_text=self.n_text)
+        return self._raster(self.o), self._raster(self.lse.unsqueeze(-1)).squeeze(-1)
 
     def backward(self, scale=None):
         dq, dk, dv = sta.backward(self.q, self.k, self.v, self.o, self.lse, self.dout, self.geom, self.index,
-                                  scale)
-        return tuple(sta.tile_reorder(x, self.geom, inverse=True) for x in (dq, dk, dv))
+                                  scale, n_text=self.n_text)
+        return tuple(self._raster(x) for x in (dq, dk, dv))
 
 
 def sample_rows(B, H, N, L, grid, tile, per_head_tiles, rows_per_tile, seed):

@@ -12,6 +12,11 @@ numpy's PCG64: tensors from seed [1234 + cfg, stream, b, h] per (batch, head)
 slab, streams 0=Q 1=K 2=V 3=dO; window offsets (stream 4) and the per-head
 window choice (stream 5) from seed [1234 + cfg, stream].  bf16 workloads
 round the draws to bf16 (round-to-nearest-even).
+
+Joint text + video workloads append n_text text tokens after the video
+tokens of every (batch, head) slab, drawn in the same slab draw (N + n_text
+rows).  The MOD-DiT README ("Token-Type-Aware Masking") puts text at about
+1% of a joint sequence: TEXT_TOKENS_720P = 1164 is 1% of 115200 + 1164.
 """
 import concurrent.futures
 import os
@@ -19,6 +24,8 @@ import os
 import numpy as np
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_OFF, STREAM_WIN = range(6)
+
+TEXT_TOKENS_720P = 1164
 
 # Window sizes (in tiles) that the per-head variant draws from.
 HEAD_WINDOW_CHOICES = ((3, 3, 3), (3, 3, 5), (5, 5, 5))
@@ -107,11 +114,12 @@ def tensors(B, H, N, D, dtype, seed, with_dout=False):
     return tuple(out)
 
 
-def workload(cfg, heads=None, with_dout=None):
+def workload(cfg, heads=None, with_dout=None, n_text=0):
     """Everything one workload needs: dict with geometry, windows, offsets and
     q, k, v (and dout for the training workload).  ``heads`` keeps only the
     first few heads (their values equal those heads of the full draw).
-    dout is drawn for the training workload, or when with_dout is True."""
+    dout is drawn for the training workload, or when with_dout is True.
+    With n_text > 0 the tensors hold N + n_text rows per slab (text last)."""
     c = dict(CONFIGS[cfg])
     if heads is not None:
         c["H"] = heads
@@ -120,8 +128,8 @@ def workload(cfg, heads=None, with_dout=None):
     w = windows_for(cfg)[: c["H"]]
     off = offsets_for(cfg)
     want = c["backward"] if with_dout is None else with_dout
-    ts = tensors(c["B"], c["H"], N, c["D"], c["dtype"], seed, with_dout=want)
-    c.update(N=N, windows=w, offsets=off, q=ts[0], k=ts[1], v=ts[2], dout=ts[3] if want else None,
+    ts = tensors(c["B"], c["H"], N + n_text, c["D"], c["dtype"], seed, with_dout=want)
+    c.update(N=N, n_text=n_text, windows=w, offsets=off, q=ts[0], k=ts[1], v=ts[2], dout=ts[3] if want else None,
              scale=1.0 / np.sqrt(c["D"]), seed=seed)
     return c
 
