@@ -14,7 +14,12 @@ One step is the whole hot path:
 Throughput counts only unmasked tile pairs: forward 4*L^2*D flop per pair,
 backward 2.5x that, as the operator's "linear in sequence length" work.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--text M]
+
+--text M measures the joint text + video variant of the same step: M text
+tokens follow the video tokens of every (b, h) slab (token-type-aware
+masking: text rows and columns dense); the counted work adds the text pairs,
+4*D*M*(2N + M) flop per (b, h) in the forward.
 
 Prints ONE JSON line.
 
@@ -55,6 +60,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="query rows and key rows of the oracle sample (CPU baseline)")
+    ap.add_argument("--text", type=int, default=0,
+                    help="text tokens appended to the video tokens (joint text + video step)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc counter_collection.csv files into profiles/traffic.json")
     return ap.parse_args()
@@ -129,15 +136,17 @@ def write_traffic(fetch_csv, write_csv):
     print(json.dumps(out))
 
 
-def cpu_baseline(w, rows):
+def cpu_baseline(w, rows, n_text=0):
     """The plain CPU oracle on a bounded sample of the same workload: forward
     and dQ for `rows` query rows plus dK/dV for `rows` key rows of head 0,
     counted as `rows` rows of the training step.  Query rows are the first
     rows (tile order) of the first query tiles; key rows those of the first
     key tiles that exactly 45 query tiles attend, so every sampled row meets
-    45 tiles of keys (or queries), as the average row of the workload does."""
+    45 tiles of keys (or queries), as the average row of the workload does
+    (plus the n_text text keys or queries of a joint sequence)."""
     from oracle import oracle    # test infrastructure: only this leg of the benchmark uses it
-    B, H, N, D = w["q"].shape
+    B, H, S, D = w["q"].shape
+    N = S - n_text
     L = int(np.prod(w["tile"]))
     oracle.load()
     inv = np.argsort(oracle.perm(w["grid"], w["tile"]))       # tile-order slot -> raster token
@@ -149,11 +158,12 @@ def cpu_baseline(w, rows):
     qslots = (np.arange(nt)[:, None] * L + np.arange(L)[None, :]).ravel()[:rows]
     kslots = (ktiles[:nt, None] * L + np.arange(L)[None, :]).ravel()[:rows]
     qrows, krows = np.sort(inv[qslots]), np.sort(inv[kslots])
-    keys_per_row = 45 * L
+    keys_per_row = 45 * L + n_text
     flop = rows * 3.5 * 4.0 * keys_per_row * D
     t0 = time.perf_counter()
-    oracle.fwd(w["q"], w["k"], w["v"], w["grid"], w["tile"], w["windows"], rows=qrows)
-    oracle.bwd(w["q"], w["k"], w["v"], w["dout"], w["grid"], w["tile"], w["windows"], qrows=qrows, krows=krows)
+    oracle.fwd(w["q"], w["k"], w["v"], w["grid"], w["tile"], w["windows"], rows=qrows, n_text=n_text)
+    oracle.bwd(w["q"], w["k"], w["v"], w["dout"], w["grid"], w["tile"], w["windows"], qrows=qrows, krows=krows,
+               n_text=n_text)
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
@@ -207,8 +217,13 @@ def main():
     import sliding_tile_attention_amd as sta
     from tests.inputs import workload
 
-    w = workload(WORKLOAD)
-    B, H, N, D = w["q"].shape
+    nt = args.text
+    if nt < 0:
+        print("--text must be >= 0", file=sys.stderr)
+        sys.exit(2)
+    w = workload(WORKLOAD, n_text=nt)
+    B, H, S, D = w["q"].shape
+    N = S - nt
     geom = sta.Geometry(tuple(w["grid"]), tuple(w["tile"]))
     L, T = geom.tile_tokens, geom.num_tiles
     windows = [tuple(x) for x in w["windows"]]
@@ -219,7 +234,7 @@ def main():
     # work buffers (tile order) and outputs (raster order)
     qt, kt, vt, ot, dot_, dqt, dkt, dvt = (torch.empty_like(q) for _ in range(8))
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     delta = torch.empty_like(lse)
     idx = sta.StaIndex(geom, windows, None)
     scale = D ** -0.5
@@ -235,22 +250,22 @@ def main():
                 evs[i].record(stream)
         mark(0)
         for src, dst in ((q, qt), (k, kt), (v, vt)):
-            sta.sta_tile_reorder(src, dst, B * H, row_bytes, geom, False, stream)
+            sta.sta_tile_reorder_ex(src, dst, B * H, row_bytes, geom, False, nt, stream)
         mark(1)
         sta.sta_build_index(geom, windows, None, idx, stream)
         mark(2)
-        sta.sta_fwd(qt, kt, vt, ot, lse, B, H, D, sta.STA_BF16, scale, geom, idx, stream)
+        sta.sta_fwd_ex(qt, kt, vt, ot, lse, B, H, D, sta.STA_BF16, scale, geom, idx, nt, stream)
         mark(3)
-        sta.sta_tile_reorder(ot, o, B * H, row_bytes, geom, True, stream)
+        sta.sta_tile_reorder_ex(ot, o, B * H, row_bytes, geom, True, nt, stream)
         mark(4)
-        sta.sta_tile_reorder(do, dot_, B * H, row_bytes, geom, False, stream)
+        sta.sta_tile_reorder_ex(do, dot_, B * H, row_bytes, geom, False, nt, stream)
         mark(5)
         for i, part in enumerate((sta.STA_BWD_DELTA, sta.STA_BWD_DKDV, sta.STA_BWD_DQ)):
-            sta.sta_bwd_parts(qt, kt, vt, ot, lse, dot_, dqt, dkt, dvt, delta, B, H, D, sta.STA_BF16, scale, geom,
-                              idx, part, stream)
+            sta.sta_bwd_ex(qt, kt, vt, ot, lse, dot_, dqt, dkt, dvt, delta, B, H, D, sta.STA_BF16, scale, geom,
+                           idx, part, nt, stream)
             mark(6 + i)
         for src, dst in ((dqt, dq), (dkt, dk), (dvt, dv)):
-            sta.sta_tile_reorder(src, dst, B * H, row_bytes, geom, True, stream)
+            sta.sta_tile_reorder_ex(src, dst, B * H, row_bytes, geom, True, nt, stream)
         mark(9)
 
     for _ in range(args.warmup):
@@ -271,6 +286,7 @@ def main():
 
     kv_cnt = idx.kv_cnt.cpu().numpy()
     fwd_flop = 4.0 * B * float(kv_cnt.sum()) * L * L * D          # counted: unmasked tile pairs
+    fwd_flop += 4.0 * B * H * D * float(nt) * (2 * N + nt)          # text rows and columns (joint step)
     step_flop = 3.5 * fwd_flop                                      # forward + backward (2.5x)
     value = step_flop / (ms_per_step * 1e-3) / 1e12
 
@@ -283,10 +299,10 @@ def main():
     achieved = alg[dominant] / (per[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "kernel": dominant,
-                "traffic": measured_traffic(dominant),
+                "traffic": measured_traffic(dominant) if nt == 0 else None,   # counters cover the video step
                 "measured_gemm_ceiling": gemm_ceiling(torch, dev)}
 
-    tensor_bytes = B * H * N * D * 2
+    tensor_bytes = B * H * S * D * 2
     reorder_gbs = 3 * 2 * tensor_bytes / (per["reorder_qkv"] * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -303,9 +319,11 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "720p training step: B=1 H=24 D=128, grid (30,48,80)=115200 tokens, tile (6,8,8), "
-                        "window 3x3x5 tiles, forward+backward",
+                        "window 3x3x5 tiles, forward+backward" +
+                        ("" if nt == 0 else ", joint with %d text tokens (dense text rows and columns)" % nt),
             "global_batch": B,
-            "seq_len": N,
+            "seq_len": S,
+            "text_tokens": nt,
             "parallelism": "none (1 GPU)",
             "counted_flop_per_step": step_flop,
             "ms_per_layer_fwd_bwd": round(ms_per_step, 3),
@@ -320,7 +338,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows, nt)
     print(json.dumps(out), flush=True)
 
 

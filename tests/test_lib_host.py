@@ -211,3 +211,34 @@ def test_index_options_reject_bad_values():
         assert st == sta.STA_ERR_INVALID
     with pytest.raises(ValueError):
         sta.sta_index_dims_ex(GEOM, [(3, 3, 3)], False, "wrap")
+
+
+def test_attn_options_reject_bad_text_counts():
+    """Joint text + video options: a negative text count is malformed and a
+    sequence beyond 2^30 rows unsupported, for every call that takes them."""
+    a = _fwd_args()
+    fwd = lambda nt: sta.sta_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["D"], a["dtype"],
+                                   a["scale"], a["geom"], a["index"], nt, 0)
+    bwd = lambda nt: sta.sta_bwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], _fake(), _fake(), _fake(), _fake(),
+                                    _fake(), a["B"], a["H"], a["D"], a["dtype"], a["scale"], a["geom"], a["index"],
+                                    sta.STA_BWD_ALL, nt, 0)
+    reorder = lambda nt: sta.sta_tile_reorder_ex(_fake(), _fake(), 1, 4, GEOM, 0, nt, 0)
+    for call in (fwd, bwd, reorder):
+        _expect(sta.STA_ERR_INVALID, call, -1)
+        _expect(sta.STA_ERR_UNSUPPORTED, call, 2 ** 30)
+    # other argument checks still apply with text tokens
+    _expect(sta.STA_ERR_INVALID, lambda: sta.sta_fwd_ex(None, a["k"], a["v"], a["o"], a["lse"], 1, 2, 64,
+                                                        sta.STA_BF16, 0.125, GEOM, a["index"], 5, 0))
+
+
+def test_attn_options_null_equals_zero_text():
+    """A NULL options pointer is accepted like n_text = 0 (argument checks
+    only: a malformed call fails the same way with either)."""
+    a = _fwd_args(B=0)
+    args = (a["q"], a["k"], a["v"], a["o"], a["lse"], 0, 2, 64, sta.STA_BF16, 0.125)
+    g, x = ctypes.byref(GEOM.c()), ctypes.byref(a["index"].c())
+    st_null = sta.lib.sta_fwd_ex(*[sta._ptr(t) if isinstance(t, torch.Tensor) else t for t in args], g, x, None,
+                                 None)
+    st_zero = sta.lib.sta_fwd_ex(*[sta._ptr(t) if isinstance(t, torch.Tensor) else t for t in args], g, x,
+                                 ctypes.byref(sta.sta_attn_opts(0)), None)
+    assert st_null == st_zero == sta.STA_ERR_INVALID
