@@ -54,7 +54,7 @@ def token_mask(grid, tile, window, offsets=None, border="shift"):
     """[N, N] bool: mask[i, j] is True when key token j may be attended by
     query token i.  offsets: None or [T, 3] (one shift per query tile)."""
     T_, H_, W_ = grid
-    nt = [g // t for g, t in zip(grid, tile)]
+    nt = [-(-g // t) for g, t in zip(grid, tile)]                                  # border tiles may be cut
     coords = np.array(list(itertools.product(range(T_), range(H_), range(W_))))  # raster order
     tc = coords // np.array(tile)                                                  # tile coords
     tid = (tc[:, 0] * nt[1] + tc[:, 1]) * nt[2] + tc[:, 2]

@@ -97,7 +97,9 @@ def _f32(x):
 
 
 def tiles_per_axis(grid, tile):
-    return tuple(g // t for g, t in zip(grid, tile))
+    """Tiles per axis, ceil(grid / tile): a tile cut by the grid border holds
+    only the tokens inside the grid."""
+    return tuple(-(-g // t) for g, t in zip(grid, tile))
 
 
 _TRUNCATE, _HEAD_OFFS = 1, 2
@@ -125,7 +127,7 @@ def perm(grid, tile):
     out = np.empty(n, dtype=np.int64)
     if not lib.oracle_perm(_ptr(_i32(grid), ctypes.c_int32), _ptr(_i32(tile), ctypes.c_int32),
                            _ptr(out, ctypes.c_int64)):
-        raise ValueError("grid is not a multiple of the tile")
+        raise ValueError("grid and tile extents must be positive")
     return out
 
 

@@ -62,14 +62,15 @@
 /* Geometry                                                            */
 /* ------------------------------------------------------------------ */
 
-/* Number of tiles along each axis; 0 if the grid is not an exact multiple
- * of the tile (non-divisible grids are outside the definition used here). */
+/* Number of tiles along each axis, ceil(grid / tile): where the tile does
+ * not divide the grid the last tile of the axis holds the remaining tokens
+ * only (no padding tokens exist).  0 for non-positive extents. */
 static int tiles_per_axis(const int grid[3], const int tile[3], int n[3])
 {
     for (int d = 0; d < 3; ++d) {
-        if (grid[d] <= 0 || tile[d] <= 0 || grid[d] % tile[d] != 0)
+        if (grid[d] <= 0 || tile[d] <= 0)
             return 0;
-        n[d] = grid[d] / tile[d];
+        n[d] = (grid[d] + tile[d] - 1) / tile[d];
     }
     return 1;
 }
@@ -143,21 +144,22 @@ static void token_tile(int64_t r, const int grid[3], const int tile[3], int tc[3
 
 /* perm[r] = position of raster token r in tile-contiguous order: tiles in
  * raster order of tile coordinates, tokens inside a tile in raster order of
- * their in-tile coordinates (R6).  Returns 0 on a non-divisible grid. */
+ * their in-tile coordinates (R6).  Positions are handed out one by one in
+ * that order, so a tile cut by the grid border holds exactly its tokens and
+ * the next tile starts right after them. */
 int oracle_perm(const int grid[3], const int tile[3], int64_t *perm)
 {
     int n[3];
     if (!tiles_per_axis(grid, tile, n))
         return 0;
-    int64_t L = (int64_t)tile[0] * tile[1] * tile[2];
-    for (int t = 0; t < grid[0]; ++t)
-        for (int h = 0; h < grid[1]; ++h)
-            for (int w = 0; w < grid[2]; ++w) {
-                int64_t r = ((int64_t)t * grid[1] + h) * grid[2] + w;
-                int64_t id = ((int64_t)(t / tile[0]) * n[1] + h / tile[1]) * n[2] + w / tile[2];
-                int64_t in = ((int64_t)(t % tile[0]) * tile[1] + h % tile[1]) * tile[2] + w % tile[2];
-                perm[r] = id * L + in;
-            }
+    int64_t pos = 0;
+    for (int a = 0; a < n[0]; ++a)
+        for (int b = 0; b < n[1]; ++b)
+            for (int c = 0; c < n[2]; ++c)
+                for (int t = a * tile[0]; t < (a + 1) * tile[0] && t < grid[0]; ++t)
+                    for (int h = b * tile[1]; h < (b + 1) * tile[1] && h < grid[1]; ++h)
+                        for (int w = c * tile[2]; w < (c + 1) * tile[2] && w < grid[2]; ++w)
+                            perm[((int64_t)t * grid[1] + h) * grid[2] + w] = pos++;
     return 1;
 }
 

@@ -11,6 +11,7 @@ from tests import test_oracle_attention as A
 from tests import test_oracle_index as I
 from tests import test_oracle_joint_text as J
 from tests import test_oracle_perm as P
+from tests import test_oracle_ragged as R
 from tests import test_oracle_window_options as W
 from tests.conftest import read_golden
 
@@ -19,6 +20,9 @@ def checks():
     yield lambda: P.test_golden_small("perm_small.txt")
     yield lambda: P.test_golden_small("perm_asym.txt")
     yield lambda: P.test_bijection_and_tile_contiguity("asym")
+    yield lambda: P.test_golden_small("perm_ragged.txt")
+    for grid, tile in P.RAGGED:
+        yield (lambda a, b: lambda: P.test_ragged_tiles_are_contiguous_and_ordered(a, b))(grid, tile)
     for row in read_golden("window_axis.txt"):
         yield (lambda r: lambda: I.test_window_axis_golden(r))(row)
     yield lambda: I.test_attendee_counts_720p_golden()
@@ -54,6 +58,12 @@ def checks():
     yield lambda: J.test_whole_grid_window_with_text_is_full_attention()
     yield lambda: J.test_zero_text_tokens_equal_video_only()
     yield lambda: J.test_text_permutation_equivariance()
+    for case in range(len(R.CASES)):
+        yield (lambda c: lambda: R.test_ragged_matches_torch_dense(c))(case)
+    for case in (0, 1):
+        yield (lambda c: lambda: R.test_ragged_equals_padded_grid_with_padding_masked(c))(case)
+    yield lambda: R.test_ragged_index_is_that_of_the_tile_grid()
+    yield lambda: R.test_ragged_whole_window_is_full_attention()
 
 
 def main(path):

@@ -180,4 +180,4 @@ def test_capacity_too_small_is_rejected():
     with pytest.raises(ValueError):
         oracle.index((4, 4, 4), (1, 1, 1), [(3, 3, 3)], max_kv=26)
     with pytest.raises(ValueError):
-        oracle.index((5, 4, 4), (2, 1, 1), [(3, 3, 3)])
+        oracle.index((5, 0, 4), (2, 1, 1), [(3, 3, 3)])

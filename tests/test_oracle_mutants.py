@@ -31,8 +31,11 @@ MUTANTS = {
     "tile-coords-transposed": ("tc[1] = (id / n[2]) % n[1];", "tc[1] = (id / n[1]) % n[2];"),
     "token-coords-transposed": ("int h = (int)((r / grid[2]) % grid[1]);",
                                 "int h = (int)((r / grid[1]) % grid[2]);"),
-    "perm-in-tile-stride": ("((int64_t)(t % tile[0]) * tile[1] + h % tile[1]) * tile[2]",
-                            "((int64_t)(t % tile[0]) * tile[2] + h % tile[1]) * tile[1]"),
+    "perm-in-tile-order-transposed": (
+        "for (int h = b * tile[1]; h < (b + 1) * tile[1] && h < grid[1]; ++h)\n"
+        "                        for (int w = c * tile[2]; w < (c + 1) * tile[2] && w < grid[2]; ++w)",
+        "for (int w = c * tile[2]; w < (c + 1) * tile[2] && w < grid[2]; ++w)\n"
+        "                        for (int h = b * tile[1]; h < (b + 1) * tile[1] && h < grid[1]; ++h)"),
     "lse-drops-max": ("return mx + log(sum);", "return log(sum);"),
     "score-drops-scale": ("ss[m] = p->scale * dot(", "ss[m] = dot("),
     "score-uses-v": ("dot(qi, row_of(p, p->k, b, h, j), p->D)", "dot(qi, row_of(p, p->v, b, h, j), p->D)"),
@@ -49,6 +52,10 @@ MUTANTS = {
                                         "((flags & ORACLE_HEAD_OFFS) ? h : 0)"),
     "text-keys-hidden-from-video": ("if (i >= p->Nv || j >= p->Nv)\n        return 1;",
                                     "if (i >= p->Nv)\n        return 1;\n    if (j >= p->Nv)\n        return 0;"),
+    "perm-cut-tiles-keep-padding-slots": ("= pos++;", "= ((int64_t)(a * n[1] + b) * n[2] + c) * tile[0] * tile[1] * tile[2] + "
+                                          "((int64_t)(t % tile[0]) * tile[1] + h % tile[1]) * tile[2] + w % tile[2];"),
+    "ragged-tiles-counted-by-floor": ("n[d] = (grid[d] + tile[d] - 1) / tile[d];",
+                                      "n[d] = grid[d] / tile[d] + (grid[d] < tile[d]);"),
     "text-queries-see-text-only": ("if (i >= p->Nv || j >= p->Nv)\n        return 1;",
                                    "if (j >= p->Nv)\n        return 1;\n    if (i >= p->Nv)\n        return 0;"),
 }
