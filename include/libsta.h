@@ -26,9 +26,18 @@
  *
  * Orders (raster = t slowest, w fastest):
  *   raster token r = (t*H + h)*W + w;
- *   tile id        = (t/tt * nh + h/th) * nw + w/tw,  n* = grid / tile;
- *   tile order     = tile id * L + ((t%tt)*th + h%th)*tw + w%tw,
+ *   tile id        = (t/tt * nh + h/th) * nw + w/tw,  n* = ceil(grid / tile);
+ *   tile order     = tiles in tile-id order, each holding its tokens in
+ *                    raster order; where the grid is a multiple of the tile
+ *                    this is tile id * L + ((t%tt)*th + h%th)*tw + w%tw,
  *                    L = tt*th*tw tokens per tile.
+ * Grids the tile does not divide: the last tile of such an axis is cut by
+ * the grid border and holds only the tokens inside the grid (fewer than L);
+ * the next tile starts right after it, so tile-order tensors keep N rows.
+ * The window rule works on the n* tiles per axis unchanged.  (The pages'
+ * grids are all multiples of their tiles; cut tiles are this library's
+ * reading of the latent grids that are not, such as (30,45,80) with
+ * (6,8,8) tiles.)
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
@@ -71,8 +80,9 @@ typedef enum {
 
 typedef struct { int32_t t, h, w; } sta_dim3;
 
-/* Token grid and tile extents; every grid extent must be a positive
- * multiple of the tile extent. */
+/* Token grid and tile extents, all positive.  A tile extent larger than the
+ * grid's is taken as the grid's (one tile along that axis).  Limits: at most
+ * 2^30 tokens, 2^20 tiles and 2^16 tokens per tile (STA_ERR_UNSUPPORTED). */
 typedef struct { sta_dim3 grid; sta_dim3 tile; } sta_geom;
 
 /* Block-sparse index.  All four arrays are caller-owned DEVICE memory:

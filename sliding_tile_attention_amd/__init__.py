@@ -115,7 +115,8 @@ class Geometry:
 
     @property
     def tiles(self):
-        return tuple(g // t for g, t in zip(self.grid, self.tile))
+        """Tiles per axis; a tile cut by the grid border counts as one."""
+        return tuple(-(-g // t) for g, t in zip(self.grid, self.tile))
 
     @property
     def num_tiles(self):

@@ -38,31 +38,39 @@ int axis_max_attendees(int n, int w)
 // Largest token count / tile count the kernels index with 32-bit ints.
 static const int64_t kMaxTokens = (int64_t)1 << 30;
 static const int64_t kMaxTiles = (int64_t)1 << 20;
+static const int64_t kMaxTileTokens = (int64_t)1 << 16;
 
 static sta_status make_geo(const sta_geom *g, Geo &out)
 {
     if (!g)
         return fail(STA_ERR_INVALID, "geometry pointer is NULL");
     const int gr[3] = {g->grid.t, g->grid.h, g->grid.w};
-    const int tl[3] = {g->tile.t, g->tile.h, g->tile.w};
+    int tl[3] = {g->tile.t, g->tile.h, g->tile.w};
+    int n[3];
+    bool ragged = false;
     for (int d = 0; d < 3; ++d) {
         if (gr[d] <= 0 || tl[d] <= 0)
             return fail(STA_ERR_INVALID, "grid and tile extents must be positive (axis %d: grid %d tile %d)",
                         d, gr[d], tl[d]);
-        if (gr[d] % tl[d] != 0)
-            return fail(STA_ERR_INVALID, "grid extent %d is not a multiple of tile extent %d on axis %d",
-                        gr[d], tl[d], d);
+        // a tile longer than the axis is one tile holding the whole axis,
+        // the same tiling as a tile exactly as long as the axis
+        tl[d] = tl[d] < gr[d] ? tl[d] : gr[d];
+        n[d] = (gr[d] + tl[d] - 1) / tl[d];
+        ragged = ragged || gr[d] % tl[d] != 0;
     }
     int64_t N = (int64_t)gr[0] * gr[1] * gr[2];
-    int64_t T = (int64_t)(gr[0] / tl[0]) * (gr[1] / tl[1]) * (gr[2] / tl[2]);
-    if (N > kMaxTokens || T > kMaxTiles)
-        return fail(STA_ERR_UNSUPPORTED, "grid too large: %lld tokens, %lld tiles", (long long)N, (long long)T);
+    int64_t T = (int64_t)n[0] * n[1] * n[2];
+    int64_t L = (int64_t)tl[0] * tl[1] * tl[2];
+    if (N > kMaxTokens || T > kMaxTiles || L > kMaxTileTokens)
+        return fail(STA_ERR_UNSUPPORTED, "grid too large: %lld tokens, %lld tiles, %lld tokens per tile",
+                    (long long)N, (long long)T, (long long)L);
     out.gt = gr[0]; out.gh = gr[1]; out.gw = gr[2];
     out.tt = tl[0]; out.th = tl[1]; out.tw = tl[2];
-    out.nt = gr[0] / tl[0]; out.nh = gr[1] / tl[1]; out.nw = gr[2] / tl[2];
+    out.nt = n[0]; out.nh = n[1]; out.nw = n[2];
     out.T = (int)T;
-    out.L = tl[0] * tl[1] * tl[2];
+    out.L = (int)L;
     out.N = N;
+    out.ragged = ragged ? 1 : 0;
     out.text = 0;
     out.Tt = 0;
     out.TT = out.T;

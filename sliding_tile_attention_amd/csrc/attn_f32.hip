@@ -5,6 +5,27 @@
 
 namespace sta {
 
+// Tile holding video row i of a slab (compact tile order: whole tile planes
+// along t, tile rows along h inside a plane, tiles along w inside a row,
+// the last of each cut by the grid border).
+__device__ inline int tile_of_row(const Geo &g, int64_t i)
+{
+    if (!g.ragged) return (int)(i / g.L);
+    const int64_t plane = (int64_t)g.tt * g.gh * g.gw;
+    int a = (int)(i / plane);
+    a = a < g.nt - 1 ? a : g.nt - 1;
+    int64_t r = i - a * plane;
+    const int vt = g.gt - a * g.tt < g.tt ? g.gt - a * g.tt : g.tt;
+    const int64_t trow = (int64_t)vt * g.th * g.gw;
+    int b = (int)(r / trow);
+    b = b < g.nh - 1 ? b : g.nh - 1;
+    r -= b * trow;
+    const int vh = g.gh - b * g.th < g.th ? g.gh - b * g.th : g.th;
+    int c = (int)(r / ((int64_t)vt * vh * g.tw));
+    c = c < g.nw - 1 ? c : g.nw - 1;
+    return (a * g.nh + b) * g.nw + c;
+}
+
 // Calls f(r) for every partner row r of row i of a slab: for a video row
 // the rows of its listed tiles, then the text rows; for a text row every
 // row (MOD-DiT README, "Token-Type-Aware Masking").
@@ -16,12 +37,12 @@ __device__ inline void for_partners(int64_t i, int h, const Geo &g, const int32_
         for (int64_t r = 0; r < g.S; ++r) f(r);
         return;
     }
-    const int t = (int)(i / g.L);
+    const int t = tile_of_row(g, i);
     const int cnt = cnt_[(int64_t)h * g.T + t];
     const int32_t *lst = idx + ((int64_t)h * g.T + t) * max_e;
     for (int e = 0; e < cnt; ++e) {
-        const int64_t r0 = (int64_t)lst[e] * g.L;
-        for (int rr = 0; rr < g.L; ++rr) f(r0 + rr);
+        const Span sp = tile_span(g, lst[e]);
+        for (int rr = 0; rr < sp.len; ++rr) f(sp.start + rr);
     }
     for (int64_t r = g.N; r < g.S; ++r) f(r);
 }

@@ -142,24 +142,23 @@ __device__ inline void static_for(F &&f)
 // the text pseudo-tiles, block by block (no divisions); the next tile id is
 // prefetched when a tile is entered.
 struct ListWalk {
-    int e, r0, tile, len, next;
+    int e, r0, next;
+    Span sp;                  // rows of the current tile
 };
 __device__ inline void walk_init(ListWalk &w, const int32_t *lst, int cnt, const Geo &g)
 {
     w.e = 0;
     w.r0 = 0;
-    w.tile = entry_tile(lst, cnt, g.T, 0);
-    w.len = tile_rows(g, w.tile);
+    w.sp = tile_span(g, entry_tile(lst, cnt, g.T, 0));
     w.next = entry_tile(lst, cnt, g.T, 1);
 }
 __device__ inline void walk_next(ListWalk &w, const int32_t *lst, int cnt, int step, const Geo &g)
 {
     w.r0 += step;
-    if (w.r0 >= w.len) {
+    if (w.r0 >= w.sp.len) {
         w.r0 = 0;
         ++w.e;
-        w.tile = w.next;
-        w.len = tile_rows(g, w.tile);
+        w.sp = tile_span(g, w.next);
         w.next = entry_tile(lst, cnt, g.T, w.e + 1);
     }
 }
@@ -197,17 +196,17 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
 
     int bh, qt, rb;
     decode_item(xcd_remap(blockIdx.x, total), rblocks, g, bh, qt, rb);
-    const int qlen = tile_rows(g, qt);               // query rows of this tile
-    if (rb * M >= qlen) return;                      // row block past a ragged text pseudo-tile
+    const Span qs = tile_span(g, qt);                // query rows of this tile
+    const int qlen = qs.len;
+    if (rb * M >= qlen) return;                      // row block past a cut tile's end
     const int h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, grp = lane >> 5;
-    const int L = g.L;
     const int64_t base = (int64_t)bh * g.S * D;
     const int row = rb * M + wave * 32 + l32;        // query row (inside the tile) of this lane
     const bool row_ok = row < qlen;
-    const int64_t grow = (int64_t)qt * L + (row_ok ? row : qlen - 1);
+    const int64_t grow = qs.start + (row_ok ? row : qlen - 1);
 
     bf16x8 qf[KS], of[KS];
 #pragma unroll
@@ -231,7 +230,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
     const bool video_q = qt < g.T;
     const int cnt = video_q ? kv_cnt[(int64_t)h * g.T + qt] : g.T;
     const int32_t *lst = video_q ? kv_idx + ((int64_t)h * g.T + qt) * max_kv : nullptr;
-    const int nblk = walk_blocks(g, cnt, BN);
+    const int nblk = walk_blocks(g, lst, cnt, BN);
 
     // LDS offsets: a row's swizzle only XORs granule bits, and the granule
     // bits that vary with the step (ks) or column block (db) sit above the
@@ -247,8 +246,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
     ListWalk cw;                                    // next key block to copy
     walk_init(cw, lst, cnt, g);
     auto gload = [&](auto bc) {
-        const int valid = cw.len - cw.r0 < BN ? cw.len - cw.r0 : BN;
-        const int64_t row0 = (int64_t)cw.tile * L + cw.r0;
+        const int valid = cw.sp.len - cw.r0 < BN ? cw.sp.len - cw.r0 : BN;
+        const int64_t row0 = cw.sp.start + cw.r0;
         rc.copy(K + base + row0 * D, valid, stage(bc), wave);
         rc.copy(V + base + row0 * D, valid, stage(bc) + BLK, wave);
         walk_next(cw, lst, cnt, BN, g);
@@ -307,7 +306,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
         });
 
     if (row_ok) {
-        __bf16 *op = dQ + base + ((int64_t)qt * L + row) * D;
+        __bf16 *op = dQ + base + (qs.start + row) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -346,18 +345,18 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 
     int bh, kt, rb;
     decode_item(xcd_remap(blockIdx.x, total), rblocks, g, bh, kt, rb);
-    const int klen = tile_rows(g, kt);               // key rows of this tile
-    if (rb * M >= klen) return;                      // row block past a ragged text pseudo-tile
+    const Span ks_ = tile_span(g, kt);               // key rows of this tile
+    const int klen = ks_.len;
+    if (rb * M >= klen) return;                      // row block past a cut tile's end
     const int h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, grp = lane >> 5;
-    const int L = g.L;
     const int64_t base = (int64_t)bh * g.S * D;
     const int64_t sbase = (int64_t)bh * g.S;
     const int krow0 = rb * M + wave * 32;            // first key row (inside the tile) of this wave
     const int krow = krow0 + l32;
-    const int64_t gk = (int64_t)kt * L + (krow < klen ? krow : klen - 1);
+    const int64_t gk = ks_.start + (krow < klen ? krow : klen - 1);
 
     bf16x8 kf[KS], vf[KS];
 #pragma unroll
@@ -376,7 +375,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     const bool video_k = kt < g.T;
     const int cnt = video_k ? q_cnt[(int64_t)h * g.T + kt] : g.T;
     const int32_t *lst = video_k ? q_idx + ((int64_t)h * g.T + kt) * max_q : nullptr;
-    const int nblk = walk_blocks(g, cnt, BQ);
+    const int nblk = walk_blocks(g, lst, cnt, BQ);
 
     // LDS offsets: a row's swizzle only XORs granule bits, and the granule
     // bits that vary with the step (ks) or column block (db) sit above the
@@ -392,8 +391,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     ListWalk cw;                                    // next query block to copy
     walk_init(cw, lst, cnt, g);
     auto gload = [&](auto bc) {
-        const int valid = cw.len - cw.r0 < BQ ? cw.len - cw.r0 : BQ;
-        const int64_t row0 = (int64_t)cw.tile * L + cw.r0;
+        const int valid = cw.sp.len - cw.r0 < BQ ? cw.sp.len - cw.r0 : BQ;
+        const int64_t row0 = cw.sp.start + cw.r0;
         __bf16 *st = stage(bc);
         rc.copy(Q + base + row0 * D, valid, st, wave);
         rc.copy(dO + base + row0 * D, valid, st + BLK, wave);
@@ -489,7 +488,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     for (int r = 0; r < 16; ++r) {
         const int kr = krow0 + mfma_row(lane, r);
         if (kr < klen) {
-            const int64_t o = base + ((int64_t)kt * L + kr) * D + l32;
+            const int64_t o = base + (ks_.start + kr) * D + l32;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 dK[o + db * 32] = (__bf16)(dk[db][r] * scale);

@@ -8,33 +8,56 @@
 
 namespace sta {
 
-// Geometry in the form the kernels use.  tile order: tile id * L + in-tile
-// raster index; tile id raster over (nt, nh, nw).
+// Geometry in the form the kernels use.  Tile order: tiles in raster order
+// of tile coordinates (nt, nh, nw), each holding its tokens in raster order;
+// where the tile does not divide the grid (`ragged`), the last tile of an
+// axis is cut by the border and holds only the tokens inside the grid, and
+// the next tile starts right after it (compact order, N rows in all).
 // Joint text + video sequences: `text` text tokens follow the N video
 // tokens of every (b, h) slab (S = N + text rows).  The kernels walk them as
-// Tt text pseudo-tiles T .. T+Tt-1 of L rows each (the last one ragged), so
-// that pseudo-tile t starts at slab row t * L like a video tile.
+// Tt text pseudo-tiles T .. T+Tt-1 of L rows each (the last one ragged)
+// starting at slab row N.
 struct Geo {
     int gt, gh, gw;   // token grid
     int tt, th, tw;   // tile extents
-    int nt, nh, nw;   // tiles per axis
+    int nt, nh, nw;   // tiles per axis, ceil(grid / tile)
     int T;            // number of tiles
-    int L;            // tokens per tile
+    int L;            // tokens per whole tile
     int64_t N;        // video tokens
+    int ragged;       // some tile is cut by the grid border
     int text;         // text tokens after the video tokens
     int Tt;           // text pseudo-tiles, ceil(text / L)
     int TT;           // T + Tt
     int64_t S;        // rows per (b, h) slab, N + text
 };
 
-// Rows of tile t: L for a video tile, the text rows it holds for a text
-// pseudo-tile.
-__host__ __device__ inline int tile_rows(const Geo &g, int t)
+// Slab rows [start, start + len) of tile t (a video tile or a text
+// pseudo-tile).
+struct Span {
+    int64_t start;
+    int len;
+};
+__host__ __device__ inline Span tile_span(const Geo &g, int t)
 {
-    if (t < g.T) return g.L;
-    const int r = g.text - (t - g.T) * g.L;
-    return r < g.L ? r : g.L;
+    if (t >= g.T) {
+        const int j = t - g.T, r = g.text - j * g.L;
+        return {g.N + (int64_t)j * g.L, r < g.L ? r : g.L};
+    }
+    if (!g.ragged) return {(int64_t)t * g.L, g.L};
+    const int a = t / (g.nh * g.nw), rem = t - a * (g.nh * g.nw);
+    const int b = rem / g.nw, c = rem - b * g.nw;
+    const int vt = g.gt - a * g.tt < g.tt ? g.gt - a * g.tt : g.tt;
+    const int vh = g.gh - b * g.th < g.th ? g.gh - b * g.th : g.th;
+    const int vw = g.gw - c * g.tw < g.tw ? g.gw - c * g.tw : g.tw;
+    // tokens of earlier tiles: whole tile planes along t, then earlier rows
+    // of tiles in this plane, then earlier tiles in this row
+    const int64_t start = (int64_t)a * g.tt * g.gh * g.gw + (int64_t)vt * b * g.th * g.gw +
+                          (int64_t)vt * vh * c * g.tw;
+    return {start, vt * vh * vw};
 }
+
+// Rows of tile t.
+__host__ __device__ inline int tile_rows(const Geo &g, int t) { return tile_span(g, t).len; }
 
 // Tile of entry e of a walk: the cnt tiles of a list (lst, or every video
 // tile in order when lst is null), then the text pseudo-tiles.  Token-type-
@@ -45,14 +68,19 @@ __host__ __device__ inline int entry_tile(const int32_t *lst, int cnt, int T, in
     return e < cnt ? (lst ? lst[e] : e) : T + (e - cnt);
 }
 
-// Blocks of `step` rows in a walk over cnt video tiles and every text
-// pseudo-tile.
-__host__ __device__ inline int walk_blocks(const Geo &g, int cnt, int step)
+// Blocks of `step` rows in a walk over the cnt video tiles of a list (lst,
+// or every video tile when lst is null) and every text pseudo-tile.
+__host__ __device__ inline int walk_blocks(const Geo &g, const int32_t *lst, int cnt, int step)
 {
     const int per = (g.L + step - 1) / step;
-    if (g.Tt == 0) return cnt * per;
+    int n = cnt * per;
+    if (g.ragged) {
+        n = 0;
+        for (int e = 0; e < cnt; ++e) n += (tile_rows(g, lst ? lst[e] : e) + step - 1) / step;
+    }
+    if (g.Tt == 0) return n;
     const int last = g.text - (g.Tt - 1) * g.L;
-    return cnt * per + (g.Tt - 1) * per + (last + step - 1) / step;
+    return n + (g.Tt - 1) * per + (last + step - 1) / step;
 }
 
 // Work item of a query- (or key-) stationary kernel: rblocks row blocks of

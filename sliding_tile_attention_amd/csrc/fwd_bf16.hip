@@ -96,9 +96,10 @@ __global__ __launch_bounds__(256) void vt_kernel(const __bf16 *__restrict__ V, _
     const int64_t bt = blockIdx.x / (unsigned)chunks;
     const int64_t bh = bt / g.TT;
     const int t = (int)(bt - bh * g.TT);
-    const int L = tile_rows(g, t);
+    const Span sp = tile_span(g, t);
+    const int L = sp.len;
     const int k0 = c * 64;
-    const __bf16 *src = V + (bh * g.S + (int64_t)t * g.L + k0) * D;
+    const __bf16 *src = V + (bh * g.S + sp.start + k0) * D;
     constexpr int RG = D / 8;                 // 16-byte granules per V row
     for (int i = threadIdx.x; i < 64 * RG; i += 256) {
         const int r = i / RG, gc = i % RG;
@@ -138,13 +139,13 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
 
     int bh, qt, rb;
     decode_item(xcd_remap(blockIdx.x, total), rblocks, g, bh, qt, rb);
-    const int qlen = tile_rows(g, qt);               // query rows of this tile
-    if (rb * C::M >= qlen) return;                   // row block past a ragged text pseudo-tile
+    const Span qs = tile_span(g, qt);                // query rows of this tile
+    const int qlen = qs.len;
+    if (rb * C::M >= qlen) return;                   // row block past a cut tile's end
     const int h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, grp = lane >> 5;
-    const int L = g.L;
     const int64_t base = (int64_t)bh * g.S * D;
     const int64_t vt_base = (int64_t)bh * g.TT * D * Lp;
     const int wrow0 = rb * C::M + wave * QB * 32;   // first row of this wave inside the tile
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int row = wrow0 + qb * 32 + l32;
-        const __bf16 *p = Q + base + ((int64_t)qt * L + row) * D + grp * 8;
+        const __bf16 *p = Q + base + (qs.start + row) * D + grp * 8;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) qf[qb][ks] = row < qlen ? ld8(p + ks * 16) : zero8();
     }
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     const bool video_q = qt < g.T;
     const int cnt = video_q ? kv_cnt[(int64_t)h * g.T + qt] : g.T;
     const int32_t *lst = video_q ? kv_idx + ((int64_t)h * g.T + qt) * max_kv : nullptr;
-    const int nblk = walk_blocks(g, cnt, BN);
+    const int nblk = walk_blocks(g, lst, cnt, BN);
 
     // ---- per-lane offsets (bf16 elements), fixed for the whole kernel ----
     // Copies: wave-wide copy i of a block fills granule slots
@@ -214,15 +215,17 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     // id of the list is prefetched when a tile is entered.
     int c_e = 0, c_k0 = 0;                               // next block to copy
     int c_tile = entry_tile(lst, cnt, g.T, 0);
-    int c_len = tile_rows(g, c_tile);
+    Span c_sp = tile_span(g, c_tile);
     int n_tile = entry_tile(lst, cnt, g.T, 1);
+    int bvalid[2];                                       // valid keys of the block in each buffer
     // Issue the asynchronous copy of the next block into LDS buffer `buf`
     // through buffer descriptors over that block: K rows past a ragged
     // tile end read as zero (their scores are masked), V^T keys past it are
     // the workspace's zero padding.
     auto gload = [&](int buf) {
-        const int valid = c_len - c_k0 < BN ? c_len - c_k0 : BN;
-        const auto rk = make_rsrc(K + base + ((int64_t)c_tile * L + c_k0) * D, valid * D * 2);
+        const int valid = c_sp.len - c_k0 < BN ? c_sp.len - c_k0 : BN;
+        bvalid[buf] = valid;
+        const auto rk = make_rsrc(K + base + (c_sp.start + c_k0) * D, valid * D * 2);
         const auto rv = make_rsrc(VT + vt_base + (int64_t)c_tile * D * Lp + c_k0, (D * Lp - c_k0) * 2);
         __bf16 *Ks = smem + buf * C::STAGE;
         __bf16 *Vs = Ks + C::BLK;
@@ -234,16 +237,14 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
             b2lds16(rv, gv[i], Vs + lds_off);
         }
         c_k0 += BN;
-        if (c_k0 >= c_len) {
+        if (c_k0 >= c_sp.len) {
             c_k0 = 0;
             ++c_e;
             c_tile = n_tile;
-            c_len = tile_rows(g, c_tile);
+            c_sp = tile_span(g, c_tile);
             n_tile = entry_tile(lst, cnt, g.T, c_e + 1);
         }
     };
-    int s_e = 0, s_k0 = 0;                               // entry and key offset of the block computed next
-    int s_len = tile_rows(g, entry_tile(lst, cnt, g.T, 0));
 
     // One key block from LDS buffer BUF (a compile-time constant, so every
     // LDS address below is a per-lane register plus an immediate).
@@ -251,16 +252,10 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         constexpr int BUF = decltype(bufc)::value;
         __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of block blk have landed
         __syncthreads();                   // ... and everyone's; the other buffer is free
+        const int valid = bvalid[BUF];
         if (blk + 1 < nblk) gload(1 - BUF);
         const __bf16 *Ks = smem + BUF * C::STAGE;
         const __bf16 *Vs = Ks + C::BLK;
-        const int valid = s_len - s_k0 < BN ? s_len - s_k0 : BN;
-        s_k0 += BN;
-        if (s_k0 >= s_len) {       // entry lengths: L for listed tiles, then the text pseudo-tiles'
-            s_k0 = 0;
-            ++s_e;
-            s_len = s_e < cnt ? L : tile_rows(g, g.T + (s_e - cnt));
-        }
 
         f32x16 s[QB][C::KB];
 #pragma unroll
@@ -354,7 +349,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         const float inv = 1.f / lt;
         const int row = wrow0 + qb * 32 + l32;
         if (row < qlen) {
-            __bf16 *op = O + base + ((int64_t)qt * L + row) * D;
+            __bf16 *op = O + base + (qs.start + row) * D;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -365,7 +360,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
                     *(bf16x4 *)(op + db * 32 + 8 * j + 4 * grp) = v;
                 }
             if (grp == 0)
-                LSE[(int64_t)bh * g.S + (int64_t)qt * L + row] = (m_i[qb] + __log2f(lt)) * 0.69314718055994531f;
+                LSE[(int64_t)bh * g.S + qs.start + row] = (m_i[qb] + __log2f(lt)) * 0.69314718055994531f;
         }
     }
 }

@@ -1,7 +1,8 @@
 // Raster <-> tile-contiguous token permutation (byte-generic gather).
 //
-// A run of tw consecutive tokens along w inside one tile is contiguous in
-// both orders, so the copy moves whole runs of tw*row_bytes bytes.  One
+// A run of consecutive tokens along w inside one tile (tw of them, fewer in
+// a tile cut by the grid border) is contiguous in both orders, so the copy
+// moves whole runs.  One
 // thread owns one vector-sized chunk of one run and walks it through all
 // `outer` slabs, so the index arithmetic is paid once per chunk position
 // and every wave reads and writes contiguous, fully coalesced memory.
@@ -27,9 +28,13 @@ __global__ __launch_bounds__(256) void reorder_kernel(const V *__restrict__ src,
             const int64_t th_ = u / g.nw;
             const int h = (int)(th_ % g.gh);
             const int t = (int)(th_ / g.gh);
+            const int vw = g.gw - jw * g.tw < g.tw ? g.gw - jw * g.tw : g.tw;   // tokens of this run
+            if (c >= vw * row_vec) continue;     // past a run cut by the grid border
             const int64_t raster = ((int64_t)t * g.gh + h) * g.gw + (int64_t)jw * g.tw;
-            const int64_t tile_id = ((int64_t)(t / g.tt) * g.nh + h / g.th) * g.nw + jw;
-            const int64_t tiled = tile_id * g.L + ((int64_t)(t % g.tt) * g.th + h % g.th) * g.tw;
+            const int tile_id = ((t / g.tt) * g.nh + h / g.th) * g.nw + jw;
+            const Span sp = tile_span(g, tile_id);
+            const int vh = g.gh - (h / g.th) * g.th < g.th ? g.gh - (h / g.th) * g.th : g.th;
+            const int64_t tiled = sp.start + ((int64_t)(t % g.tt) * vh + h % g.th) * vw;
             s0 = (inverse ? tiled : raster) * row_vec + c;
             d0 = (inverse ? raster : tiled) * row_vec + c;
         } else {                                 // text rows keep their place
@@ -62,7 +67,7 @@ static sta_status run(const void *src, void *dst, int64_t outer, int64_t row_byt
     const int64_t vb = sizeof(V);
     const int64_t row_vec = row_bytes / vb;      // units per token row
     const int64_t run_vec = g.tw * row_vec;      // units per run of tw tokens
-    const int64_t chunks = (g.N / g.tw) * run_vec;
+    const int64_t chunks = (int64_t)g.gt * g.gh * g.nw * run_vec;   // runs of the (t, h, w-tile) grid
     const int64_t text_chunks = (int64_t)g.text * row_vec;
     const int64_t slab = g.S * row_vec;
     int64_t blocks = (chunks + text_chunks + 255) / 256;

@@ -70,6 +70,20 @@ def test_index_dims_random_geometries():
             (kv_cnt.max(), q_cnt.max())
 
 
+def test_index_dims_ragged_geometries():
+    """Grids the tile does not divide (and tiles longer than the grid):
+    capacities as the oracle's lists, whose tile grid is ceil(grid/tile)."""
+    g = np.random.default_rng(8)
+    for _ in range(50):
+        grid = tuple(int(x) for x in g.integers(1, 13, size=3))
+        tile = tuple(int(x) for x in g.integers(1, 6, size=3))
+        w = g.integers(1, 8, size=(int(g.integers(1, 4)), 3))
+        _, kv_cnt, _, q_cnt = oracle.index(grid, tile, w)
+        geom = sta.Geometry(grid, tile)
+        assert geom.num_tiles == kv_cnt.shape[1]
+        assert sta.sta_index_dims(geom, w, False) == (kv_cnt.max(), q_cnt.max())
+
+
 # ---- argument checks: every call below must fail on the host -----------
 
 GEOM = sta.Geometry((4, 8, 8), (2, 4, 4))
@@ -104,7 +118,7 @@ class _FakeIndex:
 
 def test_reorder_rejects_bad_arguments():
     a, b = _fake(), _fake()
-    _expect(sta.STA_ERR_INVALID, sta.sta_tile_reorder, a, b, 1, 4, sta.Geometry((5, 8, 8), (2, 4, 4)), 0, 0)
+    _expect(sta.STA_ERR_INVALID, sta.sta_tile_reorder, a, b, 1, 4, sta.Geometry((5, 0, 8), (2, 4, 4)), 0, 0)
     _expect(sta.STA_ERR_INVALID, sta.sta_tile_reorder, a, b, 1, 4, sta.Geometry((4, 8, 8), (0, 4, 4)), 0, 0)
     _expect(sta.STA_ERR_INVALID, sta.sta_tile_reorder, None, b, 1, 4, GEOM, 0, 0)
     _expect(sta.STA_ERR_INVALID, sta.sta_tile_reorder, a, b, 0, 4, GEOM, 0, 0)
@@ -119,6 +133,7 @@ def test_build_index_rejects_bad_arguments():
     _expect(sta.STA_ERR_INVALID, sta.sta_build_index, GEOM, w, None, _FakeIndex(T=9), 0)
     _expect(sta.STA_ERR_INVALID, sta.sta_build_index, GEOM, w, None, _FakeIndex(max_kv=7), 0)
     _expect(sta.STA_ERR_INVALID, sta.sta_build_index, GEOM, w, None, _FakeIndex(max_q=7), 0)
+    # a grid the tile does not divide has ceil(grid/tile) tiles per axis: 12 here
     _expect(sta.STA_ERR_INVALID, sta.sta_build_index, sta.Geometry((4, 8, 9), (2, 4, 4)), w, None,
             _FakeIndex(), 0)
     # with shifts the transposed capacity must be the tile count
@@ -145,7 +160,8 @@ def test_fwd_rejects_bad_arguments():
         (sta.STA_ERR_INVALID, dict(dtype=7)),
         (sta.STA_ERR_INVALID, dict(k=_fake(align=2))),           # misaligned
         (sta.STA_ERR_INVALID, dict(index=_FakeIndex(T=9))),
-        (sta.STA_ERR_INVALID, dict(geom=sta.Geometry((4, 8, 7), (2, 4, 4)))),
+        (sta.STA_ERR_INVALID, dict(geom=sta.Geometry((4, 8, 9), (2, 4, 4)))),   # 12 tiles, index has 8
+        (sta.STA_ERR_INVALID, dict(geom=sta.Geometry((4, -8, 8), (2, 4, 4)))),
         (sta.STA_ERR_UNSUPPORTED, dict(D=96)),
         (sta.STA_ERR_UNSUPPORTED, dict(geom=sta.Geometry((2, 3, 3), (2, 3, 1)),
                                        index=_FakeIndex(T=3, max_kv=3, max_q=3))),  # L=6, bf16
@@ -176,7 +192,7 @@ def test_bwd_rejects_bad_arguments():
 
 def test_index_dims_rejects_bad_arguments():
     _expect(sta.STA_ERR_INVALID, sta.sta_index_dims, GEOM, [(1, 1, 0)], False)
-    _expect(sta.STA_ERR_INVALID, sta.sta_index_dims, sta.Geometry((3, 8, 8), (2, 4, 4)), [(1, 1, 1)], False)
+    _expect(sta.STA_ERR_INVALID, sta.sta_index_dims, sta.Geometry((3, 8, 8), (2, 4, -4)), [(1, 1, 1)], False)
     g = sta.lib.sta_index_dims(ctypes.byref(GEOM.c()), 0, None, 0, None, None)
     assert g == sta.STA_ERR_INVALID
 
