@@ -21,6 +21,10 @@ tokens follow the video tokens of every (b, h) slab (token-type-aware
 masking: text rows and columns dense); the counted work adds the text pairs,
 4*D*M*(2N + M) flop per (b, h) in the forward.
 
+--grid T,H,W replaces the token grid, e.g. the 720p latent grid 30,45,80 that
+the (6,8,8) tile does not divide (its last tile row along H is cut to 5
+rows); counted work then sums len(q) * len(k) over the listed tile pairs.
+
 Prints ONE JSON line.
 
 HBM traffic of the attention kernels (roofline "traffic") comes from two
@@ -60,6 +64,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="query rows and key rows of the oracle sample (CPU baseline)")
+    ap.add_argument("--grid", type=str, default=None,
+                    help="token grid T,H,W replacing the workload's (30,48,80)")
     ap.add_argument("--text", type=int, default=0,
                     help="text tokens appended to the video tokens (joint text + video step)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -221,7 +227,8 @@ def main():
     if nt < 0:
         print("--text must be >= 0", file=sys.stderr)
         sys.exit(2)
-    w = workload(WORKLOAD, n_text=nt)
+    grid = None if args.grid is None else tuple(int(x) for x in args.grid.split(","))
+    w = workload(WORKLOAD, n_text=nt, grid=grid)
     B, H, S, D = w["q"].shape
     N = S - nt
     geom = sta.Geometry(tuple(w["grid"]), tuple(w["tile"]))
@@ -285,7 +292,14 @@ def main():
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
 
     kv_cnt = idx.kv_cnt.cpu().numpy()
-    fwd_flop = 4.0 * B * float(kv_cnt.sum()) * L * L * D          # counted: unmasked tile pairs
+    kv_idx = idx.kv_idx.cpu().numpy()
+    # counted: unmasked tile pairs, len(q) * len(k) scores each (L * L unless
+    # a tile is cut by the grid border)
+    axes = [[min(t, g - i * t) for i in range(-(-g // t))] for g, t in zip(geom.grid, geom.tile)]
+    lens = np.einsum("a,b,c->abc", *[np.array(x, np.float64) for x in axes]).ravel()
+    pairs = sum(float(lens[q] * lens[kv_idx[h, q, :kv_cnt[h, q]]].sum())
+                for h in range(kv_cnt.shape[0]) for q in range(kv_cnt.shape[1]))
+    fwd_flop = 4.0 * B * pairs * D
     fwd_flop += 4.0 * B * H * D * float(nt) * (2 * N + nt)          # text rows and columns (joint step)
     step_flop = 3.5 * fwd_flop                                      # forward + backward (2.5x)
     value = step_flop / (ms_per_step * 1e-3) / 1e12
@@ -299,7 +313,7 @@ def main():
     achieved = alg[dominant] / (per[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "kernel": dominant,
-                "traffic": measured_traffic(dominant) if nt == 0 else None,   # counters cover the video step
+                "traffic": measured_traffic(dominant) if nt == 0 and grid is None else None,  # video step only
                 "measured_gemm_ceiling": gemm_ceiling(torch, dev)}
 
     tensor_bytes = B * H * S * D * 2
@@ -318,8 +332,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "720p training step: B=1 H=24 D=128, grid (30,48,80)=115200 tokens, tile (6,8,8), "
-                        "window 3x3x5 tiles, forward+backward" +
+            "workload": "720p training step: B=1 H=24 D=128, grid (%d,%d,%d)=%d tokens, tile (6,8,8), "
+                        "window 3x3x5 tiles, forward+backward" % (tuple(geom.grid) + (N,)) +
                         ("" if nt == 0 else ", joint with %d text tokens (dense text rows and columns)" % nt),
             "global_batch": B,
             "seq_len": S,
@@ -337,7 +351,7 @@ def main():
         },
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and grid is None:     # the sample assumes whole (uncut) tiles
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows, nt)
     print(json.dumps(out), flush=True)
 

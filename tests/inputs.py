@@ -114,15 +114,20 @@ def tensors(B, H, N, D, dtype, seed, with_dout=False):
     return tuple(out)
 
 
-def workload(cfg, heads=None, with_dout=None, n_text=0):
+def workload(cfg, heads=None, with_dout=None, n_text=0, grid=None):
     """Everything one workload needs: dict with geometry, windows, offsets and
     q, k, v (and dout for the training workload).  ``heads`` keeps only the
     first few heads (their values equal those heads of the full draw).
     dout is drawn for the training workload, or when with_dout is True.
-    With n_text > 0 the tensors hold N + n_text rows per slab (text last)."""
+    With n_text > 0 the tensors hold N + n_text rows per slab (text last).
+    ``grid`` replaces the workload's token grid (same tile, windows and
+    seeds), e.g. the 720p latent grid (30,45,80) that the tile does not
+    divide."""
     c = dict(CONFIGS[cfg])
     if heads is not None:
         c["H"] = heads
+    if grid is not None:
+        c["grid"] = tuple(int(x) for x in grid)
     seed = 1234 + cfg
     N = int(np.prod(c["grid"]))
     w = windows_for(cfg)[: c["H"]]
