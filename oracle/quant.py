@@ -1,0 +1,154 @@
+"""Oracle of the quantized (INT8 QK^T, FP8 PV) sliding-tile attention forward.
+
+Test infrastructure only: loaded by tests/ and never by the library.  The
+pages name quantized attention kernels only as a dependency of one of them
+(MOD-DiT README, "Project Structure" and "Acknowledgements": the
+SageAttention submodule); the scheme below is this library's own reading of
+such a kernel, so every step is spelled out here and followed by the GPU:
+
+  1. K smoothing: m = mean over the rows of K of each (b, h) (fp64, then
+     fp32).  Subtracting one vector from every key shifts all scores of a
+     query by the same amount, so the softmax is unchanged.
+  2. Q: int8 codes per row, amax = max |q|, codes = rint(q * (127 / amax))
+     in fp32, scale amax / 127.
+  3. K - m: int8 codes per block of 64 consecutive rows of a tile in tile
+     order (text pseudo-tiles of L rows likewise), same formulas.
+  4. V: e4m3 codes per channel d over all rows of (b, h): amax_d = max |v_d|,
+     codes = e4m3(v * (448 / amax_d)) in fp32, scale amax_d / 448.
+  5. Base-2 scores s_ij = (sum_d qc_id kc_jd) * sq_i * sk_j * scale * log2(e)
+     over the allowed keys j (the STA window, plus text keys).
+  6. M_i = ceil(max_j s_ij); p_ij = e4m3(2^(s_ij - M_i)).
+  7. l_i = sum_j p_ij;  o_i = (sum_j p_ij vc_j) * sv / l_i;
+     LSE_i = ln 2 * (M_i + log2 l_i) + scale * <q_i, m>  (the natural-log LSE
+     of the unsmoothed scores).
+
+e4m3 is the OCP FP8 E4M3 format (1 sign bit, 4 exponent bits with bias 7, 3
+mantissa bits, largest finite 448, subnormal spacing 2^-9), rounded to
+nearest with ties to even.
+"""
+import numpy as np
+
+from oracle import oracle
+
+E4M3_MAX = 448.0
+KEY_BLOCK = 64          # keys per K scale block
+
+
+def e4m3(x):
+    """Round to the nearest e4m3 value, ties to even (|x| <= 448)."""
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    if np.any(a >= 464.0):
+        raise ValueError("value beyond the e4m3 range")
+    # spacing of the binade of a: 2^(e - 3), with the subnormal spacing 2^-9
+    # for a < 2^-6
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    step = 2.0 ** (e - 3)
+    r = np.round(a / step) * step            # numpy rounds halves to even
+    return np.where(x < 0, -r, r)
+
+
+def int8_codes(x, amax):
+    """int8 codes of fp32 x under the fp32 group maxima amax (broadcast):
+    rint(x * (127 / amax)) in fp32; zero groups give zero codes."""
+    x = np.asarray(x, np.float32)
+    amax = np.asarray(amax, np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(amax > 0, np.float32(127.0) / np.where(amax > 0, amax, np.float32(1.0)), np.float32(0.0))
+    return np.clip(np.rint((x * inv).astype(np.float32)), -127, 127).astype(np.int32), (amax / np.float32(127.0))
+
+
+def _tile_layout(grid, tile, n_text):
+    """Per raster token (and text token): tile id and rank in the tile's rows
+    (compact tile order); text tokens form pseudo-tiles of L rows."""
+    N = int(np.prod(grid))
+    L = int(np.prod([min(a, b) for a, b in zip(grid, tile)]))
+    p = oracle.perm(grid, tile)
+    t, h, w = np.unravel_index(np.arange(N), grid)
+    n = oracle.tiles_per_axis(grid, tile)
+    tid = ((t // tile[0]) * n[1] + h // tile[1]) * n[2] + w // tile[2]
+    T = int(np.prod(n))
+    start = np.full(T, np.iinfo(np.int64).max)
+    np.minimum.at(start, tid, p)
+    rank = p - start[tid]
+    j = np.arange(n_text)
+    return (np.concatenate([tid, T + j // L]), np.concatenate([rank, j % L]), T, L)
+
+
+def quantize(q, k, v, grid, tile, n_text=0):
+    """Steps 1-4 for [B,H,S,D] float arrays in raster order (text rows last).
+    Returns a dict of codes and scales."""
+    q, k, v = (np.asarray(x, np.float32) for x in (q, k, v))
+    tid, rank, T, L = _tile_layout(grid, tile, n_text)
+    m = k.astype(np.float64).mean(axis=2, keepdims=True).astype(np.float32)       # [B,H,1,D]
+    ks = (k - m).astype(np.float32)
+    qc, sq = int8_codes(q, np.abs(q).max(axis=3, keepdims=True))
+    # K blocks: key j belongs to block (tid[j], rank[j] // 64)
+    blk = tid * ((L + KEY_BLOCK - 1) // KEY_BLOCK) + rank // KEY_BLOCK
+    nblk = int(blk.max()) + 1
+    amax_k = np.zeros(k.shape[:2] + (nblk,), np.float32)
+    for b in range(k.shape[0]):
+        for hh in range(k.shape[1]):
+            np.maximum.at(amax_k[b, hh], blk, np.abs(ks[b, hh]).max(axis=1))
+    kc, sk_blk = int8_codes(ks, amax_k[:, :, blk, None])
+    amax_v = np.abs(v).max(axis=2, keepdims=True)                                    # [B,H,1,D]
+    with np.errstate(divide="ignore"):
+        inv_v = np.where(amax_v > 0, np.float32(E4M3_MAX) / np.where(amax_v > 0, amax_v, 1), 0).astype(np.float32)
+    vc = e4m3((v * inv_v).astype(np.float32))
+    sv = (amax_v / np.float32(E4M3_MAX)).astype(np.float32)
+    return dict(m=m, qc=qc, sq=sq, kc=kc, sk=sk_blk, vc=vc, sv=sv)
+
+
+def _allowed_keys(grid, tile, windows, offsets, border, n_text, h):
+    """Callable row -> allowed key indices (raster order, text last)."""
+    N = int(np.prod(grid))
+    kv_idx, kv_cnt, _, _ = oracle.index(grid, tile, windows, offsets, border=border)
+    tid, _, T, _ = _tile_layout(grid, tile, 0)
+    members = [np.flatnonzero(tid == t) for t in range(T)]
+    text = np.arange(N, N + n_text)
+    allk = np.arange(N + n_text)
+
+    def keys(i):
+        if i >= N:
+            return allk
+        lst = kv_idx[h, tid[i], : kv_cnt[h, tid[i]]]
+        return np.concatenate([members[t] for t in lst] + [text])
+    return keys
+
+
+def fwd(q, k, v, grid, tile, windows, offsets=None, scale=None, rows=None, border="shift", n_text=0, quant=None,
+        round_p=True):
+    """Steps 5-7 on the quantized tensors.  Returns (o, lse) in float64: for
+    rows=None shaped [B,H,S,D] and [B,H,S], else [n_rows, D], [n_rows] for the
+    flat row ids (b*H + h)*S + i.  `quant` replaces step 1-4's output (a dict
+    as quantize returns); round_p=False skips the e4m3 rounding of P."""
+    B, H, S, D = np.shape(q)
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    Q = quantize(q, k, v, grid, tile, n_text) if quant is None else quant
+    windows = np.asarray(windows, np.int64).reshape(-1, 3)
+    r = np.arange(B * H * S) if rows is None else np.asarray(rows, np.int64)
+    keyfns = {}
+    o = np.zeros((len(r), D))
+    lse = np.zeros(len(r))
+    c = scale * np.log2(np.e)
+    for n_, row in enumerate(r):
+        b, hh, i = row // (H * S), (row // S) % H, row % S
+        if hh not in keyfns:
+            off = offsets
+            if offsets is not None and np.ndim(offsets) == 3:
+                off = np.asarray(offsets)[hh]
+            keyfns[hh] = _allowed_keys(grid, tile, windows[hh:hh + 1], off, border, n_text, 0)
+        j = keyfns[hh](i)
+        acc = Q["kc"][b, hh, j].astype(np.float64) @ Q["qc"][b, hh, i].astype(np.float64)
+        s = acc * float(Q["sq"][b, hh, i, 0]) * Q["sk"][b, hh, j, 0].astype(np.float64) * c
+        M = np.ceil(s.max())
+        p = np.exp2(s - M)
+        if round_p:
+            p = e4m3(p)
+        l = p.sum()
+        o[n_] = (p @ Q["vc"][b, hh, j]) * Q["sv"][b, hh, 0].astype(np.float64) / l
+        lse[n_] = np.log(2.0) * (M + np.log2(l)) + scale * float(
+            np.asarray(q, np.float64)[b, hh, i] @ Q["m"][b, hh, 0].astype(np.float64))
+    if rows is None:
+        return o.reshape(B, H, S, D), lse.reshape(B, H, S)
+    return o, lse
