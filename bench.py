@@ -21,6 +21,11 @@ tokens follow the video tokens of every (b, h) slab (token-type-aware
 masking: text rows and columns dense); the counted work adds the text pairs,
 4*D*M*(2N + M) flop per (b, h) in the forward.
 
+--forward-only times the inference layer instead (reorder Q,K,V; index;
+forward; reorder O), counted as the forward's work; --precision fp8 runs that
+forward with the quantized products (INT8 QK^T, FP8 e4m3 PV), whose roofline
+peak is the MI355X dense fp8 / int8 rate.
+
 --grid T,H,W replaces the token grid, e.g. the 720p latent grid 30,45,80 that
 the (6,8,8) tile does not divide (its last tile row along H is cut to 5
 rows); counted work then sums len(q) * len(k) over the listed tile pairs.
@@ -52,6 +57,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "effective attention TFLOP/s (unmasked tile pairs) + ms/layer, 115200-tok grid"
 PEAK_BF16_TFLOPS = 2516.6        # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_FP8_TFLOPS = 5033.2         # MI355X dense fp8 / int8 MFMA (twice the bf16 rate)
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 WORKLOAD = 5                     # the training workload of tests/inputs.py
 
@@ -64,6 +70,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024,
                     help="query rows and key rows of the oracle sample (CPU baseline)")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time the inference layer (reorder, index, forward, inverse reorder) only")
+    ap.add_argument("--precision", choices=("default", "fp8"), default="default",
+                    help="arithmetic of the forward (fp8: INT8 QK^T and FP8 PV; needs --forward-only)")
     ap.add_argument("--grid", type=str, default=None,
                     help="token grid T,H,W replacing the workload's (30,48,80)")
     ap.add_argument("--text", type=int, default=0,
@@ -227,6 +237,11 @@ def main():
     if nt < 0:
         print("--text must be >= 0", file=sys.stderr)
         sys.exit(2)
+    if args.precision == "fp8" and not args.forward_only:
+        print("--precision fp8 measures the forward only: add --forward-only", file=sys.stderr)
+        sys.exit(2)
+    fwd_only = args.forward_only
+    prec = sta.STA_PREC_FP8 if args.precision == "fp8" else sta.STA_PREC_DEFAULT
     grid = None if args.grid is None else tuple(int(x) for x in args.grid.split(","))
     w = workload(WORKLOAD, n_text=nt, grid=grid)
     B, H, S, D = w["q"].shape
@@ -261,10 +276,12 @@ def main():
         mark(1)
         sta.sta_build_index(geom, windows, None, idx, stream)
         mark(2)
-        sta.sta_fwd_ex(qt, kt, vt, ot, lse, B, H, D, sta.STA_BF16, scale, geom, idx, nt, stream)
+        sta.sta_fwd_ex(qt, kt, vt, ot, lse, B, H, D, sta.STA_BF16, scale, geom, idx, nt, stream, prec)
         mark(3)
         sta.sta_tile_reorder_ex(ot, o, B * H, row_bytes, geom, True, nt, stream)
         mark(4)
+        if fwd_only:
+            return
         sta.sta_tile_reorder_ex(do, dot_, B * H, row_bytes, geom, False, nt, stream)
         mark(5)
         for i, part in enumerate((sta.STA_BWD_DELTA, sta.STA_BWD_DKDV, sta.STA_BWD_DQ)):
@@ -289,6 +306,8 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    if fwd_only:
+        names = names[:4]
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
 
     kv_cnt = idx.kv_cnt.cpu().numpy()
@@ -301,19 +320,21 @@ def main():
                 for h in range(kv_cnt.shape[0]) for q in range(kv_cnt.shape[1]))
     fwd_flop = 4.0 * B * pairs * D
     fwd_flop += 4.0 * B * H * D * float(nt) * (2 * N + nt)          # text rows and columns (joint step)
-    step_flop = 3.5 * fwd_flop                                      # forward + backward (2.5x)
+    step_flop = fwd_flop if fwd_only else 3.5 * fwd_flop            # forward + backward (2.5x)
     value = step_flop / (ms_per_step * 1e-3) / 1e12
 
     # Algorithmic work of each attention kernel (flop per launch): the forward
     # does QK^T and PV (4 L^2 D per pair); dK/dV must form S, dP, dV and dK
     # (8 L^2 D); dQ adds only the dQ product (2 L^2 D; its S and dP are
     # recomputation).  Together the backward is 10 L^2 D = 2.5x the forward.
-    alg = {"fwd": fwd_flop, "bwd_dkdv": 2.0 * fwd_flop, "bwd_dq": 0.5 * fwd_flop}
+    alg = {"fwd": fwd_flop} if fwd_only else {"fwd": fwd_flop, "bwd_dkdv": 2.0 * fwd_flop, "bwd_dq": 0.5 * fwd_flop}
+    peak = PEAK_FP8_TFLOPS if prec == sta.STA_PREC_FP8 else PEAK_BF16_TFLOPS
     dominant = max(alg, key=lambda n: per[n])
     achieved = alg[dominant] / (per[dominant] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "kernel": dominant,
-                "traffic": measured_traffic(dominant) if nt == 0 and grid is None else None,  # video step only
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "kernel": dominant,
+                "traffic": measured_traffic(dominant) if nt == 0 and grid is None and prec == sta.STA_PREC_DEFAULT
+                else None,                                    # the counter passes cover the bf16 video step
                 "measured_gemm_ceiling": gemm_ceiling(torch, dev)}
 
     tensor_bytes = B * H * S * D * 2
@@ -329,11 +350,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "int8 QK^T + e4m3 PV, bf16 I/O" if prec == sta.STA_PREC_FP8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": "720p training step: B=1 H=24 D=128, grid (%d,%d,%d)=%d tokens, tile (6,8,8), "
-                        "window 3x3x5 tiles, forward+backward" % (tuple(geom.grid) + (N,)) +
+                        "window 3x3x5 tiles, %s" % (tuple(geom.grid) + (N, "forward only" if fwd_only else
+                                                                       "forward+backward")) +
                         ("" if nt == 0 else ", joint with %d text tokens (dense text rows and columns)" % nt),
             "global_batch": B,
             "seq_len": S,
@@ -344,14 +366,14 @@ def main():
             "ms_per_layer_fwd": round(per["reorder_qkv"] + per["index"] + per["fwd"] + per["reorder_o"], 3),
             "fwd_kernel_ms": round(per["fwd"], 3),
             "fwd_tflops": round(fwd_flop / (per["fwd"] * 1e-3) / 1e12, 1),
-            "fwd_frac_of_peak": round(fwd_flop / (per["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "bwd_kernels_ms": round(per["bwd_delta"] + per["bwd_dkdv"] + per["bwd_dq"], 3),
+            "fwd_frac_of_peak": round(fwd_flop / (per["fwd"] * 1e-3) / 1e12 / peak, 4),
+            "bwd_kernels_ms": None if fwd_only else round(per["bwd_delta"] + per["bwd_dkdv"] + per["bwd_dq"], 3),
             "reorder_qkv_gbs": round(reorder_gbs, 1),
             "per_call_ms": {n: round(t, 4) for n, t in per.items()},
         },
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline and grid is None:     # the sample assumes whole (uncut) tiles
+    if not args.no_cpu_baseline and grid is None and not fwd_only:   # a sample of the training step
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows, nt)
     print(json.dumps(out), flush=True)
 

@@ -26,6 +26,8 @@ STA_OK, STA_ERR_INVALID, STA_ERR_UNSUPPORTED, STA_ERR_HIP = 0, 1, 2, 3
 STA_BF16, STA_F32 = 0, 1
 STA_BWD_DELTA, STA_BWD_DKDV, STA_BWD_DQ, STA_BWD_ALL = 1, 2, 4, 7
 STA_BORDER_SHIFT, STA_BORDER_TRUNCATE = 0, 1
+STA_PREC_DEFAULT, STA_PREC_FP8 = 0, 1
+_PRECISIONS = {"default": STA_PREC_DEFAULT, "fp8": STA_PREC_FP8}
 EXPORTS = ("sta_status_str", "sta_last_error", "sta_version", "sta_index_dims", "sta_index_dims_ex",
            "sta_tile_reorder", "sta_tile_reorder_ex", "sta_build_index", "sta_build_index_ex", "sta_fwd",
            "sta_fwd_ex", "sta_bwd", "sta_bwd_parts", "sta_bwd_ex")
@@ -53,7 +55,7 @@ class sta_index_opts(ctypes.Structure):
 
 
 class sta_attn_opts(ctypes.Structure):
-    _fields_ = [("n_text", ctypes.c_int32)]
+    _fields_ = [("n_text", ctypes.c_int32), ("precision", ctypes.c_int32)]
 
 
 class sta_index(ctypes.Structure):
@@ -209,8 +211,8 @@ def sta_fwd(q, k, v, o, lse, B, H, D, dtype, scale, geom, index, stream=None):
                        ctypes.byref(geom.c()), ctypes.byref(index.c()), _stream(stream)))
 
 
-def sta_fwd_ex(q, k, v, o, lse, B, H, D, dtype, scale, geom, index, n_text=0, stream=None):
-    opts = sta_attn_opts(int(n_text))
+def sta_fwd_ex(q, k, v, o, lse, B, H, D, dtype, scale, geom, index, n_text=0, stream=None, precision=STA_PREC_DEFAULT):
+    opts = sta_attn_opts(int(n_text), int(precision))
     _check(lib.sta_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, D, dtype, float(scale),
                           ctypes.byref(geom.c()), ctypes.byref(index.c()), ctypes.byref(opts), _stream(stream)))
 
@@ -286,15 +288,16 @@ def tile_reorder(x, geom, inverse=False, out=None, stream=None, n_text=0):
     return out
 
 
-def forward(q, k, v, geom, index, scale=None, stream=None, n_text=0):
+def forward(q, k, v, geom, index, scale=None, stream=None, n_text=0, precision="default"):
     """q, k, v [B,H,N+n_text,D] (video rows in tile order, then the text
-    rows) -> (o [B,H,N+n_text,D], lse [B,H,N+n_text] fp32)."""
+    rows) -> (o [B,H,N+n_text,D], lse [B,H,N+n_text] fp32).  precision
+    "fp8" runs the quantized products (INT8 QK^T, FP8 PV; bf16 tensors)."""
     B, H, S, D = q.shape
     assert S == geom.tokens + n_text
     scale = D ** -0.5 if scale is None else scale
     o = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    sta_fwd_ex(q, k, v, o, lse, B, H, D, _dtype_code(q), scale, geom, index, n_text, stream)
+    sta_fwd_ex(q, k, v, o, lse, B, H, D, _dtype_code(q), scale, geom, index, n_text, stream, _PRECISIONS[precision])
     return o, lse
 
 

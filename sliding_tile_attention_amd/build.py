@@ -17,7 +17,8 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsta.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "workspace.hip", "reorder.hip", "index.hip", "attn_f32.hip", "fwd_bf16.hip", "bwd_bf16.hip"]
+SOURCES = ["api.hip", "workspace.hip", "reorder.hip", "index.hip", "attn_f32.hip", "fwd_bf16.hip", "fwd_fp8.hip",
+           "bwd_bf16.hip"]
 HEADERS = ["common.h", "mfma.h"]
 # Per-source extra compiler flags (none at present).
 EXTRA = {}

@@ -191,7 +191,7 @@ const char *sta_status_str(sta_status s)
 
 const char *sta_last_error(void) { return g_err; }
 
-int32_t sta_version(void) { return 10200; }
+int32_t sta_version(void) { return 10300; }
 
 sta_status sta_index_dims(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
                           int32_t has_offsets, int32_t *max_kv, int32_t *max_q)
@@ -306,6 +306,11 @@ sta_status sta_fwd_ex(const void *q, const void *k, const void *v, void *o, floa
     sta_status st = make_geo(g, geo);
     if (st != STA_OK) return st;
     if ((st = add_text(geo, opts)) != STA_OK) return st;
+    const int prec = opts ? opts->precision : STA_PREC_DEFAULT;
+    if (prec != STA_PREC_DEFAULT && prec != STA_PREC_FP8)
+        return fail(STA_ERR_INVALID, "unknown precision %d", prec);
+    if (prec == STA_PREC_FP8 && dtype != STA_BF16)
+        return fail(STA_ERR_UNSUPPORTED, "the FP8 forward takes bf16 tensors");
     if ((st = check_attn(geo, B, H, D, dtype, scale)) != STA_OK) return st;
     if ((st = check_index(geo, H, idx, false)) != STA_OK) return st;
     if (!q || !k || !v || !o || !lse)
@@ -315,6 +320,8 @@ sta_status sta_fwd_ex(const void *q, const void *k, const void *v, void *o, floa
     if (dtype == STA_F32)
         return launch_fwd_f32((const float *)q, (const float *)k, (const float *)v, (float *)o, lse,
                               B, H, D, scale, geo, *idx, stream);
+    if (prec == STA_PREC_FP8)
+        return launch_fwd_fp8(q, k, v, o, lse, B, H, D, scale, geo, *idx, stream);
     return launch_fwd_bf16(q, k, v, o, lse, B, H, D, scale, geo, *idx, stream);
 }
 
@@ -337,6 +344,9 @@ sta_status sta_bwd_ex(const void *q, const void *k, const void *v, const void *o
     sta_status st = make_geo(g, geo);
     if (st != STA_OK) return st;
     if ((st = add_text(geo, opts)) != STA_OK) return st;
+    if (opts && opts->precision != STA_PREC_DEFAULT)
+        return fail(opts->precision == STA_PREC_FP8 ? STA_ERR_UNSUPPORTED : STA_ERR_INVALID,
+                    "the backward runs in the tensors' dtype (precision %d requested)", opts->precision);
     if ((st = check_attn(geo, B, H, D, dtype, scale)) != STA_OK) return st;
     if (parts < 1 || parts > STA_BWD_ALL)
         return fail(STA_ERR_INVALID, "parts must be a non-empty mask of STA_BWD_DELTA|DKDV|DQ (got %d)", parts);

@@ -145,6 +145,10 @@ sta_status launch_bwd_f32(const float *q, const float *k, const float *v, const 
 sta_status launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
                            int B, int H, int D, float scale, const Geo &g, const sta_index &idx,
                            hipStream_t s);
+// quantized forward: INT8 QK^T, FP8 (e4m3) PV, bf16 tensors
+sta_status launch_fwd_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                          int B, int H, int D, float scale, const Geo &g, const sta_index &idx,
+                          hipStream_t s);
 sta_status launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
                            const float *lse, const void *dout, void *dq, void *dk, void *dv,
                            float *delta, int B, int H, int D, float scale, const Geo &g,

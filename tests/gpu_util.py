@@ -85,8 +85,9 @@ class Layer:
     def _raster(self, x):
         return sta.tile_reorder(x, self.geom, inverse=True, n_text=self.n_text)
 
-    def forward(self, scale=None):
-        self.o, self.lse = sta.forward(self.q, self.k, self.v, self.geom, self.index, scale, n_text=self.n_text)
+    def forward(self, scale=None, precision="default"):
+        self.o, self.lse = sta.forward(self.q, self.k, self.v, self.geom, self.index, scale, n_text=self.n_text,
+                                       precision=precision)
         return self._raster(self.o), self._raster(self.lse.unsqueeze(-1)).squeeze(-1)
 
     def backward(self, scale=None):

@@ -1,0 +1,93 @@
+"""GPU parity of the quantized forward (INT8 QK^T, FP8 PV): libsta against
+the oracle of the quantized method (oracle/quant.py) on identical seeded
+inputs, with the bf16 gates; and the accuracy of the method against exact
+attention at full size."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle, quant
+from tests.gpu_util import Layer, assert_close, assert_lse, errors, say, to_host
+from tests.inputs import tensors, workload
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, grid, tile, B, H, D, windows, offsets kind, border, n_text
+    ("L384-D128", (12, 16, 24), (6, 8, 8), 1, 2, 128, [(3, 3, 3), (1, 3, 3)], None, "shift", 0),
+    ("L128-D128-offsets", (4, 16, 24), (2, 8, 8), 2, 2, 128, [(3, 3, 3), (1, 1, 3)], "shared", "shift", 0),
+    ("L32-D64-partial-blocks", (4, 8, 12), (2, 4, 4), 1, 3, 64, [(3, 3, 3), (1, 3, 3), (5, 5, 5)], "head",
+     "truncate", 0),
+    ("L384-D128-text-cut", (12, 13, 16), (6, 8, 8), 1, 2, 128, [(3, 3, 3), (1, 1, 3)], None, "shift", 77),
+    ("L48-D64-text", (6, 8, 16), (3, 4, 4), 1, 2, 64, [(1, 3, 3), (3, 3, 5)], "head", "shift", 100),
+]
+
+
+def _offsets(kind, H, T, seed=13):
+    if kind is None:
+        return None
+    shape = (T, 3) if kind == "shared" else (H, T, 3)
+    return np.random.default_rng(seed).integers([-1, -2, -2], [1, 2, 2], endpoint=True,
+                                                size=shape).astype(np.int32)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: c[0])
+def test_fp8_forward_matches_quantized_oracle(case):
+    name, grid, tile, B, H, D, windows, kind, border, nt = case
+    say("fp8 fwd " + name)
+    T = int(np.prod(oracle.tiles_per_axis(grid, tile)))
+    off = _offsets(kind, H, T)
+    S = int(np.prod(grid)) + nt
+    q, k, v = tensors(B, H, S, D, "bf16", 190)
+    layer = Layer(grid, tile, windows, off, q, k, v, "bf16", border=border, n_text=nt)
+    o, lse = layer.forward(precision="fp8")
+    torch.cuda.synchronize()
+    ro, rl = quant.fwd(q, k, v, grid, tile, windows, off, border=border, n_text=nt)
+    assert_close(to_host(o), ro, "bf16", name + " O")
+    assert_lse(to_host(lse), rl, "bf16")
+
+
+def test_fp8_forward_deterministic_and_repeatable():
+    """Two calls (and a call after a call of another shape) give identical
+    bits: the statistics pass reduces in a fixed order, no atomics."""
+    grid, tile, windows = (12, 16, 24), (6, 8, 8), [(3, 3, 3)]
+    q, k, v = tensors(1, 1, int(np.prod(grid)), 128, "bf16", 191)
+    layer = Layer(grid, tile, windows, None, q, k, v, "bf16")
+    o1, l1 = (x.clone() for x in layer.forward(precision="fp8"))
+    other = Layer((4, 8, 12), (2, 4, 4), [(3, 3, 3)], None, *tensors(1, 1, 384, 128, "bf16", 192), "bf16")
+    other.forward(precision="fp8")
+    o2, l2 = layer.forward(precision="fp8")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fp8_720p_sampled_and_method_accuracy():
+    """The 720p forward (115200 tokens, 24 heads, window 3x3x5) in the FP8
+    path: sampled rows against the quantized method's oracle (bf16 gates),
+    and against exact attention, whose error is the method's own (relative
+    L2 below 8e-2: e4m3 P and V each carry a rounding of relative RMS about
+    2^-4/sqrt(3))."""
+    w = workload(3)
+    say("fp8 fwd 720p (full size)")
+    layer = Layer(w["grid"], w["tile"], w["windows"], None, w["q"], w["k"], w["v"], "bf16")
+    o, lse = layer.forward(precision="fp8")
+    torch.cuda.synchronize()
+    B, H, N, D = w["q"].shape
+    inv = np.argsort(oracle.perm(w["grid"], w["tile"]))
+    g = np.random.default_rng(193)
+    rows = []
+    for h in (0, 11, 23):
+        for t in (0, 299, 144, int(g.integers(0, 300))):
+            rows += [h * N + int(inv[t * 384 + s]) for s in g.choice(384, 4, replace=False)]
+    rows = np.array(rows, np.int64)
+    say("quantized oracle on %d rows" % len(rows))
+    ro, rl = quant.fwd(w["q"], w["k"], w["v"], w["grid"], w["tile"], w["windows"], rows=rows)
+    pick = lambda x: to_host(x.reshape(-1, D)[torch.from_numpy(rows).cuda()])
+    got = pick(o)
+    assert_close(got, ro, "bf16", "O vs quantized oracle")
+    assert_lse(to_host(lse.reshape(-1)[torch.from_numpy(rows).cuda()]), rl, "bf16")
+    eo, _ = oracle.fwd(w["q"], w["k"], w["v"], w["grid"], w["tile"], w["windows"], rows=rows)
+    max_abs, rel = errors(got, eo)
+    say("fp8 vs exact attention: max-abs %.3e rel-L2 %.3e" % (max_abs, rel))
+    assert rel < 8e-2
+    assert torch.isfinite(layer.o).all()

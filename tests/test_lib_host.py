@@ -258,3 +258,25 @@ def test_attn_options_null_equals_zero_text():
     st_zero = sta.lib.sta_fwd_ex(*[sta._ptr(t) if isinstance(t, torch.Tensor) else t for t in args], g, x,
                                  ctypes.byref(sta.sta_attn_opts(0)), None)
     assert st_null == st_zero == sta.STA_ERR_INVALID
+
+
+def test_precision_option_checks():
+    """The quantized forward takes bf16 tensors only, the backward runs in
+    the tensors' dtype, and unknown precision values are malformed."""
+    a = _fwd_args()
+
+    def fwd(prec, dtype=sta.STA_BF16):
+        opts = sta.sta_attn_opts(0, prec)
+        st = sta.lib.sta_fwd_ex(*[sta._ptr(a[n]) for n in ("q", "k", "v", "o", "lse")], 1, 2, 64, dtype, 0.125,
+                                ctypes.byref(GEOM.c()), ctypes.byref(a["index"].c()), ctypes.byref(opts), None)
+        return st
+
+    def bwd(prec):
+        opts = sta.sta_attn_opts(0, prec)
+        ptrs = [sta._ptr(_fake()) for _ in range(10)]
+        return sta.lib.sta_bwd_ex(*ptrs, 1, 2, 64, sta.STA_BF16, 0.125, ctypes.byref(GEOM.c()),
+                                  ctypes.byref(a["index"].c()), sta.STA_BWD_ALL, ctypes.byref(opts), None)
+    assert fwd(7) == sta.STA_ERR_INVALID
+    assert fwd(sta.STA_PREC_FP8, sta.STA_F32) == sta.STA_ERR_UNSUPPORTED
+    assert bwd(sta.STA_PREC_FP8) == sta.STA_ERR_UNSUPPORTED
+    assert bwd(5) == sta.STA_ERR_INVALID
