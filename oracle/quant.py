@@ -16,7 +16,10 @@ such a kernel, so every step is spelled out here and followed by the GPU:
   4. V: e4m3 codes per channel d over all rows of (b, h): amax_d = max |v_d|,
      codes = e4m3(v * (448 / amax_d)) in fp32, scale amax_d / 448.
   5. Base-2 scores s_ij = (sum_d qc_id kc_jd) * sq_i * sk_j * scale * log2(e)
-     over the allowed keys j (the STA window, plus text keys).
+     over the allowed keys j (the STA window, plus text keys).  They decide
+     the e4m3 codes of P, so they are formed in fp32 exactly as the kernel
+     forms them: s = fp32(acc * fp32(fp32(sq * c) * sk)), c = fp32(scale *
+     log2 e), and the exponent fp32(s - (M - 4)).
   6. M_i = ceil(max_j s_ij); p_ij = 2^-4 e4m3(2^(s_ij - M_i + 4)): P is
      rounded at 16 times the row-max scale, so that every probability down
      to 2^-10 of the row's largest stays in e4m3's normal range (3 mantissa
@@ -143,7 +146,8 @@ def fwd(q, k, v, grid, tile, windows, offsets=None, scale=None, rows=None, borde
         return slabs[(b, hh)]
     o = np.zeros((len(r), D))
     lse = np.zeros(len(r))
-    c = scale * np.log2(np.e)
+    f32 = np.float32
+    c = f32(f32(scale) * f32(1.4426950408889634))
     for n_, row in enumerate(r):
         b, hh, i = row // (H * S), (row // S) % H, row % S
         if hh not in keyfns:
@@ -154,11 +158,16 @@ def fwd(q, k, v, grid, tile, windows, offsets=None, scale=None, rows=None, borde
         j = keyfns[hh](i)
         Q = slab(b, hh)
         acc = Q["kc"][0, 0, j].astype(np.float64) @ Q["qc"][0, 0, i].astype(np.float64)
-        s = acc * float(Q["sq"][0, 0, i, 0]) * Q["sk"][0, 0, j, 0].astype(np.float64) * c
-        M = np.ceil(s.max())
-        p = np.exp2(s - M)
         if round_p:
-            p = e4m3(p * 2.0 ** P_SHIFT) * 2.0 ** -P_SHIFT
+            fq = f32(f32(Q["sq"][0, 0, i, 0]) * c)
+            s = (acc.astype(np.float32) * (fq * Q["sk"][0, 0, j, 0].astype(np.float32))).astype(np.float32)
+            M = float(np.ceil(s.max()))
+            x = (s - f32(M - P_SHIFT)).astype(np.float32)
+            p = e4m3(np.exp2(x.astype(np.float64)).astype(np.float32)) * 2.0 ** -P_SHIFT
+        else:
+            s = acc * float(Q["sq"][0, 0, i, 0]) * Q["sk"][0, 0, j, 0].astype(np.float64) * (scale * np.log2(np.e))
+            M = np.ceil(s.max())
+            p = np.exp2(s - M)
         l = p.sum()
         o[n_] = (p @ Q["vc"][0, 0, j]) * Q["sv"][0, 0, 0].astype(np.float64) / l
         lse[n_] = np.log(2.0) * (M + np.log2(l)) + scale * float(
