@@ -18,8 +18,9 @@ such a kernel, so every step is spelled out here and followed by the GPU:
   5. Base-2 scores s_ij = (sum_d qc_id kc_jd) * sq_i * sk_j * scale * log2(e)
      over the allowed keys j (the STA window, plus text keys).  They decide
      the e4m3 codes of P, so they are formed in fp32 exactly as the kernel
-     forms them: s = fp32(acc * fp32(fp32(sq * c) * sk)), c = fp32(scale *
-     log2 e), and the exponent fp32(s - (M - 4)).
+     forms them: with f = fp32(fp32(sq * c) * sk), c = fp32(scale * log2 e),
+     the max uses s = fp32(acc * f) and the exponent is the fused
+     fp32(acc * f - (M - 4)) (one rounding; acc * f is exact in fp64).
   6. M_i = ceil(max_j s_ij); p_ij = 2^-4 e4m3(2^(s_ij - M_i + 4)): P is
      rounded at 16 times the row-max scale, so that every probability down
      to 2^-10 of the row's largest stays in e4m3's normal range (3 mantissa
@@ -160,9 +161,10 @@ def fwd(q, k, v, grid, tile, windows, offsets=None, scale=None, rows=None, borde
         acc = Q["kc"][0, 0, j].astype(np.float64) @ Q["qc"][0, 0, i].astype(np.float64)
         if round_p:
             fq = f32(f32(Q["sq"][0, 0, i, 0]) * c)
-            s = (acc.astype(np.float32) * (fq * Q["sk"][0, 0, j, 0].astype(np.float32))).astype(np.float32)
+            f = (fq * Q["sk"][0, 0, j, 0].astype(np.float32)).astype(np.float32)
+            s = (acc.astype(np.float32) * f).astype(np.float32)
             M = float(np.ceil(s.max()))
-            x = (s - f32(M - P_SHIFT)).astype(np.float32)
+            x = (acc * f.astype(np.float64) - (M - P_SHIFT)).astype(np.float32)
             p = e4m3(np.exp2(x.astype(np.float64)).astype(np.float32)) * 2.0 ** -P_SHIFT
         else:
             s = acc * float(Q["sq"][0, 0, i, 0]) * Q["sk"][0, 0, j, 0].astype(np.float64) * (scale * np.log2(np.e))

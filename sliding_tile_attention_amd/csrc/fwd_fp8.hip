@@ -252,7 +252,7 @@ struct F8Cfg {
 };
 
 #ifndef STA_F8_MINB
-#define STA_F8_MINB 2
+#define STA_F8_MINB 3
 #endif
 
 // 4. Attention.  Workgroup = NW waves = NW*32 query rows of one tile; lane
@@ -366,6 +366,8 @@ __global__ __launch_bounds__(NW * 64, STA_F8_MINB) void fwd_fp8_kernel(
         const uint8_t *Ks = smem + BUF * C::STAGE;
         const uint8_t *Vs = Ks + C::KBYTES;
 
+        // s[kb][r]: the exact int32 dot product of register r of sub-block
+        // kb, as a float; the logit is s * f
         float s[2][16];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(NW * 64, STA_F8_MINB) void fwd_fp8_kernel(
                 a = __builtin_amdgcn_mfma_i32_32x32x32_i8(*(const i32x4 *)(Ks + kb * 32 * D + kofs[ks]), qf[ks], a, 0,
                                                           0, 0);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = (float)a[r] * f;
+            for (int r = 0; r < 16; ++r) s[kb][r] = (float)a[r];
         }
         if (valid < BN) {
 #pragma unroll
@@ -386,28 +388,33 @@ __global__ __launch_bounds__(NW * 64, STA_F8_MINB) void fwd_fp8_kernel(
                 for (int r = 0; r < 16; ++r)
                     if (kb * 32 + mfma_row_sigma(lane, r) >= valid) s[kb][r] = -INFINITY;
         }
-        // P = 2^(s - m + 4) in e4m3, byte 16kb + r of the operand = register
-        // r of sub-block kb; the row sum is taken from the rounded values.
+        // P = 2^(s*f - m + 4) in e4m3 (exponent by one fused multiply-add),
+        // byte 16kb + r of the operand = register r of sub-block kb; the row
+        // sum is taken from the rounded values, two at a time (e4m3 -> bf16
+        // is exact, then a dot product with ones).
         // The integer running max m is kept while every P of the lane stays
         // below 2^8 (e4m3 reaches 448); otherwise the block max, rounded up,
         // becomes the new max and O, l are rescaled by an exact power of two.
         i32x8 pw;
         auto probs = [&]() {
-            const float mo = m_i - 4.f;
+            const float nmo = 4.f - m_i;
+            const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
             float ls = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float p0 = __builtin_amdgcn_exp2f(s[kb][4 * j] - mo);
-                    const float p1 = __builtin_amdgcn_exp2f(s[kb][4 * j + 1] - mo);
-                    const float p2 = __builtin_amdgcn_exp2f(s[kb][4 * j + 2] - mo);
-                    const float p3 = __builtin_amdgcn_exp2f(s[kb][4 * j + 3] - mo);
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * j], f, nmo));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * j + 1], f, nmo));
+                    const float p2 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * j + 2], f, nmo));
+                    const float p3 = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * j + 3], f, nmo));
                     int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
                     w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
                     pw[4 * kb + j] = w;
-                    ls += (__builtin_amdgcn_cvt_f32_fp8(w, 0) + __builtin_amdgcn_cvt_f32_fp8(w, 1)) +
-                          (__builtin_amdgcn_cvt_f32_fp8(w, 2) + __builtin_amdgcn_cvt_f32_fp8(w, 3));
+                    ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false), one2,
+                                                         ls, false);
+                    ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true), one2,
+                                                         ls, false);
                 }
             return ls;
         };
@@ -418,7 +425,7 @@ __global__ __launch_bounds__(NW * 64, STA_F8_MINB) void fwd_fp8_kernel(
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            const float mn = ceilf(fmaxf(m_i, max_pair32(mx)));
+            const float mn = ceilf(fmaxf(m_i, max_pair32(mx) * f));
             const float alpha = __builtin_amdgcn_exp2f(m_i - mn);
             m_i = mn;
             l_i *= alpha;
