@@ -26,6 +26,11 @@ forward; reorder O), counted as the forward's work; --precision fp8 runs that
 forward with the quantized products (INT8 QK^T, FP8 e4m3 PV), whose roofline
 peak is the MI355X dense fp8 / int8 rate.
 
+--adaptive RT,RH,RW adds the window-shift producer to the step: after the
+reorder, every query tile's window shift (|shift| <= R per axis) is chosen on
+device from the tile means of Q and K (sta_window_shifts) and the index is
+built from those shifts, one set per head.
+
 --grid T,H,W replaces the token grid, e.g. the 720p latent grid 30,45,80 that
 the (6,8,8) tile does not divide (its last tile row along H is cut to 5
 rows); counted work then sums len(q) * len(k) over the listed tile pairs.
@@ -78,6 +83,8 @@ def parse():
                     help="token grid T,H,W replacing the workload's (30,48,80)")
     ap.add_argument("--text", type=int, default=0,
                     help="text tokens appended to the video tokens (joint text + video step)")
+    ap.add_argument("--adaptive", type=str, default=None, metavar="RT,RH,RW",
+                    help="choose the window shifts on device (search radius per axis) inside the step")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc counter_collection.csv files into profiles/traffic.json")
     return ap.parse_args()
@@ -258,45 +265,57 @@ def main():
     o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     delta = torch.empty_like(lse)
-    idx = sta.StaIndex(geom, windows, None)
+    radius = None if args.adaptive is None else tuple(int(x) for x in args.adaptive.split(","))
+    off = None if radius is None else torch.zeros((H, T, 3), dtype=torch.int32, device=dev)
+    idx = sta.StaIndex(geom, windows, off)          # with shifts: per-head capacity
     scale = D ** -0.5
     row_bytes = D * 2
     stream = torch.cuda.current_stream()
 
-    names = ["reorder_qkv", "index", "fwd", "reorder_o", "reorder_do", "bwd_delta", "bwd_dkdv", "bwd_dq",
-             "reorder_grads"]
+    names = ["reorder_qkv"] + (["shifts"] if radius else []) + ["index", "fwd", "reorder_o"]
+    if not fwd_only:
+        names += ["reorder_do", "bwd_delta", "bwd_dkdv", "bwd_dq", "reorder_grads"]
 
     def step(evs=None):
-        def mark(i):
+        marks = iter(range(len(names) + 1))
+
+        def mark():
+            i = next(marks)
             if evs is not None:
                 evs[i].record(stream)
-        mark(0)
+        mark()
         for src, dst in ((q, qt), (k, kt), (v, vt)):
             sta.sta_tile_reorder_ex(src, dst, B * H, row_bytes, geom, False, nt, stream)
-        mark(1)
-        sta.sta_build_index(geom, windows, None, idx, stream)
-        mark(2)
+        mark()
+        if radius:
+            sta.sta_window_shifts(qt, kt, B, H, D, sta.STA_BF16, scale, geom, windows, radius, off, "shift", False,
+                                  nt, stream)
+            mark()
+            sta.sta_build_index_ex(geom, windows, off, idx, "shift", True, stream)
+        else:
+            sta.sta_build_index(geom, windows, None, idx, stream)
+        mark()
         sta.sta_fwd_ex(qt, kt, vt, ot, lse, B, H, D, sta.STA_BF16, scale, geom, idx, nt, stream, prec)
-        mark(3)
+        mark()
         sta.sta_tile_reorder_ex(ot, o, B * H, row_bytes, geom, True, nt, stream)
-        mark(4)
+        mark()
         if fwd_only:
             return
         sta.sta_tile_reorder_ex(do, dot_, B * H, row_bytes, geom, False, nt, stream)
-        mark(5)
-        for i, part in enumerate((sta.STA_BWD_DELTA, sta.STA_BWD_DKDV, sta.STA_BWD_DQ)):
+        mark()
+        for part in (sta.STA_BWD_DELTA, sta.STA_BWD_DKDV, sta.STA_BWD_DQ):
             sta.sta_bwd_ex(qt, kt, vt, ot, lse, dot_, dqt, dkt, dvt, delta, B, H, D, sta.STA_BF16, scale, geom,
                            idx, part, nt, stream)
-            mark(6 + i)
+            mark()
         for src, dst in ((dqt, dq), (dkt, dk), (dvt, dv)):
             sta.sta_tile_reorder_ex(src, dst, B * H, row_bytes, geom, True, nt, stream)
-        mark(9)
+        mark()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
@@ -306,8 +325,6 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    if fwd_only:
-        names = names[:4]
     per = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(names)}
 
     kv_cnt = idx.kv_cnt.cpu().numpy()
@@ -334,7 +351,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "kernel": dominant,
                 "traffic": measured_traffic(dominant) if nt == 0 and grid is None and prec == sta.STA_PREC_DEFAULT
-                else None,                                    # the counter passes cover the bf16 video step
+                and radius is None else None,                 # the counter passes cover the bf16 video step
                 "measured_gemm_ceiling": gemm_ceiling(torch, dev)}
 
     tensor_bytes = B * H * S * D * 2
@@ -356,24 +373,31 @@ def main():
             "workload": "720p training step: B=1 H=24 D=128, grid (%d,%d,%d)=%d tokens, tile (6,8,8), "
                         "window 3x3x5 tiles, %s" % (tuple(geom.grid) + (N, "forward only" if fwd_only else
                                                                        "forward+backward")) +
-                        ("" if nt == 0 else ", joint with %d text tokens (dense text rows and columns)" % nt),
+                        ("" if nt == 0 else ", joint with %d text tokens (dense text rows and columns)" % nt) +
+                        ("" if radius is None else ", window shifts chosen on device (search radius %s tiles)"
+                         % (radius,)),
             "global_batch": B,
             "seq_len": S,
             "text_tokens": nt,
             "parallelism": "none (1 GPU)",
             "counted_flop_per_step": step_flop,
             "ms_per_layer_fwd_bwd": round(ms_per_step, 3),
-            "ms_per_layer_fwd": round(per["reorder_qkv"] + per["index"] + per["fwd"] + per["reorder_o"], 3),
+            "ms_per_layer_fwd": round(per["reorder_qkv"] + per.get("shifts", 0.0) + per["index"] + per["fwd"] +
+                                      per["reorder_o"], 3),
             "fwd_kernel_ms": round(per["fwd"], 3),
             "fwd_tflops": round(fwd_flop / (per["fwd"] * 1e-3) / 1e12, 1),
             "fwd_frac_of_peak": round(fwd_flop / (per["fwd"] * 1e-3) / 1e12 / peak, 4),
             "bwd_kernels_ms": None if fwd_only else round(per["bwd_delta"] + per["bwd_dkdv"] + per["bwd_dq"], 3),
             "reorder_qkv_gbs": round(reorder_gbs, 1),
+            # the producer reads Q and K once (its tile means); the choice
+            # itself touches only the means
+            "shifts_hbm_gbs": None if radius is None else round(2 * B * H * N * D * 2 / (per["shifts"] * 1e-3) / 1e9,
+                                                               1),
             "per_call_ms": {n: round(t, 4) for n, t in per.items()},
         },
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline and grid is None and not fwd_only:   # a sample of the training step
+    if not args.no_cpu_baseline and grid is None and not fwd_only and radius is None:   # a sample of the training step
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows, nt)
     print(json.dumps(out), flush=True)
 

@@ -51,8 +51,8 @@
  *     sta_last_error()); STA_ERR_HIP = a HIP launch error.
  *   - Attention tensors are [B][H][N][D], D fastest, in TILE order
  *     (sta_tile_reorder converts), 16-byte aligned, not aliasing each other.
- *   - The index is shared by every batch item; window shifts are shared by
- *     every head and batch item.
+ *   - An index holds one list set per head, shared by every batch item, or
+ *     one per (b, h) for windows shifted per batch item (see sta_index).
  *   - Thread-safe: no mutable global state apart from a thread-local
  *     error message.
  */
@@ -93,7 +93,12 @@ typedef struct { sta_dim3 grid; sta_dim3 tile; } sta_geom;
  *                                          each key tile, ascending, pad -1
  *   q_cnt  [num_heads][num_tiles]
  * Size max_kv / max_q with sta_index_dims.  q_idx/q_cnt are only needed by
- * sta_bwd and may be NULL (with max_q = 0) for forward-only use. */
+ * sta_bwd and may be NULL (with max_q = 0) for forward-only use.
+ * Attention calls with B batch items and H heads accept num_heads == H (the
+ * lists of head h serve every batch item) or num_heads == B*H (list set
+ * b*H + h serves (b, h): windows shifted per batch item).  Build the latter
+ * with sta_build_index_ex for B*H "heads" (the H windows repeated B times)
+ * and per-head offsets laid out [B][H][num_tiles][3]. */
 typedef struct {
     int32_t num_heads, num_tiles, max_kv, max_q;
     int32_t *kv_idx, *kv_cnt;
@@ -339,6 +344,58 @@ sta_status sta_bwd_ex(const void *q, const void *k, const void *v, const void *o
                       int32_t B, int32_t H, int32_t D, sta_dtype dtype, float scale,
                       const sta_geom *g, const sta_index *idx, int32_t parts, const sta_attn_opts *opts,
                       hipStream_t stream);
+
+/* Options of sta_window_shifts.  A NULL pointer means all fields 0. */
+typedef struct {
+    /* The sta_border rule of the windows the shifts are chosen for (the
+     * index built from them should use the same rule). */
+    int32_t border;
+    /* 0: one shift set for the batch, chosen on the tile means averaged
+     *    over the batch items: offsets_dev is [H][num_tiles][3];
+     * 1: one set per batch item: offsets_dev is [B][H][num_tiles][3]. */
+    int32_t per_batch;
+    /* Text rows after the N video rows of every (b, h) slab of q and k
+     * (>= 0; they take no part in the search). */
+    int32_t n_text;
+} sta_shift_opts;
+
+/*
+ * Chooses the window shift of every query tile and head from q and k
+ * ([B][H][N + n_text][D], video rows in tile order, bf16 or fp32, D 64 or
+ * 128, 16-byte aligned) and writes it to offsets_dev (DEVICE int32, the
+ * layout of sta_shift_opts.per_batch, (dt, dh, dw) in tiles), ready for
+ * sta_build_index_ex with per_head_offsets = 1.
+ * Rule (this library's reading: the pages call 3D-DSA's windows motion-
+ * adaptive but give no rule):
+ *   qbar, kbar = the mean of q and k over the tokens of each tile (a tile
+ *     cut by the grid border: over the tokens it holds), per (b, h), then
+ *     averaged over the batch items unless per_batch;
+ *   z_qk = scale * <qbar_q, kbar_k>;
+ *   mass(o) = sum over the key tiles k in the window of q shifted by o of
+ *     len_k * exp(z_qk), len_k = tokens of tile k, for every o with
+ *     |o_t| <= radius->t, |o_h| <= radius->h, |o_w| <= radius->w, windows of
+ *     windows_host[h] under the border rule (as sta_build_index_ex);
+ *   the shift of largest mass is written; among equal masses the one with
+ *   the smallest |o_t| + |o_h| + |o_w|, then the first in raster order of
+ *   (o_t, o_h, o_w).  Masses are fp32 (a choice may differ from exact
+ *   arithmetic where two masses agree to fp32 rounding); a query tile whose
+ *   masses are all non-finite gets the zero shift.
+ * Workspace: 2 * P * H * num_tiles * D * 4 bytes (P = B if per_batch, else
+ * 1) from the stream-ordered pool described at sta_fwd.
+ * Errors: STA_ERR_INVALID for NULL or misaligned pointers, B, H, D <= 0, a
+ * negative radius, a window < 1, a non-positive or non-finite scale, an
+ * unknown border or dtype, per_batch not 0/1, n_text < 0;
+ * STA_ERR_UNSUPPORTED for D other than 64 and 128, more than 4096
+ * candidate shifts ((2r_t+1)(2r_h+1)(2r_w+1)), a search region (the union
+ * of one query tile's candidate windows, at most prod_d min(n_d, w_d +
+ * 2 r_d) tiles) above 8192 tiles, or too large a launch.
+ * Source: motion-adaptive local windows of 3D-DSA ("MegaSlide-DiT",
+ * abstract).
+ */
+sta_status sta_window_shifts(const void *q, const void *k, int32_t B, int32_t H, int32_t D, sta_dtype dtype,
+                             float scale, const sta_geom *g, const sta_dim3 *windows_host,
+                             const sta_dim3 *radius, const sta_shift_opts *opts, int32_t *offsets_dev,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,7 @@ STA_PREC_DEFAULT, STA_PREC_FP8 = 0, 1
 _PRECISIONS = {"default": STA_PREC_DEFAULT, "fp8": STA_PREC_FP8}
 EXPORTS = ("sta_status_str", "sta_last_error", "sta_version", "sta_index_dims", "sta_index_dims_ex",
            "sta_tile_reorder", "sta_tile_reorder_ex", "sta_build_index", "sta_build_index_ex", "sta_fwd",
-           "sta_fwd_ex", "sta_bwd", "sta_bwd_parts", "sta_bwd_ex")
+           "sta_fwd_ex", "sta_bwd", "sta_bwd_parts", "sta_bwd_ex", "sta_window_shifts")
 
 
 class StaError(RuntimeError):
@@ -58,6 +58,10 @@ class sta_attn_opts(ctypes.Structure):
     _fields_ = [("n_text", ctypes.c_int32), ("precision", ctypes.c_int32)]
 
 
+class sta_shift_opts(ctypes.Structure):
+    _fields_ = [("border", ctypes.c_int32), ("per_batch", ctypes.c_int32), ("n_text", ctypes.c_int32)]
+
+
 class sta_index(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("num_tiles", ctypes.c_int32),
                 ("max_kv", ctypes.c_int32), ("max_q", ctypes.c_int32),
@@ -73,6 +77,7 @@ def _load():
     P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     G, X, OP = ctypes.POINTER(sta_geom), ctypes.POINTER(sta_index), ctypes.POINTER(sta_index_opts)
     AO = ctypes.POINTER(sta_attn_opts)
+    SO = ctypes.POINTER(sta_shift_opts)
     W = ctypes.POINTER(sta_dim3)
     sig = {
         "sta_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -91,6 +96,7 @@ def _load():
                                          I32, P]),
         "sta_bwd_ex": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X,
                                       I32, AO, P]),
+        "sta_window_shifts": (ctypes.c_int, [P, P, I32, I32, I32, ctypes.c_int, F32, G, W, W, SO, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -238,14 +244,35 @@ def sta_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, scal
                           ctypes.byref(index.c()), int(parts), ctypes.byref(opts), _stream(stream)))
 
 
+def sta_window_shifts(q, k, B, H, D, dtype, scale, geom, windows, radius, offsets, border="shift", per_batch=False,
+                      n_text=0, stream=None):
+    """offsets: int32 device tensor [H, num_tiles, 3] ([B, H, num_tiles, 3]
+    with per_batch), written by the call."""
+    w, nw = _windows(windows)
+    if nw != H:
+        raise ValueError("need one window per head")
+    r = sta_dim3(*[int(x) for x in radius])
+    opts = sta_shift_opts(STA_BORDER_TRUNCATE if border == "truncate" else STA_BORDER_SHIFT if border == "shift"
+                          else -1, int(bool(per_batch)), int(n_text))
+    _check(lib.sta_window_shifts(_ptr(q), _ptr(k), B, H, D, dtype, float(scale), ctypes.byref(geom.c()), w,
+                                 ctypes.byref(r), ctypes.byref(opts), _ptr(offsets), _stream(stream)))
+
+
 # ------------------------------------------------- allocation helpers --
 
 class StaIndex:
     """Device buffers of a block-sparse index (allocated with torch).
     offsets: None, an int32 device tensor [num_tiles, 3] shared by the heads,
-    or [H, num_tiles, 3] (one set per head); border: 'shift' or 'truncate'."""
+    [H, num_tiles, 3] (one set per head) or [B, H, num_tiles, 3] (one set per
+    batch item and head: the index then holds B*H list sets, list set
+    b*H + h serving (b, h)); border: 'shift' or 'truncate'."""
 
     def __init__(self, geom, windows, offsets=None, device="cuda", transposed=True, stream=None, border="shift"):
+        self.batch = 1
+        if offsets is not None and offsets.dim() == 4:
+            self.batch = offsets.shape[0]
+            windows = list(windows) * self.batch
+            offsets = offsets.reshape(-1, offsets.shape[2], 3).contiguous()
         H, T = len(windows), geom.num_tiles
         per_head = offsets is not None and offsets.dim() == 3
         self.max_kv, max_q = sta_index_dims_ex(geom, windows, offsets is not None, border, per_head)
@@ -273,6 +300,21 @@ def _dtype_code(t):
     if t.dtype == torch.float32:
         return STA_F32
     raise TypeError("libsta supports bfloat16 and float32 tensors, got %s" % t.dtype)
+
+
+def window_shifts(q, k, geom, windows, radius, scale=None, border="shift", per_batch=False, n_text=0, stream=None):
+    """Window shift of every query tile (and head, and batch item with
+    per_batch) chosen on device from q, k [B,H,N+n_text,D] (video rows in
+    tile order): int32 [H, num_tiles, 3] or [B, H, num_tiles, 3], ready for
+    StaIndex(..., offsets=...)."""
+    B, H, S, D = q.shape
+    assert S == geom.tokens + n_text and k.shape == q.shape
+    scale = D ** -0.5 if scale is None else scale
+    shape = (B, H, geom.num_tiles, 3) if per_batch else (H, geom.num_tiles, 3)
+    out = torch.empty(shape, dtype=torch.int32, device=q.device)
+    sta_window_shifts(q, k, B, H, D, _dtype_code(q), scale, geom, windows, radius, out, border, per_batch, n_text,
+                      stream)
+    return out
 
 
 def tile_reorder(x, geom, inverse=False, out=None, stream=None, n_text=0):

@@ -136,12 +136,15 @@ static sta_status index_options(const sta_index_opts *opts, bool &truncate, bool
     return STA_OK;
 }
 
-static sta_status check_index(const Geo &g, int H, const sta_index *idx, bool need_transposed)
+// An index holds one list set per head (shared by the batch), or one per
+// (b, h) for windows shifted per batch item (num_heads == B * H).
+static sta_status check_index(const Geo &g, int B, int H, const sta_index *idx, bool need_transposed)
 {
     if (!idx)
         return fail(STA_ERR_INVALID, "index pointer is NULL");
-    if (idx->num_heads != H)
-        return fail(STA_ERR_INVALID, "index has %d heads, call has %d", idx->num_heads, H);
+    if (idx->num_heads != H && (int64_t)idx->num_heads != (int64_t)B * H)
+        return fail(STA_ERR_INVALID, "index has %d list sets, call has %d heads x %d batch items",
+                    idx->num_heads, H, B);
     if (idx->num_tiles != g.T)
         return fail(STA_ERR_INVALID, "index has %d tiles, geometry has %d", idx->num_tiles, g.T);
     if (idx->max_kv < 1 || idx->max_kv > g.T || !idx->kv_idx || !idx->kv_cnt)
@@ -312,7 +315,7 @@ sta_status sta_fwd_ex(const void *q, const void *k, const void *v, void *o, floa
     if (prec == STA_PREC_FP8 && dtype != STA_BF16)
         return fail(STA_ERR_UNSUPPORTED, "the FP8 forward takes bf16 tensors");
     if ((st = check_attn(geo, B, H, D, dtype, scale)) != STA_OK) return st;
-    if ((st = check_index(geo, H, idx, false)) != STA_OK) return st;
+    if ((st = check_index(geo, B, H, idx, false)) != STA_OK) return st;
     if (!q || !k || !v || !o || !lse)
         return fail(STA_ERR_INVALID, "q, k, v, o and lse must be non-NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -350,7 +353,7 @@ sta_status sta_bwd_ex(const void *q, const void *k, const void *v, const void *o
     if ((st = check_attn(geo, B, H, D, dtype, scale)) != STA_OK) return st;
     if (parts < 1 || parts > STA_BWD_ALL)
         return fail(STA_ERR_INVALID, "parts must be a non-empty mask of STA_BWD_DELTA|DKDV|DQ (got %d)", parts);
-    if ((st = check_index(geo, H, idx, (parts & STA_BWD_DKDV) != 0)) != STA_OK) return st;
+    if ((st = check_index(geo, B, H, idx, (parts & STA_BWD_DKDV) != 0)) != STA_OK) return st;
     const bool need_do = true, need_o = (parts & STA_BWD_DELTA) != 0;
     const bool need_qkv = (parts & (STA_BWD_DKDV | STA_BWD_DQ)) != 0;
     struct { const void *p; bool need; } ins[] = {{q, need_qkv}, {k, need_qkv}, {v, need_qkv}, {o, need_o},
@@ -377,6 +380,77 @@ sta_status sta_bwd(const void *q, const void *k, const void *v, const void *o, c
 {
     return sta_bwd_parts(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, scale, g, idx,
                          STA_BWD_ALL, stream);
+}
+
+// Largest candidate count and search region of the window-shift producer.
+static const int64_t kMaxShiftCandidates = 4096;
+static const int64_t kMaxShiftRegion = 8192;
+
+sta_status sta_window_shifts(const void *q, const void *k, int32_t B, int32_t H, int32_t D, sta_dtype dtype,
+                             float scale, const sta_geom *g, const sta_dim3 *windows_host,
+                             const sta_dim3 *radius, const sta_shift_opts *opts, int32_t *offsets_dev,
+                             hipStream_t stream)
+{
+    Geo geo;
+    sta_status st = make_geo(g, geo);
+    if (st != STA_OK) return st;
+    const sta_shift_opts o = opts ? *opts : sta_shift_opts{0, 0, 0};
+    if (o.border != STA_BORDER_SHIFT && o.border != STA_BORDER_TRUNCATE)
+        return fail(STA_ERR_INVALID, "unknown border rule %d", o.border);
+    if (o.per_batch != 0 && o.per_batch != 1)
+        return fail(STA_ERR_INVALID, "per_batch must be 0 or 1 (got %d)", o.per_batch);
+    sta_attn_opts text = {o.n_text, STA_PREC_DEFAULT};
+    if ((st = add_text(geo, &text)) != STA_OK) return st;
+    if (B <= 0 || H <= 0 || D <= 0)
+        return fail(STA_ERR_INVALID, "B, H and D must be positive (B=%d H=%d D=%d)", B, H, D);
+    if (dtype != STA_BF16 && dtype != STA_F32)
+        return fail(STA_ERR_INVALID, "unknown dtype %d", (int)dtype);
+    if (!(scale > 0.0f) || !isfinite(scale))
+        return fail(STA_ERR_INVALID, "scale must be positive and finite");
+    if (!windows_host || !radius)
+        return fail(STA_ERR_INVALID, "windows and radius must be non-NULL");
+    if (radius->t < 0 || radius->h < 0 || radius->w < 0)
+        return fail(STA_ERR_INVALID, "radius must be >= 0 on every axis (%d,%d,%d)", radius->t, radius->h,
+                    radius->w);
+    if (!q || !k || !offsets_dev)
+        return fail(STA_ERR_INVALID, "q, k and offsets must be non-NULL");
+    if (!aligned16(q) || !aligned16(k))
+        return fail(STA_ERR_INVALID, "q and k must be 16-byte aligned");
+    if (D != 64 && D != 128)
+        return fail(STA_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", D);
+    if ((int64_t)B * H * geo.S * D > ((int64_t)1 << 40))
+        return fail(STA_ERR_UNSUPPORTED, "tensor too large");
+    const int64_t ncand = (2LL * radius->t + 1) * (2LL * radius->h + 1) * (2LL * radius->w + 1);
+    if (ncand > kMaxShiftCandidates)
+        return fail(STA_ERR_UNSUPPORTED, "%lld candidate shifts (at most %lld)", (long long)ncand,
+                    (long long)kMaxShiftCandidates);
+    if (H > 4096)
+        return fail(STA_ERR_UNSUPPORTED, "more than 4096 heads");
+    static thread_local int32_t wins[3 * 4096];
+    const int n[3] = {geo.nt, geo.nh, geo.nw};
+    const int r[3] = {radius->t, radius->h, radius->w};
+    int64_t region = 0;
+    for (int h = 0; h < H; ++h) {
+        const int w[3] = {windows_host[h].t, windows_host[h].h, windows_host[h].w};
+        int64_t reg = 1;
+        for (int d = 0; d < 3; ++d) {
+            if (w[d] < 1)
+                return fail(STA_ERR_INVALID, "window of head %d must be >= 1 on every axis (%d,%d,%d)", h, w[0],
+                            w[1], w[2]);
+            const int64_t span = (int64_t)w[d] + 2LL * r[d];
+            reg *= span < n[d] ? span : n[d];
+            wins[3 * h + d] = w[d];
+        }
+        region = reg > region ? reg : region;
+    }
+    if (region > kMaxShiftRegion)
+        return fail(STA_ERR_UNSUPPORTED, "search region of %lld tiles (at most %lld)", (long long)region,
+                    (long long)kMaxShiftRegion);
+    const int64_t P = o.per_batch ? B : 1;
+    if (!grid_fits(2 * P * H * geo.T, 256) || !grid_fits(P * 64 * geo.T, 256))
+        return fail(STA_ERR_UNSUPPORTED, "launch too large");
+    return launch_window_shifts(q, k, B, H, D, dtype, scale, geo, wins, r, o.border == STA_BORDER_TRUNCATE,
+                                o.per_batch == 1, (int)region, offsets_dev, stream);
 }
 
 }  // extern "C"

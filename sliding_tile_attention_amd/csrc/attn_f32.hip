@@ -52,13 +52,13 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float *__restrict__ 
                                                       const float *__restrict__ V, float *__restrict__ O,
                                                       float *__restrict__ LSE, const int32_t *__restrict__ kv_idx,
                                                       const int32_t *__restrict__ kv_cnt, int max_kv, int B,
-                                                      int H, Geo g, float scale)
+                                                      int H, int IH, Geo g, float scale)
 {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= (int64_t)B * H * g.S) return;
     const int64_t i = gid % g.S;
     const int64_t bh = gid / g.S;
-    const int h = (int)(bh % H);
+    const int h = (int)(bh % IH);   // list set: the head's, or (b, h)'s
     const float *kb = K + bh * g.S * D;
     const float *vb = V + bh * g.S * D;
     float q[D], acc[D];
@@ -101,14 +101,14 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(const float *__restrict__ Q
                                                      const float *__restrict__ V, const float *__restrict__ LSE,
                                                      const float *__restrict__ dO, const float *__restrict__ delta,
                                                      float *__restrict__ dQ, const int32_t *__restrict__ kv_idx,
-                                                     const int32_t *__restrict__ kv_cnt, int max_kv, int B, int H,
+                                                     const int32_t *__restrict__ kv_cnt, int max_kv, int B, int H, int IH,
                                                      Geo g, float scale)
 {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= (int64_t)B * H * g.S) return;
     const int64_t i = gid % g.S;
     const int64_t bh = gid / g.S;
-    const int h = (int)(bh % H);
+    const int h = (int)(bh % IH);   // list set: the head's, or (b, h)'s
     const float *kb = K + bh * g.S * D;
     const float *vb = V + bh * g.S * D;
     float q[D], go[D], acc[D];
@@ -139,14 +139,14 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(const float *__restrict__
                                                        const float *__restrict__ dO, const float *__restrict__ delta,
                                                        float *__restrict__ dK, float *__restrict__ dV,
                                                        const int32_t *__restrict__ q_idx,
-                                                       const int32_t *__restrict__ q_cnt, int max_q, int B, int H,
+                                                       const int32_t *__restrict__ q_cnt, int max_q, int B, int H, int IH,
                                                        Geo g, float scale)
 {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= (int64_t)B * H * g.S) return;
     const int64_t j = gid % g.S;
     const int64_t bh = gid / g.S;
-    const int h = (int)(bh % H);
+    const int h = (int)(bh % IH);   // list set: the head's, or (b, h)'s
     const float *qb = Q + bh * g.S * D;
     const float *ob = dO + bh * g.S * D;
     const float *lb = LSE + bh * g.S;
@@ -189,10 +189,10 @@ sta_status launch_fwd_f32(const float *q, const float *k, const float *v, float 
         return fail(STA_ERR_UNSUPPORTED, "fp32 path: too many rows");
     if (D == 64)
         hipLaunchKernelGGL(fwd_f32_kernel<64>, grid_for(rows), dim3(256), 0, s, q, k, v, o, lse, idx.kv_idx,
-                           idx.kv_cnt, idx.max_kv, B, H, g, scale);
+                           idx.kv_cnt, idx.max_kv, B, H, idx.num_heads, g, scale);
     else
         hipLaunchKernelGGL(fwd_f32_kernel<128>, grid_for(rows), dim3(256), 0, s, q, k, v, o, lse, idx.kv_idx,
-                           idx.kv_cnt, idx.max_kv, B, H, g, scale);
+                           idx.kv_cnt, idx.max_kv, B, H, idx.num_heads, g, scale);
     return check_launch();
 }
 
@@ -211,18 +211,18 @@ sta_status launch_bwd_f32(const float *q, const float *k, const float *v, const 
     if (parts & STA_BWD_DKDV) {
         if (D == 64)
             hipLaunchKernelGGL(dkdv_f32_kernel<64>, grid, blk, 0, s, q, k, v, lse, dout, delta, dk, dv, idx.q_idx,
-                               idx.q_cnt, idx.max_q, B, H, g, scale);
+                               idx.q_cnt, idx.max_q, B, H, idx.num_heads, g, scale);
         else
             hipLaunchKernelGGL(dkdv_f32_kernel<128>, grid, blk, 0, s, q, k, v, lse, dout, delta, dk, dv, idx.q_idx,
-                               idx.q_cnt, idx.max_q, B, H, g, scale);
+                               idx.q_cnt, idx.max_q, B, H, idx.num_heads, g, scale);
     }
     if (parts & STA_BWD_DQ) {
         if (D == 64)
             hipLaunchKernelGGL(dq_f32_kernel<64>, grid, blk, 0, s, q, k, v, lse, dout, delta, dq, idx.kv_idx,
-                               idx.kv_cnt, idx.max_kv, B, H, g, scale);
+                               idx.kv_cnt, idx.max_kv, B, H, idx.num_heads, g, scale);
         else
             hipLaunchKernelGGL(dq_f32_kernel<128>, grid, blk, 0, s, q, k, v, lse, dout, delta, dq, idx.kv_idx,
-                               idx.kv_cnt, idx.max_kv, B, H, g, scale);
+                               idx.kv_cnt, idx.max_kv, B, H, idx.num_heads, g, scale);
     }
     return check_launch();
 }

@@ -180,7 +180,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
     __bf16 *__restrict__ dQ, const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt, int max_kv,
-    int H, Geo g, int rblocks, int total, float scale_log2, float scale)
+    int IH, Geo g, int rblocks, int total, float scale_log2, float scale)
 {
     constexpr int THREADS = NW * 64, M = NW * 32, KS = D / 16, KB = BN / 32, DB = D / 32;
     constexpr int BLK = BN * D, STAGE = 2 * BLK;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
     const Span qs = tile_span(g, qt);                // query rows of this tile
     const int qlen = qs.len;
     if (rb * M >= qlen) return;                      // row block past a cut tile's end
-    const int h = bh % H;
+    const int h = bh % IH;                           // list set: the head's, or (b, h)'s
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, grp = lane >> 5;
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
     __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, const int32_t *__restrict__ q_idx,
-    const int32_t *__restrict__ q_cnt, int max_q, int H, Geo g, int rblocks, int total, float scale_log2,
+    const int32_t *__restrict__ q_cnt, int max_q, int IH, Geo g, int rblocks, int total, float scale_log2,
     float scale)
 {
     constexpr int THREADS = NW * 64, M = NW * 32, KS = D / 16, SB = BQ / 32, DB = D / 32;
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     const Span ks_ = tile_span(g, kt);               // key rows of this tile
     const int klen = ks_.len;
     if (rb * M >= klen) return;                      // row block past a cut tile's end
-    const int h = bh % H;
+    const int h = bh % IH;                           // list set: the head's, or (b, h)'s
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, grp = lane >> 5;
@@ -539,13 +539,13 @@ static sta_status run_bwd(const void *q, const void *k, const void *v, const voi
     }
     if (parts & STA_BWD_DKDV) {
         hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ, STA_BWD_NBUF>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
-                           (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q, H, g,
+                           (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q, idx.num_heads, g,
                            rblocks, (int)total, scale_log2, scale);
         if ((st = check_launch()) != STA_OK) return st;
     }
     if (parts & STA_BWD_DQ) {
         hipLaunchKernelGGL((dq_kernel<D, NW, BN, STA_BWD_NBUF>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
-                           (const float *)delta, (__bf16 *)dq, idx.kv_idx, idx.kv_cnt, idx.max_kv, H, g, rblocks,
+                           (const float *)delta, (__bf16 *)dq, idx.kv_idx, idx.kv_cnt, idx.max_kv, idx.num_heads, g, rblocks,
                            (int)total, scale_log2, scale);
         if ((st = check_launch()) != STA_OK) return st;
     }

@@ -154,6 +154,13 @@ sta_status launch_bwd_bf16(const void *q, const void *k, const void *v, const vo
                            float *delta, int B, int H, int D, float scale, const Geo &g,
                            const sta_index &idx, int parts, hipStream_t s);
 
+// window-shift producer: windows [H][3] host array; offsets [P][H][T][3]
+// with P = B per batch item, else 1; region_max bounds the search region's
+// tiles of every query tile
+sta_status launch_window_shifts(const void *q, const void *k, int B, int H, int D, sta_dtype dtype, float scale,
+                                const Geo &g, const int32_t *windows, const int radius[3], bool truncate,
+                                bool per_batch, int region_max, int32_t *offsets, hipStream_t s);
+
 // Stream-ordered device workspace (per-device pool that keeps freed memory
 // for reuse); the buffer may be used by work queued on `s` until the
 // matching workspace_free on the same stream.

@@ -131,7 +131,7 @@ template <int D, int NW, int QB, int BN>
 __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ VT,
     __bf16 *__restrict__ O, float *__restrict__ LSE, const int32_t *__restrict__ kv_idx,
-    const int32_t *__restrict__ kv_cnt, int max_kv, int H, Geo g, int Lp, int rblocks, int total,
+    const int32_t *__restrict__ kv_cnt, int max_kv, int IH, Geo g, int Lp, int rblocks, int total,
     float scale_log2)
 {
     using C = FwdCfg<D, NW, QB, BN>;
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     const Span qs = tile_span(g, qt);                // query rows of this tile
     const int qlen = qs.len;
     if (rb * C::M >= qlen) return;                   // row block past a cut tile's end
-    const int h = bh % H;
+    const int h = bh % IH;                           // list set: the head's, or (b, h)'s
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, grp = lane >> 5;
@@ -388,7 +388,7 @@ static sta_status run_fwd(const void *q, const void *k, const void *v, void *o, 
     const float scale_log2 = scale * 1.4426950408889634f;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BN>), dim3((unsigned)total), dim3(C::THREADS), 0, s,
                        (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)vt, (__bf16 *)o, lse, idx.kv_idx,
-                       idx.kv_cnt, idx.max_kv, H, g, Lp, rblocks, (int)total, scale_log2);
+                       idx.kv_cnt, idx.max_kv, idx.num_heads, g, Lp, rblocks, (int)total, scale_log2);
     st = check_launch();
     const sta_status fs = workspace_free(vt, s);
     return st != STA_OK ? st : fs;

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(NW * 64, STA_F8_MINB) void fwd_fp8_kernel(
     const uint8_t *__restrict__ Q8, const uint8_t *__restrict__ K8, const uint8_t *__restrict__ VT8,
     const float *__restrict__ sq, const float *__restrict__ corr, const float *__restrict__ sk,
     const float *__restrict__ vscale, __bf16 *__restrict__ O, float *__restrict__ LSE,
-    const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt, int max_kv, int H, Geo g, int Lp,
+    const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt, int max_kv, int IH, Geo g, int Lp,
     int nkb, int rblocks, int total)
 {
     using C = F8Cfg<D, NW>;
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(NW * 64, STA_F8_MINB) void fwd_fp8_kernel(
     const Span qs = tile_span(g, qt);
     const int qlen = qs.len;
     if (rb * C::M >= qlen) return;                   // row block past a cut tile's end
-    const int h = bh % H;
+    const int h = bh % IH;                           // list set: the head's, or (b, h)'s
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, grp = lane >> 5;
@@ -516,7 +516,7 @@ static sta_status run_fwd_fp8(const void *q, const void *k, const void *v, void 
                        g, nkb, c_log2, scale);
     hipLaunchKernelGGL(quant_vt_kernel<D>, dim3((unsigned)qk_blocks), dim3(256), 0, s, V, vi, vt8, g, Lp, nkb);
     hipLaunchKernelGGL((fwd_fp8_kernel<D, NW>), dim3((unsigned)total), dim3(C::THREADS), 0, s, q8, k8, vt8, sq, corr,
-                       sk, vs, (__bf16 *)o, lse, idx.kv_idx, idx.kv_cnt, idx.max_kv, H, g, Lp, nkb, rblocks,
+                       sk, vs, (__bf16 *)o, lse, idx.kv_idx, idx.kv_cnt, idx.max_kv, idx.num_heads, g, Lp, nkb, rblocks,
                        (int)total);
     st = check_launch();
     const sta_status fs = workspace_free(ws, s);

@@ -23,7 +23,7 @@ import os
 
 import numpy as np
 
-STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_OFF, STREAM_WIN = range(6)
+STREAM_Q, STREAM_K, STREAM_V, STREAM_DO, STREAM_OFF, STREAM_WIN, STREAM_TILE = range(7)
 
 TEXT_TOKENS_720P = 1164
 
@@ -112,6 +112,46 @@ def tensors(B, H, N, D, dtype, seed, with_dout=False):
     if with_dout:
         out.append(normal(shape, seed, STREAM_DO, dtype))
     return tuple(out)
+
+
+def tile_signal(B, H, grid, tile, D, dtype, seed, amp=1.0, disp=None, n_text=0, unit=False):
+    """(q, k) float32 [B,H,N+n_text,D] in raster order with a component per
+    tile on top of the N(0,1) draws of `tensors`: every video token of tile
+    t of slab (b,h) gets amp * u[b,h,t] added to q; k gets amp * u[b,h,t-d]
+    (d = disp[h], or disp[b][h] for a [B,H,3] array: the content of a tile
+    moved by d tiles) where t - d lies in the tile grid, else amp * v[b,h,t]
+    (v independent of u; the same for every tile when disp is None).  u, v
+    are i.i.d. N(0,1) from seed [seed, STREAM_TILE]; text rows keep only
+    the draws.  unit=True divides the video rows by sqrt(1 + amp^2), back
+    to unit variance.  Rounded to bf16 last when dtype is "bf16"."""
+    N = int(np.prod(grid))
+    n = tuple(-(-a // b) for a, b in zip(grid, tile))
+    T = int(np.prod(n))
+    q, k, _ = tensors(B, H, N + n_text, D, "f32", seed)
+    g = rng(seed, STREAM_TILE)
+    u = g.standard_normal((B, H, T, D)).astype(np.float32)
+    v = g.standard_normal((B, H, T, D)).astype(np.float32)
+    t, h, w = np.unravel_index(np.arange(N), grid)
+    tc = np.stack([t // tile[0], h // tile[1], w // tile[2]], 1)
+    tid = (tc[:, 0] * n[1] + tc[:, 1]) * n[2] + tc[:, 2]
+    dd = None if disp is None else np.asarray(disp, np.int64)
+    for b in range(B):
+        for hh in range(H):
+            q[b, hh, :N] += amp * u[b, hh, tid]
+            ks = v[b, hh, tid]
+            if dd is not None:
+                d = dd[hh] if dd.ndim == 2 else dd[b, hh]
+                src = tc - d
+                inside = np.all((src >= 0) & (src < np.array(n)), axis=1)
+                sid = (src[:, 0] * n[1] + src[:, 1]) * n[2] + src[:, 2]
+                ks = np.where(inside[:, None], u[b, hh, np.where(inside, sid, 0)], ks)
+            k[b, hh, :N] += amp * ks
+    if unit:
+        q[:, :, :N] /= np.float32(np.sqrt(1.0 + amp * amp))
+        k[:, :, :N] /= np.float32(np.sqrt(1.0 + amp * amp))
+    if dtype == "bf16":
+        q, k = round_bf16(q), round_bf16(k)
+    return q, k
 
 
 def workload(cfg, heads=None, with_dout=None, n_text=0, grid=None):

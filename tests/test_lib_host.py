@@ -280,3 +280,55 @@ def test_precision_option_checks():
     assert fwd(sta.STA_PREC_FP8, sta.STA_F32) == sta.STA_ERR_UNSUPPORTED
     assert bwd(sta.STA_PREC_FP8) == sta.STA_ERR_UNSUPPORTED
     assert bwd(5) == sta.STA_ERR_INVALID
+
+
+def test_index_for_batch_items_checks():
+    """An attention call takes an index of H list sets (shared by the batch)
+    or B*H (one per batch item); any other count is malformed."""
+    a = _fwd_args(B=2, H=2, index=_FakeIndex(H=3))
+    with pytest.raises(sta.StaError) as e:
+        sta.sta_fwd(**a)
+    assert e.value.status == sta.STA_ERR_INVALID and "list sets" in str(e.value)
+    a = _fwd_args(B=2, H=2, index=_FakeIndex(H=4, T=9))          # B*H sets, wrong tile count: still checked
+    with pytest.raises(sta.StaError) as e:
+        sta.sta_fwd(**a)
+    assert e.value.status == sta.STA_ERR_INVALID and "tiles" in str(e.value)
+
+
+def test_window_shifts_rejects_bad_arguments():
+    def f(**kw):
+        a = dict(q=_fake(), k=_fake(), B=1, H=2, D=64, dtype=sta.STA_BF16, scale=0.125, geom=GEOM,
+                 windows=[(1, 1, 1), (3, 3, 3)], radius=(1, 1, 1), offsets=_fake(), border="shift",
+                 per_batch=False, n_text=0)
+        a.update(kw)
+        sta.sta_window_shifts(a["q"], a["k"], a["B"], a["H"], a["D"], a["dtype"], a["scale"], a["geom"],
+                              a["windows"], a["radius"], a["offsets"], a["border"], a["per_batch"], a["n_text"], 0)
+    bad = [
+        (sta.STA_ERR_INVALID, dict(q=None)),
+        (sta.STA_ERR_INVALID, dict(offsets=None)),
+        (sta.STA_ERR_INVALID, dict(k=_fake(align=4))),
+        (sta.STA_ERR_INVALID, dict(B=0)),
+        (sta.STA_ERR_INVALID, dict(scale=-1.0)),
+        (sta.STA_ERR_INVALID, dict(scale=float("inf"))),
+        (sta.STA_ERR_INVALID, dict(dtype=3)),
+        (sta.STA_ERR_INVALID, dict(radius=(0, -1, 0))),
+        (sta.STA_ERR_INVALID, dict(windows=[(1, 1, 1), (3, 0, 3)])),
+        (sta.STA_ERR_INVALID, dict(border="sideways")),
+        (sta.STA_ERR_INVALID, dict(n_text=-2)),
+        (sta.STA_ERR_INVALID, dict(geom=sta.Geometry((4, 0, 8), (2, 4, 4)))),
+        (sta.STA_ERR_UNSUPPORTED, dict(D=96)),
+        (sta.STA_ERR_UNSUPPORTED, dict(radius=(8, 8, 8))),                       # 4913 candidates
+        (sta.STA_ERR_UNSUPPORTED, dict(geom=sta.Geometry((64, 64, 64), (2, 2, 2)),
+                                       windows=[(21, 21, 21)] * 2, radius=(0, 0, 0))),  # region 9261 tiles
+    ]
+    for status, kw in bad:
+        with pytest.raises(sta.StaError) as e:
+            f(**kw)
+        assert e.value.status == status, (kw, e.value)
+    # per_batch must be 0 or 1
+    opts = sta.sta_shift_opts(0, 2, 0)
+    w, _ = sta._windows([(1, 1, 1)] * 2)
+    st = sta.lib.sta_window_shifts(sta._ptr(_fake()), sta._ptr(_fake()), 1, 2, 64, sta.STA_BF16, 0.125,
+                                   ctypes.byref(GEOM.c()), w, ctypes.byref(sta.sta_dim3(1, 1, 1)),
+                                   ctypes.byref(opts), sta._ptr(_fake()), None)
+    assert st == sta.STA_ERR_INVALID
