@@ -125,6 +125,26 @@ def test_zero_radius_and_equal_keys():
     _check(got, q, ones, grid, tile, [(1, 3, 3), (3, 1, 1)], (1, 1, 1), what="equal keys")
 
 
+def test_raster_order_tie():
+    """Two shifts of equal size with bit-equal masses (key tiles (0,1,0) and
+    (0,0,1) carry query tile 0's content, one-tile windows): the first in
+    raster order, (0,0,1), is chosen, as in the oracle."""
+    grid, tile, D = (6, 8, 12), (2, 4, 4), 64
+    n = oracle.tiles_per_axis(grid, tile)
+    N = int(np.prod(grid))
+    t, h, w = np.unravel_index(np.arange(N), grid)
+    tid = ((t // tile[0]) * n[1] + h // tile[1]) * n[2] + w // tile[2]
+    q = np.zeros((1, 1, N, D), np.float32)
+    k = np.zeros((1, 1, N, D), np.float32)
+    q[0, 0, tid == 0, 0] = 3.0
+    for c in ((0, 1, 0), (0, 0, 1)):
+        k[0, 0, tid == (c[0] * n[1] + c[1]) * n[2] + c[2], 0] = 3.0
+    for dtype in ("bf16", "f32"):
+        got = _gpu_shifts(q, k, grid, tile, [(1, 1, 1)], (1, 1, 1), dtype)
+        assert tuple(got[0, 0]) == (0, 0, 1), (dtype, got[0, 0])
+        _check(got, q, k, grid, tile, [(1, 1, 1)], (1, 1, 1), what="raster tie " + dtype)
+
+
 def test_shifts_720p_full_size():
     """The 720p per-head workload's shapes (24 heads, windows 3x3x3 / 3x3x5 /
     5x5x5, bf16, D 128; tiles carrying content of their own on top of the
