@@ -31,6 +31,10 @@ reorder, every query tile's window shift (|shift| <= R per axis) is chosen on
 device from the tile means of Q and K (sta_window_shifts) and the index is
 built from those shifts, one set per head.
 
+--layout raster runs the step without any reorder pass: the attention
+kernels read Q, K, V, dO and write O, LSE, dQ, dK, dV in raster token order
+directly (index; forward; backward).
+
 --grid T,H,W replaces the token grid, e.g. the 720p latent grid 30,45,80 that
 the (6,8,8) tile does not divide (its last tile row along H is cut to 5
 rows); counted work then sums len(q) * len(k) over the listed tile pairs.
@@ -83,6 +87,8 @@ def parse():
                     help="token grid T,H,W replacing the workload's (30,48,80)")
     ap.add_argument("--text", type=int, default=0,
                     help="text tokens appended to the video tokens (joint text + video step)")
+    ap.add_argument("--layout", choices=("tile", "raster"), default="tile",
+                    help="raster: the kernels address raster-order tensors, no reorder passes")
     ap.add_argument("--adaptive", type=str, default=None, metavar="RT,RH,RW",
                     help="choose the window shifts on device (search radius per axis) inside the step")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -272,11 +278,40 @@ def main():
     row_bytes = D * 2
     stream = torch.cuda.current_stream()
 
-    names = ["reorder_qkv"] + (["shifts"] if radius else []) + ["index", "fwd", "reorder_o"]
-    if not fwd_only:
-        names += ["reorder_do", "bwd_delta", "bwd_dkdv", "bwd_dq", "reorder_grads"]
+    raster = args.layout == "raster"
+    if raster and (nt or radius):
+        print("--layout raster takes video rows only and no --adaptive", file=sys.stderr)
+        sys.exit(2)
+    lay = sta.STA_LAYOUT_RASTER if raster else sta.STA_LAYOUT_TILE
+    if raster:
+        names = ["index", "fwd"] + ([] if fwd_only else ["bwd_delta", "bwd_dkdv", "bwd_dq"])
+    else:
+        names = ["reorder_qkv"] + (["shifts"] if radius else []) + ["index", "fwd", "reorder_o"]
+        if not fwd_only:
+            names += ["reorder_do", "bwd_delta", "bwd_dkdv", "bwd_dq", "reorder_grads"]
+
+    def raster_step(evs=None):
+        marks = iter(range(len(names) + 1))
+
+        def mark():
+            i = next(marks)
+            if evs is not None:
+                evs[i].record(stream)
+        mark()
+        sta.sta_build_index(geom, windows, None, idx, stream)
+        mark()
+        sta.sta_fwd_ex(q, k, v, o, lse, B, H, D, sta.STA_BF16, scale, geom, idx, 0, stream, prec, lay)
+        mark()
+        if fwd_only:
+            return
+        for part in (sta.STA_BWD_DELTA, sta.STA_BWD_DKDV, sta.STA_BWD_DQ):
+            sta.sta_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, D, sta.STA_BF16, scale, geom, idx, part, 0,
+                           stream, lay)
+            mark()
 
     def step(evs=None):
+        if raster:
+            return raster_step(evs)
         marks = iter(range(len(names) + 1))
 
         def mark():
@@ -351,11 +386,11 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "kernel": dominant,
                 "traffic": measured_traffic(dominant) if nt == 0 and grid is None and prec == sta.STA_PREC_DEFAULT
-                and radius is None else None,                 # the counter passes cover the bf16 video step
+                and radius is None and not raster else None,  # the counter passes cover the bf16 video step
                 "measured_gemm_ceiling": gemm_ceiling(torch, dev)}
 
     tensor_bytes = B * H * S * D * 2
-    reorder_gbs = 3 * 2 * tensor_bytes / (per["reorder_qkv"] * 1e-3) / 1e9
+    reorder_gbs = 3 * 2 * tensor_bytes / (per["reorder_qkv"] * 1e-3) / 1e9 if "reorder_qkv" in per else None
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -375,20 +410,20 @@ def main():
                                                                        "forward+backward")) +
                         ("" if nt == 0 else ", joint with %d text tokens (dense text rows and columns)" % nt) +
                         ("" if radius is None else ", window shifts chosen on device (search radius %s tiles)"
-                         % (radius,)),
+                         % (radius,)) + (", raster layout (no reorder passes)" if raster else ""),
             "global_batch": B,
             "seq_len": S,
             "text_tokens": nt,
             "parallelism": "none (1 GPU)",
             "counted_flop_per_step": step_flop,
             "ms_per_layer_fwd_bwd": round(ms_per_step, 3),
-            "ms_per_layer_fwd": round(per["reorder_qkv"] + per.get("shifts", 0.0) + per["index"] + per["fwd"] +
-                                      per["reorder_o"], 3),
+            "ms_per_layer_fwd": round(per.get("reorder_qkv", 0.0) + per.get("shifts", 0.0) + per["index"] + per["fwd"] +
+                                      per.get("reorder_o", 0.0), 3),
             "fwd_kernel_ms": round(per["fwd"], 3),
             "fwd_tflops": round(fwd_flop / (per["fwd"] * 1e-3) / 1e12, 1),
             "fwd_frac_of_peak": round(fwd_flop / (per["fwd"] * 1e-3) / 1e12 / peak, 4),
             "bwd_kernels_ms": None if fwd_only else round(per["bwd_delta"] + per["bwd_dkdv"] + per["bwd_dq"], 3),
-            "reorder_qkv_gbs": round(reorder_gbs, 1),
+            "reorder_qkv_gbs": None if reorder_gbs is None else round(reorder_gbs, 1),
             # the producer reads Q and K once (its tile means); the choice
             # itself touches only the means
             "shifts_hbm_gbs": None if radius is None else round(2 * B * H * N * D * 2 / (per["shifts"] * 1e-3) / 1e9,
@@ -397,7 +432,7 @@ def main():
         },
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline and grid is None and not fwd_only and radius is None:   # a sample of the training step
+    if not args.no_cpu_baseline and grid is None and not fwd_only and radius is None and not raster:   # a sample of the training step
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows, nt)
     print(json.dumps(out), flush=True)
 

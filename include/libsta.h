@@ -50,7 +50,8 @@
  *     STA_ERR_UNSUPPORTED = well-formed but not implemented (reason in
  *     sta_last_error()); STA_ERR_HIP = a HIP launch error.
  *   - Attention tensors are [B][H][N][D], D fastest, in TILE order
- *     (sta_tile_reorder converts), 16-byte aligned, not aliasing each other.
+ *     (sta_tile_reorder converts) unless an _ex call asks for raster order
+ *     (sta_layout), 16-byte aligned, not aliasing each other.
  *   - An index holds one list set per head, shared by every batch item, or
  *     one per (b, h) for windows shifted per batch item (see sta_index).
  *   - Thread-safe: no mutable global state apart from a thread-local
@@ -287,6 +288,19 @@ typedef enum {
     STA_PREC_FP8 = 1
 } sta_precision;
 
+/* Row order of the attention tensors (sta_attn_opts.layout). */
+typedef enum {
+    /* Tile order: the rows of a tile are contiguous (sta_tile_reorder makes
+     * it from raster order).  Every geometry. */
+    STA_LAYOUT_TILE = 0,
+    /* Raster order: the video rows of a slab are the tokens in raster order
+     * (t slowest, w fastest) and the kernels gather each tile's rows where
+     * its tokens sit, so no reorder pass is needed.  Grids the tile divides
+     * and n_text = 0 only; with bf16 tensors also tw | 16, th*tw a power of
+     * two and 32 | L (else STA_ERR_UNSUPPORTED). */
+    STA_LAYOUT_RASTER = 1
+} sta_layout;
+
 /* Options of the attention calls.  A NULL pointer means all fields 0. */
 typedef struct {
     /* Text tokens appended after the N video tokens of every (b, h) slab
@@ -299,6 +313,10 @@ typedef struct {
     /* An sta_precision value (sta_fwd_ex only; sta_bwd_ex needs
      * STA_PREC_DEFAULT and sta_tile_reorder_ex ignores it). */
     int32_t precision;
+    /* An sta_layout value: the row order of q, k, v, o, lse, dout, dq, dk,
+     * dv and delta_ws (sta_tile_reorder_ex ignores it).  The forward and the
+     * backward of one layer must use the same layout. */
+    int32_t layout;
 } sta_attn_opts;
 
 /*
@@ -357,12 +375,14 @@ typedef struct {
     /* Text rows after the N video rows of every (b, h) slab of q and k
      * (>= 0; they take no part in the search). */
     int32_t n_text;
+    /* An sta_layout value: the row order of q and k. */
+    int32_t layout;
 } sta_shift_opts;
 
 /*
  * Chooses the window shift of every query tile and head from q and k
- * ([B][H][N + n_text][D], video rows in tile order, bf16 or fp32, D 64 or
- * 128, 16-byte aligned) and writes it to offsets_dev (DEVICE int32, the
+ * ([B][H][N + n_text][D], video rows in the order of opts->layout, bf16 or
+ * fp32, D 64 or 128, 16-byte aligned) and writes it to offsets_dev (DEVICE int32, the
  * layout of sta_shift_opts.per_batch, (dt, dh, dw) in tiles), ready for
  * sta_build_index_ex with per_head_offsets = 1.
  * Rule (this library's reading: the pages call 3D-DSA's windows motion-
@@ -384,7 +404,7 @@ typedef struct {
  * 1) from the stream-ordered pool described at sta_fwd.
  * Errors: STA_ERR_INVALID for NULL or misaligned pointers, B, H, D <= 0, a
  * negative radius, a window < 1, a non-positive or non-finite scale, an
- * unknown border or dtype, per_batch not 0/1, n_text < 0;
+ * unknown border, layout or dtype, per_batch not 0/1, n_text < 0;
  * STA_ERR_UNSUPPORTED for D other than 64 and 128, more than 4096
  * candidate shifts ((2r_t+1)(2r_h+1)(2r_w+1)), a search region (the union
  * of one query tile's candidate windows, at most prod_d min(n_d, w_d +

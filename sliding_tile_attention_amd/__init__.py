@@ -28,6 +28,8 @@ STA_BWD_DELTA, STA_BWD_DKDV, STA_BWD_DQ, STA_BWD_ALL = 1, 2, 4, 7
 STA_BORDER_SHIFT, STA_BORDER_TRUNCATE = 0, 1
 STA_PREC_DEFAULT, STA_PREC_FP8 = 0, 1
 _PRECISIONS = {"default": STA_PREC_DEFAULT, "fp8": STA_PREC_FP8}
+STA_LAYOUT_TILE, STA_LAYOUT_RASTER = 0, 1
+_LAYOUTS = {"tile": STA_LAYOUT_TILE, "raster": STA_LAYOUT_RASTER}
 EXPORTS = ("sta_status_str", "sta_last_error", "sta_version", "sta_index_dims", "sta_index_dims_ex",
            "sta_tile_reorder", "sta_tile_reorder_ex", "sta_build_index", "sta_build_index_ex", "sta_fwd",
            "sta_fwd_ex", "sta_bwd", "sta_bwd_parts", "sta_bwd_ex", "sta_window_shifts")
@@ -55,11 +57,12 @@ class sta_index_opts(ctypes.Structure):
 
 
 class sta_attn_opts(ctypes.Structure):
-    _fields_ = [("n_text", ctypes.c_int32), ("precision", ctypes.c_int32)]
+    _fields_ = [("n_text", ctypes.c_int32), ("precision", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 class sta_shift_opts(ctypes.Structure):
-    _fields_ = [("border", ctypes.c_int32), ("per_batch", ctypes.c_int32), ("n_text", ctypes.c_int32)]
+    _fields_ = [("border", ctypes.c_int32), ("per_batch", ctypes.c_int32), ("n_text", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
 
 class sta_index(ctypes.Structure):
@@ -217,8 +220,9 @@ def sta_fwd(q, k, v, o, lse, B, H, D, dtype, scale, geom, index, stream=None):
                        ctypes.byref(geom.c()), ctypes.byref(index.c()), _stream(stream)))
 
 
-def sta_fwd_ex(q, k, v, o, lse, B, H, D, dtype, scale, geom, index, n_text=0, stream=None, precision=STA_PREC_DEFAULT):
-    opts = sta_attn_opts(int(n_text), int(precision))
+def sta_fwd_ex(q, k, v, o, lse, B, H, D, dtype, scale, geom, index, n_text=0, stream=None, precision=STA_PREC_DEFAULT,
+               layout=STA_LAYOUT_TILE):
+    opts = sta_attn_opts(int(n_text), int(precision), int(layout))
     _check(lib.sta_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, D, dtype, float(scale),
                           ctypes.byref(geom.c()), ctypes.byref(index.c()), ctypes.byref(opts), _stream(stream)))
 
@@ -237,15 +241,15 @@ def sta_bwd_parts(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, s
 
 
 def sta_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, scale, geom, index, parts,
-               n_text=0, stream=None):
-    opts = sta_attn_opts(int(n_text))
+               n_text=0, stream=None, layout=STA_LAYOUT_TILE):
+    opts = sta_attn_opts(int(n_text), STA_PREC_DEFAULT, int(layout))
     _check(lib.sta_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                           _ptr(dv), _ptr(delta_ws), B, H, D, dtype, float(scale), ctypes.byref(geom.c()),
                           ctypes.byref(index.c()), int(parts), ctypes.byref(opts), _stream(stream)))
 
 
 def sta_window_shifts(q, k, B, H, D, dtype, scale, geom, windows, radius, offsets, border="shift", per_batch=False,
-                      n_text=0, stream=None):
+                      n_text=0, stream=None, layout=STA_LAYOUT_TILE):
     """offsets: int32 device tensor [H, num_tiles, 3] ([B, H, num_tiles, 3]
     with per_batch), written by the call."""
     w, nw = _windows(windows)
@@ -253,7 +257,7 @@ def sta_window_shifts(q, k, B, H, D, dtype, scale, geom, windows, radius, offset
         raise ValueError("need one window per head")
     r = sta_dim3(*[int(x) for x in radius])
     opts = sta_shift_opts(STA_BORDER_TRUNCATE if border == "truncate" else STA_BORDER_SHIFT if border == "shift"
-                          else -1, int(bool(per_batch)), int(n_text))
+                          else -1, int(bool(per_batch)), int(n_text), int(layout))
     _check(lib.sta_window_shifts(_ptr(q), _ptr(k), B, H, D, dtype, float(scale), ctypes.byref(geom.c()), w,
                                  ctypes.byref(r), ctypes.byref(opts), _ptr(offsets), _stream(stream)))
 
@@ -302,18 +306,19 @@ def _dtype_code(t):
     raise TypeError("libsta supports bfloat16 and float32 tensors, got %s" % t.dtype)
 
 
-def window_shifts(q, k, geom, windows, radius, scale=None, border="shift", per_batch=False, n_text=0, stream=None):
+def window_shifts(q, k, geom, windows, radius, scale=None, border="shift", per_batch=False, n_text=0, stream=None,
+                  layout="tile"):
     """Window shift of every query tile (and head, and batch item with
     per_batch) chosen on device from q, k [B,H,N+n_text,D] (video rows in
-    tile order): int32 [H, num_tiles, 3] or [B, H, num_tiles, 3], ready for
-    StaIndex(..., offsets=...)."""
+    tile order, or raster order with layout="raster"): int32 [H, num_tiles,
+    3] or [B, H, num_tiles, 3], ready for StaIndex(..., offsets=...)."""
     B, H, S, D = q.shape
     assert S == geom.tokens + n_text and k.shape == q.shape
     scale = D ** -0.5 if scale is None else scale
     shape = (B, H, geom.num_tiles, 3) if per_batch else (H, geom.num_tiles, 3)
     out = torch.empty(shape, dtype=torch.int32, device=q.device)
     sta_window_shifts(q, k, B, H, D, _dtype_code(q), scale, geom, windows, radius, out, border, per_batch, n_text,
-                      stream)
+                      stream, _LAYOUTS[layout])
     return out
 
 
@@ -330,20 +335,23 @@ def tile_reorder(x, geom, inverse=False, out=None, stream=None, n_text=0):
     return out
 
 
-def forward(q, k, v, geom, index, scale=None, stream=None, n_text=0, precision="default"):
+def forward(q, k, v, geom, index, scale=None, stream=None, n_text=0, precision="default", layout="tile"):
     """q, k, v [B,H,N+n_text,D] (video rows in tile order, then the text
     rows) -> (o [B,H,N+n_text,D], lse [B,H,N+n_text] fp32).  precision
-    "fp8" runs the quantized products (INT8 QK^T, FP8 PV; bf16 tensors)."""
+    "fp8" runs the quantized products (INT8 QK^T, FP8 PV; bf16 tensors).
+    layout "raster": every tensor holds the video rows in raster token order
+    (no reorder needed; grids the tile divides, no text rows)."""
     B, H, S, D = q.shape
     assert S == geom.tokens + n_text
     scale = D ** -0.5 if scale is None else scale
     o = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    sta_fwd_ex(q, k, v, o, lse, B, H, D, _dtype_code(q), scale, geom, index, n_text, stream, _PRECISIONS[precision])
+    sta_fwd_ex(q, k, v, o, lse, B, H, D, _dtype_code(q), scale, geom, index, n_text, stream, _PRECISIONS[precision],
+               _LAYOUTS[layout])
     return o, lse
 
 
-def backward(q, k, v, o, lse, dout, geom, index, scale=None, stream=None, n_text=0):
+def backward(q, k, v, o, lse, dout, geom, index, scale=None, stream=None, n_text=0, layout="tile"):
     """Gradients (dq, dk, dv) of forward(); same layout as forward()."""
     B, H, S, D = q.shape
     assert S == geom.tokens + n_text
@@ -351,5 +359,5 @@ def backward(q, k, v, o, lse, dout, geom, index, scale=None, stream=None, n_text
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     sta_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, D, _dtype_code(q), scale, geom, index,
-               STA_BWD_ALL, n_text, stream)
+               STA_BWD_ALL, n_text, stream, _LAYOUTS[layout])
     return dq, dk, dv

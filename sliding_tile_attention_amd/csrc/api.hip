@@ -75,6 +75,9 @@ static sta_status make_geo(const sta_geom *g, Geo &out)
     out.Tt = 0;
     out.TT = out.T;
     out.S = N;
+    out.raster = 0;
+    out.rs_step = out.rs_jump = out.rs_16 = out.rs_span = out.rs_pmask = out.rs_lt = out.rs_lp = 0;
+    out.rs_per = 1;
     return STA_OK;
 }
 
@@ -91,6 +94,39 @@ static sta_status add_text(Geo &g, const sta_attn_opts *opts)
     g.Tt = (g.text + g.L - 1) / g.L;
     g.TT = g.T + g.Tt;
     g.S = g.N + g.text;
+    return STA_OK;
+}
+
+// Sets the row layout of the attention tensors (sta_layout).  Raster order
+// needs whole tiles and no text rows; the bf16 kernels also copy 32-row
+// blocks of a tile with one per-lane pattern (raster_step) formed with
+// shifts, which needs tw | 16, th*tw a power of two (so one of th*tw and 32
+// divides the other) and tiles of a multiple of 32 rows.
+static sta_status set_layout(Geo &g, int layout, bool bf16)
+{
+    if (layout != STA_LAYOUT_TILE && layout != STA_LAYOUT_RASTER)
+        return fail(STA_ERR_INVALID, "unknown layout %d", layout);
+    if (layout == STA_LAYOUT_TILE) return STA_OK;
+    if (g.ragged)
+        return fail(STA_ERR_UNSUPPORTED, "raster layout needs a grid the tile divides (grid %dx%dx%d, tile %dx%dx%d)",
+                    g.gt, g.gh, g.gw, g.tt, g.th, g.tw);
+    if (g.text > 0)
+        return fail(STA_ERR_UNSUPPORTED, "raster layout takes video rows only (n_text = %d)", g.text);
+    const int plane = g.th * g.tw;
+    if (bf16 && (16 % g.tw != 0 || (plane & (plane - 1)) != 0 || g.L % 32 != 0))
+        return fail(STA_ERR_UNSUPPORTED, "raster layout of bf16 tensors needs tw | 16, th*tw a power of two and "
+                    "32 | L (tile %dx%dx%d)", g.tt, g.th, g.tw);
+    g.raster = 1;
+    const RasterStep rs = raster_steps(g, 32);
+    g.rs_step = rs.step;
+    g.rs_jump = rs.jump;
+    g.rs_per = rs.per;
+    g.rs_16 = (int)raster_step(g, 16);
+    g.rs_span = (int)raster_step(g, 31) + 1;
+    g.rs_pmask = plane > 32 ? plane - 1 : 0;
+    g.rs_lt = g.rs_lp = 0;
+    while ((1 << g.rs_lt) < g.tw) ++g.rs_lt;
+    while ((1 << g.rs_lp) < plane) ++g.rs_lp;
     return STA_OK;
 }
 
@@ -194,7 +230,7 @@ const char *sta_status_str(sta_status s)
 
 const char *sta_last_error(void) { return g_err; }
 
-int32_t sta_version(void) { return 10300; }
+int32_t sta_version(void) { return 10400; }
 
 sta_status sta_index_dims(const sta_geom *g, int32_t H, const sta_dim3 *windows_host,
                           int32_t has_offsets, int32_t *max_kv, int32_t *max_q)
@@ -312,6 +348,7 @@ sta_status sta_fwd_ex(const void *q, const void *k, const void *v, void *o, floa
     const int prec = opts ? opts->precision : STA_PREC_DEFAULT;
     if (prec != STA_PREC_DEFAULT && prec != STA_PREC_FP8)
         return fail(STA_ERR_INVALID, "unknown precision %d", prec);
+    if ((st = set_layout(geo, opts ? opts->layout : STA_LAYOUT_TILE, dtype == STA_BF16)) != STA_OK) return st;
     if (prec == STA_PREC_FP8 && dtype != STA_BF16)
         return fail(STA_ERR_UNSUPPORTED, "the FP8 forward takes bf16 tensors");
     if ((st = check_attn(geo, B, H, D, dtype, scale)) != STA_OK) return st;
@@ -350,6 +387,7 @@ sta_status sta_bwd_ex(const void *q, const void *k, const void *v, const void *o
     if (opts && opts->precision != STA_PREC_DEFAULT)
         return fail(opts->precision == STA_PREC_FP8 ? STA_ERR_UNSUPPORTED : STA_ERR_INVALID,
                     "the backward runs in the tensors' dtype (precision %d requested)", opts->precision);
+    if ((st = set_layout(geo, opts ? opts->layout : STA_LAYOUT_TILE, dtype == STA_BF16)) != STA_OK) return st;
     if ((st = check_attn(geo, B, H, D, dtype, scale)) != STA_OK) return st;
     if (parts < 1 || parts > STA_BWD_ALL)
         return fail(STA_ERR_INVALID, "parts must be a non-empty mask of STA_BWD_DELTA|DKDV|DQ (got %d)", parts);
@@ -394,13 +432,14 @@ sta_status sta_window_shifts(const void *q, const void *k, int32_t B, int32_t H,
     Geo geo;
     sta_status st = make_geo(g, geo);
     if (st != STA_OK) return st;
-    const sta_shift_opts o = opts ? *opts : sta_shift_opts{0, 0, 0};
+    const sta_shift_opts o = opts ? *opts : sta_shift_opts{0, 0, 0, 0};
     if (o.border != STA_BORDER_SHIFT && o.border != STA_BORDER_TRUNCATE)
         return fail(STA_ERR_INVALID, "unknown border rule %d", o.border);
     if (o.per_batch != 0 && o.per_batch != 1)
         return fail(STA_ERR_INVALID, "per_batch must be 0 or 1 (got %d)", o.per_batch);
-    sta_attn_opts text = {o.n_text, STA_PREC_DEFAULT};
+    sta_attn_opts text = {o.n_text, STA_PREC_DEFAULT, STA_LAYOUT_TILE};
     if ((st = add_text(geo, &text)) != STA_OK) return st;
+    if ((st = set_layout(geo, o.layout, false)) != STA_OK) return st;
     if (B <= 0 || H <= 0 || D <= 0)
         return fail(STA_ERR_INVALID, "B, H and D must be positive (B=%d H=%d D=%d)", B, H, D);
     if (dtype != STA_BF16 && dtype != STA_F32)

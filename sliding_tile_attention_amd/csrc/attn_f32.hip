@@ -7,9 +7,14 @@ namespace sta {
 
 // Tile holding video row i of a slab (compact tile order: whole tile planes
 // along t, tile rows along h inside a plane, tiles along w inside a row,
-// the last of each cut by the grid border).
+// the last of each cut by the grid border; or raster order).
 __device__ inline int tile_of_row(const Geo &g, int64_t i)
 {
+    if (g.raster) {                    // raster order, whole tiles
+        const int64_t plane = (int64_t)g.gh * g.gw;
+        const int t = (int)(i / plane), h = (int)((i / g.gw) % g.gh), w = (int)(i % g.gw);
+        return ((t / g.tt) * g.nh + h / g.th) * g.nw + w / g.tw;
+    }
     if (!g.ragged) return (int)(i / g.L);
     const int64_t plane = (int64_t)g.tt * g.gh * g.gw;
     int a = (int)(i / plane);
@@ -41,8 +46,8 @@ __device__ inline void for_partners(int64_t i, int h, const Geo &g, const int32_
     const int cnt = cnt_[(int64_t)h * g.T + t];
     const int32_t *lst = idx + ((int64_t)h * g.T + t) * max_e;
     for (int e = 0; e < cnt; ++e) {
-        const Span sp = tile_span(g, lst[e]);
-        for (int rr = 0; rr < sp.len; ++rr) f(sp.start + rr);
+        const int len = tile_rows(g, lst[e]);
+        for (int rr = 0; rr < len; ++rr) f(tile_row(g, lst[e], rr));
     }
     for (int64_t r = g.N; r < g.S; ++r) f(r);
 }

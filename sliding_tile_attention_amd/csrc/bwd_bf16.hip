@@ -111,6 +111,39 @@ struct RowCopy {
     }
 };
 
+// RowCopy for a block of ROWS rows of a whole video tile in raster order:
+// row r of the block sits raster_step(r) rows after its first row.  Copy i
+// moves the rows of copy 0 shifted by i*ROWS_PER_COPY rows of the tile; with
+// at most two copies of 16 rows that is g.rs_16 rows further on (a kernel
+// argument), so one register per lane suffices.
+template <int D, int THREADS, int ROWS>
+struct RowCopyRaster {
+    static constexpr int GR = D / 8;
+    static constexpr int W = THREADS / 64;
+    static constexpr int COPIES = ROWS * D / (THREADS * 8);
+    static constexpr int ROWS_PER_COPY = W * 64 / GR;
+    static_assert(ROWS_PER_COPY % 16 == 0, "copies must keep the swizzle phase");
+    static_assert(COPIES == 1 || (COPIES == 2 && ROWS_PER_COPY == 16), "copy shift is raster_step(16)");
+    int off;
+    __device__ RowCopyRaster(int tid, const Geo &g)
+    {
+        const int wave = tid >> 6, lane = tid & 63;
+        const int slot = wave * 64 + lane;
+        const int r = slot / GR, pg = slot % GR;
+        off = (raster_step_p2(g, r) * D + (pg ^ swz_u<GR>(r)) * 8) * 2;
+    }
+    // Asynchronous copy of a block whose first row is at src; `bytes` bounds
+    // the descriptor (every row of a whole tile exists).
+    __device__ void copy(const __bf16 *src, int bytes, __bf16 *lds, int wave, const Geo &g) const
+    {
+        const auto rs = make_rsrc(src, bytes);
+#pragma unroll
+        for (int i = 0; i < COPIES; ++i) b2lds16(rs, off, lds + (i * W + wave) * 512, i * g.rs_16 * D * 2);
+    }
+};
+
+
+
 // NBUF-slot ring of LDS stages: block b lives in slot b mod NBUF and is
 // copied NBUF-1 blocks ahead.  At block blk a wave waits until its copies of
 // blk have landed (those of the NBUF-2 later blocks, PER copies each, may
@@ -141,24 +174,40 @@ __device__ inline void static_for(F &&f)
 // Position in a walk over the tiles of a key- or query-tile list and then
 // the text pseudo-tiles, block by block (no divisions); the next tile id is
 // prefetched when a tile is entered.
+// With RASTER (video tiles only), `roff` follows the raster row of the
+// current 32-row block (no divisions per block: the step of g.rs_step, and
+// g.rs_jump more where a tile plane ends).
 struct ListWalk {
     int e, r0, next;
     Span sp;                  // rows of the current tile
+    int roff;                 // raster layout: first row of the block
 };
+template <bool RASTER>
+__device__ inline void walk_enter(ListWalk &w, int tile, const Geo &g)
+{
+    w.sp = tile_span(g, tile);
+    if constexpr (RASTER) w.roff = (int)raster_base(g, tile);
+}
+template <bool RASTER>
 __device__ inline void walk_init(ListWalk &w, const int32_t *lst, int cnt, const Geo &g)
 {
     w.e = 0;
     w.r0 = 0;
-    w.sp = tile_span(g, entry_tile(lst, cnt, g.T, 0));
+    walk_enter<RASTER>(w, entry_tile(lst, cnt, g.T, 0), g);
     w.next = entry_tile(lst, cnt, g.T, 1);
 }
+template <bool RASTER>
 __device__ inline void walk_next(ListWalk &w, const int32_t *lst, int cnt, int step, const Geo &g)
 {
     w.r0 += step;
+    if constexpr (RASTER) {          // 32-row blocks: the walk of g.rs_*
+        w.roff += g.rs_step;
+        if ((w.r0 & g.rs_pmask) == 0) w.roff += g.rs_jump;
+    }
     if (w.r0 >= w.sp.len) {
         w.r0 = 0;
         ++w.e;
-        w.sp = tile_span(g, w.next);
+        walk_enter<RASTER>(w, w.next, g);
         w.next = entry_tile(lst, cnt, g.T, w.e + 1);
     }
 }
@@ -175,7 +224,7 @@ __device__ inline int lds_at(int r, int c)
 // ---------------------------------------------------------------------------
 // 2. dQ (query-stationary).
 // ---------------------------------------------------------------------------
-template <int D, int NW, int BN, int NBUF>
+template <int D, int NW, int BN, int NBUF, bool RASTER>
 __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
@@ -206,7 +255,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
     const int64_t base = (int64_t)bh * g.S * D;
     const int row = rb * M + wave * 32 + l32;        // query row (inside the tile) of this lane
     const bool row_ok = row < qlen;
-    const int64_t grow = qs.start + (row_ok ? row : qlen - 1);
+    const int64_t grow = slab_row<RASTER>(g, qt, qs, row_ok ? row : qlen - 1);
 
     bf16x8 qf[KS], of[KS];
 #pragma unroll
@@ -242,15 +291,24 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) tbase[hh] = lds_at<D>(8 * grp + 4 * hh + vj, 16 * ((lane >> 4) & 1) + 4 * vc);
 
+    static_assert(!RASTER || BN == 32, "raster walk of 32-row blocks");
     const RowCopy<D, THREADS, BN> rc(tid);
+    const RowCopyRaster<D, THREADS, BN> rcr(tid, g);
     ListWalk cw;                                    // next key block to copy
-    walk_init(cw, lst, cnt, g);
+    walk_init<RASTER>(cw, lst, cnt, g);
     auto gload = [&](auto bc) {
-        const int valid = cw.sp.len - cw.r0 < BN ? cw.sp.len - cw.r0 : BN;
-        const int64_t row0 = cw.sp.start + cw.r0;
-        rc.copy(K + base + row0 * D, valid, stage(bc), wave);
-        rc.copy(V + base + row0 * D, valid, stage(bc) + BLK, wave);
-        walk_next(cw, lst, cnt, BN, g);
+        if constexpr (RASTER) {
+            // video tiles only (no text rows in the raster layout); the
+            // descriptor spans the block's rows (g.rs_span from its first)
+            rcr.copy(K + base + (int64_t)cw.roff * D, g.rs_span * D * 2, stage(bc), wave, g);
+            rcr.copy(V + base + (int64_t)cw.roff * D, g.rs_span * D * 2, stage(bc) + BLK, wave, g);
+        } else {
+            const int valid = cw.sp.len - cw.r0 < BN ? cw.sp.len - cw.r0 : BN;
+            const int64_t row0 = cw.sp.start + cw.r0;
+            rc.copy(K + base + row0 * D, valid, stage(bc), wave);
+            rc.copy(V + base + row0 * D, valid, stage(bc) + BLK, wave);
+        }
+        walk_next<RASTER>(cw, lst, cnt, BN, g);
     };
 
     auto step = [&](auto bufc, int blk) {
@@ -306,7 +364,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
         });
 
     if (row_ok) {
-        __bf16 *op = dQ + base + (qs.start + row) * D;
+        __bf16 *op = dQ + base + slab_row<RASTER>(g, qt, qs, row) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -322,7 +380,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
 // ---------------------------------------------------------------------------
 // 3. dK, dV (key-stationary, over the transposed lists).
 // ---------------------------------------------------------------------------
-template <int D, int NW, int BQ, int NBUF>
+template <int D, int NW, int BQ, int NBUF, bool RASTER>
 __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
@@ -356,7 +414,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     const int64_t sbase = (int64_t)bh * g.S;
     const int krow0 = rb * M + wave * 32;            // first key row (inside the tile) of this wave
     const int krow = krow0 + l32;
-    const int64_t gk = ks_.start + (krow < klen ? krow : klen - 1);
+    const int64_t gk = slab_row<RASTER>(g, kt, ks_, krow < klen ? krow : klen - 1);
 
     bf16x8 kf[KS], vf[KS];
 #pragma unroll
@@ -387,24 +445,40 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) tbase[hh] = lds_at<D>(8 * grp + 4 * hh + vj, 16 * ((lane >> 4) & 1) + 4 * vc);
 
+    static_assert(!RASTER || BQ == 32, "raster walk of 32-row blocks");
     const RowCopy<D, THREADS, BQ> rc(tid);
+    const RowCopyRaster<D, THREADS, BQ> rcr(tid, g);
     ListWalk cw;                                    // next query block to copy
-    walk_init(cw, lst, cnt, g);
+    walk_init<RASTER>(cw, lst, cnt, g);
     auto gload = [&](auto bc) {
-        const int valid = cw.sp.len - cw.r0 < BQ ? cw.sp.len - cw.r0 : BQ;
-        const int64_t row0 = cw.sp.start + cw.r0;
-        __bf16 *st = stage(bc);
-        rc.copy(Q + base + row0 * D, valid, st, wave);
-        rc.copy(dO + base + row0 * D, valid, st + BLK, wave);
+        int valid;
+        int64_t row0;
+        int lo = lane * 4;
+        if constexpr (RASTER) {
+            // video tiles only (no text rows in the raster layout); the
+            // descriptors span the block's rows (g.rs_span from its first)
+            rcr.copy(Q + base + (int64_t)cw.roff * D, g.rs_span * D * 2, stage(bc), wave, g);
+            rcr.copy(dO + base + (int64_t)cw.roff * D, g.rs_span * D * 2, stage(bc) + BLK, wave, g);
+            row0 = cw.roff;
+            valid = g.rs_span;
+            // slot `lane` holds row raster_step(lane); slots past the block
+            // read past the descriptor, i.e. zero
+            lo = lane < BQ ? raster_step_p2(g, lane) * 4 : 0x7ffffffc;
+        } else {
+            valid = cw.sp.len - cw.r0 < BQ ? cw.sp.len - cw.r0 : BQ;
+            row0 = cw.sp.start + cw.r0;
+            rc.copy(Q + base + row0 * D, valid, stage(bc), wave);
+            rc.copy(dO + base + row0 * D, valid, stage(bc) + BLK, wave);
+        }
         if (wave == 0) {                            // LSE and Delta of the block's rows (zero past the end)
             const auto rl = make_rsrc(LSE + sbase + row0, valid * 4);
             const auto rd = make_rsrc(Delta + sbase + row0, valid * 4);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void *)(st + 2 * BLK), 4,
-                                                     lane * 4, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void *)(stage(bc) + 2 * BLK),
+                                                     4, lo, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rd, (__attribute__((address_space(3))) void *)(st + 2 * BLK + 2 * SROWS), 4, lane * 4, 0, 0, 0);
+                rd, (__attribute__((address_space(3))) void *)(stage(bc) + 2 * BLK + 2 * SROWS), 4, lo, 0, 0, 0);
         }
-        walk_next(cw, lst, cnt, BQ, g);
+        walk_next<RASTER>(cw, lst, cnt, BQ, g);
     };
 
     auto step = [&](auto bufc, int blk) {
@@ -484,11 +558,16 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
         });
 
     // lane holds column d = 32*db + l%32 of key rows 8*(r/4) + 4*grp + r%4.
+    // Raster: krow0 starts a 32-row block, so row krow0 + x sits
+    // raster_step(x) rows after row krow0; lane x of `rstep_x` holds that.
+    const int64_t rrow0 = RASTER ? slab_row<RASTER>(g, kt, ks_, krow0) : 0;
+    const int rstep_x = RASTER ? raster_step_p2(g, l32) : 0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int kr = krow0 + mfma_row(lane, r);
         if (kr < klen) {
-            const int64_t o = base + (ks_.start + kr) * D + l32;
+            const int64_t orow = RASTER ? rrow0 + __shfl(rstep_x, mfma_row(lane, r)) : ks_.start + kr;
+            const int64_t o = base + orow * D + l32;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 dK[o + db * 32] = (__bf16)(dk[db][r] * scale);
@@ -538,15 +617,25 @@ static sta_status run_bwd(const void *q, const void *k, const void *v, const voi
         if ((st = check_launch()) != STA_OK) return st;
     }
     if (parts & STA_BWD_DKDV) {
-        hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ, STA_BWD_NBUF>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
-                           (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q, idx.num_heads, g,
-                           rblocks, (int)total, scale_log2, scale);
+        if (g.raster)
+            hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ, STA_BWD_NBUF, true>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K,
+                               V, dO, lse, (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q,
+                               idx.num_heads, g, rblocks, (int)total, scale_log2, scale);
+        else
+            hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ, STA_BWD_NBUF, false>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K,
+                               V, dO, lse, (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q,
+                               idx.num_heads, g, rblocks, (int)total, scale_log2, scale);
         if ((st = check_launch()) != STA_OK) return st;
     }
     if (parts & STA_BWD_DQ) {
-        hipLaunchKernelGGL((dq_kernel<D, NW, BN, STA_BWD_NBUF>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V, dO, lse,
-                           (const float *)delta, (__bf16 *)dq, idx.kv_idx, idx.kv_cnt, idx.max_kv, idx.num_heads, g, rblocks,
-                           (int)total, scale_log2, scale);
+        if (g.raster)
+            hipLaunchKernelGGL((dq_kernel<D, NW, BN, STA_BWD_NBUF, true>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V,
+                               dO, lse, (const float *)delta, (__bf16 *)dq, idx.kv_idx, idx.kv_cnt, idx.max_kv, idx.num_heads,
+                               g, rblocks, (int)total, scale_log2, scale);
+        else
+            hipLaunchKernelGGL((dq_kernel<D, NW, BN, STA_BWD_NBUF, false>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V,
+                               dO, lse, (const float *)delta, (__bf16 *)dq, idx.kv_idx, idx.kv_cnt, idx.max_kv, idx.num_heads,
+                               g, rblocks, (int)total, scale_log2, scale);
         if ((st = check_launch()) != STA_OK) return st;
     }
     return st;

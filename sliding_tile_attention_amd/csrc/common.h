@@ -17,6 +17,9 @@ namespace sta {
 // tokens of every (b, h) slab (S = N + text rows).  The kernels walk them as
 // Tt text pseudo-tiles T .. T+Tt-1 of L rows each (the last one ragged)
 // starting at slab row N.
+// Raster layout (`raster`, grids the tile divides only): the video rows of
+// a slab are in raster token order and a tile's rows are gathered where its
+// tokens sit (tile_row); text rows follow them as in tile order.
 struct Geo {
     int gt, gh, gw;   // token grid
     int tt, th, tw;   // tile extents
@@ -29,6 +32,14 @@ struct Geo {
     int Tt;           // text pseudo-tiles, ceil(text / L)
     int TT;           // T + Tt
     int64_t S;        // rows per (b, h) slab, N + text
+    int raster;       // video rows in raster order (whole tiles only)
+    // raster layout: walk of 32-row blocks (raster_steps(g, 32)) and the
+    // raster distance of row 16 of a tile, as kernel arguments so that the
+    // kernels reload them instead of holding registers
+    int rs_step, rs_jump, rs_per, rs_16;
+    int rs_span;      // rows from a 32-row block's first row to past its last, raster_step(31) + 1
+    int rs_pmask;     // th*tw - 1 when th*tw > 32 (a power of two), else 0
+    int rs_lt, rs_lp; // log2(tw), log2(th*tw) (powers of two in the bf16 raster layout)
 };
 
 // Slab rows [start, start + len) of tile t (a video tile or a text
@@ -58,6 +69,66 @@ __host__ __device__ inline Span tile_span(const Geo &g, int t)
 
 // Rows of tile t.
 __host__ __device__ inline int tile_rows(const Geo &g, int t) { return tile_span(g, t).len; }
+
+// Raster index of the first token of video tile t (whole tiles).
+__host__ __device__ inline int64_t raster_base(const Geo &g, int t)
+{
+    const int a = t / (g.nh * g.nw), b = (t / g.nw) % g.nh, c = t % g.nw;
+    return ((int64_t)a * g.tt * g.gh + (int64_t)b * g.th) * g.gw + (int64_t)c * g.tw;
+}
+
+// Raster distance of row r of a whole tile from its first token (rows of a
+// tile in raster order of its tokens).  For a block of `rows` rows starting
+// at a multiple of `rows`, raster_step(k0 + x) = raster_step(k0) +
+// raster_step(x) whenever tw divides `rows` and one of th*tw, `rows`
+// divides the other: the block is whole rows of one tile plane, or whole
+// planes.
+__host__ __device__ inline int64_t raster_step(const Geo &g, int r)
+{
+    const int plane = g.th * g.tw;
+    const int i = r / plane, rem = r - i * plane, j = rem / g.tw, l = rem - j * g.tw;
+    return ((int64_t)i * g.gh + j) * g.gw + l;
+}
+
+// Walk of the raster offsets of consecutive `rows`-row blocks of a whole
+// tile (rows a multiple of tw; one of th*tw and rows dividing the other):
+// after each block the offset moves by `step`, and after every `per` blocks
+// (one tile plane, or the planes a block spans) by `jump` more.  No
+// divisions per block.
+// (Rows of a slab stay below 2^30, so offsets fit an int.)
+struct RasterStep {
+    int step, jump, per;
+};
+__host__ __device__ inline RasterStep raster_steps(const Geo &g, int rows)
+{
+    const int plane = g.th * g.tw;
+    if (rows <= plane) return {(rows / g.tw) * g.gw, (g.gh - g.th) * g.gw, plane / rows};
+    return {0, (rows / plane) * g.gh * g.gw, 1};
+}
+
+// raster_step when tw and th*tw are powers of two (shifts and masks).
+__device__ inline int raster_step_p2(const Geo &g, int r)
+{
+    const int i = r >> g.rs_lp, j = (r & ((1 << g.rs_lp) - 1)) >> g.rs_lt, l = r & ((1 << g.rs_lt) - 1);
+    return (i * g.gh + j) * g.gw + l;
+}
+
+// Slab row of row r of tile t whose tile-order span sp is known: raster
+// position for a video tile under RASTER, else sp.start + r.
+template <bool RASTER>
+__device__ inline int64_t slab_row(const Geo &g, int t, const Span &sp, int r)
+{
+    if constexpr (RASTER)
+        if (t < g.T) return raster_base(g, t) + raster_step(g, r);
+    return sp.start + r;
+}
+
+// Slab row of row r of tile t (a video tile or a text pseudo-tile).
+__host__ __device__ inline int64_t tile_row(const Geo &g, int t, int r)
+{
+    if (!g.raster || t >= g.T) return tile_span(g, t).start + r;
+    return raster_base(g, t) + raster_step(g, r);
+}
 
 // Tile of entry e of a walk: the cnt tiles of a list (lst, or every video
 // tile in order when lst is null), then the text pseudo-tiles.  Token-type-

@@ -99,12 +99,12 @@ __global__ __launch_bounds__(256) void vt_kernel(const __bf16 *__restrict__ V, _
     const Span sp = tile_span(g, t);
     const int L = sp.len;
     const int k0 = c * 64;
-    const __bf16 *src = V + (bh * g.S + sp.start + k0) * D;
+    const __bf16 *src = V + bh * g.S * D;
     constexpr int RG = D / 8;                 // 16-byte granules per V row
     for (int i = threadIdx.x; i < 64 * RG; i += 256) {
         const int r = i / RG, gc = i % RG;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (k0 + r < L) v = __builtin_nontemporal_load((const u32x4 *)(src + (int64_t)r * D + gc * 8));
+        if (k0 + r < L) v = __builtin_nontemporal_load((const u32x4 *)(src + tile_row(g, t, k0 + r) * D + gc * 8));
 #pragma unroll
         for (int t = 0; t < 4; ++t) tile[r][gc * 4 + t] = v[t];
     }
@@ -127,7 +127,9 @@ __global__ __launch_bounds__(256) void vt_kernel(const __bf16 *__restrict__ V, _
     }
 }
 
-template <int D, int NW, int QB, int BN>
+// RASTER: q, k, o, lse in raster order (whole tiles; rows of a video tile
+// gathered by tile_row, K blocks by a per-lane raster pattern).
+template <int D, int NW, int QB, int BN, bool RASTER>
 __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ VT,
     __bf16 *__restrict__ O, float *__restrict__ LSE, const int32_t *__restrict__ kv_idx,
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int row = wrow0 + qb * 32 + l32;
-        const __bf16 *p = Q + base + (qs.start + row) * D + grp * 8;
+        const __bf16 *p = Q + base + slab_row<RASTER>(g, qt, qs, row) * D + grp * 8;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) qf[qb][ks] = row < qlen ? ld8(p + ks * 16) : zero8();
     }
@@ -183,11 +185,13 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     // (i*NW + wave)*64 + lane, i.e. row r = slot / (granules per row) and
     // physical granule p, which must receive logical granule p ^ f(r).
     int gk[C::COPIES], gv[C::COPIES];     // byte offsets inside a K block / V^T tile
+    int gkr[RASTER ? C::COPIES : 1];      // raster: K row r of a video block sits raster_step(r) rows on
 #pragma unroll
     for (int i = 0; i < C::COPIES; ++i) {
         const int slot = (i * NW + wave) * 64 + lane;
         const int r = slot / C::GR, pg = slot % C::GR;
         gk[i] = (r * D + (pg ^ swz_row<C::GR>(r)) * 8) * 2;
+        if constexpr (RASTER) gkr[i] = (raster_step_p2(g, r) * D + (pg ^ swz_row<C::GR>(r)) * 8) * 2;
         const int rv = slot / C::GV, pv = slot % C::GV;
         gv[i] = (rv * Lp + (pv ^ swz_row<C::GV>(rv)) * 8) * 2;
     }
@@ -218,6 +222,8 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     Span c_sp = tile_span(g, c_tile);
     int n_tile = entry_tile(lst, cnt, g.T, 1);
     int bvalid[2];                                       // valid keys of the block in each buffer
+    static_assert(!RASTER || BN == 32, "raster walk of 32-row blocks");
+    int c_roff = RASTER ? (int)raster_base(g, c_tile) : 0;   // raster row of the block (video tiles only)
     // Issue the asynchronous copy of the next block into LDS buffer `buf`
     // through buffer descriptors over that block: K rows past a ragged
     // tile end read as zero (their scores are masked), V^T keys past it are
@@ -225,24 +231,43 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     auto gload = [&](int buf) {
         const int valid = c_sp.len - c_k0 < BN ? c_sp.len - c_k0 : BN;
         bvalid[buf] = valid;
-        const auto rk = make_rsrc(K + base + (c_sp.start + c_k0) * D, valid * D * 2);
         const auto rv = make_rsrc(VT + vt_base + (int64_t)c_tile * D * Lp + c_k0, (D * Lp - c_k0) * 2);
         __bf16 *Ks = smem + buf * C::STAGE;
         __bf16 *Vs = Ks + C::BLK;
+        if (RASTER) {
+            // whole video tile (no text rows in the raster layout): every row
+            // of the block exists; the descriptor spans the block's rows
+            // (g.rs_span from its first)
+            const auto rk = make_rsrc(K + base + (int64_t)c_roff * D, g.rs_span * D * 2);
 #pragma unroll
-        for (int i = 0; i < C::COPIES; ++i) {
-            if (!copy_live(i)) continue;
-            const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
-            b2lds16(rk, gk[i], Ks + lds_off);
-            b2lds16(rv, gv[i], Vs + lds_off);
+            for (int i = 0; i < C::COPIES; ++i) {
+                if (!copy_live(i)) continue;
+                const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
+                b2lds16(rk, gkr[RASTER ? i : 0], Ks + lds_off);
+                b2lds16(rv, gv[i], Vs + lds_off);
+            }
+        } else {
+            const auto rk = make_rsrc(K + base + (c_sp.start + c_k0) * D, valid * D * 2);
+#pragma unroll
+            for (int i = 0; i < C::COPIES; ++i) {
+                if (!copy_live(i)) continue;
+                const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
+                b2lds16(rk, gk[i], Ks + lds_off);
+                b2lds16(rv, gv[i], Vs + lds_off);
+            }
         }
         c_k0 += BN;
+        if constexpr (RASTER) {          // the walk of g.rs_*: no divisions per block
+            c_roff += g.rs_step;
+            if ((c_k0 & g.rs_pmask) == 0) c_roff += g.rs_jump;
+        }
         if (c_k0 >= c_sp.len) {
             c_k0 = 0;
             ++c_e;
             c_tile = n_tile;
             c_sp = tile_span(g, c_tile);
             n_tile = entry_tile(lst, cnt, g.T, c_e + 1);
+            if constexpr (RASTER) c_roff = (int)raster_base(g, c_tile);
         }
     };
 
@@ -349,7 +374,8 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         const float inv = 1.f / lt;
         const int row = wrow0 + qb * 32 + l32;
         if (row < qlen) {
-            __bf16 *op = O + base + (qs.start + row) * D;
+            const int64_t orow = slab_row<RASTER>(g, qt, qs, row);
+            __bf16 *op = O + base + orow * D;
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -360,7 +386,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
                     *(bf16x4 *)(op + db * 32 + 8 * j + 4 * grp) = v;
                 }
             if (grp == 0)
-                LSE[(int64_t)bh * g.S + qs.start + row] = (m_i[qb] + __log2f(lt)) * 0.69314718055994531f;
+                LSE[(int64_t)bh * g.S + orow] = (m_i[qb] + __log2f(lt)) * 0.69314718055994531f;
         }
     }
 }
@@ -386,9 +412,14 @@ static sta_status run_fwd(const void *q, const void *k, const void *v, void *o, 
     hipLaunchKernelGGL(vt_kernel<D>, dim3((unsigned)vt_blocks), dim3(256), 0, s, (const __bf16 *)v, (__bf16 *)vt,
                        g, Lp, chunks);
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BN>), dim3((unsigned)total), dim3(C::THREADS), 0, s,
-                       (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)vt, (__bf16 *)o, lse, idx.kv_idx,
-                       idx.kv_cnt, idx.max_kv, idx.num_heads, g, Lp, rblocks, (int)total, scale_log2);
+    if (g.raster)
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BN, true>), dim3((unsigned)total), dim3(C::THREADS), 0, s,
+                           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)vt, (__bf16 *)o, lse, idx.kv_idx,
+                           idx.kv_cnt, idx.max_kv, idx.num_heads, g, Lp, rblocks, (int)total, scale_log2);
+    else
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BN, false>), dim3((unsigned)total), dim3(C::THREADS), 0, s,
+                           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)vt, (__bf16 *)o, lse, idx.kv_idx,
+                           idx.kv_cnt, idx.max_kv, idx.num_heads, g, Lp, rblocks, (int)total, scale_log2);
     st = check_launch();
     const sta_status fs = workspace_free(vt, s);
     return st != STA_OK ? st : fs;

@@ -130,15 +130,17 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const __bf16 *__restrict_
     if (rows <= 0) return;                           // block past a cut tile's end (uniform)
     const int r = threadIdx.x / TPR, part = threadIdx.x % TPR;
     const bool live = r < rows;
+    // codes, scales: tile order (the attention kernel's); inputs: the layout's rows
     const int64_t row = bh * g.S + sp.start + (int64_t)blk * kKeyBlock + (live ? r : 0);
+    const int64_t src = bh * g.S + tile_row(g, t, blk * kKeyBlock + (live ? r : 0));
     const float *mk = kmean + bh * D + part * E;
     float q[E], k[E];
 #pragma unroll
     for (int c = 0; c < E / 8; ++c) {
         bf16x8 a = zero8(), b = zero8();
         if (live) {
-            a = ld8(Q + row * D + part * E + 8 * c);
-            b = ld8(K + row * D + part * E + 8 * c);
+            a = ld8(Q + src * D + part * E + 8 * c);
+            b = ld8(K + src * D + part * E + 8 * c);
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -211,12 +213,12 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(const __bf16 *__restrict_
     const int t = (int)(bt - bh * g.TT);
     const Span sp = tile_span(g, t);
     const int k0 = c * kKeyBlock;
-    const __bf16 *src = V + (bh * g.S + sp.start + k0) * D;
+    const __bf16 *src = V + bh * g.S * D;
     const float *vi = vinv + bh * D;
     for (int i = threadIdx.x; i < kKeyBlock * D / 8; i += 256) {
         const int r = i / (D / 8), gc = i % (D / 8);
         bf16x8 v = zero8();
-        if (k0 + r < sp.len) v = ld8(src + (int64_t)r * D + gc * 8);
+        if (k0 + r < sp.len) v = ld8(src + tile_row(g, t, k0 + r) * D + gc * 8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) tv[r][gc * 8 + j] = (float)v[j] * vi[gc * 8 + j];
     }
@@ -457,7 +459,8 @@ __global__ __launch_bounds__(NW * 64, STA_F8_MINB) void fwd_fp8_kernel(
     const float lt = sum_pair32(l_i);
     const float inv = 1.f / lt;
     if (row_ok) {
-        __bf16 *op = O + base + (qs.start + row) * D;
+        const int64_t orow = tile_row(g, qt, row);   // the layout's row of the output
+        __bf16 *op = O + base + orow * D;
         const float *svp = vscale + (int64_t)bh * D;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
@@ -470,7 +473,7 @@ __global__ __launch_bounds__(NW * 64, STA_F8_MINB) void fwd_fp8_kernel(
                 *(bf16x4 *)(op + db * 32 + 8 * j + 4 * grp) = v;
             }
         if (grp == 0)
-            LSE[(int64_t)bh * g.S + qs.start + row] = (m_i - 4.f + __log2f(lt)) * 0.69314718055994531f + cq;
+            LSE[(int64_t)bh * g.S + orow] = (m_i - 4.f + __log2f(lt)) * 0.69314718055994531f + cq;
     }
 }
 

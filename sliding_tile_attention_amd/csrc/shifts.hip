@@ -19,7 +19,8 @@
 //
 // Kernels:
 //   tile_mean_kernel  one workgroup per (tensor, set, head, tile).  A tile's
-//                     rows are one contiguous run of its tile-order slab, so
+//                     rows are one contiguous run of its tile-order slab (in
+//                     the raster layout they are gathered row by row), so
 //                     the workgroup streams it with 16-byte loads, rows
 //                     spread over the threads, and reduces the partial sums
 //                     in LDS in a fixed order (deterministic).  It reads Q
@@ -102,11 +103,16 @@ __global__ __launch_bounds__(kThreads) void tile_mean_kernel(const E *__restrict
     float total = 0.f;
     for (int bi = 0; bi < nb; ++bi) {
         const int64_t b = (int64_t)p * nb + bi;
-        const E *src = X + ((b * H + h) * g.S + sp.start) * D + col * V::n;
         float acc[V::n];
 #pragma unroll
         for (int j = 0; j < V::n; ++j) acc[j] = 0.f;
         int r = r0;
+        if (g.raster) {              // rows of the tile where its tokens sit
+            const E *slab = X + (b * H + h) * g.S * D + col * V::n;
+            for (; r < sp.len; r += RPP)
+                V::add(acc, *reinterpret_cast<const typename V::raw *>(slab + tile_row(g, tile, r) * D));
+        }
+        const E *src = X + ((b * H + h) * g.S + sp.start) * D + col * V::n;
         for (; r + 3 * RPP < sp.len; r += 4 * RPP) {
             typename V::raw u[4];
 #pragma unroll

@@ -332,3 +332,42 @@ def test_window_shifts_rejects_bad_arguments():
                                    ctypes.byref(GEOM.c()), w, ctypes.byref(sta.sta_dim3(1, 1, 1)),
                                    ctypes.byref(opts), sta._ptr(_fake()), None)
     assert st == sta.STA_ERR_INVALID
+
+
+def test_layout_option_checks():
+    """Raster layout: unknown values are malformed; grids the tile does not
+    divide, text rows, and bf16 tiles whose rows the 32-row copy pattern
+    cannot gather are unsupported.  Checked before anything is launched."""
+    def fwd(layout, geom=GEOM, n_text=0, dtype=sta.STA_BF16, index=None):
+        a = _fwd_args()
+        opts = sta.sta_attn_opts(n_text, 0, layout)
+        idx = index or a["index"]
+        return sta.lib.sta_fwd_ex(*[sta._ptr(a[n]) for n in ("q", "k", "v", "o", "lse")], 1, 2, 64, dtype, 0.125,
+                                  ctypes.byref(geom.c()), ctypes.byref(idx.c()), ctypes.byref(opts), None)
+
+    def bwd(layout, geom=GEOM, n_text=0):
+        a = _fwd_args()
+        opts = sta.sta_attn_opts(n_text, 0, layout)
+        ptrs = [sta._ptr(_fake()) for _ in range(10)]
+        return sta.lib.sta_bwd_ex(*ptrs, 1, 2, 64, sta.STA_BF16, 0.125, ctypes.byref(geom.c()),
+                                  ctypes.byref(a["index"].c()), sta.STA_BWD_ALL, ctypes.byref(opts), None)
+    for call in (fwd, bwd):
+        assert call(2) == sta.STA_ERR_INVALID
+        assert call(-1) == sta.STA_ERR_INVALID
+        # (5,8,8) with (2,4,4) tiles: 3x2x2 = 12 tiles, the last t-tile cut
+        assert call(sta.STA_LAYOUT_RASTER, geom=sta.Geometry((5, 8, 8), (2, 4, 4))) == sta.STA_ERR_UNSUPPORTED
+        assert call(sta.STA_LAYOUT_RASTER, n_text=3) == sta.STA_ERR_UNSUPPORTED
+    # tw = 32 does not divide the 16-row copies of the bf16 kernels
+    wide = sta.Geometry((4, 4, 64), (2, 2, 32))
+    assert fwd(sta.STA_LAYOUT_RASTER, geom=wide, index=_FakeIndex(T=8)) == sta.STA_ERR_UNSUPPORTED
+    # th*tw = 24 is not a power of two
+    odd = sta.Geometry((4, 12, 8), (2, 6, 4))
+    assert fwd(sta.STA_LAYOUT_RASTER, geom=odd, index=_FakeIndex(T=8)) == sta.STA_ERR_UNSUPPORTED
+    # the window-shift producer takes the same layout values
+    w, _ = sta._windows([(1, 1, 1)] * 2)
+    for layout, want in ((3, sta.STA_ERR_INVALID),):
+        opts = sta.sta_shift_opts(0, 0, 0, layout)
+        st = sta.lib.sta_window_shifts(sta._ptr(_fake()), sta._ptr(_fake()), 1, 2, 64, sta.STA_BF16, 0.125,
+                                       ctypes.byref(GEOM.c()), w, ctypes.byref(sta.sta_dim3(1, 1, 1)),
+                                       ctypes.byref(opts), sta._ptr(_fake()), None)
+        assert st == want
