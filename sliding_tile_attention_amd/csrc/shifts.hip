@@ -191,16 +191,30 @@ __global__ __launch_bounds__(kThreads) void shift_kernel(const float *__restrict
     float qv[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) qv[j] = qm[j];
-    for (int i = wave; i < RT; i += kThreads / 64) {
-        const int a = i / (R[1] * R[2]), b = (i / R[2]) % R[1], c = i % R[2];
-        const int k = ((lo[0] + a) * g.nh + lo[1] + b) * g.nw + lo[2] + c;
-        const float *kr = km + (int64_t)k * D;
-        float s = 0.f;
+    // four key tiles per wave and pass, so that four loads are in flight
+    constexpr int WAVES = kThreads / 64, U = 4;
+    for (int i0 = wave; i0 < RT; i0 += WAVES * U) {
+        float sv[U];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) s = fmaf(qv[j], kr[j], s);
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * WAVES;
+            sv[u] = 0.f;
+            if (i < RT) {
+                const int a = i / (R[1] * R[2]), b = (i / R[2]) % R[1], c = i % R[2];
+                const int k = ((lo[0] + a) * g.nh + lo[1] + b) * g.nw + lo[2] + c;
+                const float *kr = km + (int64_t)k * D;
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-        if (lane == 0) e[i] = scale * s;
+                for (int j = 0; j < PER; ++j) sv[u] = fmaf(qv[j], kr[j], sv[u]);
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1)
+#pragma unroll
+            for (int u = 0; u < U; ++u) sv[u] += __shfl_xor(sv[u], m);
+        if (lane == 0)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (i0 + u * WAVES < RT) e[i0 + u * WAVES] = scale * sv[u];
     }
     __syncthreads();
 
