@@ -25,7 +25,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ inline int sigma32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
@@ -43,17 +42,6 @@ __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
 __device__ inline bf16x8 zero8() { return __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u}); }
 
 __device__ inline bf16x8 ld8(const __bf16 *p) { return *(const bf16x8 *)p; }
-
-// Registers off..off+7 of an accumulator, rounded to bf16 (nearest even).
-__device__ inline bf16x8 cvt8(const f32x16 &s, int off)
-{
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = (__bf16)s[off + i];
-    return r;
-}
-
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 // max / sum of x over lanes l and l^32 (v_permlane32_swap: each lane gets
 // its own value and its partner's, in some order).
@@ -107,19 +95,6 @@ __device__ inline void wait_vmem()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Wait until at most n vector-memory operations are in flight, n a runtime
-// multiple of STEP no larger than MAXN (dispatched to constant waits).
-template <int MAXN, int STEP>
-__device__ inline void wait_vmem_le(int n)
-{
-    if constexpr (MAXN <= 0) {
-        wait_vmem<0>();
-    } else {
-        if (n >= MAXN) wait_vmem<MAXN>();
-        else wait_vmem_le<MAXN - STEP, STEP>(n);
-    }
-}
-
 // Workgroup barrier without the release fence of __syncthreads() (which
 // waits for every outstanding memory operation, LDS copies in flight
 // included).  Callers make the LDS data they hand over visible themselves:
@@ -131,13 +106,6 @@ __device__ inline void barrier_nofence()
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-}
-
-// Asynchronous 16-byte global -> LDS copy: lane l's 16 bytes land at
-// lds_base + 16*l (lds_base must be the same for the whole wave).
-__device__ inline void g2lds16(const void *src, void *lds_base)
-{
-    __builtin_amdgcn_global_load_lds((const void *)src, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
 // Buffer descriptor over `bytes` bytes from `base` (raw addressing: loads at
@@ -155,16 +123,6 @@ __device__ inline void b2lds16(__amdgpu_buffer_rsrc_t r, int voffset, void *lds_
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, voffset,
                                              soffset, 0, 0);
-}
-
-// Packs element i of four 8-wide bf16 rows (as raw words) into 4 bf16
-// (row 0 in the low half of the first word): one column of a 4x8 block.
-__device__ inline u32x2 column4(const u32x4 &a, const u32x4 &b, const u32x4 &c, const u32x4 &d, int i)
-{
-    const int w = i >> 1;
-    if (i & 1)
-        return (u32x2){(a[w] >> 16) | (b[w] & 0xffff0000u), (c[w] >> 16) | (d[w] & 0xffff0000u)};
-    return (u32x2){(a[w] & 0xffffu) | (b[w] << 16), (c[w] & 0xffffu) | (d[w] << 16)};
 }
 
 }  // namespace sta

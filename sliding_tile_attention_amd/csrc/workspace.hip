@@ -36,7 +36,7 @@ static sta_status pool_for(hipStream_t s, hipMemPool_t &pool)
         uint64_t keep = UINT64_MAX;
         e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
         if (e != hipSuccess) {
-            hipMemPoolDestroy(p);
+            (void)hipMemPoolDestroy(p);   // the attribute error is the one reported
             return fail(STA_ERR_HIP, "hipMemPoolSetAttribute: %s", hipGetErrorString(e));
         }
         g_pool[dev] = p;
