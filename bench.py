@@ -221,6 +221,25 @@ def gemm_ceiling(torch, dev, n=8192, reps=10):
             "what": "bf16 %dx%dx%d torch.matmul (hipBLASLt), mean of %d" % (n, n, n, reps)}
 
 
+def copy_ceiling(torch, x, reps=10):
+    """Attainable HBM rate of a plain device copy of a tensor the size of one
+    attention input (torch's copy_, read + write), beside the 8 TB/s peak."""
+    y = torch.empty_like(x)
+    for _ in range(2):
+        y.copy_(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del y
+    return {"value": round(2.0 * x.numel() * x.element_size() / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "what": "torch copy_ of %d bytes (read + write), mean of %d" % (x.numel() * x.element_size(), reps)}
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -424,6 +443,7 @@ def main():
             "fwd_frac_of_peak": round(fwd_flop / (per["fwd"] * 1e-3) / 1e12 / peak, 4),
             "bwd_kernels_ms": None if fwd_only else round(per["bwd_delta"] + per["bwd_dkdv"] + per["bwd_dq"], 3),
             "reorder_qkv_gbs": None if reorder_gbs is None else round(reorder_gbs, 1),
+            "measured_copy_ceiling": copy_ceiling(torch, q),
             # the producer reads Q and K once (its tile means); the choice
             # itself touches only the means
             "shifts_hbm_gbs": None if radius is None else round(2 * B * H * N * D * 2 / (per["shifts"] * 1e-3) / 1e9,
