@@ -58,6 +58,10 @@ CASES = [
     ("L256-D128-truncate", (8, 24, 24), (4, 8, 8), 1, 2, 128, [(3, 3, 3), (1, 1, 3)], "shared", "truncate"),
     ("L64-per-batch", (6, 8, 16), (1, 8, 8), 2, 2, 128, [(3, 1, 3), (1, 3, 1)], "batch", "shift"),
     ("plane32-D64", (4, 16, 16), (4, 4, 8), 2, 1, 64, [(1, 3, 3)], "shared", "shift"),
+    # the walk's other branches: planes of 8 rows (a block spans four planes), tw = 16, tw = 1
+    ("plane8-L32", (8, 4, 12), (4, 2, 4), 1, 2, 64, [(3, 3, 3), (1, 1, 3)], "head", "shift"),
+    ("tw16-plane128-L256", (4, 16, 32), (2, 8, 16), 1, 2, 128, [(3, 1, 1), (1, 3, 1)], None, "truncate"),
+    ("tw1-plane16-L64", (8, 32, 3), (4, 16, 1), 1, 1, 64, [(1, 3, 3)], "shared", "shift"),
 ]
 
 
