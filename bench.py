@@ -68,7 +68,7 @@ METRIC = "effective attention TFLOP/s (unmasked tile pairs) + ms/layer, 115200-t
 PEAK_BF16_TFLOPS = 2516.6        # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_FP8_TFLOPS = 5033.2         # MI355X dense fp8 / int8 MFMA (twice the bf16 rate)
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
-WORKLOAD = 5                     # the training workload of tests/inputs.py
+WORKLOAD = "720p-train"          # the training workload of tests/inputs.py
 
 
 def parse():

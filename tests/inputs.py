@@ -8,10 +8,11 @@ comparison see identical values.
 Workloads stand in for the pages' 5-second 720P video generation ("Fast
 Video Generation with Sliding Tile Attention", abstract): a (30,48,80) latent
 token grid, 24 heads of width 128.  Values are i.i.d. N(0,1), drawn with
-numpy's PCG64: tensors from seed [1234 + cfg, stream, b, h] per (batch, head)
+numpy's PCG64: tensors from seed [seed, stream, b, h] per (batch, head)
 slab, streams 0=Q 1=K 2=V 3=dO; window offsets (stream 4) and the per-head
-window choice (stream 5) from seed [1234 + cfg, stream].  bf16 workloads
-round the draws to bf16 (round-to-nearest-even).
+window choice (stream 5) from seed [seed, stream], with each workload's own
+seed (1235 .. 1239).  bf16 workloads round the draws to bf16
+(round-to-nearest-even).
 
 Joint text + video workloads append n_text text tokens after the video
 tokens of every (batch, head) slab, drawn in the same slab draw (N + n_text
@@ -30,18 +31,22 @@ TEXT_TOKENS_720P = 1164
 # Window sizes (in tiles) that the per-head variant draws from.
 HEAD_WINDOW_CHOICES = ((3, 3, 3), (3, 3, 5), (5, 5, 5))
 
+# The workloads, by name: the tiny fp32 forward on a 4x8x8 grid, the
+# 7680-token forward, the 720P-shaped forward, the same with per-head
+# windows and per-query-tile shifts, and the 720P training step.
 CONFIGS = {
-    1: dict(name="tiny-fp32", B=1, H=2, D=64, dtype="f32", grid=(4, 8, 8), tile=(2, 4, 4),
-            window=(3, 3, 3), offsets=False, per_head=False, backward=False),
-    2: dict(name="mid-7680", B=1, H=24, D=128, dtype="bf16", grid=(8, 24, 40), tile=(4, 8, 8),
-            window=(3, 3, 3), offsets=False, per_head=False, backward=False),
-    3: dict(name="720p-115200", B=1, H=24, D=128, dtype="bf16", grid=(30, 48, 80), tile=(6, 8, 8),
-            window=(3, 3, 5), offsets=False, per_head=False, backward=False),
-    4: dict(name="720p-offsets-perhead", B=1, H=24, D=128, dtype="bf16", grid=(30, 48, 80),
-            tile=(6, 8, 8), window=None, offsets=True, per_head=True, backward=False),
-    5: dict(name="720p-train", B=1, H=24, D=128, dtype="bf16", grid=(30, 48, 80), tile=(6, 8, 8),
-            window=(3, 3, 5), offsets=False, per_head=False, backward=True),
+    "tiny-fp32": dict(seed=1235, B=1, H=2, D=64, dtype="f32", grid=(4, 8, 8), tile=(2, 4, 4),
+                      window=(3, 3, 3), offsets=False, per_head=False, backward=False),
+    "mid-7680": dict(seed=1236, B=1, H=24, D=128, dtype="bf16", grid=(8, 24, 40), tile=(4, 8, 8),
+                     window=(3, 3, 3), offsets=False, per_head=False, backward=False),
+    "720p": dict(seed=1237, B=1, H=24, D=128, dtype="bf16", grid=(30, 48, 80), tile=(6, 8, 8),
+                 window=(3, 3, 5), offsets=False, per_head=False, backward=False),
+    "720p-shifted-perhead": dict(seed=1238, B=1, H=24, D=128, dtype="bf16", grid=(30, 48, 80),
+                                 tile=(6, 8, 8), window=None, offsets=True, per_head=True, backward=False),
+    "720p-train": dict(seed=1239, B=1, H=24, D=128, dtype="bf16", grid=(30, 48, 80), tile=(6, 8, 8),
+                       window=(3, 3, 5), offsets=False, per_head=False, backward=True),
 }
+WORKLOADS = tuple(CONFIGS)
 
 
 def tiles_per_axis(grid, tile):
@@ -86,21 +91,21 @@ def normal(shape, seed, stream, dtype):
 
 
 def windows_for(cfg, seed=None):
-    """[H,3] int32 window sizes (tiles) for a workload."""
-    c = CONFIGS[cfg] if isinstance(cfg, int) else cfg
+    """[H,3] int32 window sizes (tiles) for a workload (its name, or its dict)."""
+    c = CONFIGS[cfg] if isinstance(cfg, str) else cfg
     if not c["per_head"]:
         return np.tile(np.asarray(c["window"], np.int32), (c["H"], 1))
-    seed = 1234 + cfg if seed is None else seed
+    seed = c["seed"] if seed is None else seed
     pick = rng(seed, STREAM_WIN).integers(0, len(HEAD_WINDOW_CHOICES), size=c["H"])
     return np.asarray([HEAD_WINDOW_CHOICES[i] for i in pick], np.int32)
 
 
 def offsets_for(cfg, seed=None, lo=(-1, -2, -2), hi=(1, 2, 2)):
     """[T,3] int32 per-query-tile window shifts (tiles), or None."""
-    c = CONFIGS[cfg] if isinstance(cfg, int) else cfg
+    c = CONFIGS[cfg] if isinstance(cfg, str) else cfg
     if not c["offsets"]:
         return None
-    seed = 1234 + cfg if seed is None else seed
+    seed = c["seed"] if seed is None else seed
     T = num_tiles(c["grid"], c["tile"])
     return rng(seed, STREAM_OFF).integers(lo, hi, endpoint=True, size=(T, 3)).astype(np.int32)
 
@@ -168,7 +173,7 @@ def workload(cfg, heads=None, with_dout=None, n_text=0, grid=None):
         c["H"] = heads
     if grid is not None:
         c["grid"] = tuple(int(x) for x in grid)
-    seed = 1234 + cfg
+    seed = c["seed"]
     N = int(np.prod(c["grid"]))
     w = windows_for(cfg)[: c["H"]]
     off = offsets_for(cfg)

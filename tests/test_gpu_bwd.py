@@ -49,8 +49,8 @@ def test_bwd_bf16_small_full(case):
 
 def test_bwd_f32_tiny():
     """fp32 path (tiny workload geometry, whole-grid window) vs the oracle."""
-    w = workload(1, with_dout=True)
-    say("bwd f32 workload 1")
+    w = workload("tiny-fp32", with_dout=True)
+    say("bwd f32 tiny-fp32 workload")
     layer = Layer(w["grid"], w["tile"], w["windows"], None, w["q"], w["k"], w["v"], "f32", dout=w["dout"])
     layer.forward()
     dq, dk, dv = layer.backward()
@@ -81,8 +81,8 @@ def test_bwd_720p_training_sampled():
     configuration; sampled dQ rows and sampled dK/dV rows (from the least and
     the most attended key tiles) are checked against the oracle, and two
     exact identities are checked on the whole tensors."""
-    w = workload(5)
-    say("bwd bf16 workload 5 (full size)")
+    w = workload("720p-train")
+    say("bwd bf16 720p-train workload (full size)")
     layer = Layer(w["grid"], w["tile"], w["windows"], None, w["q"], w["k"], w["v"], "bf16", dout=w["dout"])
     layer.forward()
     dq, dk, dv = layer.backward()

@@ -67,7 +67,7 @@ def test_fp8_720p_sampled_and_method_accuracy():
     and against exact attention, whose error is the method's own (relative
     L2 below 8e-2: e4m3 P and V each carry a rounding of relative RMS about
     2^-4/sqrt(3))."""
-    w = workload(3)
+    w = workload("720p")
     say("fp8 fwd 720p (full size)")
     layer = Layer(w["grid"], w["tile"], w["windows"], None, w["q"], w["k"], w["v"], "bf16")
     o, lse = layer.forward(precision="fp8")

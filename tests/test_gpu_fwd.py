@@ -45,8 +45,8 @@ def test_fwd_bf16_small_full(case):
 
 def test_fwd_f32_tiny_workload():
     """Tiny fp32 workload: full tensor against the oracle (also = dense)."""
-    w = workload(1)
-    say("fwd f32 workload 1")
+    w = workload("tiny-fp32")
+    say("fwd f32 tiny-fp32 workload")
     layer = Layer(w["grid"], w["tile"], w["windows"], None, w["q"], w["k"], w["v"], "f32")
     o, lse = layer.forward()
     torch.cuda.synchronize()
@@ -71,8 +71,8 @@ def test_fwd_f32_offsets_d128():
 
 def test_fwd_mid_workload():
     """Mid workload (7680 tokens, 24 heads): two heads in full, every head sampled."""
-    w = workload(2)
-    say("fwd bf16 workload 2")
+    w = workload("mid-7680")
+    say("fwd bf16 mid-7680 workload")
     layer = Layer(w["grid"], w["tile"], w["windows"], None, w["q"], w["k"], w["v"], "bf16")
     o, lse = layer.forward()
     torch.cuda.synchronize()
@@ -86,17 +86,17 @@ def test_fwd_mid_workload():
     assert_lse(lse.reshape(-1)[rows], rl, "bf16")
 
 
-@pytest.mark.parametrize("cfg", [3, 4])
+@pytest.mark.parametrize("cfg", ["720p", "720p-shifted-perhead"])
 def test_fwd_720p_sampled(cfg):
     """Full 115200-token shape, every head, in the launch configuration the
     benchmark times; sampled rows (corner tiles + seeded tiles) vs oracle."""
     w = workload(cfg)
-    say("fwd bf16 workload %d (full size, sampled check)" % cfg)
+    say("fwd bf16 workload %s (full size, sampled check)" % cfg)
     layer = Layer(w["grid"], w["tile"], w["windows"], w["offsets"], w["q"], w["k"], w["v"], "bf16")
     o, lse = layer.forward()
     torch.cuda.synchronize()
     B, H, N, D = w["q"].shape
-    rows = sample_rows(B, H, N, 384, w["grid"], w["tile"], 2, 4, seed=cfg)
+    rows = sample_rows(B, H, N, 384, w["grid"], w["tile"], 2, 4, seed=w["seed"])
     ro, rl = oracle.fwd(w["q"], w["k"], w["v"], w["grid"], w["tile"], w["windows"], w["offsets"], rows=rows)
     o = o.reshape(-1, D)[torch.from_numpy(rows).cuda()]
     assert_close(to_host(o), ro, "bf16", "O")

@@ -125,7 +125,7 @@ def test_joint_720p_sampled():
     identities sum_j dV_j = sum_i dO_i and sum_j dK_j = 0, which include
     them."""
     nt = TEXT_TOKENS_720P
-    w = workload(5, n_text=nt)
+    w = workload("720p-train", n_text=nt)
     say("joint bf16 720p + %d text (full size)" % nt)
     layer = Layer(w["grid"], w["tile"], w["windows"], None, w["q"], w["k"], w["v"], "bf16", dout=w["dout"],
                   n_text=nt)

@@ -7,7 +7,7 @@ import torch
 import sliding_tile_attention_amd as sta
 from oracle import oracle
 from tests.gpu_util import say
-from tests.inputs import CONFIGS, offsets_for, windows_for
+from tests.inputs import CONFIGS, WORKLOADS, offsets_for, windows_for
 
 pytestmark = pytest.mark.gpu
 
@@ -58,10 +58,10 @@ def _check_index(grid, tile, windows, offsets, border="shift"):
         assert np.array_equal(a, b), name
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", WORKLOADS)
 def test_index_workloads(cfg):
     c = CONFIGS[cfg]
-    say("index workload %d" % cfg)
+    say("index workload %s" % cfg)
     _check_index(c["grid"], c["tile"], windows_for(cfg), offsets_for(cfg))
 
 
@@ -80,12 +80,12 @@ def test_index_random_geometries(seed):
 
 def test_index_forward_only():
     """Without transposed buffers only the forward lists are written."""
-    c = CONFIGS[2]
+    c = CONFIGS["mid-7680"]
     geom = sta.Geometry(c["grid"], c["tile"])
     say("index forward only")
-    idx = sta.StaIndex(geom, windows_for(2), None, transposed=False)
+    idx = sta.StaIndex(geom, windows_for("mid-7680"), None, transposed=False)
     torch.cuda.synchronize()
-    ref = oracle.index(c["grid"], c["tile"], windows_for(2), None, max_kv=idx.max_kv)
+    ref = oracle.index(c["grid"], c["tile"], windows_for("mid-7680"), None, max_kv=idx.max_kv)
     assert np.array_equal(idx.kv_idx.cpu().numpy(), ref[0])
     assert np.array_equal(idx.kv_cnt.cpu().numpy(), ref[1])
 
@@ -113,9 +113,9 @@ def test_index_options_random_geometries(seed):
 
 def test_index_options_720p_shape():
     """Per-head windows, per-head shifts and truncation at the 720P tile grid."""
-    c = CONFIGS[4]
+    c = CONFIGS["720p-shifted-perhead"]
     H = 24
     g = np.random.default_rng(77)
     offsets = g.integers([-1, -2, -2], [1, 2, 2], endpoint=True, size=(H, 300, 3)).astype(np.int32)
     say("index options 720p")
-    _check_index(c["grid"], c["tile"], windows_for(4), offsets, "truncate")
+    _check_index(c["grid"], c["tile"], windows_for("720p-shifted-perhead"), offsets, "truncate")

@@ -151,7 +151,7 @@ def test_shifts_720p_full_size():
     N(0,1) draws) with a search radius of one tile: every choice against
     the oracle's masses."""
     grid, tile = (30, 48, 80), (6, 8, 8)
-    windows = windows_for(4)
+    windows = windows_for("720p-shifted-perhead")
     say("shifts 720p full size")
     q, k = tile_signal(1, 24, grid, tile, 128, "bf16", 74, amp=1.0)
     got = _gpu_shifts(q, k, grid, tile, windows, (1, 1, 1), "bf16")

@@ -12,7 +12,7 @@ import torch
 
 import sliding_tile_attention_amd as sta
 from oracle import oracle
-from tests.inputs import CONFIGS, offsets_for, windows_for
+from tests.inputs import CONFIGS, WORKLOADS, offsets_for, windows_for
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "libsta.h")
@@ -43,7 +43,7 @@ def test_status_strings_and_version():
     assert sta.lib.sta_version() >= 10000
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", WORKLOADS)
 def test_index_dims_match_oracle(cfg):
     c = CONFIGS[cfg]
     geom = sta.Geometry(c["grid"], c["tile"])

@@ -39,11 +39,11 @@ def test_forward_backward_match_torch_dense(seed, offsets):
 
 def test_whole_grid_window_is_full_attention():
     """Tiny fp32 workload: window (3,3,3) over a 2x2x2 tile grid = 3D full attention."""
-    c = CONFIGS[1]
+    c = CONFIGS["tiny-fp32"]
     N = int(np.prod(c["grid"]))
     q, k, v, do = tensors(c["B"], c["H"], N, c["D"], "f32", 1235, with_dout=True)
-    o, lse = oracle.fwd(q, k, v, c["grid"], c["tile"], windows_for(1))
-    dq, dk, dv = oracle.bwd(q, k, v, do, c["grid"], c["tile"], windows_for(1))
+    o, lse = oracle.fwd(q, k, v, c["grid"], c["tile"], windows_for("tiny-fp32"))
+    dq, dk, dv = oracle.bwd(q, k, v, do, c["grid"], c["tile"], windows_for("tiny-fp32"))
     tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
     to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)
     to.backward(torch.tensor(do, dtype=torch.float64))

@@ -35,8 +35,8 @@ def test_window_axis_golden(row):
 
 def test_attendee_counts_720p_golden():
     rows = {r[0]: list(map(int, r[1:])) for r in read_golden("attendee_counts_720p.txt")}
-    c = CONFIGS[3]
-    _, kv_cnt, q_idx, q_cnt = oracle.index(c["grid"], c["tile"], windows_for(3)[:1])
+    c = CONFIGS["720p"]
+    _, kv_cnt, q_idx, q_cnt = oracle.index(c["grid"], c["tile"], windows_for("720p")[:1])
     n = (5, 6, 10)
     expect = np.einsum("i,j,k->ijk", rows["t"], rows["h"], rows["w"]).reshape(-1)
     assert np.array_equal(q_cnt[0], expect)
@@ -160,17 +160,17 @@ def test_zero_offsets_equal_no_offsets_and_large_offsets_saturate():
 
 def test_tiny_fp32_workload_is_dense():
     """Window (3,3,3) over a 2x2x2 tile grid covers everything."""
-    c = CONFIGS[1]
-    kv_idx, kv_cnt, q_idx, q_cnt = oracle.index(c["grid"], c["tile"], windows_for(1))
+    c = CONFIGS["tiny-fp32"]
+    kv_idx, kv_cnt, q_idx, q_cnt = oracle.index(c["grid"], c["tile"], windows_for("tiny-fp32"))
     assert np.all(kv_cnt == 8) and np.all(q_cnt == 8)
     assert np.all(kv_idx[:, :, :8] == np.arange(8))
 
 
 def test_offsets_workload_counts():
     """Per-head windows of the offsets workload: 27/45/125 tiles per query."""
-    c = CONFIGS[4]
-    w = windows_for(4)
-    kv_idx, kv_cnt, q_idx, q_cnt = oracle.index(c["grid"], c["tile"], w, offsets_for(4))
+    c = CONFIGS["720p-shifted-perhead"]
+    w = windows_for("720p-shifted-perhead")
+    kv_idx, kv_cnt, q_idx, q_cnt = oracle.index(c["grid"], c["tile"], w, offsets_for("720p-shifted-perhead"))
     for h in range(c["H"]):
         assert np.all(kv_cnt[h] == np.prod(w[h]))
         assert q_cnt[h].sum() == kv_cnt[h].sum()

@@ -13,7 +13,7 @@ def test_golden_small(name):
     assert oracle.perm(rows["grid"], rows["tile"]).tolist() == rows["perm"]
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, "asym"])
+@pytest.mark.parametrize("cfg", ["tiny-fp32", "mid-7680", "720p", "asym"])
 def test_bijection_and_tile_contiguity(cfg):
     grid, tile = ((4, 6, 6), (2, 3, 2)) if cfg == "asym" else (CONFIGS[cfg]["grid"], CONFIGS[cfg]["tile"])
     p = oracle.perm(grid, tile)
