@@ -275,3 +275,22 @@ def test_producer_feeds_per_batch_attention():
         assert_lse(to_host(lse[sl]), rl, "bf16")
         for got, ref, nm in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
             assert_close(to_host(got[sl]), ref, "bf16", "%s b=%d" % (nm, b))
+
+
+def test_per_batch_index_with_quantized_forward():
+    """The quantized forward with one list set per (b, h): every batch item
+    against the quantized method's oracle run with that item's shifts."""
+    from oracle import quant
+    grid, tile, B, H, D = (6, 8, 16), (2, 8, 8), 2, 2, 128
+    windows = [(3, 1, 3), (1, 3, 1)]
+    say("per-batch quantized forward")
+    off = _per_batch_offsets(B, H, grid, tile, 87)
+    q, k, v = tensors(B, H, int(np.prod(grid)), D, "bf16", 88)
+    layer = Layer(grid, tile, windows, off, q, k, v, "bf16")
+    o, lse = layer.forward(precision="fp8")
+    torch.cuda.synchronize()
+    for b in range(B):
+        sl = slice(b, b + 1)
+        ro, rl = quant.fwd(q[sl], k[sl], v[sl], grid, tile, windows, off[b])
+        assert_close(to_host(o[sl]), ro, "bf16", "fp8 O b=%d" % b)
+        assert_lse(to_host(lse[sl]), rl, "bf16", "fp8 LSE b=%d" % b)
