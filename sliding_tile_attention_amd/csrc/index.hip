@@ -4,9 +4,9 @@
 // of three axis ranges (shifted inward, or truncated at the border), so
 // walking t, then h, then w inside it emits tile ids in ascending order with
 // no sorting.  Shifts are shared by the heads or given per head.
-// Transposed lists: one thread per (head, key tile), scanning every query
-// tile in ascending order and testing its (possibly shifted) window.  No
-// atomics, so both list sets are deterministic.
+// Transposed lists: one wave per (head, key tile); its lanes test 64 query
+// tiles' (possibly shifted) windows at a time and a ballot compacts the hits
+// in ascending order.  No atomics, so both list sets are deterministic.
 #include "common.h"
 
 namespace sta {
@@ -61,27 +61,36 @@ __global__ __launch_bounds__(256) void index_fwd_kernel(Geo g, int h0, int nhead
     for (int j = n; j < max_kv; ++j) row[j] = -1;
 }
 
-__global__ __launch_bounds__(256) void index_bwd_kernel(Geo g, int h0, int nheads, Windows wins,
+// Heads hl0 .. hl0 + nheads - 1 of the launch's window set (h0 + hl globally).
+__global__ __launch_bounds__(256) void index_bwd_kernel(Geo g, int h0, int hl0, int nheads, Windows wins,
                                                         const int32_t *__restrict__ offsets, bool per_head,
                                                         bool truncate, int32_t *__restrict__ q_idx,
                                                         int32_t *__restrict__ q_cnt, int max_q)
 {
-    const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= nheads * g.T) return;
-    const int hl = gid / g.T, k = gid % g.T, h = h0 + hl;
+    const int64_t wid = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int lane = threadIdx.x & 63;
+    if (wid >= (int64_t)nheads * g.T) return;       // uniform per wave
+    const int hl = hl0 + (int)(wid / g.T), k = (int)(wid % g.T), h = h0 + hl;
     const int32_t *hoff = head_offsets(offsets, per_head, h, g.T);
     const int kt = k / (g.nh * g.nw), kh = (k / g.nw) % g.nh, kw = k % g.nw;
     int32_t *row = q_idx + ((int64_t)h * g.T + k) * max_q;
-    int n = 0;
-    for (int q = 0; q < g.T; ++q) {
-        int s[3], c[3];
-        tile_window(g, wins.w[hl], hoff, truncate, q, s, c);
-        const bool in = kt >= s[0] && kt < s[0] + c[0] && kh >= s[1] && kh < s[1] + c[1] &&
-                        kw >= s[2] && kw < s[2] + c[2];
-        if (in && n < max_q) row[n++] = q;
+    int n = 0;                                       // hits so far (uniform)
+    for (int q0 = 0; q0 < g.T; q0 += 64) {
+        const int q = q0 + lane;
+        bool in = false;
+        if (q < g.T) {
+            int s[3], c[3];
+            tile_window(g, wins.w[hl], hoff, truncate, q, s, c);
+            in = kt >= s[0] && kt < s[0] + c[0] && kh >= s[1] && kh < s[1] + c[1] && kw >= s[2] && kw < s[2] + c[2];
+        }
+        const uint64_t hits = __ballot(in);
+        const int pos = n + __popcll(hits & ((1ull << lane) - 1ull));   // rank among this pass's hits
+        if (in && pos < max_q) row[pos] = q;
+        n += __popcll(hits);
     }
-    q_cnt[(int64_t)h * g.T + k] = n;
-    for (int j = n; j < max_q; ++j) row[j] = -1;
+    n = n < max_q ? n : max_q;
+    if (lane == 0) q_cnt[(int64_t)h * g.T + k] = n;
+    for (int j = n + lane; j < max_q; j += 64) row[j] = -1;
 }
 
 sta_status launch_build_index(const Geo &g, int H, const int32_t *windows, const int32_t *offsets,
@@ -100,9 +109,17 @@ sta_status launch_build_index(const Geo &g, int H, const int32_t *windows, const
         sta_status st = check_launch();
         if (st != STA_OK) return st;
         if (idx.q_idx) {
-            hipLaunchKernelGGL(index_bwd_kernel, grid, dim3(256), 0, s, g, h0, nh, w, offsets, per_head,
-                               truncate, idx.q_idx, idx.q_cnt, idx.max_q);
-            if ((st = check_launch()) != STA_OK) return st;
+            // one wave per (head, key tile), 4 per workgroup; heads split so
+            // that a launch stays below 2^32 work items
+            int per = (int)((((int64_t)1 << 32) - 1) / ((int64_t)g.T * 64));
+            per = per < 1 ? 1 : per;
+            for (int hs = 0; hs < nh; hs += per) {
+                const int n = nh - hs < per ? nh - hs : per;
+                const dim3 wgrid((unsigned)(((int64_t)n * g.T + 3) / 4));
+                hipLaunchKernelGGL(index_bwd_kernel, wgrid, dim3(256), 0, s, g, h0, hs, n, w, offsets, per_head,
+                                   truncate, idx.q_idx, idx.q_cnt, idx.max_q);
+                if ((st = check_launch()) != STA_OK) return st;
+            }
         }
     }
     return STA_OK;
