@@ -106,3 +106,33 @@ def test_more_heads_than_one_launch():
         ro, rl = oracle.fwd(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], grid, tile, [windows[h]], off[h:h + 1])
         assert_close(to_host(o[:, h:h + 1]), ro, "bf16", "head %d O" % h)
         assert_lse(to_host(lse[:, h:h + 1]), rl, "bf16")
+
+
+@pytest.mark.parametrize("border", ["shift", "truncate"])
+def test_even_window_sizes(border):
+    """Even window sizes start half a window below the centre (the start
+    q + o - floor(w/2)); with both border rules and shifts, attention against
+    the oracle."""
+    grid, tile, B, H, D = (6, 8, 12), (2, 4, 4), 1, 2, 64
+    T = int(np.prod(oracle.tiles_per_axis(grid, tile)))
+    off = np.random.default_rng(177).integers(-1, 1, endpoint=True, size=(T, 3)).astype(np.int32)
+    say("edge even windows " + border)
+    q, k, v, do = tensors(B, H, int(np.prod(grid)), D, "bf16", 178, with_dout=True)
+    windows = [(2, 2, 2), (2, 1, 4)]
+    layer = Layer(grid, tile, windows, off, q, k, v, "bf16", dout=do, border=border)
+    o, lse = layer.forward()
+    dq, dk, dv = layer.backward()
+    torch.cuda.synchronize()
+    ro, rl = oracle.fwd(q, k, v, grid, tile, windows, off, border=border)
+    rq, rk, rv = oracle.bwd(q, k, v, do, grid, tile, windows, off, border=border)
+    assert_close(to_host(o), ro, "bf16", "even O")
+    assert_lse(to_host(lse), rl, "bf16")
+    for got, ref, nm in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        assert_close(to_host(got), ref, "bf16", "even " + nm)
+
+
+def test_batch_of_four():
+    """B = 4 (16 slabs with H = 4) sharing one index: every slab against the
+    oracle."""
+    _layer_vs_oracle("batch of four", (4, 8, 12), (2, 4, 4), 4, 4, 128, [(3, 3, 3), (1, 3, 3), (3, 1, 1), (1, 1, 3)],
+                     "bf16", 179)
