@@ -67,14 +67,23 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enums below are int-sized.  In C++ they take int32_t as their fixed
+ * underlying type, so any int32 value a C caller passes for one is a valid
+ * value of the type, which the argument checks then refuse as unknown. */
+#ifdef __cplusplus
+#define STA_ENUM enum : int32_t
+#else
+#define STA_ENUM enum
+#endif
+
+typedef STA_ENUM {
     STA_OK = 0,
     STA_ERR_INVALID = 1,
     STA_ERR_UNSUPPORTED = 2,
     STA_ERR_HIP = 3
 } sta_status;
 
-typedef enum {
+typedef STA_ENUM {
     STA_BF16 = 0,   /* bf16 storage, fp32 accumulation (MFMA path)        */
     STA_F32 = 1     /* fp32 storage and arithmetic (small shapes, checks) */
 } sta_dtype;
@@ -117,7 +126,7 @@ const char *sta_last_error(void);
 int32_t sta_version(void);
 
 /* Border rule of a query tile's key-tile window, per axis. */
-typedef enum {
+typedef STA_ENUM {
     /* The window keeps its size min(w, n) and its start q + o - floor(w/2)
      * is moved inside [0, n - size]: every query tile of a head sees the
      * same number of key tiles (the default). */
@@ -252,7 +261,7 @@ sta_status sta_bwd(const void *q, const void *k, const void *v, const void *o, c
                    const sta_geom *g, const sta_index *idx, hipStream_t stream);
 
 /* Stages of the backward, for sta_bwd_parts. */
-typedef enum {
+typedef STA_ENUM {
     STA_BWD_DELTA = 1,   /* delta_ws = rowsum(dout o o)                     */
     STA_BWD_DKDV = 2,    /* dk, dv   (reads delta_ws)                        */
     STA_BWD_DQ = 4,      /* dq       (reads delta_ws)                        */
@@ -273,7 +282,7 @@ sta_status sta_bwd_parts(const void *q, const void *k, const void *v, const void
                          const sta_geom *g, const sta_index *idx, int32_t parts, hipStream_t stream);
 
 /* Arithmetic of the forward (sta_attn_opts.precision). */
-typedef enum {
+typedef STA_ENUM {
     /* The tensors' dtype: bf16 MFMA with fp32 accumulation, or fp32. */
     STA_PREC_DEFAULT = 0,
     /* bf16 tensors, quantized products: per (b, h) K is smoothed by its
@@ -289,7 +298,7 @@ typedef enum {
 } sta_precision;
 
 /* Row order of the attention tensors (sta_attn_opts.layout). */
-typedef enum {
+typedef STA_ENUM {
     /* Tile order: the rows of a tile are contiguous (sta_tile_reorder makes
      * it from raster order).  Every geometry. */
     STA_LAYOUT_TILE = 0,

@@ -40,6 +40,18 @@ static const int64_t kMaxTokens = (int64_t)1 << 30;
 static const int64_t kMaxTiles = (int64_t)1 << 20;
 static const int64_t kMaxTileTokens = (int64_t)1 << 16;
 
+// Product of three positive extents, or -1 once it passes `limit` (at most
+// 2^30): every partial product stays below 2^61, so nothing overflows.
+static int64_t bounded_product(const int v[3], int64_t limit)
+{
+    int64_t p = 1;
+    for (int d = 0; d < 3; ++d) {
+        p *= v[d];
+        if (p > limit) return -1;
+    }
+    return p;
+}
+
 static sta_status make_geo(const sta_geom *g, Geo &out)
 {
     if (!g)
@@ -55,15 +67,17 @@ static sta_status make_geo(const sta_geom *g, Geo &out)
         // a tile longer than the axis is one tile holding the whole axis,
         // the same tiling as a tile exactly as long as the axis
         tl[d] = tl[d] < gr[d] ? tl[d] : gr[d];
-        n[d] = (gr[d] + tl[d] - 1) / tl[d];
+        n[d] = (gr[d] - 1) / tl[d] + 1;
         ragged = ragged || gr[d] % tl[d] != 0;
     }
-    int64_t N = (int64_t)gr[0] * gr[1] * gr[2];
-    int64_t T = (int64_t)n[0] * n[1] * n[2];
-    int64_t L = (int64_t)tl[0] * tl[1] * tl[2];
-    if (N > kMaxTokens || T > kMaxTiles || L > kMaxTileTokens)
-        return fail(STA_ERR_UNSUPPORTED, "grid too large: %lld tokens, %lld tiles, %lld tokens per tile",
-                    (long long)N, (long long)T, (long long)L);
+    const int64_t N = bounded_product(gr, kMaxTokens);
+    const int64_t T = bounded_product(n, kMaxTiles);
+    const int64_t L = bounded_product(tl, kMaxTileTokens);
+    if (N < 0 || T < 0 || L < 0)
+        return fail(STA_ERR_UNSUPPORTED,
+                    "grid (%d,%d,%d) with tile (%d,%d,%d) too large: at most %lld tokens, %lld tiles, "
+                    "%lld tokens per tile", gr[0], gr[1], gr[2], tl[0], tl[1], tl[2], (long long)kMaxTokens,
+                    (long long)kMaxTiles, (long long)kMaxTileTokens);
     out.gt = gr[0]; out.gh = gr[1]; out.gw = gr[2];
     out.tt = tl[0]; out.th = tl[1]; out.tw = tl[2];
     out.nt = n[0]; out.nh = n[1]; out.nw = n[2];

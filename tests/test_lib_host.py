@@ -195,6 +195,12 @@ def test_index_dims_rejects_bad_arguments():
     _expect(sta.STA_ERR_INVALID, sta.sta_index_dims, sta.Geometry((3, 8, 8), (2, 4, -4)), [(1, 1, 1)], False)
     g = sta.lib.sta_index_dims(ctypes.byref(GEOM.c()), 0, None, 0, None, None)
     assert g == sta.STA_ERR_INVALID
+    # extents near the int32 limit are refused as too large, not wrapped
+    big = 2 ** 31 - 1
+    for grid, tile in (((big, 2, 2), (1, 1, 1)), ((big, big, big), (7, 7, 7)), ((big, 1, 1), (big, 1, 1))):
+        _expect(sta.STA_ERR_UNSUPPORTED, sta.sta_index_dims, sta.Geometry(grid, tile), [(1, 1, 1)], False)
+    # status codes outside the enum still get a name
+    assert sta.lib.sta_status_str(-1).decode() == sta.lib.sta_status_str(99).decode() == "STA_ERR_UNKNOWN"
 
 
 def test_index_dims_ex_match_oracle_with_options():
