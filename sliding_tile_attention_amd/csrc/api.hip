@@ -229,6 +229,12 @@ static sta_status check_attn(const Geo &g, int B, int H, int D, sta_dtype dt, fl
 
 using namespace sta;
 
+// C callers see the ABI enums as plain int-sized enums; the C++ side must
+// agree on their size.
+static_assert(sizeof(sta_status) == 4 && sizeof(sta_dtype) == 4 && sizeof(sta_border) == 4 &&
+                  sizeof(sta_bwd_part) == 4 && sizeof(sta_precision) == 4 && sizeof(sta_layout) == 4,
+              "ABI enums are 32-bit");
+
 extern "C" {
 
 const char *sta_status_str(sta_status s)

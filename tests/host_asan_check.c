@@ -20,6 +20,9 @@
 
 #include "libsta.h"
 
+/* the C side of the ABI: enums are int-sized, as the library assumes */
+_Static_assert(sizeof(sta_status) == 4 && sizeof(sta_dtype) == 4 && sizeof(sta_layout) == 4, "32-bit enums");
+
 static int failures = 0;
 #define EXPECT(c, ...)                      \
     do {                                    \
