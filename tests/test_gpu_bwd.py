@@ -47,6 +47,32 @@ def test_bwd_bf16_small_full(case):
     assert_close(to_host(dv), rv, "bf16", name + " dV")
 
 
+def test_bwd_bf16_deterministic():
+    """No atomics and a fixed reduction order: repeated backward calls, and a
+    call on a second stream, give bit-identical dQ, dK and dV (here on a
+    720P-shaped slab two tiles deep, 4 heads with shifted windows, about 1400
+    workgroups per kernel)."""
+    grid, tile, windows = (12, 48, 80), (6, 8, 8), [(3, 3, 5), (1, 3, 3)]
+    say("bwd bf16 determinism " + str(grid))
+    off = _offsets(grid, tile, True, seed=17)
+    q, k, v, do = tensors(1, 4, int(np.prod(grid)), 128, "bf16", 93, with_dout=True)
+    layer = Layer(grid, tile, windows * 2, off, q, k, v, "bf16", dout=do)
+    layer.forward()
+    first = [t.clone() for t in layer.backward()]
+    for rep in range(3):
+        for a, b, nm in zip(layer.backward(), first, ("dQ", "dK", "dV")):
+            assert torch.equal(a, b), "repeat %d: %s differs" % (rep, nm)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        again = [t.clone() for t in layer.backward()]
+    side.synchronize()
+    for a, b, nm in zip(again, first, ("dQ", "dK", "dV")):
+        assert torch.equal(a, b), "second stream: %s differs" % nm
+    for t in first:
+        assert torch.isfinite(t.float()).all()
+
+
 def test_bwd_f32_tiny():
     """fp32 path (tiny workload geometry, whole-grid window) vs the oracle."""
     w = workload("tiny-fp32", with_dout=True)
