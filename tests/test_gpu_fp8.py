@@ -20,6 +20,9 @@ CASES = [
      "truncate", 0),
     ("L384-D128-text-cut", (12, 13, 16), (6, 8, 8), 1, 2, 128, [(3, 3, 3), (1, 1, 3)], None, "shift", 77),
     ("L48-D64-text", (6, 8, 16), (3, 4, 4), 1, 2, 64, [(1, 3, 3), (3, 3, 5)], "head", "shift", 100),
+    # cut tiles of 384, 240, 192 and 120 tokens (partial 64-key blocks) under truncated, per-head shifted windows
+    ("L384-D128-cut-truncate-head", (12, 13, 20), (6, 8, 8), 1, 2, 128, [(3, 3, 5), (1, 3, 3)], "head",
+     "truncate", 0),
 ]
 
 
