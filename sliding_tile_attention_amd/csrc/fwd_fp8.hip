@@ -26,6 +26,7 @@
 // that the 32 bytes a lane half feeds the PV product are contiguous), then
 // the attention kernel.  The work decomposition, list walk, copies and
 // swizzles are those of the bf16 forward.
+#include <cfloat>
 #include <type_traits>
 
 #include "common.h"
@@ -49,26 +50,30 @@ __device__ inline int swz8(int r)
     else return (r / (16 / G)) & (G - 1);
 }
 
-// 1a. Partial column sums of K and column maxima of |V| over one chunk of
-// the rows of one (b, h): part[bh][chunk][0 = sum K, 1 = max |V|][D].
+// 1a. Partial column sums of K in fp64 (a bf16 value is added exactly while
+// the sum stays below 2^45 times its magnitude, so the mean, rounded once to
+// fp32, is that of the exact mean unless the two straddle an fp32 rounding
+// boundary) and column maxima of |V| over one chunk of the rows of one
+// (b, h): part[bh][chunk][0 = sum K, 1 = max |V|][D].
 template <int D>
 __global__ __launch_bounds__(256) void qstat_kernel(const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
-                                                    float *__restrict__ part, int64_t S)
+                                                    double *__restrict__ part, int64_t S)
 {
     constexpr int P = D / 2;            // column pairs
     constexpr int RG = 256 / P;         // row groups
-    __shared__ float red[2][RG][D];
+    __shared__ double red[2][RG][D];
     const int chunk = (int)(blockIdx.x % kStatChunks);
     const int64_t bh = blockIdx.x / kStatChunks;
     const int cp = threadIdx.x % P, rg = threadIdx.x / P;
     const int64_t r0 = S * chunk / kStatChunks, r1 = S * (chunk + 1) / kStatChunks;
     const __bf16 *kb = K + bh * S * D + 2 * cp, *vb = V + bh * S * D + 2 * cp;
-    float s0 = 0.f, s1 = 0.f, m0 = 0.f, m1 = 0.f;
+    double s0 = 0.0, s1 = 0.0;
+    float m0 = 0.f, m1 = 0.f;
     for (int64_t r = r0 + rg; r < r1; r += RG) {
         const bf16x2 k2 = *(const bf16x2 *)(kb + r * D);
         const bf16x2 v2 = *(const bf16x2 *)(vb + r * D);
-        s0 += (float)k2[0];
-        s1 += (float)k2[1];
+        s0 += (double)(float)k2[0];
+        s1 += (double)(float)k2[1];
         m0 = fmaxf(m0, fabsf((float)v2[0]));
         m1 = fmaxf(m1, fabsf((float)v2[1]));
     }
@@ -79,15 +84,16 @@ __global__ __launch_bounds__(256) void qstat_kernel(const __bf16 *__restrict__ K
     __syncthreads();
     for (int i = threadIdx.x; i < 2 * D; i += 256) {
         const int w = i / D, d = i % D;
-        float a = red[w][0][d];
-        for (int j = 1; j < RG; ++j) a = w ? fmaxf(a, red[w][j][d]) : a + red[w][j][d];
+        double a = red[w][0][d];
+        for (int j = 1; j < RG; ++j) a = w ? fmax(a, red[w][j][d]) : a + red[w][j][d];
         part[((bh * kStatChunks + chunk) * 2 + w) * D + d] = a;
     }
 }
 
-// 1b. Per (b, h, d): the smoothing mean of K and V's channel scale.
+// 1b. Per (b, h, d): the smoothing mean of K (the fp64 sum over the rows
+// divided by their count, rounded once to fp32) and V's channel scale.
 template <int D>
-__global__ __launch_bounds__(256) void qstat_final_kernel(const float *__restrict__ part, float *__restrict__ kmean,
+__global__ __launch_bounds__(256) void qstat_final_kernel(const double *__restrict__ part, float *__restrict__ kmean,
                                                           float *__restrict__ vscale, float *__restrict__ vinv,
                                                           int64_t S, int BH)
 {
@@ -95,12 +101,13 @@ __global__ __launch_bounds__(256) void qstat_final_kernel(const float *__restric
     if (i >= BH * D) return;
     const int64_t bh = i / D;
     const int d = i % D;
-    float s = 0.f, m = 0.f;
+    double s = 0.0;
+    float m = 0.f;
     for (int c = 0; c < kStatChunks; ++c) {
         s += part[((bh * kStatChunks + c) * 2 + 0) * D + d];
-        m = fmaxf(m, part[((bh * kStatChunks + c) * 2 + 1) * D + d]);
+        m = fmaxf(m, (float)part[((bh * kStatChunks + c) * 2 + 1) * D + d]);
     }
-    kmean[i] = s / (float)S;
+    kmean[i] = (float)(s / (double)S);
     vscale[i] = m / kE4M3Max;
     vinv[i] = m > 0.f ? kE4M3Max / m : 0.f;
 }
@@ -363,7 +370,12 @@ __global__ __launch_bounds__(NW * 64, STA_F8_MINB) void fwd_fp8_kernel(
         __builtin_amdgcn_s_waitcnt(0);               // this wave's copies of block blk have landed
         __syncthreads();                             // ... and everyone's; the other buffer is free
         const int valid = bvalid[BUF];
-        const float f = fq * bscale[BUF];
+        // Logit factor of the block.  Masked keys get s = -inf below, and f is
+        // zero for an all-zero Q row or a K block equal to the smoothing mean
+        // (-inf * 0 would be NaN); raising f to the smallest normal float
+        // keeps them at -inf and changes nothing else: such a row or block
+        // has all-zero codes, so its unmasked s are 0 either way.
+        const float f = fmaxf(fq * bscale[BUF], FLT_MIN);
         if (blk + 1 < nblk) gload(1 - BUF);
         const uint8_t *Ks = smem + BUF * C::STAGE;
         const uint8_t *Vs = Ks + C::KBYTES;
@@ -500,7 +512,7 @@ static sta_status run_fwd_fp8(const void *q, const void *k, const void *v, void 
     const size_t off_sq = off_vt + align256(n_vt), off_corr = off_sq + align256(n_rows * 4);
     const size_t off_sk = off_corr + align256(n_rows * 4), off_km = off_sk + align256(n_sk * 4);
     const size_t off_vs = off_km + align256(n_ch * 4), off_vi = off_vs + align256(n_ch * 4);
-    const size_t off_part = off_vi + align256(n_ch * 4), bytes = off_part + align256(n_part * 4);
+    const size_t off_part = off_vi + align256(n_ch * 4), bytes = off_part + align256(n_part * 8);
     void *ws = nullptr;
     sta_status st = workspace_alloc(&ws, bytes, s);
     if (st != STA_OK) return st;
@@ -508,7 +520,7 @@ static sta_status run_fwd_fp8(const void *q, const void *k, const void *v, void 
     uint8_t *q8 = (uint8_t *)(w + off_q8), *k8 = (uint8_t *)(w + off_k8), *vt8 = (uint8_t *)(w + off_vt);
     float *sq = (float *)(w + off_sq), *corr = (float *)(w + off_corr), *sk = (float *)(w + off_sk);
     float *km = (float *)(w + off_km), *vs = (float *)(w + off_vs), *vi = (float *)(w + off_vi);
-    float *part = (float *)(w + off_part);
+    double *part = (double *)(w + off_part);
     const __bf16 *Q = (const __bf16 *)q, *K = (const __bf16 *)k, *V = (const __bf16 *)v;
     const float c_log2 = scale * 1.4426950408889634f;
 

@@ -61,6 +61,34 @@ def assert_close(got, ref, dtype, what=""):
     return max_abs, rel_l2
 
 
+def assert_fp8(got_o, got_lse, ref, what=""):
+    """The quantized forward against its oracle, run with bound=True
+    (oracle/quant.py): element by element,
+        |O - O_ref| <= bound + 2^-8 |O_ref| + 1e-4 a + 1e-7,
+        |LSE - LSE_ref| <= bound + 1e-5 (1 + |LSE_ref|),
+    where the bounds cover the codes of P that a fp32 evaluation of the
+    logits may round the other way, 2^-8 |O| the bf16 rounding of the output
+    (2^-9) with room, and a = sum_j p_j |w_j| / l the scale of the fp32
+    accumulation error (about sqrt(n) 2^-24 of it over n <= 5e4 keys, 1.3e-5).
+    Returns (rows whose bound is nonzero, max |dO|)."""
+    ro, rl, ob, lb, oa = (np.asarray(x, np.float64) for x in ref)
+    o = np.asarray(got_o, np.float64).reshape(ro.shape)
+    lse = np.asarray(got_lse, np.float64).reshape(rl.shape)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), what + ": non-finite output"
+    tol = ob + 2.0 ** -8 * np.abs(ro) + 1e-4 * oa + 1e-7
+    err = np.abs(o - ro)
+    bad = err > tol
+    assert not bad.any(), "%s: %d of %d elements of O outside the bound (worst |dO| %.3e against %.3e)" % (
+        what, bad.sum(), bad.size, err[bad].max(), tol[bad][np.argmax(err[bad])])
+    lerr = np.abs(lse - rl)
+    lbad = lerr > lb + 1e-5 * (1 + np.abs(rl))
+    assert not lbad.any(), "%s: %d LSE values outside the bound (worst %.3e)" % (what, lbad.sum(), lerr.max())
+    flagged = int(np.count_nonzero(lb.reshape(-1) > 0))
+    say("%s: max |dO| %.3e, max |dLSE| %.3e, %d rows with codes a fp32 evaluation may move" % (
+        what, float(err.max()) if err.size else 0.0, float(lerr.max()) if lerr.size else 0.0, flagged))
+    return flagged, float(err.max()) if err.size else 0.0
+
+
 class Layer:
     """Device state of one attention layer: inputs reordered to tile order,
     the index, and the outputs converted back to raster order.  With n_text

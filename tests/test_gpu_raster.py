@@ -16,7 +16,7 @@ import torch
 
 import sliding_tile_attention_amd as sta
 from oracle import oracle
-from tests.gpu_util import Layer, assert_close, assert_lse, say, to_dev, to_host
+from tests.gpu_util import Layer, assert_close, assert_fp8, assert_lse, say, to_dev, to_host
 from tests.inputs import tensors, tile_signal, windows_for
 
 pytestmark = pytest.mark.gpu
@@ -134,9 +134,7 @@ def test_raster_fp8_matches_quantized_oracle():
     layer = Layer(grid, tile, windows, None, q, k, v, "bf16")
     to, tl = layer.forward(precision="fp8")
     torch.cuda.synchronize()
-    ro, rl = quant.fwd(q, k, v, grid, tile, windows)
-    assert_close(to_host(o), ro, "bf16", "raster fp8 O")
-    assert_lse(to_host(lse), rl, "bf16", "raster fp8 LSE")
+    assert_fp8(to_host(o), to_host(lse), quant.fwd(q, k, v, grid, tile, windows, bound=True), "raster fp8")
     assert_close(to_host(o), to_host(to), "bf16", "raster fp8 O vs tile order")
     assert float((lse - tl).abs().max()) <= 1e-5
 

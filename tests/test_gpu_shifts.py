@@ -21,7 +21,7 @@ import torch
 
 import sliding_tile_attention_amd as sta
 from oracle import oracle, shift
-from tests.gpu_util import Layer, assert_close, assert_lse, say, to_dev, to_host
+from tests.gpu_util import Layer, assert_close, assert_fp8, assert_lse, say, to_dev, to_host
 from tests.inputs import tensors, tile_signal, windows_for
 
 pytestmark = pytest.mark.gpu
@@ -291,6 +291,5 @@ def test_per_batch_index_with_quantized_forward():
     torch.cuda.synchronize()
     for b in range(B):
         sl = slice(b, b + 1)
-        ro, rl = quant.fwd(q[sl], k[sl], v[sl], grid, tile, windows, off[b])
-        assert_close(to_host(o[sl]), ro, "bf16", "fp8 O b=%d" % b)
-        assert_lse(to_host(lse[sl]), rl, "bf16", "fp8 LSE b=%d" % b)
+        assert_fp8(to_host(o[sl]), to_host(lse[sl]), quant.fwd(q[sl], k[sl], v[sl], grid, tile, windows, off[b],
+                                                             bound=True), "fp8 b=%d" % b)
