@@ -262,6 +262,75 @@ def sta_window_shifts(q, k, B, H, D, dtype, scale, geom, windows, radius, offset
                                  ctypes.byref(r), ctypes.byref(opts), _ptr(offsets), _stream(stream)))
 
 
+# ------------------------------------------------- argument checks --
+# The C ABI takes bare pointers and cannot see strides, dtypes or devices, so
+# the wrappers below check them before any pointer is passed: a transposed
+# view (say q.transpose(1, 2) of a [B, S, H, D] tensor) or a tensor of
+# another dtype would otherwise be read as if it were contiguous [B, H, S, D].
+# Device checks come last, after every layout check.
+
+def _check_attn(geom, n_text, tensors, lse=None, index=None):
+    """tensors: [(name, tensor)] that must be contiguous [B, H, S, D] of one
+    shape, dtype (bfloat16 or float32) and device, with S = geom.tokens +
+    n_text; lse: a contiguous float32 [B, H, S] tensor on that device; index:
+    a StaIndex of H or B*H list sets on that device."""
+    name0, ref = tensors[0]
+    for name, t in tensors:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a torch tensor" % name)
+        if t.dim() != 4:
+            raise ValueError("%s must be [B, H, S, D], got shape %s" % (name, tuple(t.shape)))
+        if t.shape != ref.shape:
+            raise ValueError("%s has shape %s, %s has %s" % (name, tuple(t.shape), name0, tuple(ref.shape)))
+        if t.dtype != ref.dtype:
+            raise TypeError("%s is %s, %s is %s" % (name, t.dtype, name0, ref.dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous [B, H, S, D] (a transposed view is not)" % name)
+    _dtype_code(ref)
+    B, H, S, D = ref.shape
+    if S != geom.tokens + n_text:
+        raise ValueError("token axis holds %d rows, the geometry %d (+ %d text)" % (S, geom.tokens, n_text))
+    if lse is not None:
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [B, H, S] = %s tensor, got %s %s" % (
+                (B, H, S), lse.dtype, tuple(lse.shape)))
+    if index is not None and index.num_heads not in (H, B * H):
+        raise ValueError("index holds %d list sets; H = %d heads (or B*H = %d) expected" % (
+            index.num_heads, H, B * H))
+    others = ([("lse", lse)] if lse is not None else []) + ([("index", index.kv_idx)] if index is not None else [])
+    for name, t in tensors + others:
+        if t.device != ref.device:
+            raise ValueError("%s is on %s, %s on %s" % (name, t.device, name0, ref.device))
+    if ref.device.type != "cuda":
+        raise ValueError("libsta computes on a GPU: tensors are on %s" % ref.device)
+
+
+def _device(d):
+    """torch.device of d, a bare "cuda" resolved to the current device."""
+    d = torch.device(d)
+    if d.type == "cuda" and d.index is None and torch.cuda.is_available():
+        d = torch.device("cuda", torch.cuda.current_device())
+    return d
+
+
+def _check_offsets(offsets, geom, H, device):
+    """offsets: int32, contiguous, [T, 3], [H, T, 3] or [B, H, T, 3] for the
+    geometry's T tiles and the H windows, on the index's device."""
+    if not isinstance(offsets, torch.Tensor):
+        raise TypeError("offsets must be a torch tensor")
+    if offsets.dtype != torch.int32:
+        raise TypeError("offsets must be int32, got %s" % offsets.dtype)
+    T = geom.num_tiles
+    shp = tuple(offsets.shape)
+    if not (shp == (T, 3) or shp == (H, T, 3) or (len(shp) == 4 and shp[1:] == (H, T, 3) and shp[0] >= 1)):
+        raise ValueError("offsets must be [T, 3], [H, T, 3] or [B, H, T, 3] with T = %d tiles and H = %d windows, "
+                         "got %s" % (T, H, shp))
+    if not offsets.is_contiguous():
+        raise ValueError("offsets must be contiguous")
+    if offsets.device != _device(device):
+        raise ValueError("offsets are on %s, the index on %s" % (offsets.device, _device(device)))
+
+
 # ------------------------------------------------- allocation helpers --
 
 class StaIndex:
@@ -272,6 +341,10 @@ class StaIndex:
     b*H + h serving (b, h)); border: 'shift' or 'truncate'."""
 
     def __init__(self, geom, windows, offsets=None, device="cuda", transposed=True, stream=None, border="shift"):
+        if offsets is not None:
+            _check_offsets(offsets, geom, len(windows), device)
+        if torch.device(device).type != "cuda":
+            raise ValueError("the index is built on a GPU device, not %s" % device)
         self.batch = 1
         if offsets is not None and offsets.dim() == 4:
             self.batch = offsets.shape[0]
@@ -313,7 +386,7 @@ def window_shifts(q, k, geom, windows, radius, scale=None, border="shift", per_b
     tile order, or raster order with layout="raster"): int32 [H, num_tiles,
     3] or [B, H, num_tiles, 3], ready for StaIndex(..., offsets=...)."""
     B, H, S, D = q.shape
-    assert S == geom.tokens + n_text and k.shape == q.shape
+    _check_attn(geom, n_text, [("q", q), ("k", k)])
     scale = D ** -0.5 if scale is None else scale
     shape = (B, H, geom.num_tiles, 3) if per_batch else (H, geom.num_tiles, 3)
     out = torch.empty(shape, dtype=torch.int32, device=q.device)
@@ -341,8 +414,8 @@ def forward(q, k, v, geom, index, scale=None, stream=None, n_text=0, precision="
     "fp8" runs the quantized products (INT8 QK^T, FP8 PV; bf16 tensors).
     layout "raster": every tensor holds the video rows in raster token order
     (no reorder needed; grids the tile divides, no text rows)."""
+    _check_attn(geom, n_text, [("q", q), ("k", k), ("v", v)], index=index)
     B, H, S, D = q.shape
-    assert S == geom.tokens + n_text
     scale = D ** -0.5 if scale is None else scale
     o = torch.empty_like(q)
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
@@ -353,8 +426,8 @@ def forward(q, k, v, geom, index, scale=None, stream=None, n_text=0, precision="
 
 def backward(q, k, v, o, lse, dout, geom, index, scale=None, stream=None, n_text=0, layout="tile"):
     """Gradients (dq, dk, dv) of forward(); same layout as forward()."""
+    _check_attn(geom, n_text, [("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)], lse, index)
     B, H, S, D = q.shape
-    assert S == geom.tokens + n_text
     scale = D ** -0.5 if scale is None else scale
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
