@@ -41,8 +41,14 @@
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library never synchronises or prints; the only memory it obtains is
- *     the stream-ordered workspace of the bf16 forward (see sta_fwd).
+ *     library never synchronises or prints.  Three calls take temporary
+ *     device memory: the bf16 forward (V^T tiles, see sta_fwd), the
+ *     quantized forward (codes and scales, see sta_fwd_ex) and
+ *     sta_window_shifts (tile means).  They take it stream-ordered
+ *     (hipMallocFromPoolAsync / hipFreeAsync on the call's stream) from one
+ *     memory pool per device, created on first use and kept, with the
+ *     memory it holds, until the process ends; a failed allocation returns
+ *     STA_ERR_HIP before anything is launched.
  *   - Work is enqueued on the given HIP stream (0 = the null stream) and
  *     is asynchronous; device faults surface at the caller's next sync.
  *   - Arguments are checked on the host before anything is launched: on
@@ -54,8 +60,10 @@
  *     (sta_layout), 16-byte aligned, not aliasing each other.
  *   - An index holds one list set per head, shared by every batch item, or
  *     one per (b, h) for windows shifted per batch item (see sta_index).
- *   - Thread-safe: no mutable global state apart from a thread-local
- *     error message.
+ *   - Thread-safe.  Mutable global state: a thread-local error message,
+ *     and the table of per-device workspace pools, whose creation is
+ *     guarded by a mutex (the pools themselves are HIP objects, safe to use
+ *     from several threads and streams).
  */
 #ifndef LIBSTA_H
 #define LIBSTA_H

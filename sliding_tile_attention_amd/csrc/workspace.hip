@@ -1,5 +1,6 @@
 // Stream-ordered device workspace for kernels that need a temporary buffer
-// (the forward's transposed V tiles).  Each device gets one memory pool of
+// (the bf16 forward's transposed V tiles, the quantized forward's codes, the
+// window-shift producer's tile means).  Each device gets one memory pool of
 // its own whose release threshold is unlimited: memory freed on a stream
 // goes back to the pool, not to the driver, so a steady-state caller that
 // repeats a shape allocates from the driver only on its first call.  The
