@@ -434,6 +434,29 @@ sta_status sta_window_shifts(const void *q, const void *k, int32_t B, int32_t H,
                              const sta_dim3 *radius, const sta_shift_opts *opts, int32_t *offsets_dev,
                              hipStream_t stream);
 
+/*
+ * sta_window_shifts for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, rule, outputs and errors as
+ * sta_window_shifts, and the same kernels; the tile means live in a static
+ * device array of 16 MiB instead of pool workspace, so the call allocates
+ * and frees nothing.  That array (one per GPU, held from the library's
+ * first use on that GPU until the process ends) limits a call to
+ * 2 * P * H * num_tiles * D * 4 <= 16 MiB (P = B if per_batch, else 1; the
+ * 720P shape, 24 heads of 300 tiles at D = 128, fits up to P = 2):
+ * STA_ERR_UNSUPPORTED beyond it, before anything is launched.  Every call on
+ * a GPU shares that GPU's array, which keeps the last call's contents (each
+ * call writes every value it reads, so nothing needs clearing): calls that
+ * overlap on one GPU (on different streams, or from different threads
+ * without ordering) race on it and give undefined results.  The first call
+ * on a GPU looks the array's address up (hipGetSymbolAddress, with that GPU
+ * made current for the lookup and the previous device restored).
+ */
+sta_status sta_window_shifts_noalloc(const void *q, const void *k, int32_t B, int32_t H, int32_t D,
+                                     sta_dtype dtype, float scale, const sta_geom *g,
+                                     const sta_dim3 *windows_host, const sta_dim3 *radius,
+                                     const sta_shift_opts *opts, int32_t *offsets_dev, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,7 @@ STA_LAYOUT_TILE, STA_LAYOUT_RASTER = 0, 1
 _LAYOUTS = {"tile": STA_LAYOUT_TILE, "raster": STA_LAYOUT_RASTER}
 EXPORTS = ("sta_status_str", "sta_last_error", "sta_version", "sta_index_dims", "sta_index_dims_ex",
            "sta_tile_reorder", "sta_tile_reorder_ex", "sta_build_index", "sta_build_index_ex", "sta_fwd",
-           "sta_fwd_ex", "sta_bwd", "sta_bwd_parts", "sta_bwd_ex", "sta_window_shifts")
+           "sta_fwd_ex", "sta_bwd", "sta_bwd_parts", "sta_bwd_ex", "sta_window_shifts", "sta_window_shifts_noalloc")
 
 
 class StaError(RuntimeError):
@@ -100,6 +100,7 @@ def _load():
         "sta_bwd_ex": (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, I32, I32, I32, ctypes.c_int, F32, G, X,
                                       I32, AO, P]),
         "sta_window_shifts": (ctypes.c_int, [P, P, I32, I32, I32, ctypes.c_int, F32, G, W, W, SO, P, P]),
+        "sta_window_shifts_noalloc": (ctypes.c_int, [P, P, I32, I32, I32, ctypes.c_int, F32, G, W, W, SO, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -249,17 +250,19 @@ def sta_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, scal
 
 
 def sta_window_shifts(q, k, B, H, D, dtype, scale, geom, windows, radius, offsets, border="shift", per_batch=False,
-                      n_text=0, stream=None, layout=STA_LAYOUT_TILE):
+                      n_text=0, stream=None, layout=STA_LAYOUT_TILE, noalloc=False):
     """offsets: int32 device tensor [H, num_tiles, 3] ([B, H, num_tiles, 3]
-    with per_batch), written by the call."""
+    with per_batch), written by the call.  noalloc=True calls
+    sta_window_shifts_noalloc (static scratch, no allocation)."""
     w, nw = _windows(windows)
     if nw != H:
         raise ValueError("need one window per head")
     r = sta_dim3(*[int(x) for x in radius])
     opts = sta_shift_opts(STA_BORDER_TRUNCATE if border == "truncate" else STA_BORDER_SHIFT if border == "shift"
                           else -1, int(bool(per_batch)), int(n_text), int(layout))
-    _check(lib.sta_window_shifts(_ptr(q), _ptr(k), B, H, D, dtype, float(scale), ctypes.byref(geom.c()), w,
-                                 ctypes.byref(r), ctypes.byref(opts), _ptr(offsets), _stream(stream)))
+    fn = lib.sta_window_shifts_noalloc if noalloc else lib.sta_window_shifts
+    _check(fn(_ptr(q), _ptr(k), B, H, D, dtype, float(scale), ctypes.byref(geom.c()), w, ctypes.byref(r),
+              ctypes.byref(opts), _ptr(offsets), _stream(stream)))
 
 
 # ------------------------------------------------- argument checks --
@@ -380,7 +383,7 @@ def _dtype_code(t):
 
 
 def window_shifts(q, k, geom, windows, radius, scale=None, border="shift", per_batch=False, n_text=0, stream=None,
-                  layout="tile"):
+                  layout="tile", noalloc=False):
     """Window shift of every query tile (and head, and batch item with
     per_batch) chosen on device from q, k [B,H,N+n_text,D] (video rows in
     tile order, or raster order with layout="raster"): int32 [H, num_tiles,
@@ -391,7 +394,7 @@ def window_shifts(q, k, geom, windows, radius, scale=None, border="shift", per_b
     shape = (B, H, geom.num_tiles, 3) if per_batch else (H, geom.num_tiles, 3)
     out = torch.empty(shape, dtype=torch.int32, device=q.device)
     sta_window_shifts(q, k, B, H, D, _dtype_code(q), scale, geom, windows, radius, out, border, per_batch, n_text,
-                      stream, _LAYOUTS[layout])
+                      stream, _LAYOUTS[layout], noalloc)
     return out
 
 

@@ -235,6 +235,82 @@ static_assert(sizeof(sta_status) == 4 && sizeof(sta_dtype) == 4 && sizeof(sta_bo
                   sizeof(sta_bwd_part) == 4 && sizeof(sta_precision) == 4 && sizeof(sta_layout) == 4,
               "ABI enums are 32-bit");
 
+static const int64_t kMaxShiftCandidates = 4096;
+static const int64_t kMaxShiftRegion = 8192;
+
+// Argument checks shared by sta_window_shifts and its allocation-free
+// variant: fills the geometry, windows (thread-local [H][3]), radius and the
+// largest search region.
+static sta_status check_window_shifts(const void *q, const void *k, int32_t B, int32_t H, int32_t D,
+                                      sta_dtype dtype, float scale, const sta_geom *g, const sta_dim3 *windows_host,
+                                      const sta_dim3 *radius, const sta_shift_opts *opts, int32_t *offsets_dev,
+                                      Geo &geo, sta_shift_opts &o, const int32_t *&wins_out, int r[3],
+                                      int64_t &region)
+{
+    sta_status st = make_geo(g, geo);
+    if (st != STA_OK) return st;
+    o = opts ? *opts : sta_shift_opts{0, 0, 0, 0};
+    if (o.border != STA_BORDER_SHIFT && o.border != STA_BORDER_TRUNCATE)
+        return fail(STA_ERR_INVALID, "unknown border rule %d", o.border);
+    if (o.per_batch != 0 && o.per_batch != 1)
+        return fail(STA_ERR_INVALID, "per_batch must be 0 or 1 (got %d)", o.per_batch);
+    sta_attn_opts text = {o.n_text, STA_PREC_DEFAULT, STA_LAYOUT_TILE};
+    if ((st = add_text(geo, &text)) != STA_OK) return st;
+    if ((st = set_layout(geo, o.layout, false)) != STA_OK) return st;
+    if (B <= 0 || H <= 0 || D <= 0)
+        return fail(STA_ERR_INVALID, "B, H and D must be positive (B=%d H=%d D=%d)", B, H, D);
+    if (dtype != STA_BF16 && dtype != STA_F32)
+        return fail(STA_ERR_INVALID, "unknown dtype %d", (int)dtype);
+    if (!(scale > 0.0f) || !isfinite(scale))
+        return fail(STA_ERR_INVALID, "scale must be positive and finite");
+    if (!windows_host || !radius)
+        return fail(STA_ERR_INVALID, "windows and radius must be non-NULL");
+    if (radius->t < 0 || radius->h < 0 || radius->w < 0)
+        return fail(STA_ERR_INVALID, "radius must be >= 0 on every axis (%d,%d,%d)", radius->t, radius->h,
+                    radius->w);
+    if (!q || !k || !offsets_dev)
+        return fail(STA_ERR_INVALID, "q, k and offsets must be non-NULL");
+    if (!aligned16(q) || !aligned16(k))
+        return fail(STA_ERR_INVALID, "q and k must be 16-byte aligned");
+    if (D != 64 && D != 128)
+        return fail(STA_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", D);
+    if ((int64_t)B * H * geo.S * D > ((int64_t)1 << 40))
+        return fail(STA_ERR_UNSUPPORTED, "tensor too large");
+    const int64_t ncand = (2LL * radius->t + 1) * (2LL * radius->h + 1) * (2LL * radius->w + 1);
+    if (ncand > kMaxShiftCandidates)
+        return fail(STA_ERR_UNSUPPORTED, "%lld candidate shifts (at most %lld)", (long long)ncand,
+                    (long long)kMaxShiftCandidates);
+    if (H > 4096)
+        return fail(STA_ERR_UNSUPPORTED, "more than 4096 heads");
+    static thread_local int32_t wins[3 * 4096];
+    const int n[3] = {geo.nt, geo.nh, geo.nw};
+    r[0] = radius->t;
+    r[1] = radius->h;
+    r[2] = radius->w;
+    region = 0;
+    for (int h = 0; h < H; ++h) {
+        const int w[3] = {windows_host[h].t, windows_host[h].h, windows_host[h].w};
+        int64_t reg = 1;
+        for (int d = 0; d < 3; ++d) {
+            if (w[d] < 1)
+                return fail(STA_ERR_INVALID, "window of head %d must be >= 1 on every axis (%d,%d,%d)", h, w[0],
+                            w[1], w[2]);
+            const int64_t span = (int64_t)w[d] + 2LL * r[d];
+            reg *= span < n[d] ? span : n[d];
+            wins[3 * h + d] = w[d];
+        }
+        region = reg > region ? reg : region;
+    }
+    if (region > kMaxShiftRegion)
+        return fail(STA_ERR_UNSUPPORTED, "search region of %lld tiles (at most %lld)", (long long)region,
+                    (long long)kMaxShiftRegion);
+    const int64_t P = o.per_batch ? B : 1;
+    if (!grid_fits(2 * P * H * geo.T, 256) || !grid_fits(P * 64 * geo.T, 256))
+        return fail(STA_ERR_UNSUPPORTED, "launch too large");
+    wins_out = wins;
+    return STA_OK;
+}
+
 extern "C" {
 
 const char *sta_status_str(sta_status s)
@@ -441,8 +517,6 @@ sta_status sta_bwd(const void *q, const void *k, const void *v, const void *o, c
 }
 
 // Largest candidate count and search region of the window-shift producer.
-static const int64_t kMaxShiftCandidates = 4096;
-static const int64_t kMaxShiftRegion = 8192;
 
 sta_status sta_window_shifts(const void *q, const void *k, int32_t B, int32_t H, int32_t D, sta_dtype dtype,
                              float scale, const sta_geom *g, const sta_dim3 *windows_host,
@@ -450,66 +524,32 @@ sta_status sta_window_shifts(const void *q, const void *k, int32_t B, int32_t H,
                              hipStream_t stream)
 {
     Geo geo;
-    sta_status st = make_geo(g, geo);
+    sta_shift_opts o;
+    const int32_t *wins;
+    int r[3];
+    int64_t region;
+    const sta_status st = check_window_shifts(q, k, B, H, D, dtype, scale, g, windows_host, radius, opts,
+                                              offsets_dev, geo, o, wins, r, region);
     if (st != STA_OK) return st;
-    const sta_shift_opts o = opts ? *opts : sta_shift_opts{0, 0, 0, 0};
-    if (o.border != STA_BORDER_SHIFT && o.border != STA_BORDER_TRUNCATE)
-        return fail(STA_ERR_INVALID, "unknown border rule %d", o.border);
-    if (o.per_batch != 0 && o.per_batch != 1)
-        return fail(STA_ERR_INVALID, "per_batch must be 0 or 1 (got %d)", o.per_batch);
-    sta_attn_opts text = {o.n_text, STA_PREC_DEFAULT, STA_LAYOUT_TILE};
-    if ((st = add_text(geo, &text)) != STA_OK) return st;
-    if ((st = set_layout(geo, o.layout, false)) != STA_OK) return st;
-    if (B <= 0 || H <= 0 || D <= 0)
-        return fail(STA_ERR_INVALID, "B, H and D must be positive (B=%d H=%d D=%d)", B, H, D);
-    if (dtype != STA_BF16 && dtype != STA_F32)
-        return fail(STA_ERR_INVALID, "unknown dtype %d", (int)dtype);
-    if (!(scale > 0.0f) || !isfinite(scale))
-        return fail(STA_ERR_INVALID, "scale must be positive and finite");
-    if (!windows_host || !radius)
-        return fail(STA_ERR_INVALID, "windows and radius must be non-NULL");
-    if (radius->t < 0 || radius->h < 0 || radius->w < 0)
-        return fail(STA_ERR_INVALID, "radius must be >= 0 on every axis (%d,%d,%d)", radius->t, radius->h,
-                    radius->w);
-    if (!q || !k || !offsets_dev)
-        return fail(STA_ERR_INVALID, "q, k and offsets must be non-NULL");
-    if (!aligned16(q) || !aligned16(k))
-        return fail(STA_ERR_INVALID, "q and k must be 16-byte aligned");
-    if (D != 64 && D != 128)
-        return fail(STA_ERR_UNSUPPORTED, "head dim %d not supported (64 or 128)", D);
-    if ((int64_t)B * H * geo.S * D > ((int64_t)1 << 40))
-        return fail(STA_ERR_UNSUPPORTED, "tensor too large");
-    const int64_t ncand = (2LL * radius->t + 1) * (2LL * radius->h + 1) * (2LL * radius->w + 1);
-    if (ncand > kMaxShiftCandidates)
-        return fail(STA_ERR_UNSUPPORTED, "%lld candidate shifts (at most %lld)", (long long)ncand,
-                    (long long)kMaxShiftCandidates);
-    if (H > 4096)
-        return fail(STA_ERR_UNSUPPORTED, "more than 4096 heads");
-    static thread_local int32_t wins[3 * 4096];
-    const int n[3] = {geo.nt, geo.nh, geo.nw};
-    const int r[3] = {radius->t, radius->h, radius->w};
-    int64_t region = 0;
-    for (int h = 0; h < H; ++h) {
-        const int w[3] = {windows_host[h].t, windows_host[h].h, windows_host[h].w};
-        int64_t reg = 1;
-        for (int d = 0; d < 3; ++d) {
-            if (w[d] < 1)
-                return fail(STA_ERR_INVALID, "window of head %d must be >= 1 on every axis (%d,%d,%d)", h, w[0],
-                            w[1], w[2]);
-            const int64_t span = (int64_t)w[d] + 2LL * r[d];
-            reg *= span < n[d] ? span : n[d];
-            wins[3 * h + d] = w[d];
-        }
-        region = reg > region ? reg : region;
-    }
-    if (region > kMaxShiftRegion)
-        return fail(STA_ERR_UNSUPPORTED, "search region of %lld tiles (at most %lld)", (long long)region,
-                    (long long)kMaxShiftRegion);
-    const int64_t P = o.per_batch ? B : 1;
-    if (!grid_fits(2 * P * H * geo.T, 256) || !grid_fits(P * 64 * geo.T, 256))
-        return fail(STA_ERR_UNSUPPORTED, "launch too large");
     return launch_window_shifts(q, k, B, H, D, dtype, scale, geo, wins, r, o.border == STA_BORDER_TRUNCATE,
                                 o.per_batch == 1, (int)region, offsets_dev, stream);
+}
+
+sta_status sta_window_shifts_noalloc(const void *q, const void *k, int32_t B, int32_t H, int32_t D,
+                                     sta_dtype dtype, float scale, const sta_geom *g,
+                                     const sta_dim3 *windows_host, const sta_dim3 *radius,
+                                     const sta_shift_opts *opts, int32_t *offsets_dev, hipStream_t stream)
+{
+    Geo geo;
+    sta_shift_opts o;
+    const int32_t *wins;
+    int r[3];
+    int64_t region;
+    const sta_status st = check_window_shifts(q, k, B, H, D, dtype, scale, g, windows_host, radius, opts,
+                                              offsets_dev, geo, o, wins, r, region);
+    if (st != STA_OK) return st;
+    return launch_window_shifts_scratch(q, k, B, H, D, dtype, scale, geo, wins, r, o.border == STA_BORDER_TRUNCATE,
+                                        o.per_batch == 1, (int)region, offsets_dev, stream);
 }
 
 }  // extern "C"

@@ -232,6 +232,14 @@ sta_status launch_window_shifts(const void *q, const void *k, int B, int H, int 
                                 const Geo &g, const int32_t *windows, const int radius[3], bool truncate,
                                 bool per_batch, int region_max, int32_t *offsets, hipStream_t s);
 
+// As launch_window_shifts, with the tile means in a static device scratch
+// array of fixed size instead of pool workspace (no allocation);
+// STA_ERR_UNSUPPORTED when they do not fit.
+sta_status launch_window_shifts_scratch(const void *q, const void *k, int B, int H, int D, sta_dtype dtype,
+                                        float scale, const Geo &g, const int32_t *windows, const int radius[3],
+                                        bool truncate, bool per_batch, int region_max, int32_t *offsets,
+                                        hipStream_t s);
+
 // Stream-ordered device workspace (per-device pool that keeps freed memory
 // for reuse); the buffer may be used by work queued on `s` until the
 // matching workspace_free on the same stream.

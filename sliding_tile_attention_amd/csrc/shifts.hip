@@ -33,6 +33,9 @@
 #include <limits.h>
 #include <math.h>
 
+#include <mutex>
+#include <type_traits>
+
 #include "common.h"
 
 namespace sta {
@@ -291,16 +294,21 @@ __global__ __launch_bounds__(kThreads) void shift_kernel(const float *__restrict
     }
 }
 
+// Bytes of tile means the producer keeps: [2][P][H][T][D] fp32.
+static size_t means_bytes(int B, int H, int D, const Geo &g, bool per_batch)
+{
+    return (size_t)2 * (per_batch ? B : 1) * H * g.T * D * sizeof(float);
+}
+
+// The two launches on a means buffer of means_bytes() (every value is
+// written by the first before the second reads it).
 template <int D, typename E>
 sta_status run_shifts(const E *q, const E *k, int B, int H, float scale, const Geo &g, const int32_t *windows,
                       const int radius[3], bool truncate, bool per_batch, int region_max, int32_t *offsets,
-                      hipStream_t s)
+                      float *means, hipStream_t s)
 {
     const int P = per_batch ? B : 1, nb = per_batch ? 1 : B;
-    float *means = nullptr;
-    const size_t bytes = (size_t)2 * P * H * g.T * D * sizeof(float);
-    sta_status st = workspace_alloc((void **)&means, bytes, s);
-    if (st != STA_OK) return st;
+    sta_status st = STA_OK;
     const int64_t mean_blocks = (int64_t)2 * P * H * g.T;
     hipLaunchKernelGGL((tile_mean_kernel<D, E>), dim3((unsigned)mean_blocks), dim3(kThreads), 0, s, q, k, means,
                        H, P, nb, g);
@@ -316,8 +324,56 @@ sta_status run_shifts(const E *q, const E *k, int B, int H, float scale, const G
                            radius[2], truncate, scale, offsets);
         st = check_launch();
     }
-    const sta_status fr = workspace_free(means, s);
-    return st != STA_OK ? st : fr;
+    return st;
+}
+
+template <typename F>
+sta_status dispatch(int D, sta_dtype dtype, const void *q, const void *k, F &&run)
+{
+    if (dtype == STA_BF16) {
+        if (D == 128) return run(std::integral_constant<int, 128>{}, (const __bf16 *)q, (const __bf16 *)k);
+        return run(std::integral_constant<int, 64>{}, (const __bf16 *)q, (const __bf16 *)k);
+    }
+    if (D == 128) return run(std::integral_constant<int, 128>{}, (const float *)q, (const float *)k);
+    return run(std::integral_constant<int, 64>{}, (const float *)q, (const float *)k);
+}
+
+// Scratch of the allocation-free producer: room for the tile means of one
+// call of up to kShiftScratchBytes (16 MiB: the 720P shape, 24 heads of 300
+// tiles at D = 128, for up to two batch items with per-item shifts).  Every
+// GPU the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// host code uses only the per-device address from hipGetSymbolAddress.
+constexpr size_t kShiftScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) float scratch[kShiftScratchBytes / sizeof(float)];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch[kMaxScratchDevices];
+
+// Device address of `scratch` on the device of stream s, looked up once per
+// device with that device current (restored afterwards).
+sta_status scratch_for(hipStream_t s, float *&ptr)
+{
+    hipDevice_t dev = 0;
+    hipError_t e = hipStreamGetDevice(s, &dev);
+    if (e != hipSuccess) return fail(STA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices) return fail(STA_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return fail(STA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(STA_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(e));
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return fail(STA_ERR_HIP, "hipGetSymbolAddress: %s", hipGetErrorString(e));
+        if (back != hipSuccess) return fail(STA_ERR_HIP, "hipSetDevice: %s", hipGetErrorString(back));
+        g_scratch[dev] = (float *)p;
+    }
+    ptr = g_scratch[dev];
+    return STA_OK;
 }
 
 }  // namespace
@@ -326,18 +382,33 @@ sta_status launch_window_shifts(const void *q, const void *k, int B, int H, int 
                                 const Geo &g, const int32_t *windows, const int radius[3], bool truncate,
                                 bool per_batch, int region_max, int32_t *offsets, hipStream_t s)
 {
-    if (dtype == STA_BF16) {
-        if (D == 128)
-            return run_shifts<128>((const __bf16 *)q, (const __bf16 *)k, B, H, scale, g, windows, radius, truncate,
-                                   per_batch, region_max, offsets, s);
-        return run_shifts<64>((const __bf16 *)q, (const __bf16 *)k, B, H, scale, g, windows, radius, truncate,
-                              per_batch, region_max, offsets, s);
-    }
-    if (D == 128)
-        return run_shifts<128>((const float *)q, (const float *)k, B, H, scale, g, windows, radius, truncate,
-                               per_batch, region_max, offsets, s);
-    return run_shifts<64>((const float *)q, (const float *)k, B, H, scale, g, windows, radius, truncate, per_batch,
-                          region_max, offsets, s);
+    float *means = nullptr;
+    sta_status st = workspace_alloc((void **)&means, means_bytes(B, H, D, g, per_batch), s);
+    if (st != STA_OK) return st;
+    st = dispatch(D, dtype, q, k, [&](auto dc, auto qp, auto kp) {
+        return run_shifts<decltype(dc)::value>(qp, kp, B, H, scale, g, windows, radius, truncate, per_batch,
+                                               region_max, offsets, means, s);
+    });
+    const sta_status fr = workspace_free(means, s);
+    return st != STA_OK ? st : fr;
+}
+
+sta_status launch_window_shifts_scratch(const void *q, const void *k, int B, int H, int D, sta_dtype dtype,
+                                        float scale, const Geo &g, const int32_t *windows, const int radius[3],
+                                        bool truncate, bool per_batch, int region_max, int32_t *offsets,
+                                        hipStream_t s)
+{
+    const size_t bytes = means_bytes(B, H, D, g, per_batch);
+    if (bytes > kShiftScratchBytes)
+        return fail(STA_ERR_UNSUPPORTED, "tile means of %zu bytes exceed the %zu-byte scratch of the allocation-free "
+                                         "call (2 * P * H * num_tiles * D * 4 bytes)", bytes, kShiftScratchBytes);
+    float *means = nullptr;
+    const sta_status st = scratch_for(s, means);
+    if (st != STA_OK) return st;
+    return dispatch(D, dtype, q, k, [&](auto dc, auto qp, auto kp) {
+        return run_shifts<decltype(dc)::value>(qp, kp, B, H, scale, g, windows, radius, truncate, per_batch,
+                                               region_max, offsets, means, s);
+    });
 }
 
 }  // namespace sta

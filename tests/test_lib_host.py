@@ -340,6 +340,30 @@ def test_window_shifts_rejects_bad_arguments():
     assert st == sta.STA_ERR_INVALID
 
 
+def test_window_shifts_noalloc_checks_before_launching():
+    """The allocation-free producer takes the same argument checks, and
+    rejects tile means beyond its 16 MiB scratch before anything runs: the
+    720P shape (24 heads of 300 tiles, D = 128) fits for up to 2 batch items
+    with per-item shifts, not for 3; without per-item shifts the means are
+    pooled and any batch fits."""
+    geom = sta.Geometry((30, 48, 80), (6, 8, 8))
+
+    def call(B, per_batch, **kw):
+        a = dict(q=_fake(), D=128, windows=[(3, 3, 5)] * 24)
+        a.update(kw)
+        sta.sta_window_shifts(a["q"], _fake(), B, 24, a["D"], sta.STA_BF16, 0.088, geom, a["windows"],
+                              (1, 1, 1), _fake(), "shift", per_batch, 0, 0, noalloc=True)
+    for kw, status in ((dict(q=None), sta.STA_ERR_INVALID), (dict(D=96), sta.STA_ERR_UNSUPPORTED),
+                       (dict(windows=[(3, 0, 5)] * 24), sta.STA_ERR_INVALID)):
+        with pytest.raises(sta.StaError) as e:
+            call(1, False, **kw)
+        assert e.value.status == status, kw
+    with pytest.raises(sta.StaError) as e:
+        call(3, True)
+    assert e.value.status == sta.STA_ERR_UNSUPPORTED and "scratch" in str(e.value)
+    assert 2 * 2 * 24 * 300 * 128 * 4 <= 16 << 20 < 2 * 3 * 24 * 300 * 128 * 4
+
+
 def test_layout_option_checks():
     """Raster layout: unknown values are malformed; grids the tile does not
     divide, text rows, and bf16 tiles whose rows the 32-row copy pattern
