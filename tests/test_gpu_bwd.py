@@ -101,52 +101,140 @@ def test_bwd_f32_offsets_d128():
         assert_close(to_host(got), ref, "f32", nm)
 
 
-def test_bwd_720p_training_sampled():
-    """Training workload at full size (115200 tokens, 24 heads, window 3x3x5):
-    the whole forward + backward runs on the GPU in the benchmark's launch
-    configuration; sampled dQ rows and sampled dK/dV rows (from the least and
-    the most attended key tiles) are checked against the oracle, and two
-    exact identities are checked on the whole tensors."""
-    w = workload("720p-train")
-    say("bwd bf16 720p-train workload (full size)")
-    layer = Layer(w["grid"], w["tile"], w["windows"], None, w["q"], w["k"], w["v"], "bf16", dout=w["dout"])
+def _identities(dq, dk, dv, dout, what):
+    """Whole-tensor identities (rows of P sum to 1, rows of dS to 0): per
+    (b, h), sum_j dV_j = sum_i dO_i and sum_j dK_j = 0.  With bf16 storage the
+    residual is of order 2^-9 |dV_j| sqrt(N) per component, tiny next to
+    |sum_i dO_i| ~ sqrt(N); the gates leave a wide margin."""
+    N = dv.shape[2]
+    sdv = dv.float().sum(2)
+    sdo = torch.from_numpy(dout).cuda().sum(2)
+    rel = (torch.linalg.norm(sdv - sdo) / torch.linalg.norm(sdo)).item()
+    assert rel < 1e-3, "%s: sum dV vs sum dO: rel %.2e" % (what, rel)
+    sdk = dk.float().sum(2)
+    scale_k = torch.sqrt((dk.float() ** 2).sum(2) * N).clamp_min(1e-30)   # |sum| if all rows aligned
+    worst = (sdk.abs() / scale_k).max().item()
+    assert worst < 1e-2, "%s: sum dK: %.2e" % (what, worst)
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t).all()
+
+
+def _tile_rows(inv, h, N, L, t, slots):
+    """Flat row ids (head h, batch 0) of tile-order slots of tile t."""
+    return [h * N + int(inv[t * L + x]) for x in slots]
+
+
+def _check_rows(w, dq, dk, dv, qrows, krows, what, offsets=None):
+    """dQ on qrows, dK and dV on krows, against the oracle."""
+    B, H, N, D = w["q"].shape
+    qrows, krows = np.array(qrows, np.int64), np.array(krows, np.int64)
+    say("%s: oracle on %d dQ rows, %d dK/dV rows" % (what, len(qrows), len(krows)))
+    rq, rk, rv = oracle.bwd(w["q"], w["k"], w["v"], w["dout"], w["grid"], w["tile"], w["windows"], offsets,
+                            qrows=qrows, krows=krows)
+    pick = lambda t, rows: to_host(t.reshape(-1, D)[torch.from_numpy(rows).cuda()])
+    assert_close(pick(dq, qrows), rq, "bf16", what + " dQ")
+    assert_close(pick(dk, krows), rk, "bf16", what + " dK")
+    assert_close(pick(dv, krows), rv, "bf16", what + " dV")
+
+
+def _run(w, offsets=None):
+    layer = Layer(w["grid"], w["tile"], w["windows"], offsets, w["q"], w["k"], w["v"], "bf16", dout=w["dout"])
     layer.forward()
     dq, dk, dv = layer.backward()
     torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def test_bwd_720p_training_sampled():
+    """Training workload at full size (115200 tokens, 24 heads, window 3x3x5)
+    in the benchmark's launch configuration.  dQ: rows of the 8 corner tiles
+    and one seeded tile in every head.  dK/dV: the whole key tiles 0 (12
+    query tiles attend it) and (2,2,4) = 144 (140 attend it) in heads 3 and
+    17.  Plus the whole-tensor identities."""
+    w = workload("720p-train")
+    say("bwd bf16 720p-train workload (full size)")
+    dq, dk, dv = _run(w)
     B, H, N, D = w["q"].shape
     L = 384
     inv = np.argsort(oracle.perm(w["grid"], w["tile"]))          # tile-order slot -> raster token
     g = np.random.default_rng(55)
-    # dQ: 3 heads x (2 corner tiles + 1 random tile) x 4 rows
+    corners = [0, 9, 50, 59, 240, 249, 290, 299]                 # tile grid 5 x 6 x 10
     qrows = []
-    for h in (0, 11, 23):
-        for t in (0, 299, int(g.integers(0, 300))):
-            qrows += [h * N + int(inv[t * L + s]) for s in g.choice(L, 4, replace=False)]
-    # dK/dV: head 3, key tile 0 (12 query tiles attend it) and tile (2,2,4)=144 (140 attend it)
+    for h in range(H):
+        for t in corners + [int(g.integers(0, 300))]:
+            qrows += _tile_rows(inv, h, N, L, t, g.choice(L, 2, replace=False))
     krows = []
-    for t in (0, 144):
-        krows += [3 * N + int(inv[t * L + s]) for s in g.choice(L, 3, replace=False)]
-    qrows, krows = np.array(qrows, np.int64), np.array(krows, np.int64)
-    say("oracle: %d dQ rows, %d dK/dV rows" % (len(qrows), len(krows)))
-    rq, rk, rv = oracle.bwd(w["q"], w["k"], w["v"], w["dout"], w["grid"], w["tile"], w["windows"],
-                            qrows=qrows, krows=krows)
-    pick = lambda t, rows: to_host(t.reshape(-1, D)[torch.from_numpy(rows).cuda()])
-    assert_close(pick(dq, qrows), rq, "bf16", "dQ")
-    assert_close(pick(dk, krows), rk, "bf16", "dK")
-    assert_close(pick(dv, krows), rv, "bf16", "dV")
-    # Identities (rows of P sum to 1, rows of dS to 0): per (b, h)
-    #   sum_j dV_j = sum_i dO_i   and   sum_j dK_j = 0.
-    # With bf16 storage the residual is of order 2^-9 * |dV_j| * sqrt(N) per
-    # component, tiny next to |sum_i dO_i| ~ sqrt(N); gates leave a wide margin.
-    sdv = dv.float().sum(2)
-    sdo = torch.from_numpy(w["dout"]).cuda().sum(2)
-    rel = (torch.linalg.norm(sdv - sdo) / torch.linalg.norm(sdo)).item()
-    assert rel < 1e-3, "sum dV vs sum dO: rel %.2e" % rel
-    sdk = dk.float().sum(2)
-    scale_k = torch.sqrt((dk.float() ** 2).sum(2) * N).clamp_min(1e-30)   # |sum| if all rows aligned
-    assert (sdk.abs() / scale_k).max().item() < 1e-2
-    for t in (dq, dk, dv):
-        assert torch.isfinite(t).all()
+    for h in (3, 17):
+        for t in (0, 144):
+            krows += _tile_rows(inv, h, N, L, t, range(L))
+    _check_rows(w, dq, dk, dv, qrows, krows, "720p-train")
+    _identities(dq, dk, dv, w["dout"], "720p-train")
+
+
+def test_bwd_mid_7680():
+    """The mid workload (7680 tokens, 24 heads, D 128, tile (4,8,8), window
+    3x3x3 on a 2x3x5 tile grid): heads 0 and 1 in full, and in every head
+    dQ rows of two seeded tiles and dK/dV rows of one seeded key tile.  Plus
+    the whole-tensor identities."""
+    w = workload("mid-7680", with_dout=True)
+    say("bwd bf16 mid-7680 workload")
+    dq, dk, dv = _run(w)
+    B, H, N, D = w["q"].shape
+    sl = lambda x: x[:, :2]
+    rq, rk, rv = oracle.bwd(sl(w["q"]), sl(w["k"]), sl(w["v"]), sl(w["dout"]), w["grid"], w["tile"],
+                            w["windows"][:2])
+    for got, ref, nm in ((dq, rq, "dQ"), (dk, rk, "dK"), (dv, rv, "dV")):
+        assert_close(to_host(got[:, :2]), ref, "bf16", "mid-7680 heads 0-1 " + nm)
+    L = 256
+    inv = np.argsort(oracle.perm(w["grid"], w["tile"]))
+    g = np.random.default_rng(56)
+    qrows, krows = [], []
+    for h in range(H):
+        for t in g.choice(30, 2, replace=False):
+            qrows += _tile_rows(inv, h, N, L, int(t), g.choice(L, 4, replace=False))
+        krows += _tile_rows(inv, h, N, L, int(g.integers(0, 30)), g.choice(L, 8, replace=False))
+    _check_rows(w, dq, dk, dv, qrows, krows, "mid-7680")
+    _identities(dq, dk, dv, w["dout"], "mid-7680")
+
+
+def test_bwd_720p_shifted_perhead():
+    """The shifted, per-head-window workload at full size (115200 tokens, 24
+    heads with windows 3x3x3, 3x3x5 or 5x5x5 tiles, a seeded shift per query
+    tile) through the backward: dQ rows of corner and seeded tiles in three
+    heads of every window class; dK/dV on whole key tiles: the least and the
+    most attended under the shifts for a 3x3x3 head (6 and 85 query tiles),
+    the least attended for a 3x3x5 head (9) and a 5x5x5 head (41).  (The
+    oracle forms the statistics of every query row attending a key tile:
+    the most attended tiles of the wider windows, 141 and 211 query tiles,
+    would take it minutes; the training test covers a 140-attendee tile.)
+    Plus the whole-tensor identities."""
+    w = workload("720p-shifted-perhead", with_dout=True)
+    say("bwd bf16 720p-shifted-perhead workload (full size)")
+    off = w["offsets"]
+    dq, dk, dv = _run(w, off)
+    B, H, N, D = w["q"].shape
+    L = 384
+    inv = np.argsort(oracle.perm(w["grid"], w["tile"]))
+    _, _, _, q_cnt = oracle.index(w["grid"], w["tile"], w["windows"], off)
+    classes = {}
+    for h in range(H):
+        classes.setdefault(tuple(int(x) for x in w["windows"][h]), []).append(h)
+    assert sorted(classes) == [(3, 3, 3), (3, 3, 5), (5, 5, 5)]
+    g = np.random.default_rng(57)
+    qrows = []
+    for cls, heads in sorted(classes.items()):
+        for h in heads[:3]:
+            for t in (0, 59, 240, 299, int(g.integers(0, 300))):
+                qrows += _tile_rows(inv, h, N, L, t, g.choice(L, 2, replace=False))
+    krows = []
+    for cls, which in (((3, 3, 3), ("min", "max")), ((3, 3, 5), ("min",)), ((5, 5, 5), ("min",))):
+        h = classes[cls][0]
+        for kind in which:
+            t = int(np.argmin(q_cnt[h]) if kind == "min" else np.argmax(q_cnt[h]))
+            say("  head %d %s: key tile %d attended by %d query tiles" % (h, cls, t, q_cnt[h][t]))
+            krows += _tile_rows(inv, h, N, L, t, range(L))
+    _check_rows(w, dq, dk, dv, qrows, krows, "720p-shifted-perhead", off)
+    _identities(dq, dk, dv, w["dout"], "720p-shifted-perhead")
 
 
 @pytest.mark.parametrize("case", __import__("tests.test_gpu_fwd", fromlist=["OPTION_CASES"]).OPTION_CASES,
