@@ -39,6 +39,12 @@ directly (index; forward; backward).
 the (6,8,8) tile does not divide (its last tile row along H is cut to 5
 rows); counted work then sums len(q) * len(k) over the listed tile pairs.
 
+--workload 720p-shifted-perhead runs the step on the deformable-window
+workload of the same shape: every head draws its window from {3x3x3, 3x3x5,
+5x5x5} tiles and every query tile a seeded window shift in
+[-1,1]x[-2,2]x[-2,2] tiles (tests/inputs.py); the counted work sums the
+tile pairs of the built lists (27, 45 or 125 key tiles per query tile).
+
 Prints ONE JSON line.
 
 HBM traffic of the attention kernels (roofline "traffic") comes from two
@@ -91,6 +97,8 @@ def parse():
                     help="raster: the kernels address raster-order tensors, no reorder passes")
     ap.add_argument("--adaptive", type=str, default=None, metavar="RT,RH,RW",
                     help="choose the window shifts on device (search radius per axis) inside the step")
+    ap.add_argument("--workload", choices=(WORKLOAD, "720p-shifted-perhead"), default=WORKLOAD,
+                    help="720p-shifted-perhead: per-head windows and seeded window shifts (the deformable variant)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc counter_collection.csv files into profiles/traffic.json")
     return ap.parse_args()
@@ -275,7 +283,12 @@ def main():
     fwd_only = args.forward_only
     prec = sta.STA_PREC_FP8 if args.precision == "fp8" else sta.STA_PREC_DEFAULT
     grid = None if args.grid is None else tuple(int(x) for x in args.grid.split(","))
-    w = workload(WORKLOAD, n_text=nt, grid=grid)
+    shifted = args.workload != WORKLOAD
+    if shifted and (nt or grid or args.adaptive or args.layout == "raster"):
+        print("--workload %s takes none of --text, --grid, --adaptive, --layout raster" % args.workload,
+              file=sys.stderr)
+        sys.exit(2)
+    w = workload(args.workload, n_text=nt, grid=grid, with_dout=True)
     B, H, S, D = w["q"].shape
     N = S - nt
     geom = sta.Geometry(tuple(w["grid"]), tuple(w["tile"]))
@@ -292,6 +305,8 @@ def main():
     delta = torch.empty_like(lse)
     radius = None if args.adaptive is None else tuple(int(x) for x in args.adaptive.split(","))
     off = None if radius is None else torch.zeros((H, T, 3), dtype=torch.int32, device=dev)
+    if shifted:                                     # the workload's seeded shifts, shared by the heads
+        off = torch.from_numpy(np.ascontiguousarray(w["offsets"], np.int32)).to(dev)
     idx = sta.StaIndex(geom, windows, off)          # with shifts: per-head capacity
     scale = D ** -0.5
     row_bytes = D * 2
@@ -347,7 +362,7 @@ def main():
             mark()
             sta.sta_build_index_ex(geom, windows, off, idx, "shift", True, stream)
         else:
-            sta.sta_build_index(geom, windows, None, idx, stream)
+            sta.sta_build_index(geom, windows, off, idx, stream)
         mark()
         sta.sta_fwd_ex(qt, kt, vt, ot, lse, B, H, D, sta.STA_BF16, scale, geom, idx, nt, stream, prec)
         mark()
@@ -405,7 +420,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "kernel": dominant,
                 "traffic": measured_traffic(dominant) if nt == 0 and grid is None and prec == sta.STA_PREC_DEFAULT
-                and radius is None and not raster else None,  # the counter passes cover the bf16 video step
+                and radius is None and not raster and not shifted else None,  # counters cover the default step
                 "measured_gemm_ceiling": gemm_ceiling(torch, dev)}
 
     tensor_bytes = B * H * S * D * 2
@@ -424,9 +439,11 @@ def main():
         "dtype": "int8 QK^T + e4m3 PV, bf16 I/O" if prec == sta.STA_PREC_FP8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "720p training step: B=1 H=24 D=128, grid (%d,%d,%d)=%d tokens, tile (6,8,8), "
-                        "window 3x3x5 tiles, %s" % (tuple(geom.grid) + (N, "forward only" if fwd_only else
-                                                                       "forward+backward")) +
+            "workload": ("720p %s: B=1 H=24 D=128, grid (%d,%d,%d)=%d tokens, tile (6,8,8), %s, %s" % (
+                ("deformable-window step" if shifted else "training step",) + tuple(geom.grid) + (N,
+                "per-head windows %s and a seeded shift per query tile (%d head-tile pairs listed)" % (
+                    "/".join("%dx%dx%d" % c for c in sorted(set(windows))), int(kv_cnt.sum()))
+                if shifted else "window 3x3x5 tiles", "forward only" if fwd_only else "forward+backward"))) +
                         ("" if nt == 0 else ", joint with %d text tokens (dense text rows and columns)" % nt) +
                         ("" if radius is None else ", window shifts chosen on device (search radius %s tiles)"
                          % (radius,)) + (", raster layout (no reorder passes)" if raster else ""),
@@ -452,7 +469,8 @@ def main():
         },
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline and grid is None and not fwd_only and radius is None and not raster:   # a sample of the training step
+    if (not args.no_cpu_baseline and grid is None and not fwd_only and radius is None and not raster
+            and not shifted):                                           # a sample of the training step
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows, nt)
     print(json.dumps(out), flush=True)
 

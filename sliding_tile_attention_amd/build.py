@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libsta.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "workspace.hip", "reorder.hip", "index.hip", "attn_f32.hip", "fwd_bf16.hip", "fwd_fp8.hip",
-           "bwd_bf16.hip", "shifts.hip"]
+           "bwd_bf16.hip", "shifts.hip", "schedule.hip"]
 HEADERS = ["common.h", "mfma.h"]
 # Per-source extra compiler flags (none at present).
 EXTRA = {}

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
     __bf16 *__restrict__ dQ, const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt, int max_kv,
-    int IH, Geo g, int rblocks, int total, float scale_log2, float scale)
+    int IH, Geo g, int rblocks, const int *__restrict__ split, float scale_log2, float scale)
 {
     constexpr int THREADS = NW * 64, M = NW * 32, KS = D / 16, KB = BN / 32, DB = D / 32;
     constexpr int BLK = BN * D, STAGE = 2 * BLK;
@@ -244,7 +244,13 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
     };
 
     int bh, qt, rb;
-    decode_item(xcd_remap(blockIdx.x, total), rblocks, g, bh, qt, rb);
+    {
+        // XCD x = block index mod 8 takes the range [split[x], split[x+1]) of
+        // the work order; blocks past it exit
+        const int x = blockIdx.x & 7, work = split[x] + (int)(blockIdx.x >> 3);
+        if (work >= split[x + 1]) return;
+        decode_item(work, rblocks, g, bh, qt, rb);
+    }
     const Span qs = tile_span(g, qt);                // query rows of this tile
     const int qlen = qs.len;
     if (rb * M >= qlen) return;                      // row block past a cut tile's end
@@ -385,7 +391,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
     __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, const int32_t *__restrict__ q_idx,
-    const int32_t *__restrict__ q_cnt, int max_q, int IH, Geo g, int rblocks, int total, float scale_log2,
+    const int32_t *__restrict__ q_cnt, int max_q, int IH, Geo g, int rblocks, const int *__restrict__ split, float scale_log2,
     float scale)
 {
     constexpr int THREADS = NW * 64, M = NW * 32, KS = D / 16, SB = BQ / 32, DB = D / 32;
@@ -402,7 +408,13 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     };
 
     int bh, kt, rb;
-    decode_item(xcd_remap(blockIdx.x, total), rblocks, g, bh, kt, rb);
+    {
+        // XCD x = block index mod 8 takes the range [split[x], split[x+1]) of
+        // the work order; blocks past it exit
+        const int x = blockIdx.x & 7, work = split[x] + (int)(blockIdx.x >> 3);
+        if (work >= split[x + 1]) return;
+        decode_item(work, rblocks, g, bh, kt, rb);
+    }
     const Span ks_ = tile_span(g, kt);               // key rows of this tile
     const int klen = ks_.len;
     if (rb * M >= klen) return;                      // row block past a cut tile's end
@@ -604,41 +616,58 @@ static sta_status run_bwd(const void *q, const void *k, const void *v, const voi
     const int64_t rows = (int64_t)B * H * g.S;
     const int rblocks = (g.L + M - 1) / M;
     const int64_t total = (int64_t)B * H * g.TT * rblocks;
-    if (!grid_fits(total, NW * 64) || !grid_fits((rows * (D / 8) + 255) / 256, 256))
+    const int64_t blocks = work_blocks(total);
+    if (!grid_fits(blocks, NW * 64) || !grid_fits((rows * (D / 8) + 255) / 256, 256))
         return fail(STA_ERR_UNSUPPORTED, "too many work items");
     const float scale_log2 = scale * 1.4426950408889634f;
     const __bf16 *Q = (const __bf16 *)q, *K = (const __bf16 *)k, *V = (const __bf16 *)v;
     const __bf16 *O = (const __bf16 *)o, *dO = (const __bf16 *)dout;
 
     sta_status st = STA_OK;
+    // the per-XCD work split (both walks have the same cost per slab: the
+    // listed tile pairs, counted from either list)
+    void *ws = nullptr;
+    const int *split = nullptr;
+    if (parts & (STA_BWD_DKDV | STA_BWD_DQ)) {
+        if ((st = workspace_alloc(&ws, plan_bytes(idx.num_heads), s)) != STA_OK) return st;
+        if ((st = plan_work(g, idx.kv_cnt, idx.num_heads, (int64_t)B * H, rblocks, blocks, ws, s, &split)) !=
+            STA_OK) {
+            (void)workspace_free(ws, s);      // the launch error is the one reported
+            return st;
+        }
+    }
+    auto done = [&](sta_status r) {
+        const sta_status fs = workspace_free(ws, s);
+        return r != STA_OK ? r : fs;
+    };
     if (parts & STA_BWD_DELTA) {
         hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, s, O, dO,
                            delta, rows);
-        if ((st = check_launch()) != STA_OK) return st;
+        if ((st = check_launch()) != STA_OK) return done(st);
     }
     if (parts & STA_BWD_DKDV) {
         if (g.raster)
-            hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ, STA_BWD_NBUF, true>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K,
+            hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ, STA_BWD_NBUF, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, s, Q, K,
                                V, dO, lse, (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q,
-                               idx.num_heads, g, rblocks, (int)total, scale_log2, scale);
+                               idx.num_heads, g, rblocks, split, scale_log2, scale);
         else
-            hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ, STA_BWD_NBUF, false>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K,
+            hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ, STA_BWD_NBUF, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, s, Q, K,
                                V, dO, lse, (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q,
-                               idx.num_heads, g, rblocks, (int)total, scale_log2, scale);
-        if ((st = check_launch()) != STA_OK) return st;
+                               idx.num_heads, g, rblocks, split, scale_log2, scale);
+        if ((st = check_launch()) != STA_OK) return done(st);
     }
     if (parts & STA_BWD_DQ) {
         if (g.raster)
-            hipLaunchKernelGGL((dq_kernel<D, NW, BN, STA_BWD_NBUF, true>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V,
+            hipLaunchKernelGGL((dq_kernel<D, NW, BN, STA_BWD_NBUF, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, s, Q, K, V,
                                dO, lse, (const float *)delta, (__bf16 *)dq, idx.kv_idx, idx.kv_cnt, idx.max_kv, idx.num_heads,
-                               g, rblocks, (int)total, scale_log2, scale);
+                               g, rblocks, split, scale_log2, scale);
         else
-            hipLaunchKernelGGL((dq_kernel<D, NW, BN, STA_BWD_NBUF, false>), dim3((unsigned)total), dim3(NW * 64), 0, s, Q, K, V,
+            hipLaunchKernelGGL((dq_kernel<D, NW, BN, STA_BWD_NBUF, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, s, Q, K, V,
                                dO, lse, (const float *)delta, (__bf16 *)dq, idx.kv_idx, idx.kv_cnt, idx.max_kv, idx.num_heads,
-                               g, rblocks, (int)total, scale_log2, scale);
-        if ((st = check_launch()) != STA_OK) return st;
+                               g, rblocks, split, scale_log2, scale);
+        if ((st = check_launch()) != STA_OK) return done(st);
     }
-    return st;
+    return done(st);
 }
 
 sta_status launch_bwd_bf16(const void *q, const void *k, const void *v, const void *o, const float *lse,

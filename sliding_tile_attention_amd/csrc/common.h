@@ -167,6 +167,22 @@ __device__ inline void decode_item(int work, int rblocks, const Geo &g, int &bh,
     tile = t < g.Tt ? g.T + t : t - g.Tt;
 }
 
+// Maps a launch-order block index to a work index so that each of the
+// chip's 8 XCDs (which take blocks round-robin) receives a contiguous range
+// of the work order, keeping neighbouring work in one XCD's L2.
+__device__ inline int xcd_remap(int bid, int total)
+{
+    constexpr int X = 8;
+    int per = total / X, rem = total % X;
+    int xcd = bid % X, slot = bid / X;
+    return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+// Blocks of a query- or key-stationary launch of `total` work items: 8
+// times twice the mean share of an XCD, room for cost-balanced ranges of up
+// to twice the mean item count (plan_work caps them there).
+inline int64_t work_blocks(int64_t total) { return 8 * 2 * ((total + 7) / 8); }
+
 // Window start and count on one axis (window rule of the library header).
 __host__ __device__ inline void axis_window(int n, int w, int q, int o, int &s, int &c)
 {
@@ -240,6 +256,14 @@ sta_status launch_window_shifts_scratch(const void *q, const void *k, int B, int
                                         bool truncate, bool per_batch, int region_max, int32_t *offsets,
                                         hipStream_t s);
 
+// The per-XCD cut points of the work order (schedule.hip) for a launch of
+// `blocks` blocks (work_blocks): a one-workgroup launch on stream s writes
+// int[9] at the start of ws (plan_bytes(IH) bytes of device workspace,
+// which also hold its scratch) and points *split there.
+size_t plan_bytes(int IH);
+sta_status plan_work(const Geo &g, const int32_t *kv_cnt, int IH, int64_t BH, int rblocks, int64_t blocks, void *ws,
+                     hipStream_t s, const int **split);
+
 // Stream-ordered device workspace (per-device pool that keeps freed memory
 // for reuse); the buffer may be used by work queued on `s` until the
 // matching workspace_free on the same stream.
@@ -259,17 +283,6 @@ inline sta_status check_launch()
     if (e != hipSuccess)
         return fail(STA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
     return STA_OK;
-}
-
-// Maps a launch-order block index to a work index so that each of the
-// chip's 8 XCDs (which take blocks round-robin) receives a contiguous range
-// of the work order, keeping neighbouring work in one XCD's L2.
-__device__ inline int xcd_remap(int bid, int total)
-{
-    constexpr int X = 8;
-    int per = total / X, rem = total % X;
-    int xcd = bid % X, slot = bid / X;
-    return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
 }  // namespace sta

@@ -23,9 +23,10 @@
 //
 // Work decomposition
 //   workgroup = NW waves = M = NW*QB*32 consecutive query rows of one query
-//   tile of one (b, h); work items are ordered head-major and spread over the
-//   8 XCDs in contiguous ranges (xcd_remap) so that the workgroups sharing an
-//   XCD's L2 walk neighbouring windows of the same head.
+//   tile of one (b, h); work items are ordered head-major and each of the 8
+//   XCDs takes one contiguous range of that order, cut at equal cost
+//   (schedule.hip), so that the workgroups sharing an XCD's L2 walk
+//   neighbouring windows of the same head.
 //   The key loop runs over (listed key tile, BN-key block) pairs.  K and V^T
 //   blocks travel HBM -> LDS directly (global_load_lds, no staging
 //   registers) into a double buffer: the copy of block j+1 runs while block j
@@ -133,14 +134,20 @@ template <int D, int NW, int QB, int BN, bool RASTER>
 __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ VT,
     __bf16 *__restrict__ O, float *__restrict__ LSE, const int32_t *__restrict__ kv_idx,
-    const int32_t *__restrict__ kv_cnt, int max_kv, int IH, Geo g, int Lp, int rblocks, int total,
+    const int32_t *__restrict__ kv_cnt, int max_kv, int IH, Geo g, int Lp, int rblocks, const int *__restrict__ split,
     float scale_log2)
 {
     using C = FwdCfg<D, NW, QB, BN>;
     __shared__ __attribute__((aligned(1024))) __bf16 smem[2 * C::STAGE];
 
     int bh, qt, rb;
-    decode_item(xcd_remap(blockIdx.x, total), rblocks, g, bh, qt, rb);
+    {
+        // XCD x = block index mod 8 takes the range [split[x], split[x+1]) of
+        // the work order; blocks past it exit
+        const int x = blockIdx.x & 7, work = split[x] + (int)(blockIdx.x >> 3);
+        if (work >= split[x + 1]) return;
+        decode_item(work, rblocks, g, bh, qt, rb);
+    }
     const Span qs = tile_span(g, qt);                // query rows of this tile
     const int qlen = qs.len;
     if (rb * C::M >= qlen) return;                   // row block past a cut tile's end
@@ -400,28 +407,37 @@ static sta_status run_fwd(const void *q, const void *k, const void *v, void *o, 
     static_assert(kVtPad % BN == 0, "V^T padding must be a multiple of the key block");
     const int rblocks = (g.L + C::M - 1) / C::M;
     const int64_t total = (int64_t)B * H * g.TT * rblocks;
+    const int64_t blocks = work_blocks(total);
     const int chunks = (g.L + kVtPad - 1) / kVtPad;
     const int Lp = chunks * kVtPad;
     const int64_t vt_blocks = (int64_t)B * H * g.TT * chunks;
-    if (!grid_fits(total, C::THREADS) || !grid_fits(vt_blocks, 256))
+    if (!grid_fits(blocks, C::THREADS) || !grid_fits(vt_blocks, 256))
         return fail(STA_ERR_UNSUPPORTED, "too many work items");
+    // workspace: the per-XCD work split, then the V^T tiles
+    const size_t plan = (plan_bytes(idx.num_heads) + 255) & ~(size_t)255;
     const size_t vt_bytes = (size_t)B * H * g.TT * D * Lp * sizeof(__bf16);
-    void *vt = nullptr;
-    sta_status st = workspace_alloc(&vt, vt_bytes, s);
+    void *ws = nullptr;
+    sta_status st = workspace_alloc(&ws, plan + vt_bytes, s);
     if (st != STA_OK) return st;
+    void *vt = (char *)ws + plan;
+    const int *split = nullptr;
+    if ((st = plan_work(g, idx.kv_cnt, idx.num_heads, (int64_t)B * H, rblocks, blocks, ws, s, &split)) != STA_OK) {
+        (void)workspace_free(ws, s);          // the launch error is the one reported
+        return st;
+    }
     hipLaunchKernelGGL(vt_kernel<D>, dim3((unsigned)vt_blocks), dim3(256), 0, s, (const __bf16 *)v, (__bf16 *)vt,
                        g, Lp, chunks);
     const float scale_log2 = scale * 1.4426950408889634f;
     if (g.raster)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BN, true>), dim3((unsigned)total), dim3(C::THREADS), 0, s,
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BN, true>), dim3((unsigned)blocks), dim3(C::THREADS), 0, s,
                            (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)vt, (__bf16 *)o, lse, idx.kv_idx,
-                           idx.kv_cnt, idx.max_kv, idx.num_heads, g, Lp, rblocks, (int)total, scale_log2);
+                           idx.kv_cnt, idx.max_kv, idx.num_heads, g, Lp, rblocks, split, scale_log2);
     else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BN, false>), dim3((unsigned)total), dim3(C::THREADS), 0, s,
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BN, false>), dim3((unsigned)blocks), dim3(C::THREADS), 0, s,
                            (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)vt, (__bf16 *)o, lse, idx.kv_idx,
-                           idx.kv_cnt, idx.max_kv, idx.num_heads, g, Lp, rblocks, (int)total, scale_log2);
+                           idx.kv_cnt, idx.max_kv, idx.num_heads, g, Lp, rblocks, split, scale_log2);
     st = check_launch();
-    const sta_status fs = workspace_free(vt, s);
+    const sta_status fs = workspace_free(ws, s);
     return st != STA_OK ? st : fs;
 }
 

@@ -273,14 +273,20 @@ __global__ __launch_bounds__(NW * 64, STA_F8_MINB) void fwd_fp8_kernel(
     const float *__restrict__ sq, const float *__restrict__ corr, const float *__restrict__ sk,
     const float *__restrict__ vscale, __bf16 *__restrict__ O, float *__restrict__ LSE,
     const int32_t *__restrict__ kv_idx, const int32_t *__restrict__ kv_cnt, int max_kv, int IH, Geo g, int Lp,
-    int nkb, int rblocks, int total)
+    int nkb, int rblocks, const int *__restrict__ split)
 {
     using C = F8Cfg<D, NW>;
     constexpr int BN = C::BN;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * C::STAGE];
 
     int bh, qt, rb;
-    decode_item(xcd_remap(blockIdx.x, total), rblocks, g, bh, qt, rb);
+    {
+        // XCD x = block index mod 8 takes the range [split[x], split[x+1]) of
+        // the work order; blocks past it exit
+        const int x = blockIdx.x & 7, work = split[x] + (int)(blockIdx.x >> 3);
+        if (work >= split[x + 1]) return;
+        decode_item(work, rblocks, g, bh, qt, rb);
+    }
     const Span qs = tile_span(g, qt);
     const int qlen = qs.len;
     if (rb * C::M >= qlen) return;                   // row block past a cut tile's end
@@ -501,8 +507,9 @@ static sta_status run_fwd_fp8(const void *q, const void *k, const void *v, void 
     const int64_t BH = (int64_t)B * H;
     const int rblocks = (g.L + C::M - 1) / C::M;
     const int64_t total = BH * g.TT * rblocks;
+    const int64_t blocks = work_blocks(total);
     const int64_t qk_blocks = BH * g.TT * nkb;
-    if (!grid_fits(total, C::THREADS) || !grid_fits(qk_blocks, 256) || !grid_fits(BH * kStatChunks, 256))
+    if (!grid_fits(blocks, C::THREADS) || !grid_fits(qk_blocks, 256) || !grid_fits(BH * kStatChunks, 256))
         return fail(STA_ERR_UNSUPPORTED, "too many work items");
     // workspace: codes, scales and statistics
     const size_t n_codes = (size_t)BH * g.S * D, n_vt = (size_t)BH * g.TT * D * Lp;
@@ -512,7 +519,8 @@ static sta_status run_fwd_fp8(const void *q, const void *k, const void *v, void 
     const size_t off_sq = off_vt + align256(n_vt), off_corr = off_sq + align256(n_rows * 4);
     const size_t off_sk = off_corr + align256(n_rows * 4), off_km = off_sk + align256(n_sk * 4);
     const size_t off_vs = off_km + align256(n_ch * 4), off_vi = off_vs + align256(n_ch * 4);
-    const size_t off_part = off_vi + align256(n_ch * 4), bytes = off_part + align256(n_part * 8);
+    const size_t off_part = off_vi + align256(n_ch * 4), off_plan = off_part + align256(n_part * 8);
+    const size_t bytes = off_plan + align256(plan_bytes(idx.num_heads));
     void *ws = nullptr;
     sta_status st = workspace_alloc(&ws, bytes, s);
     if (st != STA_OK) return st;
@@ -521,6 +529,11 @@ static sta_status run_fwd_fp8(const void *q, const void *k, const void *v, void 
     float *sq = (float *)(w + off_sq), *corr = (float *)(w + off_corr), *sk = (float *)(w + off_sk);
     float *km = (float *)(w + off_km), *vs = (float *)(w + off_vs), *vi = (float *)(w + off_vi);
     double *part = (double *)(w + off_part);
+    const int *split = nullptr;
+    if ((st = plan_work(g, idx.kv_cnt, idx.num_heads, BH, rblocks, blocks, w + off_plan, s, &split)) != STA_OK) {
+        (void)workspace_free(ws, s);          // the launch error is the one reported
+        return st;
+    }
     const __bf16 *Q = (const __bf16 *)q, *K = (const __bf16 *)k, *V = (const __bf16 *)v;
     const float c_log2 = scale * 1.4426950408889634f;
 
@@ -530,9 +543,9 @@ static sta_status run_fwd_fp8(const void *q, const void *k, const void *v, void 
     hipLaunchKernelGGL(quant_qk_kernel<D>, dim3((unsigned)qk_blocks), dim3(256), 0, s, Q, K, km, q8, k8, sq, corr, sk,
                        g, nkb, c_log2, scale);
     hipLaunchKernelGGL(quant_vt_kernel<D>, dim3((unsigned)qk_blocks), dim3(256), 0, s, V, vi, vt8, g, Lp, nkb);
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, NW>), dim3((unsigned)total), dim3(C::THREADS), 0, s, q8, k8, vt8, sq, corr,
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, NW>), dim3((unsigned)blocks), dim3(C::THREADS), 0, s, q8, k8, vt8, sq, corr,
                        sk, vs, (__bf16 *)o, lse, idx.kv_idx, idx.kv_cnt, idx.max_kv, idx.num_heads, g, Lp, nkb, rblocks,
-                       (int)total);
+                       split);
     st = check_launch();
     const sta_status fs = workspace_free(ws, s);
     return st != STA_OK ? st : fs;
