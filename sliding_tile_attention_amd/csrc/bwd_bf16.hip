@@ -246,10 +246,11 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
     int bh, qt, rb;
     {
         // XCD x = block index mod 8 takes the range [split[x], split[x+1]) of
-        // the work order; blocks past it exit
+        // the work order (slabs by descending cost); blocks past it exit
         const int x = blockIdx.x & 7, work = split[x] + (int)(blockIdx.x >> 3);
         if (work >= split[x + 1]) return;
         decode_item(work, rblocks, g, bh, qt, rb);
+        bh = plan_slab(split, bh);
     }
     const Span qs = tile_span(g, qt);                // query rows of this tile
     const int qlen = qs.len;
@@ -410,10 +411,11 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     int bh, kt, rb;
     {
         // XCD x = block index mod 8 takes the range [split[x], split[x+1]) of
-        // the work order; blocks past it exit
+        // the work order (slabs by descending cost); blocks past it exit
         const int x = blockIdx.x & 7, work = split[x] + (int)(blockIdx.x >> 3);
         if (work >= split[x + 1]) return;
         decode_item(work, rblocks, g, bh, kt, rb);
+        bh = plan_slab(split, bh);
     }
     const Span ks_ = tile_span(g, kt);               // key rows of this tile
     const int klen = ks_.len;
@@ -629,7 +631,7 @@ static sta_status run_bwd(const void *q, const void *k, const void *v, const voi
     void *ws = nullptr;
     const int *split = nullptr;
     if (parts & (STA_BWD_DKDV | STA_BWD_DQ)) {
-        if ((st = workspace_alloc(&ws, plan_bytes(idx.num_heads), s)) != STA_OK) return st;
+        if ((st = workspace_alloc(&ws, plan_bytes(idx.num_heads, (int64_t)B * H), s)) != STA_OK) return st;
         if ((st = plan_work(g, idx.kv_cnt, idx.num_heads, (int64_t)B * H, rblocks, blocks, ws, s, &split)) !=
             STA_OK) {
             (void)workspace_free(ws, s);      // the launch error is the one reported

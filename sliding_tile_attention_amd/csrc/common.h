@@ -178,6 +178,8 @@ __device__ inline int xcd_remap(int bid, int total)
     return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
+__device__ inline int plan_slab(const int *plan, int rank) { return plan[16 + rank]; }
+
 // Blocks of a query- or key-stationary launch of `total` work items: 8
 // times twice the mean share of an XCD, room for cost-balanced ranges of up
 // to twice the mean item count (plan_work caps them there).
@@ -256,11 +258,13 @@ sta_status launch_window_shifts_scratch(const void *q, const void *k, int B, int
                                         bool truncate, bool per_batch, int region_max, int32_t *offsets,
                                         hipStream_t s);
 
-// The per-XCD cut points of the work order (schedule.hip) for a launch of
-// `blocks` blocks (work_blocks): a one-workgroup launch on stream s writes
-// int[9] at the start of ws (plan_bytes(IH) bytes of device workspace,
-// which also hold its scratch) and points *split there.
-size_t plan_bytes(int IH);
+// The work plan (schedule.hip) for a launch of `blocks` blocks
+// (work_blocks): a one-workgroup launch on stream s writes, at the start of
+// ws (plan_bytes(IH, BH) bytes of device workspace, which also hold its
+// scratch), the per-XCD cut points of the work order (int[9]) and, 16 ints
+// on, the slab of every rank (int[BH]); *split points there.
+// plan_slab(split, r) is the slab (b*H + h) of rank r.
+size_t plan_bytes(int IH, int64_t BH);
 sta_status plan_work(const Geo &g, const int32_t *kv_cnt, int IH, int64_t BH, int rblocks, int64_t blocks, void *ws,
                      hipStream_t s, const int **split);
 

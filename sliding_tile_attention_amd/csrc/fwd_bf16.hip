@@ -143,10 +143,11 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     int bh, qt, rb;
     {
         // XCD x = block index mod 8 takes the range [split[x], split[x+1]) of
-        // the work order; blocks past it exit
+        // the work order (slabs by descending cost); blocks past it exit
         const int x = blockIdx.x & 7, work = split[x] + (int)(blockIdx.x >> 3);
         if (work >= split[x + 1]) return;
         decode_item(work, rblocks, g, bh, qt, rb);
+        bh = plan_slab(split, bh);
     }
     const Span qs = tile_span(g, qt);                // query rows of this tile
     const int qlen = qs.len;
@@ -414,7 +415,7 @@ static sta_status run_fwd(const void *q, const void *k, const void *v, void *o, 
     if (!grid_fits(blocks, C::THREADS) || !grid_fits(vt_blocks, 256))
         return fail(STA_ERR_UNSUPPORTED, "too many work items");
     // workspace: the per-XCD work split, then the V^T tiles
-    const size_t plan = (plan_bytes(idx.num_heads) + 255) & ~(size_t)255;
+    const size_t plan = (plan_bytes(idx.num_heads, (int64_t)B * H) + 255) & ~(size_t)255;
     const size_t vt_bytes = (size_t)B * H * g.TT * D * Lp * sizeof(__bf16);
     void *ws = nullptr;
     sta_status st = workspace_alloc(&ws, plan + vt_bytes, s);

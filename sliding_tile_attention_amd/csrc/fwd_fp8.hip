@@ -282,10 +282,11 @@ __global__ __launch_bounds__(NW * 64, STA_F8_MINB) void fwd_fp8_kernel(
     int bh, qt, rb;
     {
         // XCD x = block index mod 8 takes the range [split[x], split[x+1]) of
-        // the work order; blocks past it exit
+        // the work order (slabs by descending cost); blocks past it exit
         const int x = blockIdx.x & 7, work = split[x] + (int)(blockIdx.x >> 3);
         if (work >= split[x + 1]) return;
         decode_item(work, rblocks, g, bh, qt, rb);
+        bh = plan_slab(split, bh);
     }
     const Span qs = tile_span(g, qt);
     const int qlen = qs.len;
@@ -520,7 +521,7 @@ static sta_status run_fwd_fp8(const void *q, const void *k, const void *v, void 
     const size_t off_sk = off_corr + align256(n_rows * 4), off_km = off_sk + align256(n_sk * 4);
     const size_t off_vs = off_km + align256(n_ch * 4), off_vi = off_vs + align256(n_ch * 4);
     const size_t off_part = off_vi + align256(n_ch * 4), off_plan = off_part + align256(n_part * 8);
-    const size_t bytes = off_plan + align256(plan_bytes(idx.num_heads));
+    const size_t bytes = off_plan + align256(plan_bytes(idx.num_heads, (int64_t)B * H));
     void *ws = nullptr;
     sta_status st = workspace_alloc(&ws, bytes, s);
     if (st != STA_OK) return st;
