@@ -53,10 +53,13 @@ summarised into profiles/traffic.json by
 
     python bench.py --write-traffic FETCH_CSV WRITE_CSV
 
-Each counter is scaled by what it reads for the raster->tile reorder kernel of
-the same step, a plain permutation copy whose bytes are known (every byte of
-its input read once and written once).  The summary records a digest of the
-kernel sources; when they change, "traffic" is reported as null.
+Each counter is scaled by what it reads for one launch of a plain streaming
+copy probe (libsta_probe.so, copy_probe_kernel) of one attention input's bytes,
+which every run of this benchmark makes once after the timed steps: its bytes
+are known exactly (every source byte read once, every destination byte written
+once), so the reorder kernel's traffic is measured like the others.  The
+summary records a digest of the kernel sources; when they change, "traffic" is
+reported as null.
 """
 import argparse
 import hashlib
@@ -106,8 +109,9 @@ def parse():
 
 # Kernel name fragments (as rocprofv3 reports them) -> benchmark names, and
 # the sources each kernel is built from.
-KERNELS = {"fwd_bf16_kernel": "fwd", "dkdv_kernel": "bwd_dkdv", "dq_kernel": "bwd_dq"}
+KERNELS = {"fwd_bf16_kernel": "fwd", "dkdv_kernel": "bwd_dkdv", "dq_kernel": "bwd_dq", "reorder_kernel": "reorder"}
 KERNEL_SOURCES = {"fwd": ["fwd_bf16.hip", "mfma.h", "common.h"],
+                  "reorder": ["reorder.hip", "common.h"],
                   "bwd_dkdv": ["bwd_bf16.hip", "mfma.h", "common.h"],
                   "bwd_dq": ["bwd_bf16.hip", "mfma.h", "common.h"]}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
@@ -136,14 +140,14 @@ def measured_traffic(kernel):
 
 def write_traffic(fetch_csv, write_csv):
     """profiles/traffic.json from the FETCH_SIZE and WRITE_SIZE passes (KiB
-    per dispatch), calibrated on the reorder kernel (a permutation copy)."""
+    per dispatch), calibrated on the copy probe (a plain streaming copy)."""
     import csv
     import collections
     from tests.inputs import CONFIGS
 
     c = CONFIGS[WORKLOAD]
     n = int(np.prod(c["grid"]))
-    copy_bytes = c["B"] * c["H"] * n * c["D"] * 2          # one reorder launch reads and writes this
+    copy_bytes = c["B"] * c["H"] * n * c["D"] * 2          # the copy probe reads and writes this
     means = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         vals = collections.defaultdict(list)
@@ -152,15 +156,15 @@ def write_traffic(fetch_csv, write_csv):
                 if row["Counter_Name"] != counter:
                     continue
                 name = row["Kernel_Name"]
-                key = "reorder" if "reorder_kernel" in name else next(
+                key = "copy_probe" if "copy_probe_kernel" in name else next(
                     (v for k, v in KERNELS.items() if k in name), None)
                 if key:
                     vals[key].append(float(row["Counter_Value"]) * 1024.0)
         means[counter] = {k: float(np.mean(v)) for k, v in vals.items()}
-    cal = {ctr: copy_bytes / means[ctr]["reorder"] for ctr in means}
-    out = {"_calibration": {"kernel": "reorder_kernel (raster <-> tile order copy)", "bytes_per_launch": copy_bytes,
-                            "FETCH_SIZE_bytes": means["FETCH_SIZE"]["reorder"],
-                            "WRITE_SIZE_bytes": means["WRITE_SIZE"]["reorder"],
+    cal = {ctr: copy_bytes / means[ctr]["copy_probe"] for ctr in means}
+    out = {"_calibration": {"kernel": "copy_probe_kernel (plain streaming copy)", "bytes_per_launch": copy_bytes,
+                            "FETCH_SIZE_bytes": means["FETCH_SIZE"]["copy_probe"],
+                            "WRITE_SIZE_bytes": means["WRITE_SIZE"]["copy_probe"],
                             "fetch_factor": cal["FETCH_SIZE"], "write_factor": cal["WRITE_SIZE"]}}
     for key in KERNELS.values():
         fb = means["FETCH_SIZE"][key] * cal["FETCH_SIZE"]
@@ -246,6 +250,56 @@ def copy_ceiling(torch, x, reps=10):
     del y
     return {"value": round(2.0 * x.numel() * x.element_size() / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
             "what": "torch copy_ of %d bytes (read + write), mean of %d" % (x.numel() * x.element_size(), reps)}
+
+
+def probe_lib():
+    """The measurement probes (libsta_probe.so, built beside libsta)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "sliding_tile_attention_amd", "libsta_probe.so"))
+    lib.sta_probe_exp.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.sta_probe_exp.restype = ctypes.c_int
+    lib.sta_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.sta_probe_copy.restype = ctypes.c_int
+    return lib
+
+
+def calibration_copy(torch, x):
+    """One launch of the copy probe over x's bytes (the traffic counters'
+    calibration: it reads and writes exactly that many bytes)."""
+    import ctypes
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    if probe_lib().sta_probe_copy(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                                  x.numel() * x.element_size(),
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) != 0:
+        raise RuntimeError("copy probe failed to launch")
+    torch.cuda.synchronize()
+    del y
+
+
+def exp_rate(torch, dev, blocks=2048, iters=1024, reps=5):
+    """Measured rate of the hardware exponential (v_exp_f32) on this GPU: a
+    probe launch of 2048 workgroups of 256 threads, each thread 1024 rounds of
+    16 independent exponentials, timed with HIP events; exponentials per
+    second."""
+    import ctypes
+    lib = probe_lib()
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    launch = lambda: lib.sta_probe_exp(ctypes.c_void_p(out.data_ptr()), blocks, iters,
+                                       ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(2):
+        if launch() != 0:
+            raise RuntimeError("exponential-rate probe failed to launch")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return blocks * 256.0 * iters * 16 / (ms * 1e-3)
 
 
 def cpu_model():
@@ -415,14 +469,21 @@ def main():
     # recomputation).  Together the backward is 10 L^2 D = 2.5x the forward.
     alg = {"fwd": fwd_flop} if fwd_only else {"fwd": fwd_flop, "bwd_dkdv": 2.0 * fwd_flop, "bwd_dq": 0.5 * fwd_flop}
     peak = PEAK_FP8_TFLOPS if prec == sta.STA_PREC_FP8 else PEAK_BF16_TFLOPS
+    default_step = (nt == 0 and grid is None and prec == sta.STA_PREC_DEFAULT and radius is None and not raster
+                    and not shifted)
     dominant = max(alg, key=lambda n: per[n])
     achieved = alg[dominant] / (per[dominant] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "kernel": dominant,
-                "traffic": measured_traffic(dominant) if nt == 0 and grid is None and prec == sta.STA_PREC_DEFAULT
-                and radius is None and not raster and not shifted else None,  # counters cover the default step
+                "traffic": measured_traffic(dominant) if default_step else None,  # counters cover the default step
                 "measured_gemm_ceiling": gemm_ceiling(torch, dev)}
 
+    calibration_copy(torch, q)
+    scores = fwd_flop / (4.0 * D)
+    rate = exp_rate(torch, dev)
+    exp_bound = {"exps_per_fwd": scores, "measured_exp_rate_per_s": round(rate, -6),
+                 "exp_ms_at_that_rate": round(scores / rate * 1e3, 3),
+                 "share_of_fwd_kernel": round(scores / rate * 1e3 / per["fwd"], 4)}
     tensor_bytes = B * H * S * D * 2
     reorder_gbs = 3 * 2 * tensor_bytes / (per["reorder_qkv"] * 1e-3) / 1e9 if "reorder_qkv" in per else None
     out = {
@@ -460,12 +521,19 @@ def main():
             "fwd_frac_of_peak": round(fwd_flop / (per["fwd"] * 1e-3) / 1e12 / peak, 4),
             "bwd_kernels_ms": None if fwd_only else round(per["bwd_delta"] + per["bwd_dkdv"] + per["bwd_dq"], 3),
             "reorder_qkv_gbs": None if reorder_gbs is None else round(reorder_gbs, 1),
+            # HBM bytes of one reorder launch from the counters (the
+            # algorithmic figure is 2 * one input: read once, written once)
+            "reorder_traffic_per_launch": measured_traffic("reorder") if default_step else None,
+            "reorder_algorithmic_bytes": 2 * tensor_bytes,
             "measured_copy_ceiling": copy_ceiling(torch, q),
             # the producer reads Q and K once (its tile means); the choice
             # itself touches only the means
             "shifts_hbm_gbs": None if radius is None else round(2 * B * H * N * D * 2 / (per["shifts"] * 1e-3) / 1e9,
                                                                1),
             "per_call_ms": {n: round(t, 4) for n, t in per.items()},
+            # the forward's secondary bound: one hardware exponential per
+            # counted score (the lazy-max rule redoes a fraction of a percent)
+            "exp_bound": exp_bound,
         },
         "roofline": roofline,
     }

@@ -48,6 +48,24 @@ def _compile(src, force):
     return o
 
 
+PROBE_SRC = "probes.hip"             # measurement probes of bench.py, a library of their own
+PROBE_LIB = os.path.join(HERE, "libsta_probe.so")
+
+
+def build_probe(force=True):
+    """The measurement probes that bench.py runs (not part of libsta)."""
+    src = os.path.join(CSRC, PROBE_SRC)
+    if not force and os.path.exists(PROBE_LIB) and os.path.getmtime(PROBE_LIB) >= os.path.getmtime(src):
+        return PROBE_LIB
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + ["-shared", src, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (PROBE_SRC, " ".join(cmd), r.stderr))
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(force=True, jobs=None):
     """Compile every HIP source and link libsta.so.  force=True recompiles
     everything (the default: a build step must really build)."""
@@ -61,6 +79,7 @@ def build(force=True, jobs=None):
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
     os.replace(tmp, LIB)
+    build_probe(force)
     return LIB
 
 
