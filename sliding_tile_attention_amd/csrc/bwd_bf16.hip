@@ -416,6 +416,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
         if (work >= split[x + 1]) return;
         decode_item(work, rblocks, g, bh, kt, rb);
         bh = plan_slab(split, bh);
+        if (kt < g.T) kt = plan_tile(split, bh % IH, g.T, kt);    // longest transposed lists first
     }
     const Span ks_ = tile_span(g, kt);               // key rows of this tile
     const int klen = ks_.len;
@@ -630,10 +631,13 @@ static sta_status run_bwd(const void *q, const void *k, const void *v, const voi
     // listed tile pairs, counted from either list)
     void *ws = nullptr;
     const int *split = nullptr;
+    // (with dK/dV, the key tiles in order of their transposed-list lengths)
     if (parts & (STA_BWD_DKDV | STA_BWD_DQ)) {
-        if ((st = workspace_alloc(&ws, plan_bytes(idx.num_heads, (int64_t)B * H), s)) != STA_OK) return st;
-        if ((st = plan_work(g, idx.kv_cnt, idx.num_heads, (int64_t)B * H, rblocks, blocks, ws, s, &split)) !=
-            STA_OK) {
+        const bool kv = parts & STA_BWD_DKDV;
+        if ((st = workspace_alloc(&ws, plan_bytes(idx.num_heads, (int64_t)B * H, kv ? &g : nullptr), s)) != STA_OK)
+            return st;
+        if ((st = plan_work(g, idx.kv_cnt, idx.num_heads, (int64_t)B * H, rblocks, blocks, ws, s, &split,
+                            kv ? idx.q_cnt : nullptr)) != STA_OK) {
             (void)workspace_free(ws, s);      // the launch error is the one reported
             return st;
         }

@@ -180,6 +180,14 @@ __device__ inline int xcd_remap(int bid, int total)
 
 __device__ inline int plan_slab(const int *plan, int rank) { return plan[16 + rank]; }
 
+// Video tile at position t of list set h's key-stationary walk: the plan's
+// tile order if it has one (plan[9] >= 0), else t itself.
+__device__ inline int plan_tile(const int *plan, int h, int T, int t)
+{
+    const int at = plan[9];
+    return at < 0 ? t : plan[at + h * T + t];
+}
+
 // Blocks of a query- or key-stationary launch of `total` work items: 8
 // times twice the mean share of an XCD, room for cost-balanced ranges of up
 // to twice the mean item count (plan_work caps them there).
@@ -259,14 +267,19 @@ sta_status launch_window_shifts_scratch(const void *q, const void *k, int B, int
                                         hipStream_t s);
 
 // The work plan (schedule.hip) for a launch of `blocks` blocks
-// (work_blocks): a one-workgroup launch on stream s writes, at the start of
-// ws (plan_bytes(IH, BH) bytes of device workspace, which also hold its
-// scratch), the per-XCD cut points of the work order (int[9]) and, 16 ints
-// on, the slab of every rank (int[BH]); *split points there.
-// plan_slab(split, r) is the slab (b*H + h) of rank r.
-size_t plan_bytes(int IH, int64_t BH);
+// (work_blocks): launches on stream s write, at the start of ws
+// (plan_bytes bytes of device workspace, which also hold their scratch),
+// the per-XCD cut points of the work order (int[9]) and, 16 ints on, the
+// slab of every rank (int[BH]); *split points there.  plan_slab(split, r)
+// is the slab (b*H + h) of rank r.  With walk_cnt (the [IH][T] list
+// lengths of a key-stationary walk; plan_bytes then takes the geometry)
+// the plan also orders each list set's video tiles by descending length,
+// read with plan_tile; grids of more than kMaxOrderedTiles tiles keep tile
+// order.
+constexpr int kMaxOrderedTiles = 4096;
+size_t plan_bytes(int IH, int64_t BH, const Geo *tile_order = nullptr);
 sta_status plan_work(const Geo &g, const int32_t *kv_cnt, int IH, int64_t BH, int rblocks, int64_t blocks, void *ws,
-                     hipStream_t s, const int **split);
+                     hipStream_t s, const int **split, const int32_t *walk_cnt = nullptr);
 
 // Stream-ordered device workspace (per-device pool that keeps freed memory
 // for reuse); the buffer may be used by work queued on `s` until the
