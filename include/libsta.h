@@ -41,10 +41,14 @@
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library never synchronises or prints.  Three calls take temporary
- *     device memory: the bf16 forward (V^T tiles, see sta_fwd), the
- *     quantized forward (codes and scales, see sta_fwd_ex) and
- *     sta_window_shifts (tile means).  They take it stream-ordered
+ *     library never synchronises or prints.  These calls take temporary
+ *     device memory: every bf16 attention call (sta_fwd, sta_bwd and their
+ *     variants, the quantized forward included) its work plan (how the
+ *     work splits over the chip's XCDs: about 4*B*H + 12*I*(TT + 1) bytes
+ *     for an index of I list sets and TT tiles and text pseudo-tiles), the
+ *     bf16 forward also V^T tiles (see sta_fwd), the quantized forward
+ *     codes and scales (see sta_fwd_ex) and sta_window_shifts tile means.
+ *     They take it stream-ordered
  *     (hipMallocFromPoolAsync / hipFreeAsync on the call's stream) from one
  *     memory pool per device, created on first use and kept, with the
  *     memory it holds, until the process ends; a failed allocation returns
@@ -61,9 +65,11 @@
  *   - An index holds one list set per head, shared by every batch item, or
  *     one per (b, h) for windows shifted per batch item (see sta_index).
  *   - Thread-safe.  Mutable global state: a thread-local error message,
- *     and the table of per-device workspace pools, whose creation is
- *     guarded by a mutex (the pools themselves are HIP objects, safe to use
- *     from several threads and streams).
+ *     the table of per-device workspace pools, whose creation is guarded
+ *     by a mutex (the pools themselves are HIP objects, safe to use from
+ *     several threads and streams), and sta_window_shifts_noalloc's static
+ *     device array with its per-device address table (filled under a
+ *     mutex; the array is shared by every call on a GPU, see there).
  */
 #ifndef LIBSTA_H
 #define LIBSTA_H
@@ -232,9 +238,10 @@ sta_status sta_build_index_ex(const sta_geom *g, int32_t H, const sta_dim3 *wind
  * q, k, v, o: [B][H][N][D] in tile order; lse: [B][H][N] fp32 in tile
  * order.  D must be 64 or 128.  bf16 uses MFMA with fp32 accumulation; the
  * probabilities are rounded to bf16 before the PV product.
- * Workspace (bf16 only): the call first writes V transposed per tile,
- * B*H*num_tiles*D*Lp*2 bytes with Lp = L rounded up to a multiple of 64,
- * into memory taken from a per-device pool on `stream` and given back on
+ * Workspace (bf16 only): the work plan (Conventions), then V transposed
+ * per tile, B*H*num_tiles*D*Lp*2 bytes with Lp = L rounded up to a
+ * multiple of 64, in memory taken from a per-device pool on `stream` and
+ * given back on
  * `stream` after the attention kernel (hipMallocFromPoolAsync /
  * hipFreeAsync).  The pool keeps freed memory for reuse, so repeated calls
  * of one shape reach the driver only once; it holds at most the largest
@@ -258,7 +265,10 @@ sta_status sta_fwd(const void *q, const void *k, const void *v, void *o, float *
  * All tensors [B][H][N][D] in tile order; dq, dk, dv are fully written
  * (no accumulation into existing contents); no atomics, deterministic.
  * Needs the transposed lists (idx->q_idx, idx->q_cnt).  delta_ws is a
- * caller-owned device workspace of B*H*N floats.
+ * caller-owned device workspace of B*H*N floats.  bf16: the dK/dV and dQ
+ * stages take their work plan (Conventions) from the pool described at
+ * sta_fwd; with dK/dV it also orders each list set's key tiles by the
+ * length of their transposed lists (grids of at most 4096 tiles).
  * Source: the pages' system adapts a pre-trained DiT by full-parameter
  * training through the local attention operator ("MegaSlide-DiT",
  * abstract), which needs these gradients.
