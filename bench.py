@@ -102,6 +102,8 @@ def parse():
                     help="choose the window shifts on device (search radius per axis) inside the step")
     ap.add_argument("--workload", choices=(WORKLOAD, "720p-shifted-perhead"), default=WORKLOAD,
                     help="720p-shifted-perhead: per-head windows and seeded window shifts (the deformable variant)")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the socket power and clock samples taken after the timed steps")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 --pmc counter_collection.csv files into profiles/traffic.json")
     return ap.parse_args()
@@ -302,6 +304,52 @@ def exp_rate(torch, dev, blocks=2048, iters=1024, reps=5):
     return blocks * 256.0 * iters * 16 / (ms * 1e-3)
 
 
+def power_samples(torch, calls, seconds=2.0):
+    """Socket power and GFX clock while each call in `calls` (name -> fn)
+    runs back to back for `seconds`, read every ~10 ms through amdsmi (the
+    driver's sensors; no GPU setting is touched).  Means of the samples after
+    the first third (the clock settles), with the board's power limit and an
+    idle reading; None where amdsmi is missing or fails."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        hd = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception:
+        return None
+
+    def read():
+        p = amdsmi.amdsmi_get_power_info(hd)
+        c = amdsmi.amdsmi_get_clock_info(hd, amdsmi.AmdSmiClkType.GFX)
+        return float(p["current_socket_power"]), float(c["clk"]), p.get("power_limit")
+
+    try:
+        torch.cuda.synchronize()
+        time.sleep(0.2)
+        idle_w, _, limit = read()
+        out = {"idle_socket_w": idle_w,
+               "power_limit_w": float(limit) / 1e6 if isinstance(limit, (int, float)) else None}
+        for name, fn in calls.items():
+            torch.cuda.synchronize()
+            t0, got = time.time(), []
+            while time.time() - t0 < seconds:
+                fn()
+                fn()
+                time.sleep(0.01)
+                got.append(read()[:2])
+                torch.cuda.synchronize()
+            got = got[len(got) // 3:]
+            out[name] = {"socket_w": round(float(np.mean([g[0] for g in got])), 1),
+                         "gfx_mhz": round(float(np.mean([g[1] for g in got])), 1), "samples": len(got)}
+        return out
+    except Exception:
+        return None
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -479,6 +527,25 @@ def main():
                 "measured_gemm_ceiling": gemm_ceiling(torch, dev)}
 
     calibration_copy(torch, q)
+    power = None
+    if not args.no_power:
+        if raster:
+            calls = {"fwd": lambda: sta.sta_fwd_ex(q, k, v, o, lse, B, H, D, sta.STA_BF16, scale, geom, idx, 0, stream,
+                                                   prec, lay)}
+            bwd_args = (q, k, v, o, lse, do, dq, dk, dv, delta)
+        else:
+            calls = {"fwd": lambda: sta.sta_fwd_ex(qt, kt, vt, ot, lse, B, H, D, sta.STA_BF16, scale, geom, idx, nt,
+                                                   stream, prec)}
+            bwd_args = (qt, kt, vt, ot, lse, dot_, dqt, dkt, dvt, delta)
+        if not fwd_only:
+            for name, part in (("bwd_dkdv", sta.STA_BWD_DKDV), ("bwd_dq", sta.STA_BWD_DQ)):
+                calls[name] = (lambda part=part: sta.sta_bwd_ex(*bwd_args, B, H, D, sta.STA_BF16, scale, geom, idx,
+                                                               part, 0 if raster else nt, stream, lay))
+        ga = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+        gb = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+        calls["gemm_8192"] = lambda: torch.matmul(ga, gb)
+        power = power_samples(torch, calls)
+        del ga, gb
     scores = fwd_flop / (4.0 * D)
     rate = exp_rate(torch, dev)
     exp_bound = {"exps_per_fwd": scores, "measured_exp_rate_per_s": round(rate, -6),
@@ -534,6 +601,9 @@ def main():
             # the forward's secondary bound: one hardware exponential per
             # counted score (the lazy-max rule redoes a fraction of a percent)
             "exp_bound": exp_bound,
+            # socket power and GFX clock while each call runs back to back
+            # (after the timed steps; amdsmi sensors)
+            "power": power,
         },
         "roofline": roofline,
     }

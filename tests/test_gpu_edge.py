@@ -136,3 +136,36 @@ def test_batch_of_four():
     oracle."""
     _layer_vs_oracle("batch of four", (4, 8, 12), (2, 4, 4), 4, 4, 128, [(3, 3, 3), (1, 3, 3), (3, 1, 1), (1, 1, 3)],
                      "bf16", 179)
+
+
+@pytest.mark.parametrize("tiles_w", [64, 68])
+def test_key_tile_order_at_and_past_its_limit(tiles_w):
+    """The work plan orders dK/dV's key tiles by transposed-list length on
+    grids of up to 4096 tiles and keeps tile order beyond: 4 x 16 x 64 = 4096
+    tiles (ordered) and 4 x 16 x 68 = 4352 (plain order), 16-token tiles,
+    moved-inward 3x3x5 windows whose transposed lists differ in length at
+    the border.  dK/dV on whole key tiles (the least and the most attended,
+    and two seeded), dQ on rows of corner and seeded tiles, against the
+    oracle."""
+    grid, tile, windows, D = (4, 64, 4 * tiles_w), (1, 4, 4), [(3, 3, 5)], 64
+    name = "key-tile order, %d tiles" % (4 * 16 * tiles_w)
+    say("edge " + name)
+    N = int(np.prod(grid))
+    q, k, v, do = tensors(1, 1, N, D, "bf16", 181, with_dout=True)
+    layer = Layer(grid, tile, windows, None, q, k, v, "bf16", dout=do)
+    layer.forward()
+    dq, dk, dv = layer.backward()
+    torch.cuda.synchronize()
+    L, T = 16, 4 * 16 * tiles_w
+    inv = np.argsort(oracle.perm(grid, tile))                    # tile-order slot -> raster token
+    q_cnt = np.asarray(oracle.index(grid, tile, windows, None)[3])[0]
+    g = np.random.default_rng(182)
+    ktiles = [int(np.argmin(q_cnt)), int(np.argmax(q_cnt))] + [int(x) for x in g.choice(T, 2, replace=False)]
+    krows = np.sort(np.concatenate([inv[t * L:(t + 1) * L] for t in ktiles]))
+    qtiles = [0, T - 1] + [int(x) for x in g.choice(T, 2, replace=False)]
+    qrows = np.sort(np.concatenate([inv[t * L:(t + 1) * L] for t in qtiles]))
+    rq, rk, rv = oracle.bwd(q, k, v, do, grid, tile, windows, None, qrows=qrows, krows=krows)
+    pick = lambda t, rows: to_host(t.reshape(-1, D)[torch.from_numpy(rows).cuda()])
+    assert_close(pick(dq, qrows), rq, "bf16", name + " dQ")
+    assert_close(pick(dk, krows), rk, "bf16", name + " dK")
+    assert_close(pick(dv, krows), rv, "bf16", name + " dV")
