@@ -306,10 +306,13 @@ def exp_rate(torch, dev, blocks=2048, iters=1024, reps=5):
 
 def power_samples(torch, calls, seconds=2.0):
     """Socket power and GFX clock while each call in `calls` (name -> fn)
-    runs back to back for `seconds`, read every ~10 ms through amdsmi (the
-    driver's sensors; no GPU setting is touched).  Means of the samples after
-    the first third (the clock settles), with the board's power limit and an
-    idle reading; None where amdsmi is missing or fails."""
+    runs back to back for `seconds`, read through amdsmi (the driver's
+    sensors; no GPU setting is touched).  The calls are enqueued in chunks of
+    ~50 ms with the next chunk always queued, and the sensors are read only
+    while a chunk is still running, so every sample sees the GPU busy with
+    that call.  Means of the samples after the first third (the clock
+    settles), with the board's power limit and an idle reading; None where
+    amdsmi is missing or fails."""
     try:
         import amdsmi
         amdsmi.amdsmi_init()
@@ -329,17 +332,29 @@ def power_samples(torch, calls, seconds=2.0):
         out = {"idle_socket_w": idle_w,
                "power_limit_w": float(limit) / 1e6 if isinstance(limit, (int, float)) else None}
         for name, fn in calls.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
-            t0, got = time.time(), []
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            chunk = max(1, int(50.0 / max(e0.elapsed_time(e1), 1e-3)))
+            t0, got, running = time.time(), [], None
             while time.time() - t0 < seconds:
-                fn()
-                fn()
-                time.sleep(0.01)
-                got.append(read()[:2])
-                torch.cuda.synchronize()
+                for _ in range(chunk):
+                    fn()
+                queued = torch.cuda.Event()
+                queued.record()
+                if running is not None:
+                    while not running.query():
+                        got.append(read()[:2])
+                        time.sleep(0.005)
+                running = queued
+            torch.cuda.synchronize()
             got = got[len(got) // 3:]
-            out[name] = {"socket_w": round(float(np.mean([g[0] for g in got])), 1),
-                         "gfx_mhz": round(float(np.mean([g[1] for g in got])), 1), "samples": len(got)}
+            out[name] = {"socket_w": round(float(np.mean([g[0] for g in got])), 1) if got else None,
+                         "gfx_mhz": round(float(np.mean([g[1] for g in got])), 1) if got else None,
+                         "samples": len(got)}
         return out
     except Exception:
         return None
