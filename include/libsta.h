@@ -48,13 +48,21 @@
  *     for an index of I list sets and TT tiles and text pseudo-tiles), the
  *     bf16 forward also V^T tiles (see sta_fwd), the quantized forward
  *     codes and scales (see sta_fwd_ex) and sta_window_shifts tile means.
- *     They take it stream-ordered
- *     (hipMallocFromPoolAsync / hipFreeAsync on the call's stream) from one
- *     memory pool per device, created on first use and kept, with the
- *     memory it holds, until the process ends; a failed allocation returns
- *     STA_ERR_HIP before anything is launched.
+ *     They take it stream-ordered: each stream the library is called on
+ *     (up to 16 per device) keeps one cached buffer, as large as the
+ *     largest request on it, which later calls on that stream take again
+ *     without allocating or freeing (a replaced or evicted buffer is freed
+ *     with hipFreeAsync after its last use); calls under graph capture and
+ *     calls that find the buffer in use take memory from one pool per
+ *     device (hipMallocFromPoolAsync) and free it at their end
+ *     (hipFreeAsync).  Pool and buffers are created on first use and kept
+ *     until the process ends; a failed allocation returns STA_ERR_HIP
+ *     before anything is launched.
  *   - Work is enqueued on the given HIP stream (0 = the null stream) and
- *     is asynchronous; device faults surface at the caller's next sync.
+ *     is asynchronous: a call returns without waiting for the GPU (a
+ *     hipFreeAsync, taken only when a workspace grows or is not cached,
+ *     can wait for the device's previous free); device faults surface at
+ *     the caller's next sync.
  *   - Arguments are checked on the host before anything is launched: on
  *     any error nothing is written.  STA_ERR_INVALID = malformed arguments;
  *     STA_ERR_UNSUPPORTED = well-formed but not implemented (reason in
@@ -65,9 +73,10 @@
  *   - An index holds one list set per head, shared by every batch item, or
  *     one per (b, h) for windows shifted per batch item (see sta_index).
  *   - Thread-safe.  Mutable global state: a thread-local error message,
- *     the table of per-device workspace pools, whose creation is guarded
- *     by a mutex (the pools themselves are HIP objects, safe to use from
- *     several threads and streams), and sta_window_shifts_noalloc's static
+ *     the per-device workspace pools and the per-stream cached buffers,
+ *     guarded by a mutex (a buffer in use by one call is not handed to
+ *     another: concurrent calls on one stream from two threads take pool
+ *     memory), and sta_window_shifts_noalloc's static
  *     device array with its per-device address table (filled under a
  *     mutex; the array is shared by every call on a GPU, see there).
  */
@@ -240,12 +249,8 @@ sta_status sta_build_index_ex(const sta_geom *g, int32_t H, const sta_dim3 *wind
  * probabilities are rounded to bf16 before the PV product.
  * Workspace (bf16 only): the work plan (Conventions), then V transposed
  * per tile, B*H*num_tiles*D*Lp*2 bytes with Lp = L rounded up to a
- * multiple of 64, in memory taken from a per-device pool on `stream` and
- * given back on
- * `stream` after the attention kernel (hipMallocFromPoolAsync /
- * hipFreeAsync).  The pool keeps freed memory for reuse, so repeated calls
- * of one shape reach the driver only once; it holds at most the largest
- * concurrently used workspaces until the process ends.  A failed
+ * multiple of 64, in `stream`'s cached workspace (Conventions), so repeated
+ * calls of one shape on a stream reach the driver only once.  A failed
  * allocation returns STA_ERR_HIP before anything is launched.
  * Source: attention restricted to the sliding 3D window ("Fast Video
  * Generation with Sliding Tile Attention", abstract).
@@ -266,8 +271,8 @@ sta_status sta_fwd(const void *q, const void *k, const void *v, void *o, float *
  * (no accumulation into existing contents); no atomics, deterministic.
  * Needs the transposed lists (idx->q_idx, idx->q_cnt).  delta_ws is a
  * caller-owned device workspace of B*H*N floats.  bf16: the dK/dV and dQ
- * stages take their work plan (Conventions) from the pool described at
- * sta_fwd; with dK/dV it also orders each list set's key tiles by the
+ * stages take their work plan from the stream-ordered workspace
+ * (Conventions); with dK/dV it also orders each list set's key tiles by the
  * length of their transposed lists (grids of at most 4096 tiles).
  * Source: the pages' system adapts a pre-trained DiT by full-parameter
  * training through the local attention operator ("MegaSlide-DiT",
@@ -428,7 +433,7 @@ typedef struct {
  *   arithmetic where two masses agree to fp32 rounding); a query tile whose
  *   masses are all non-finite gets the zero shift.
  * Workspace: 2 * P * H * num_tiles * D * 4 bytes (P = B if per_batch, else
- * 1) from the stream-ordered pool described at sta_fwd.
+ * 1) from the stream-ordered workspace (Conventions).
  * Errors: STA_ERR_INVALID for NULL or misaligned pointers, B, H, D <= 0, a
  * negative radius, a window < 1, a non-positive or non-finite scale, an
  * unknown border, layout or dtype, per_batch not 0/1, n_text < 0;
