@@ -112,10 +112,10 @@ def parse():
 # Kernel name fragments (as rocprofv3 reports them) -> benchmark names, and
 # the sources each kernel is built from.
 KERNELS = {"fwd_bf16_kernel": "fwd", "dkdv_kernel": "bwd_dkdv", "dq_kernel": "bwd_dq", "reorder_kernel": "reorder"}
-KERNEL_SOURCES = {"fwd": ["fwd_bf16.hip", "mfma.h", "common.h"],
+KERNEL_SOURCES = {"fwd": ["fwd_bf16.hip", "tiles.h", "mfma.h", "common.h"],
                   "reorder": ["reorder.hip", "common.h"],
-                  "bwd_dkdv": ["bwd_bf16.hip", "mfma.h", "common.h"],
-                  "bwd_dq": ["bwd_bf16.hip", "mfma.h", "common.h"]}
+                  "bwd_dkdv": ["bwd_bf16.hip", "tiles.h", "mfma.h", "common.h"],
+                  "bwd_dq": ["bwd_bf16.hip", "tiles.h", "mfma.h", "common.h"]}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 

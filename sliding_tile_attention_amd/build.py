@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.hip", "workspace.hip", "reorder.hip", "index.hip", "attn_f32.hip", "fwd_bf16.hip", "fwd_fp8.hip",
            "bwd_bf16.hip", "shifts.hip", "schedule.hip"]
-HEADERS = ["common.h", "mfma.h"]
+HEADERS = ["common.h", "mfma.h", "tiles.h"]
 # Per-source extra compiler flags (none at present).
 EXTRA = {}
 

@@ -5,16 +5,6 @@
 // mask is tile-granular, so a workgroup that owns rows of one query tile
 // walks that tile's key-tile list and never masks inside a tile.
 //
-// Two launches:
-//   1. vt_kernel: V^T of every tile (and text pseudo-tile), [b,h,tile][D][Lp]
-//      with the key axis padded with zeros to Lp (a multiple of the key
-//      block), into a stream-ordered workspace.  Every V tile is read by ~45 query tiles'
-//      workgroups, so transposing it once lets the PV product fetch its
-//      operand with full-width LDS reads instead of transposing reads,
-//      which move half the bytes per LDS instruction -- the LDS port, not
-//      the matrix cores, is what bounds this kernel.
-//   2. fwd_bf16_kernel, below.
-//
 // Joint text + video sequences (MOD-DiT README, "Token-Type-Aware
 // Masking"): after its listed tiles a video query tile walks the text
 // pseudo-tiles; a text pseudo-tile's queries walk every video tile and then
@@ -22,123 +12,61 @@
 // those past any block end.
 //
 // Work decomposition
-//   workgroup = NW waves = M = NW*QB*32 consecutive query rows of one query
+//   workgroup = NW waves = M = NW*32 consecutive query rows of one query
 //   tile of one (b, h); work items are ordered head-major and each of the 8
 //   XCDs takes one contiguous range of that order, cut at equal cost
 //   (schedule.hip), so that the workgroups sharing an XCD's L2 walk
 //   neighbouring windows of the same head.
-//   The key loop runs over (listed key tile, BN-key block) pairs.  K and V^T
+//   The key loop runs over (listed key tile, BN-key block) pairs.  K and V
 //   blocks travel HBM -> LDS directly (global_load_lds, no staging
-//   registers) into a double buffer: the copy of block j+1 runs while block j
-//   is computed; one barrier per block.
+//   registers) as row tiles (tiles.h) into an NBUF-slot ring: the copy of
+//   block j+NBUF-1 runs while block j is computed; one barrier per block.
 //
-// Per wave and 32-row query block (lane l owns query row l%32):
+// Per wave (lane l owns query row l%32):
 //   S^T[BN x 32] = K_blk Q^T    (MFMA: A = K rows from LDS, B = Q in VGPRs)
 //   online softmax along the key axis, in base 2 with scale*log2(e) folded
-//   into one FMA; the running max is only moved when a block max exceeds it
-//   by more than 8 (2^8 headroom), which leaves the result exact and skips
-//   almost every rescale of the O accumulator;
-//   O^T[D x 32] += V^T_blk P^T  (MFMA: A = V^T rows from LDS, B = P in VGPRs)
+//   into one FMA; the running max is only moved when a block's partial sum
+//   of probabilities would reach 2^8, which leaves the result exact and
+//   skips almost every rescale of the O accumulator;
+//   O^T[D x 32] += V_blk^T P^T  (MFMA: A = V^T by LDS transposing reads of
+//                                the V rows, B = P in VGPRs)
 // K rows are fed permuted by sigma so that each lane's S^T registers hold 8
 // consecutive keys -- the B operand of the PV product without any shuffle.
-//
-// LDS layout: the K block is row-major [BN][D], the V^T block [D][BN]; the
-// 16-byte granules of each row are XOR-swizzled (granule c of row r stored
-// at c ^ f(r)) so that 16 lanes reading 16 consecutive rows at one logical
-// granule touch 16 distinct 16-byte bank groups -- conflict free, no padding.
+// The transposing reads (ds_read_b64_tr_b16) fetch V^T fragments straight
+// from the row tile, so V needs no transposed copy in HBM.
 #include <type_traits>
 
 #include "common.h"
 #include "mfma.h"
+#include "tiles.h"
 
 namespace sta {
-
-template <int D, int NW, int QB, int BN>
-struct FwdCfg {
-    static constexpr int THREADS = NW * 64;
-    static constexpr int M = NW * QB * 32;     // query rows per workgroup
-    static constexpr int KS = D / 16;           // reduction steps of QK^T
-    static constexpr int KB = BN / 32;          // 32-key sub-blocks
-    static constexpr int DB = D / 32;           // 32-wide column blocks of O^T
-    static constexpr int GR = D / 8;            // 16-byte granules per K row
-    static constexpr int GV = BN / 8;           // 16-byte granules per V^T row
-    static constexpr int BLK = BN * D;          // bf16 elements of one K (or V^T) block
-    static constexpr int STAGE = 2 * BLK;       // K + V^T
-    static constexpr int WAVE_ELEMS = 512;      // one wave-wide 16-byte copy = 1 KB
-    static constexpr int GRANULES = BLK / 8;    // 16-byte granules of one block
-    static constexpr int COPIES = (GRANULES + THREADS - 1) / THREADS;   // copies per thread per block
-    static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-    static_assert(GRANULES % 64 == 0, "a block is a whole number of wave-wide copies");
-};
-
-// Swizzle of a row of G 16-byte granules: rows r = 0..15 read at one logical
-// granule land in 16 distinct 16-byte slots of a 256-byte bank line.
-template <int G>
-__device__ inline int swz_row(int r)
-{
-    if constexpr (G >= 16) return r & 15;
-    else return (r / (16 / G)) & (G - 1);
-}
 
 #ifndef STA_FWD_MINB
 #define STA_FWD_MINB 3
 #endif
 
-// Key padding of the V^T workspace (a multiple of every key block size).
-constexpr int kVtPad = 64;
-
-template <int D>
-__global__ __launch_bounds__(256) void vt_kernel(const __bf16 *__restrict__ V, __bf16 *__restrict__ VT, Geo g,
-                                                 int Lp, int chunks)
-{
-    // one workgroup per 64-key chunk of one (b, h, tile)
-    __shared__ uint32_t tile[64][D / 2 + 1];   // 64 keys x D values as bf16 pairs; odd stride: no conflicts
-    const int c = (int)(blockIdx.x % (unsigned)chunks);
-    const int64_t bt = blockIdx.x / (unsigned)chunks;
-    const int64_t bh = bt / g.TT;
-    const int t = (int)(bt - bh * g.TT);
-    const Span sp = tile_span(g, t);
-    const int L = sp.len;
-    const int k0 = c * 64;
-    const __bf16 *src = V + bh * g.S * D;
-    constexpr int RG = D / 8;                 // 16-byte granules per V row
-    for (int i = threadIdx.x; i < 64 * RG; i += 256) {
-        const int r = i / RG, gc = i % RG;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (k0 + r < L) v = __builtin_nontemporal_load((const u32x4 *)(src + tile_row(g, t, k0 + r) * D + gc * 8));
-#pragma unroll
-        for (int t = 0; t < 4; ++t) tile[r][gc * 4 + t] = v[t];
-    }
-    __syncthreads();
-    // unit u: column pair p (rows 2p, 2p+1 of V^T), key group kg (8 keys)
-    __bf16 *dst = VT + bt * D * Lp + k0;
-    for (int u = threadIdx.x; u < (D / 2) * 8; u += 256) {
-        const int p = u / 8, kg = u % 8;
-        uint32_t w[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) w[j] = tile[kg * 8 + j][p];
-        u32x4 lo, hi;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            lo[t] = (w[2 * t] & 0xffffu) | (w[2 * t + 1] << 16);
-            hi[t] = (w[2 * t] >> 16) | (w[2 * t + 1] & 0xffff0000u);
-        }
-        __builtin_nontemporal_store(lo, (u32x4 *)(dst + (int64_t)(2 * p) * Lp + kg * 8));
-        __builtin_nontemporal_store(hi, (u32x4 *)(dst + (int64_t)(2 * p + 1) * Lp + kg * 8));
-    }
-}
-
-// RASTER: q, k, o, lse in raster order (whole tiles; rows of a video tile
-// gathered by tile_row, K blocks by a per-lane raster pattern).
-template <int D, int NW, int QB, int BN, bool RASTER>
+// RASTER: q, k, v, o, lse in raster order (whole tiles; rows of a video
+// tile gathered by tile_row, K and V blocks by a per-lane raster pattern).
+template <int D, int NW, int BN, int NBUF, bool RASTER>
 __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
-    const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ VT,
+    const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
     __bf16 *__restrict__ O, float *__restrict__ LSE, const int32_t *__restrict__ kv_idx,
-    const int32_t *__restrict__ kv_cnt, int max_kv, int IH, Geo g, int Lp, int rblocks, const int *__restrict__ split,
+    const int32_t *__restrict__ kv_cnt, int max_kv, int IH, Geo g, int rblocks, const int *__restrict__ split,
     float scale_log2)
 {
-    using C = FwdCfg<D, NW, QB, BN>;
-    __shared__ __attribute__((aligned(1024))) __bf16 smem[2 * C::STAGE];
+    constexpr int THREADS = NW * 64, M = NW * 32, KS = D / 16, KB = BN / 32, DB = D / 32;
+    constexpr int BLK = BN * D, STAGE = 2 * BLK;
+    static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+    // one array per ring slot: the compiler then sees that LDS reads of one
+    // slot never alias the copies in flight into another
+    __shared__ __attribute__((aligned(1024))) __bf16 slot0[STAGE], slot1[STAGE], slot2[NBUF > 2 ? STAGE : 1];
+    auto stage = [&](auto bc) -> __bf16 * {
+        constexpr int b = decltype(bc)::value;
+        if constexpr (b == 0) return slot0;
+        else if constexpr (b == 1) return slot1;
+        else return slot2;
+    };
 
     int bh, qt, rb;
     {
@@ -151,36 +79,30 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     }
     const Span qs = tile_span(g, qt);                // query rows of this tile
     const int qlen = qs.len;
-    if (rb * C::M >= qlen) return;                   // row block past a cut tile's end
+    if (rb * M >= qlen) return;                      // row block past a cut tile's end
     const int h = bh % IH;                           // list set: the head's, or (b, h)'s
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, grp = lane >> 5;
     const int64_t base = (int64_t)bh * g.S * D;
-    const int64_t vt_base = (int64_t)bh * g.TT * D * Lp;
-    const int wrow0 = rb * C::M + wave * QB * 32;   // first row of this wave inside the tile
+    const int row = rb * M + wave * 32 + l32;        // query row (inside the tile) of this lane
+    const bool row_ok = row < qlen;
 
     // Q fragments: B operand of S^T = K Q^T, lane = query row, 8 columns.
-    bf16x8 qf[QB][C::KS];
+    bf16x8 qf[KS];
+    {
+        const __bf16 *p = Q + base + slab_row<RASTER>(g, qt, qs, row_ok ? row : qlen - 1) * D + grp * 8;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = wrow0 + qb * 32 + l32;
-        const __bf16 *p = Q + base + slab_row<RASTER>(g, qt, qs, row) * D + grp * 8;
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) qf[qb][ks] = row < qlen ? ld8(p + ks * 16) : zero8();
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = row_ok ? ld8(p + ks * 16) : zero8();
     }
+    wait_vmem<0>();          // Q complete before the first copy (later waits leave copies in flight)
 
-    f32x16 acc[QB][C::DB];
-    float m_i[QB], l_i[QB];
+    f32x16 acc[DB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m_i[qb] = -INFINITY;
-        l_i[qb] = 0.f;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[qb][db][r] = 0.f;
-    }
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    float m_i = -INFINITY, l_i = 0.f;
 
     // key tiles: the window's list, or every video tile for a text query
     const bool video_q = qt < g.T;
@@ -188,121 +110,67 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     const int32_t *lst = video_q ? kv_idx + ((int64_t)h * g.T + qt) * max_kv : nullptr;
     const int nblk = walk_blocks(g, lst, cnt, BN);
 
-    // ---- per-lane offsets (bf16 elements), fixed for the whole kernel ----
-    // Copies: wave-wide copy i of a block fills granule slots
-    // (i*NW + wave)*64 + lane, i.e. row r = slot / (granules per row) and
-    // physical granule p, which must receive logical granule p ^ f(r).
-    int gk[C::COPIES], gv[C::COPIES];     // byte offsets inside a K block / V^T tile
-    int gkr[RASTER ? C::COPIES : 1];      // raster: K row r of a video block sits raster_step(r) rows on
+    // LDS offsets: a row's swizzle only XORs granule bits, and the granule
+    // bits that vary with the step (ks) or column block (db) sit above the
+    // lane's own, so every offset is one per-lane base XOR a constant.
+    const int kbase = lds_at<D>(sigma32(l32), 8 * grp);            // S^T operand, step ks: ^ 16*ks
+    const int vj = (lane & 15) >> 2, vc = lane & 3;
+    // V^T operand by transposing reads (the swizzle of row r depends on
+    // r mod 16, so each half has its own base); column block db: ^ 32*db
+    int tbase[2];
 #pragma unroll
-    for (int i = 0; i < C::COPIES; ++i) {
-        const int slot = (i * NW + wave) * 64 + lane;
-        const int r = slot / C::GR, pg = slot % C::GR;
-        gk[i] = (r * D + (pg ^ swz_row<C::GR>(r)) * 8) * 2;
-        if constexpr (RASTER) gkr[i] = (raster_step_p2(g, r) * D + (pg ^ swz_row<C::GR>(r)) * 8) * 2;
-        const int rv = slot / C::GV, pv = slot % C::GV;
-        gv[i] = (rv * Lp + (pv ^ swz_row<C::GV>(rv)) * 8) * 2;
-    }
-    // A copy slot past the block (workgroups whose thread count does not
-    // divide the block) is skipped; the test is uniform per wave.
-    auto copy_live = [&](int i) { return C::GRANULES % C::THREADS == 0 || (i * NW + wave) * 64 < C::GRANULES; };
-    // S^T operand: lane feeds K row sigma(l%32) of each 32-key sub-block;
-    // the swizzle of that row does not depend on the sub-block.
-    const int arow = sigma32(l32);
-    int kofs[C::KS];
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) kofs[ks] = arow * D + ((2 * ks + grp) ^ swz_row<C::GR>(arow)) * 8;
-    // PV operand: lane feeds V^T row d = db*32 + l%32, keys kb*32 + kk*16 +
-    // 8*grp .. +7, i.e. logical granule 4kb + 2kk + grp of that row; the
-    // swizzle depends only on l%32.
-    int vofs[C::KB][2];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            vofs[kb][kk] = l32 * BN + (((4 * kb + 2 * kk + grp) ^ swz_row<C::GV>(l32)) << 3);
+    for (int hh = 0; hh < 2; ++hh) tbase[hh] = lds_at<D>(8 * grp + 4 * hh + vj, 16 * ((lane >> 4) & 1) + 4 * vc);
 
-    // The key-block stream is walked with counters (no divisions): the
-    // copy stream is one block ahead of the compute stream; the next tile
-    // id of the list is prefetched when a tile is entered.
-    int c_e = 0, c_k0 = 0;                               // next block to copy
-    int c_tile = entry_tile(lst, cnt, g.T, 0);
-    Span c_sp = tile_span(g, c_tile);
-    int n_tile = entry_tile(lst, cnt, g.T, 1);
-    int bvalid[2];                                       // valid keys of the block in each buffer
     static_assert(!RASTER || BN == 32, "raster walk of 32-row blocks");
-    int c_roff = RASTER ? (int)raster_base(g, c_tile) : 0;   // raster row of the block (video tiles only)
-    // Issue the asynchronous copy of the next block into LDS buffer `buf`
-    // through buffer descriptors over that block: K rows past a ragged
-    // tile end read as zero (their scores are masked), V^T keys past it are
-    // the workspace's zero padding.
-    auto gload = [&](int buf) {
-        const int valid = c_sp.len - c_k0 < BN ? c_sp.len - c_k0 : BN;
-        bvalid[buf] = valid;
-        const auto rv = make_rsrc(VT + vt_base + (int64_t)c_tile * D * Lp + c_k0, (D * Lp - c_k0) * 2);
-        __bf16 *Ks = smem + buf * C::STAGE;
-        __bf16 *Vs = Ks + C::BLK;
-        if (RASTER) {
-            // whole video tile (no text rows in the raster layout): every row
-            // of the block exists; the descriptor spans the block's rows
-            // (g.rs_span from its first)
-            const auto rk = make_rsrc(K + base + (int64_t)c_roff * D, g.rs_span * D * 2);
-#pragma unroll
-            for (int i = 0; i < C::COPIES; ++i) {
-                if (!copy_live(i)) continue;
-                const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
-                b2lds16(rk, gkr[RASTER ? i : 0], Ks + lds_off);
-                b2lds16(rv, gv[i], Vs + lds_off);
-            }
+    const RowCopy<D, THREADS, BN> rc(tid);
+    const RowCopyRaster<D, THREADS, BN> rcr(tid, g);
+    ListWalk cw;                                     // next key block to copy
+    walk_init<RASTER>(cw, lst, cnt, g);
+    int bvalid[NBUF];                                // valid keys of the block in each slot
+    // Asynchronous copy of the next K and V block into ring slot bc: rows
+    // past a ragged tile end read as zero (their scores are masked below).
+    auto gload = [&](auto bc) {
+        constexpr int b = decltype(bc)::value;
+        if constexpr (RASTER) {
+            // video tiles only (no text rows in the raster layout); the
+            // descriptor spans the block's rows (g.rs_span from its first)
+            bvalid[b] = BN;
+            rcr.copy(K + base + (int64_t)cw.roff * D, g.rs_span * D * 2, stage(bc), wave, g);
+            rcr.copy(V + base + (int64_t)cw.roff * D, g.rs_span * D * 2, stage(bc) + BLK, wave, g);
         } else {
-            const auto rk = make_rsrc(K + base + (c_sp.start + c_k0) * D, valid * D * 2);
-#pragma unroll
-            for (int i = 0; i < C::COPIES; ++i) {
-                if (!copy_live(i)) continue;
-                const int lds_off = (i * NW + wave) * C::WAVE_ELEMS;
-                b2lds16(rk, gk[i], Ks + lds_off);
-                b2lds16(rv, gv[i], Vs + lds_off);
-            }
+            const int valid = cw.sp.len - cw.r0 < BN ? cw.sp.len - cw.r0 : BN;
+            const int64_t row0 = cw.sp.start + cw.r0;
+            bvalid[b] = valid;
+            rc.copy(K + base + row0 * D, valid, stage(bc), wave);
+            rc.copy(V + base + row0 * D, valid, stage(bc) + BLK, wave);
         }
-        c_k0 += BN;
-        if constexpr (RASTER) {          // the walk of g.rs_*: no divisions per block
-            c_roff += g.rs_step;
-            if ((c_k0 & g.rs_pmask) == 0) c_roff += g.rs_jump;
-        }
-        if (c_k0 >= c_sp.len) {
-            c_k0 = 0;
-            ++c_e;
-            c_tile = n_tile;
-            c_sp = tile_span(g, c_tile);
-            n_tile = entry_tile(lst, cnt, g.T, c_e + 1);
-            if constexpr (RASTER) c_roff = (int)raster_base(g, c_tile);
-        }
+        walk_next<RASTER>(cw, lst, cnt, BN, g);
     };
 
-    // One key block from LDS buffer BUF (a compile-time constant, so every
+    // One key block from ring slot BUF (a compile-time constant, so every
     // LDS address below is a per-lane register plus an immediate).
     auto step = [&](auto bufc, int blk) {
         constexpr int BUF = decltype(bufc)::value;
-        __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of block blk have landed
-        __syncthreads();                   // ... and everyone's; the other buffer is free
+        ring_wait<NBUF, 2 * decltype(rc)::COPIES>(blk, nblk);
+        if (blk + NBUF - 1 < nblk) gload(std::integral_constant<int, (BUF + NBUF - 1) % NBUF>{});
+        const __bf16 *Ks = stage(bufc);
+        const __bf16 *Vs = Ks + BLK;
         const int valid = bvalid[BUF];
-        if (blk + 1 < nblk) gload(1 - BUF);
-        const __bf16 *Ks = smem + BUF * C::STAGE;
-        const __bf16 *Vs = Ks + C::BLK;
 
-        f32x16 s[QB][C::KB];
+        f32x16 s[KB];
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+            for (int ks = 0; ks < KS; ++ks) s[kb] = mfma32(ld8(Ks + kb * 32 * D + (kbase ^ (16 * ks))), qf[ks], s[kb]);
+        }
+        if (valid < BN) {
 #pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-                const bf16x8 a = ld8(Ks + kb * 32 * D + kofs[ks]);
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(a, qf[qb][ks], s[qb][kb]);
-            }
+                for (int r = 0; r < 16; ++r)
+                    if (kb * 32 + mfma_row_sigma(lane, r) >= valid) s[kb][r] = -INFINITY;
         }
 
         // Probabilities, rounded to bf16 (the PV operand), and their sum.
@@ -310,155 +178,131 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         // below 2^8 cannot overflow and is accepted as is.  Otherwise (first
         // block, or scores that jumped) the true max is taken, O and l are
         // rescaled, and the block is recomputed.
-        bf16x8 pf[QB][C::KB][2];
+        bf16x8 pf[KB][2];
+        auto probs = [&]() {
+            const float mneg = -m_i;
+            float ls = 0.f;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            if (valid < BN) {
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int kb = 0; kb < C::KB; ++kb)
+                for (int hf = 0; hf < 2; ++hf) {
+                    bf16x8 v;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (kb * 32 + mfma_row_sigma(lane, r) >= valid) s[qb][kb][r] = -INFINITY;
-            }
-            auto probs = [&]() {
-                const float mneg = -m_i[qb];
-                float ls = 0.f;
+                    for (int i = 0; i < 8; ++i)
+                        v[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + i], scale_log2, mneg));
+                    pf[kb][hf] = v;
+                    ls = sum8(v, ls);
+                }
+            return ls;
+        };
+        float ls = probs();
+        if (__any(!(ls < 256.f))) {
+            float mx = -INFINITY;
 #pragma unroll
-                for (int kb = 0; kb < C::KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        bf16x8 v;
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = max_pair32(mx) * scale_log2;
+            const float mn = fmaxf(m_i, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_i - mn);
+            m_i = mn;
+            l_i *= alpha;
 #pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            v[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[qb][kb][8 * hf + i], scale_log2, mneg));
-                        pf[qb][kb][hf] = v;
-                        ls = sum8(v, ls);
-                    }
-                return ls;
-            };
-            float ls = probs();
-            if (__any(!(ls < 256.f))) {
-                float mx = -INFINITY;
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-                mx = max_pair32(mx) * scale_log2;
-                const float mn = fmaxf(m_i[qb], mx);
-                const float alpha = __builtin_amdgcn_exp2f(m_i[qb] - mn);
-                m_i[qb] = mn;
-                l_i[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
-                ls = probs();
-            }
-            l_i[qb] += ls;
+                for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+            ls = probs();
         }
+        l_i += ls;
 
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 a = ld8(Vs + db * 32 * BN + vofs[kb][kk]);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a, pf[qb][kb][kk], acc[qb][db]);
+                    const __bf16 *vp = Vs + (kb * 32 + kk * 16) * D;
+                    acc[db] = mfma32(cat8(ld_tr4(vp + (tbase[0] ^ (32 * db))), ld_tr4(vp + (tbase[1] ^ (32 * db)))),
+                                     pf[kb][kk], acc[db]);
                 }
     };
 
-    if (nblk > 0) gload(0);
-    for (int blk = 0; blk < nblk; blk += 2) {
-        step(std::integral_constant<int, 0>{}, blk);
-        if (blk + 1 < nblk) step(std::integral_constant<int, 1>{}, blk + 1);
-    }
+    static_for<0, NBUF - 1>([&](auto bc) {
+        if ((int)decltype(bc)::value < nblk) gload(bc);
+    });
+    for (int blk = 0; blk < nblk; blk += NBUF)
+        static_for<0, NBUF>([&](auto bc) {
+            if (blk + (int)decltype(bc)::value < nblk) step(bc, blk + (int)decltype(bc)::value);
+        });
 
     // Epilogue: lanes l and l^32 hold the two halves of row l%32's sum.
+    const float lt = sum_pair32(l_i);
+    const float inv = 1.f / lt;
+    if (row_ok) {
+        const int64_t orow = slab_row<RASTER>(g, qt, qs, row);
+        __bf16 *op = O + base + orow * D;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float lt = sum_pair32(l_i[qb]);
-        const float inv = 1.f / lt;
-        const int row = wrow0 + qb * 32 + l32;
-        if (row < qlen) {
-            const int64_t orow = slab_row<RASTER>(g, qt, qs, row);
-            __bf16 *op = O + base + orow * D;
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db)
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 v;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    bf16x4 v;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = (__bf16)(acc[qb][db][4 * j + t] * inv);
-                    *(bf16x4 *)(op + db * 32 + 8 * j + 4 * grp) = v;
-                }
-            if (grp == 0)
-                LSE[(int64_t)bh * g.S + orow] = (m_i[qb] + __log2f(lt)) * 0.69314718055994531f;
-        }
+                for (int t = 0; t < 4; ++t) v[t] = (__bf16)(acc[db][4 * j + t] * inv);
+                *(bf16x4 *)(op + db * 32 + 8 * j + 4 * grp) = v;
+            }
+        if (grp == 0) LSE[(int64_t)bh * g.S + orow] = (m_i + __log2f(lt)) * 0.69314718055994531f;
     }
 }
 
-// V^T workspace + transpose, then the attention kernel.
-template <int D, int NW, int QB, int BN>
+// Tile shape: waves per workgroup, keys per LDS block, ring slots.
+// Overridable at compile time for tuning sweeps.
+#ifndef STA_FWD_NW
+#define STA_FWD_NW 4
+#endif
+#ifndef STA_FWD_BN
+#define STA_FWD_BN 32
+#endif
+#ifndef STA_FWD_NBUF
+#define STA_FWD_NBUF 2
+#endif
+
+// The work plan, then the attention kernel.
+template <int D>
 static sta_status run_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                           float scale, const Geo &g, const sta_index &idx, hipStream_t s)
 {
-    using C = FwdCfg<D, NW, QB, BN>;
-    static_assert(kVtPad % BN == 0, "V^T padding must be a multiple of the key block");
-    const int rblocks = (g.L + C::M - 1) / C::M;
+    constexpr int NW = STA_FWD_NW, BN = STA_FWD_BN, NBUF = STA_FWD_NBUF, M = NW * 32;
+    const int rblocks = (g.L + M - 1) / M;
     const int64_t total = (int64_t)B * H * g.TT * rblocks;
     const int64_t blocks = work_blocks(total);
-    const int chunks = (g.L + kVtPad - 1) / kVtPad;
-    const int Lp = chunks * kVtPad;
-    const int64_t vt_blocks = (int64_t)B * H * g.TT * chunks;
-    if (!grid_fits(blocks, C::THREADS) || !grid_fits(vt_blocks, 256))
-        return fail(STA_ERR_UNSUPPORTED, "too many work items");
-    // workspace: the per-XCD work split, then the V^T tiles
-    const size_t plan = (plan_bytes(idx.num_heads, (int64_t)B * H) + 255) & ~(size_t)255;
-    const size_t vt_bytes = (size_t)B * H * g.TT * D * Lp * sizeof(__bf16);
+    if (!grid_fits(blocks, NW * 64)) return fail(STA_ERR_UNSUPPORTED, "too many work items");
     void *ws = nullptr;
-    sta_status st = workspace_alloc(&ws, plan + vt_bytes, s);
+    sta_status st = workspace_alloc(&ws, plan_bytes(idx.num_heads, (int64_t)B * H), s);
     if (st != STA_OK) return st;
-    void *vt = (char *)ws + plan;
     const int *split = nullptr;
     if ((st = plan_work(g, idx.kv_cnt, idx.num_heads, (int64_t)B * H, rblocks, blocks, ws, s, &split)) != STA_OK) {
         (void)workspace_free(ws, s);          // the launch error is the one reported
         return st;
     }
-    hipLaunchKernelGGL(vt_kernel<D>, dim3((unsigned)vt_blocks), dim3(256), 0, s, (const __bf16 *)v, (__bf16 *)vt,
-                       g, Lp, chunks);
     const float scale_log2 = scale * 1.4426950408889634f;
     if (g.raster)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BN, true>), dim3((unsigned)blocks), dim3(C::THREADS), 0, s,
-                           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)vt, (__bf16 *)o, lse, idx.kv_idx,
-                           idx.kv_cnt, idx.max_kv, idx.num_heads, g, Lp, rblocks, split, scale_log2);
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, NBUF, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, s,
+                           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (__bf16 *)o, lse, idx.kv_idx,
+                           idx.kv_cnt, idx.max_kv, idx.num_heads, g, rblocks, split, scale_log2);
     else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BN, false>), dim3((unsigned)blocks), dim3(C::THREADS), 0, s,
-                           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)vt, (__bf16 *)o, lse, idx.kv_idx,
-                           idx.kv_cnt, idx.max_kv, idx.num_heads, g, Lp, rblocks, split, scale_log2);
+        hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, NBUF, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, s,
+                           (const __bf16 *)q, (const __bf16 *)k, (const __bf16 *)v, (__bf16 *)o, lse, idx.kv_idx,
+                           idx.kv_cnt, idx.max_kv, idx.num_heads, g, rblocks, split, scale_log2);
     st = check_launch();
     const sta_status fs = workspace_free(ws, s);
     return st != STA_OK ? st : fs;
 }
 
-// Tile shape: waves per workgroup, 32-row query blocks per wave, keys per
-// LDS block.  Overridable at compile time for tuning sweeps.
-#ifndef STA_FWD_NW
-#define STA_FWD_NW 4
-#endif
-#ifndef STA_FWD_QB
-#define STA_FWD_QB 1
-#endif
-#ifndef STA_FWD_BN
-#define STA_FWD_BN 32
-#endif
-
 sta_status launch_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
                            int D, float scale, const Geo &g, const sta_index &idx, hipStream_t s)
 {
-    if (D == 128) return run_fwd<128, STA_FWD_NW, STA_FWD_QB, STA_FWD_BN>(q, k, v, o, lse, B, H, scale, g, idx, s);
-    return run_fwd<64, STA_FWD_NW, STA_FWD_QB, STA_FWD_BN>(q, k, v, o, lse, B, H, scale, g, idx, s);
+    if (D == 128) return run_fwd<128>(q, k, v, o, lse, B, H, scale, g, idx, s);
+    return run_fwd<64>(q, k, v, o, lse, B, H, scale, g, idx, s);
 }
 
 }  // namespace sta
