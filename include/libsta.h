@@ -46,8 +46,8 @@
  *     variants, the quantized forward included) its work plan (how the
  *     work splits over the chip's XCDs: about 4*B*H + 12*I*(TT + 1) bytes
  *     for an index of I list sets and TT tiles and text pseudo-tiles), the
- *     bf16 forward also V^T tiles (see sta_fwd), the quantized forward
- *     codes and scales (see sta_fwd_ex) and sta_window_shifts tile means.
+ *     quantized forward also codes and scales (see sta_fwd_ex), and
+ *     sta_window_shifts tile means.
  *     They take it stream-ordered: each stream the library is called on
  *     (up to 16 per device) keeps one cached buffer, as large as the
  *     largest request on it, which later calls on that stream take again
@@ -247,11 +247,9 @@ sta_status sta_build_index_ex(const sta_geom *g, int32_t H, const sta_dim3 *wind
  * q, k, v, o: [B][H][N][D] in tile order; lse: [B][H][N] fp32 in tile
  * order.  D must be 64 or 128.  bf16 uses MFMA with fp32 accumulation; the
  * probabilities are rounded to bf16 before the PV product.
- * Workspace (bf16 only): the work plan (Conventions), then V transposed
- * per tile, B*H*num_tiles*D*Lp*2 bytes with Lp = L rounded up to a
- * multiple of 64, in `stream`'s cached workspace (Conventions), so repeated
- * calls of one shape on a stream reach the driver only once.  A failed
- * allocation returns STA_ERR_HIP before anything is launched.
+ * Workspace: only the work plan (Conventions), a few tens of KB, in
+ * `stream`'s cached workspace.  A failed allocation returns STA_ERR_HIP
+ * before anything is launched.
  * Source: attention restricted to the sliding 3D window ("Fast Video
  * Generation with Sliding Tile Attention", abstract).
  */
@@ -365,8 +363,7 @@ sta_status sta_tile_reorder_ex(const void *src, void *dst, int64_t outer, int64_
  * sta_fwd with options (opts may be NULL = sta_fwd).  With opts->n_text = M
  * > 0, for query row i of a slab of N + M rows the keys j are: for i < N
  * (video) the rows of the tiles listed for tile(i) and the text rows N..;
- * for i >= N (text) every row.  Formulas, dtypes and errors as sta_fwd; the
- * bf16 workspace grows to B*H*(num_tiles + ceil(M/L))*D*Lp*2 bytes.
+ * for i >= N (text) every row.  Formulas, dtypes and errors as sta_fwd.
  * With opts->precision = STA_PREC_FP8 (bf16 tensors only) the forward runs
  * the quantized products described at sta_precision; its stream-ordered
  * workspace holds the codes and scales, about B*H*(2*(N+M) + (num_tiles +

@@ -105,11 +105,11 @@ def test_fwd_720p_sampled(cfg):
 
 
 def test_fwd_workspace_reuse_and_streams():
-    """The bf16 forward takes its V^T workspace from a stream-ordered pool:
-    interleaved calls of two shapes (the pool hands memory back and forth),
-    and a call on a second stream, must give bit-identical results to the
-    first call of each shape (the kernels are deterministic), and that first
-    call matches the oracle."""
+    """The bf16 forward takes its work plan from the stream's cached
+    workspace: interleaved calls of two shapes (the buffer is reused and
+    grows), and a call on a second stream, must give bit-identical results
+    to the first call of each shape (the kernels are deterministic), and
+    that first call matches the oracle."""
     say("fwd bf16 workspace reuse / streams")
     shapes = [((4, 8, 12), (2, 4, 4), 1, 2, 128, [(3, 3, 3), (1, 3, 3)]),
               ((6, 8, 8), (3, 4, 4), 2, 1, 128, [(3, 3, 3)])]
