@@ -236,10 +236,14 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         });
 
     // Epilogue: lanes l and l^32 hold the two halves of row l%32's sum.
+    // The lane's row is formed anew from its lane id (mbcnt), so that no
+    // address or index has to stay live through the key loop.
     const float lt = sum_pair32(l_i);
     const float inv = 1.f / lt;
-    if (row_ok) {
-        const int64_t orow = slab_row<RASTER>(g, qt, qs, row);
+    const int elane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int erow = rb * M + wave * 32 + (elane & 31), egrp = elane >> 5;
+    if (erow < qlen) {
+        const int64_t orow = slab_row<RASTER>(g, qt, qs, erow);
         __bf16 *op = O + base + orow * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -248,9 +252,9 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
                 bf16x4 v;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) v[t] = (__bf16)(acc[db][4 * j + t] * inv);
-                *(bf16x4 *)(op + db * 32 + 8 * j + 4 * grp) = v;
+                *(bf16x4 *)(op + db * 32 + 8 * j + 4 * egrp) = v;
             }
-        if (grp == 0) LSE[(int64_t)bh * g.S + orow] = (m_i + __log2f(lt)) * 0.69314718055994531f;
+        if (egrp == 0) LSE[(int64_t)bh * g.S + orow] = (m_i + __log2f(lt)) * 0.69314718055994531f;
     }
 }
 
