@@ -109,19 +109,29 @@ __global__ __launch_bounds__(256) void tile_order_kernel(const int32_t *__restri
 // the 9 cut points.  A cut inside a slab falls at its share of the slab's
 // cost: by the running slot costs when the plan orders tiles (the slots'
 // costs then fall along the slab), else spread evenly over the items.
+// Costs and order are worked on in LDS when they fit (the slab order is
+// then written out for the kernels), in the workspace otherwise.
+constexpr int kLdsSets = 1024, kLdsSlabs = 2048;
 __global__ __launch_bounds__(256) void split_kernel(const int32_t *__restrict__ cnt, int IH, int BH, Geo g,
                                                     int rblocks, int G, int tiles_at,
                                                     const long long *__restrict__ prefix, int *__restrict__ split,
                                                     int *__restrict__ order, long long *__restrict__ cost)
 {
-    if (threadIdx.x == 0) split[9] = tiles_at;
-    for (int h = threadIdx.x; h < IH; h += blockDim.x) {
+    __shared__ long long s_cost[kLdsSets];
+    __shared__ int s_order[kLdsSlabs];
+    long long *cst = IH <= kLdsSets ? s_cost : cost;
+    int *ord = BH <= kLdsSlabs ? s_order : order;
+    // one wave per list set at a time: lanes stride over its tiles, then a
+    // butterfly sum (exact: integers)
+    const int lane = threadIdx.x & 63, nwaves = blockDim.x >> 6;
+    for (int h = threadIdx.x >> 6; h < IH; h += nwaves) {
         long long c = 0;
-        for (int t = 0; t < g.T; ++t) c += cnt[(int64_t)h * g.T + t];
+        for (int t = lane; t < g.T; t += 64) c += cnt[(int64_t)h * g.T + t];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) c += __shfl_xor(c, m, 64);
         // every video row block also walks the text pseudo-tiles; every text
         // row block walks every tile
-        c += (long long)g.T * g.Tt + (long long)g.Tt * g.TT;
-        cost[h] = c;
+        if (lane == 0) cst[h] = c + (long long)g.T * g.Tt + (long long)g.Tt * g.TT;
     }
     __syncthreads();
     // rank of slab b: the slabs of higher cost, and the earlier ones of
@@ -130,34 +140,37 @@ __global__ __launch_bounds__(256) void split_kernel(const int32_t *__restrict__ 
     // slabs and list sets together keep the given order.)
     const bool sort = (long long)BH * IH <= (1LL << 26);
     for (int b = threadIdx.x; b < BH; b += blockDim.x) {
-        const long long cb = cost[b % IH];
+        const long long cb = cst[b % IH];
         long long r = 0;
         for (int j = 0; sort && j < IH; ++j) {
-            const long long cj = cost[j];
+            const long long cj = cst[j];
             if (cj > cb) r += (BH - j + IH - 1) / IH;
             else if (cj == cb) r += (b - j + IH - 1) / IH;
         }
-        order[sort ? r : b] = b;
+        ord[sort ? r : b] = b;
     }
     __syncthreads();
+    if (ord != order)
+        for (int b = threadIdx.x; b < BH; b += blockDim.x) order[b] = ord[b];
     if (threadIdx.x != 0) return;
     long long C = 0;
-    for (int b = 0; b < BH; ++b) C += cost[b % IH];
+    for (int b = 0; b < BH; ++b) C += cst[b % IH];
     const long long per = (long long)g.TT * rblocks;    // items of a slab
     const long long total = (long long)BH * per;
-    split[0] = 0;
+    int cut[9];
+    cut[0] = 0;
     long long cum = 0;
     int r = 0;                                          // slab rank
     for (int x = 1; x < 8; ++x) {
         const long long target = C * x / 8;
-        while (r < BH && cum + cost[order[r] % IH] <= target) cum += cost[order[r++] % IH];
+        while (r < BH && cum + cst[ord[r] % IH] <= target) cum += cst[ord[r++] % IH];
         long long item = (long long)r * per;
-        if (r < BH && cost[order[r] % IH] > 0) {
+        if (r < BH && cst[ord[r] % IH] > 0) {
             const long long rem = target - cum;
             if (prefix) {
                 // last slot whose running cost is <= rem, then the share of
                 // its row blocks
-                const long long *pre = prefix + (int64_t)(order[r] % IH) * (g.TT + 1);
+                const long long *pre = prefix + (int64_t)(ord[r] % IH) * (g.TT + 1);
                 int lo = 0, hi = g.TT;
                 while (hi - lo > 1) {
                     const int mid = (lo + hi) / 2;
@@ -167,17 +180,20 @@ __global__ __launch_bounds__(256) void split_kernel(const int32_t *__restrict__ 
                 const long long sc = pre[lo + 1] - pre[lo];
                 item += (long long)lo * rblocks + (sc > 0 ? (rem - pre[lo]) * rblocks / sc : 0);
             } else {
-                item += (long long)((double)rem / (double)cost[order[r] % IH] * (double)per);
+                item += (long long)((double)rem / (double)cst[ord[r] % IH] * (double)per);
             }
         }
         // at most G items per range, and no more left than the later
         // ranges can take
-        long long lo = split[x - 1], hi = lo + G;
+        long long lo = cut[x - 1], hi = lo + G;
         lo = total - (long long)(8 - x) * G > lo ? total - (long long)(8 - x) * G : lo;
         hi = hi < total ? hi : total;
-        split[x] = (int)(item < lo ? lo : item > hi ? hi : item);
+        cut[x] = (int)(item < lo ? lo : item > hi ? hi : item);
     }
-    split[8] = (int)total;
+    cut[8] = (int)total;
+#pragma unroll
+    for (int x = 0; x < 9; ++x) split[x] = cut[x];
+    split[9] = tiles_at;
 }
 
 size_t plan_bytes(int IH, int64_t BH, const Geo *tile_order) { return plan_layout(IH, BH, tile_order).bytes; }
