@@ -21,8 +21,10 @@ BF16_LSE_MAX_ABS = 2.5e-3
 
 
 def say(msg):
-    print("[gpu] " + msg, flush=True)
-    sys.stdout.flush()
+    """A progress line on the process's own stderr (not captured by pytest),
+    so that a long oracle check shows what it is doing while it runs."""
+    sys.__stderr__.write("[gpu] " + msg + "\n")
+    sys.__stderr__.flush()
 
 
 def to_dev(x, dtype):

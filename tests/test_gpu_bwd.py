@@ -145,18 +145,23 @@ def _run(w, offsets=None):
     return dq, dk, dv
 
 
+def _train_720p():
+    w = workload("720p-train")
+    say("bwd bf16 720p-train workload (full size)")
+    dq, dk, dv = _run(w)
+    inv = np.argsort(oracle.perm(w["grid"], w["tile"]))          # tile-order slot -> raster token
+    return w, dq, dk, dv, inv
+
+
 def test_bwd_720p_training_sampled():
     """Training workload at full size (115200 tokens, 24 heads, window 3x3x5)
     in the benchmark's launch configuration.  dQ: rows of the 8 corner tiles
     and one seeded tile in every head.  dK/dV: the whole key tiles 0 (12
     query tiles attend it) and (2,2,4) = 144 (140 attend it) in heads 3 and
     17.  Plus the whole-tensor identities."""
-    w = workload("720p-train")
-    say("bwd bf16 720p-train workload (full size)")
-    dq, dk, dv = _run(w)
+    w, dq, dk, dv, inv = _train_720p()
     B, H, N, D = w["q"].shape
     L = 384
-    inv = np.argsort(oracle.perm(w["grid"], w["tile"]))          # tile-order slot -> raster token
     g = np.random.default_rng(55)
     corners = [0, 9, 50, 59, 240, 249, 290, 299]                 # tile grid 5 x 6 x 10
     qrows = []
@@ -169,6 +174,24 @@ def test_bwd_720p_training_sampled():
             krows += _tile_rows(inv, h, N, L, t, range(L))
     _check_rows(w, dq, dk, dv, qrows, krows, "720p-train")
     _identities(dq, dk, dv, w["dout"], "720p-train")
+
+
+def test_bwd_720p_training_seeded_key_tiles():
+    """The same training backward: dK/dV on four more whole key tiles, seeded
+    (with the two of the test above, six key tiles in each of heads 3 and
+    17), and dQ on the rows of one seeded tile per head."""
+    w, dq, dk, dv, inv = _train_720p()
+    B, H, N, D = w["q"].shape
+    L = 384
+    g = np.random.default_rng(58)
+    ktiles = [int(t) for t in g.choice([t for t in range(300) if t not in (0, 144)], 4, replace=False)]
+    qrows, krows = [], []
+    for h in range(H):
+        qrows += _tile_rows(inv, h, N, L, int(g.integers(0, 300)), g.choice(L, 2, replace=False))
+    for h in (3, 17):
+        for t in ktiles:
+            krows += _tile_rows(inv, h, N, L, t, range(L))
+    _check_rows(w, dq, dk, dv, qrows, krows, "720p-train seeded key tiles %s" % ktiles)
 
 
 def test_bwd_mid_7680():

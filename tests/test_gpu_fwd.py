@@ -96,7 +96,7 @@ def test_fwd_720p_sampled(cfg):
     o, lse = layer.forward()
     torch.cuda.synchronize()
     B, H, N, D = w["q"].shape
-    rows = sample_rows(B, H, N, 384, w["grid"], w["tile"], 2, 4, seed=w["seed"])
+    rows = sample_rows(B, H, N, 384, w["grid"], w["tile"], 4, 4, seed=w["seed"])   # 8 corner + 4 seeded tiles
     ro, rl = oracle.fwd(w["q"], w["k"], w["v"], w["grid"], w["tile"], w["windows"], w["offsets"], rows=rows)
     o = o.reshape(-1, D)[torch.from_numpy(rows).cuda()]
     assert_close(to_host(o), ro, "bf16", "O")
