@@ -437,3 +437,31 @@ def backward(q, k, v, o, lse, dout, geom, index, scale=None, stream=None, n_text
     sta_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, D, _dtype_code(q), scale, geom, index,
                STA_BWD_ALL, n_text, stream, _LAYOUTS[layout])
     return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    """forward() and backward() as one differentiable operation: the forward
+    keeps q, k, v, o and lse for the backward, which runs on the stream that
+    autograd runs it on."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, geom, index, scale, n_text, layout):
+        o, lse = forward(q, k, v, geom, index, scale, n_text=n_text, layout=layout)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.args = (geom, index, scale, n_text, layout)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        geom, index, scale, n_text, layout = ctx.args
+        dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), geom, index, scale, n_text=n_text, layout=layout)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def attention(q, k, v, geom, index, scale=None, n_text=0, layout="tile"):
+    """Differentiable sliding-tile attention: o = forward(q, k, v, ...)[0],
+    with gradients for q, k and v through backward() (training through the
+    operator, "MegaSlide-DiT", abstract).  Same tensors, layouts and checks
+    as forward(); bf16 or fp32."""
+    return _Attention.apply(q, k, v, geom, index, scale, n_text, layout)

@@ -86,3 +86,9 @@ def test_index_rejects_bad_offsets(bad, exc, match):
 
 def test_index_is_built_on_a_gpu_device():
     _raises(ValueError, "GPU device", sta.StaIndex, GEOM, [(3, 3, 3)] * H, None, device="cpu")
+
+
+def test_attention_function_checks_like_forward():
+    q, k, v = _qkv()
+    _raises(ValueError, "GPU", sta.attention, q, k, v, GEOM, _index())
+    _raises(TypeError, "k is torch.float32", sta.attention, q, k.float(), v, GEOM, _index())
