@@ -87,3 +87,44 @@ def test_calls_return_before_the_gpu_finishes():
     t2 = time.perf_counter()
     say("workspace: enqueue %.2f ms, GPU done after %.2f ms" % ((t1 - t0) * 1e3, (t2 - t0) * 1e3))
     assert t1 - t0 < 0.3 * (t2 - t0)
+
+
+def test_threads_on_streams_and_one_shared_stream():
+    """Four host threads, each calling forward + backward ten times on a
+    stream of its own, then on one shared stream (a buffer in use by one
+    thread's call sends the other to pool memory): every result identical to
+    the single-thread reference."""
+    import threading
+    grid, tile, windows = (4, 16, 24), (2, 8, 8), [(3, 3, 3), (1, 3, 3)]
+    geom = sta.Geometry(grid, tile)
+    idx = sta.StaIndex(geom, windows)
+    main = torch.cuda.current_stream()
+    ins = [_inputs(grid, tile, 2, 64, 330 + i) for i in range(4)]
+    ref = [_layer(*x, geom, idx, main) for x in ins]
+    torch.cuda.synchronize()
+    shared = torch.cuda.Stream()
+    for label, streams in (("own streams", [torch.cuda.Stream() for _ in ins]), ("one stream", [shared] * 4)):
+        say("workspace: 4 threads, %s" % label)
+        for s in set(streams):
+            s.wait_stream(main)
+        errors = []
+
+        def work(t):
+            try:
+                torch.cuda.set_device(0)
+                for _ in range(10):
+                    got = _layer(*ins[t], geom, idx, streams[t])
+                    streams[t].synchronize()
+                    if not all(torch.equal(a, b) for a, b in zip(got, ref[t])):
+                        errors.append("thread %d differs" % t)
+                        return
+            except Exception as e:                      # reported below
+                errors.append("thread %d: %r" % (t, e))
+
+        threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+        torch.cuda.synchronize()
+        assert not errors, errors
