@@ -119,6 +119,8 @@ __device__ inline unsigned i8code(float x, float inv) { return (unsigned)(int)ri
 // pseudo-tile) of one (b, h); 4 threads per row.  Q: per-row scale folded
 // with scale * log2(e) (sq) and the LSE correction scale * <q, mean K>
 // (corr); K - mean: one scale per block (sk[bh][tile][block]).
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
 template <int D>
 __global__ __launch_bounds__(256) void quant_qk_kernel(const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K,
                                                        const float *__restrict__ kmean, uint8_t *__restrict__ Q8,
@@ -126,7 +128,11 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const __bf16 *__restrict_
                                                        float *__restrict__ corr, float *__restrict__ sk, Geo g,
                                                        int nkb, float c_log2, float scale)
 {
-    constexpr int TPR = 4, E = D / TPR;
+    // TPR threads per row, 8 consecutive values (16 bytes) each, so that the
+    // lanes of a wave read whole rows with consecutive 16-byte loads; the
+    // 64 rows of the block are taken PASSES at a time.
+    constexpr int TPR = D / 8, RPP = 256 / TPR, PASSES = kKeyBlock / RPP;
+    static_assert(kKeyBlock % RPP == 0, "block of whole passes");
     __shared__ float wmax[4];
     const int blk = (int)(blockIdx.x % nkb);
     const int64_t bt = blockIdx.x / nkb;
@@ -135,62 +141,72 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const __bf16 *__restrict_
     const Span sp = tile_span(g, t);
     const int rows = sp.len - blk * kKeyBlock < kKeyBlock ? sp.len - blk * kKeyBlock : kKeyBlock;
     if (rows <= 0) return;                           // block past a cut tile's end (uniform)
-    const int r = threadIdx.x / TPR, part = threadIdx.x % TPR;
-    const bool live = r < rows;
-    // codes, scales: tile order (the attention kernel's); inputs: the layout's rows
-    const int64_t row = bh * g.S + sp.start + (int64_t)blk * kKeyBlock + (live ? r : 0);
-    const int64_t src = bh * g.S + tile_row(g, t, blk * kKeyBlock + (live ? r : 0));
-    const float *mk = kmean + bh * D + part * E;
-    float q[E], k[E];
+    const int part = threadIdx.x % TPR;
+    const float *mk = kmean + bh * D + part * 8;
+    float m[8];
 #pragma unroll
-    for (int c = 0; c < E / 8; ++c) {
+    for (int j = 0; j < 8; ++j) m[j] = mk[j];
+    float k[PASSES][8];
+    float ka = 0.f;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+        const int r = ps * RPP + threadIdx.x / TPR;
+        const bool live = r < rows;
+        // codes, scales: tile order (the attention kernel's); inputs: the layout's rows
+        const int64_t row = bh * g.S + sp.start + (int64_t)blk * kKeyBlock + (live ? r : 0);
+        const int64_t src = bh * g.S + tile_row(g, t, blk * kKeyBlock + (live ? r : 0));
         bf16x8 a = zero8(), b = zero8();
         if (live) {
-            a = ld8(Q + src * D + part * E + 8 * c);
-            b = ld8(K + src * D + part * E + 8 * c);
+            a = ld8(Q + src * D + part * 8);
+            b = ld8(K + src * D + part * 8);
         }
+        float q[8];
+        float qa = 0.f, dq = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            q[8 * c + j] = (float)a[j];
-            k[8 * c + j] = live ? (float)b[j] - mk[8 * c + j] : 0.f;
+            q[j] = (float)a[j];
+            k[ps][j] = live ? (float)b[j] - m[j] : 0.f;
+            qa = fmaxf(qa, fabsf(q[j]));
+            ka = fmaxf(ka, fabsf(k[ps][j]));
+            dq = fmaf(q[j], m[j], dq);
+        }
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) {
+            qa = fmaxf(qa, __shfl_xor(qa, o, 64));
+            dq += __shfl_xor(dq, o, 64);
+        }
+        const float qinv = qa > 0.f ? 127.f / qa : 0.f;
+        if (live) {
+            u32x2 wq;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                wq[j] = i8code(q[4 * j], qinv) | i8code(q[4 * j + 1], qinv) << 8 | i8code(q[4 * j + 2], qinv) << 16 |
+                        i8code(q[4 * j + 3], qinv) << 24;
+            *(u32x2 *)(Q8 + row * D + part * 8) = wq;
+            if (part == 0) {
+                sq[row] = qa / 127.f * c_log2;
+                corr[row] = scale * dq;
+            }
         }
     }
-    float qa = 0.f, ka = 0.f, dq = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        qa = fmaxf(qa, fabsf(q[e]));
-        ka = fmaxf(ka, fabsf(k[e]));
-        dq = fmaf(q[e], mk[e], dq);
-    }
-    qa = fmaxf(qa, __shfl_xor(qa, 1, 64));
-    qa = fmaxf(qa, __shfl_xor(qa, 2, 64));
-    dq += __shfl_xor(dq, 1, 64);
-    dq += __shfl_xor(dq, 2, 64);
+    // the block's K scale: max |k - mean| over its rows
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) ka = fmaxf(ka, __shfl_xor(ka, o, 64));
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = ka;
     __syncthreads();
     ka = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    const float qinv = qa > 0.f ? 127.f / qa : 0.f;
     const float kinv = ka > 0.f ? 127.f / ka : 0.f;
-    if (live) {
 #pragma unroll
-        for (int c = 0; c < E / 16; ++c) {
-            u32x4 wq, wk;
+    for (int ps = 0; ps < PASSES; ++ps) {
+        const int r = ps * RPP + threadIdx.x / TPR;
+        if (r < rows) {
+            const int64_t row = bh * g.S + sp.start + (int64_t)blk * kKeyBlock + r;
+            u32x2 wk;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int e = 16 * c + 4 * j;
-                wq[j] = i8code(q[e], qinv) | i8code(q[e + 1], qinv) << 8 | i8code(q[e + 2], qinv) << 16 |
-                        i8code(q[e + 3], qinv) << 24;
-                wk[j] = i8code(k[e], kinv) | i8code(k[e + 1], kinv) << 8 | i8code(k[e + 2], kinv) << 16 |
-                        i8code(k[e + 3], kinv) << 24;
-            }
-            *(u32x4 *)(Q8 + row * D + part * E + 16 * c) = wq;
-            *(u32x4 *)(K8 + row * D + part * E + 16 * c) = wk;
-        }
-        if (part == 0) {
-            sq[row] = qa / 127.f * c_log2;
-            corr[row] = scale * dq;
+            for (int j = 0; j < 2; ++j)
+                wk[j] = i8code(k[ps][4 * j], kinv) | i8code(k[ps][4 * j + 1], kinv) << 8 |
+                        i8code(k[ps][4 * j + 2], kinv) << 16 | i8code(k[ps][4 * j + 3], kinv) << 24;
+            *(u32x2 *)(K8 + row * D + part * 8) = wk;
         }
     }
     if (threadIdx.x == 0) sk[bh * ((int64_t)g.TT * nkb) + (int64_t)t * nkb + blk] = ka / 127.f;
