@@ -59,28 +59,35 @@ template <int D>
 __global__ __launch_bounds__(256) void qstat_kernel(const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
                                                     double *__restrict__ part, int64_t S)
 {
-    constexpr int P = D / 2;            // column pairs
-    constexpr int RG = 256 / P;         // row groups
+    constexpr int TPR = D / 8;          // threads per row, 8 columns (16 bytes) each
+    constexpr int RG = 256 / TPR;       // row groups
     __shared__ double red[2][RG][D];
     const int chunk = (int)(blockIdx.x % kStatChunks);
     const int64_t bh = blockIdx.x / kStatChunks;
-    const int cp = threadIdx.x % P, rg = threadIdx.x / P;
+    const int cg = threadIdx.x % TPR, rg = threadIdx.x / TPR;
     const int64_t r0 = S * chunk / kStatChunks, r1 = S * (chunk + 1) / kStatChunks;
-    const __bf16 *kb = K + bh * S * D + 2 * cp, *vb = V + bh * S * D + 2 * cp;
-    double s0 = 0.0, s1 = 0.0;
-    float m0 = 0.f, m1 = 0.f;
-    for (int64_t r = r0 + rg; r < r1; r += RG) {
-        const bf16x2 k2 = *(const bf16x2 *)(kb + r * D);
-        const bf16x2 v2 = *(const bf16x2 *)(vb + r * D);
-        s0 += (double)(float)k2[0];
-        s1 += (double)(float)k2[1];
-        m0 = fmaxf(m0, fabsf((float)v2[0]));
-        m1 = fmaxf(m1, fabsf((float)v2[1]));
+    const __bf16 *kb = K + bh * S * D + 8 * cg, *vb = V + bh * S * D + 8 * cg;
+    double sum[8];
+    float mx[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        sum[j] = 0.0;
+        mx[j] = 0.f;
     }
-    red[0][rg][2 * cp] = s0;
-    red[0][rg][2 * cp + 1] = s1;
-    red[1][rg][2 * cp] = m0;
-    red[1][rg][2 * cp + 1] = m1;
+    for (int64_t r = r0 + rg; r < r1; r += RG) {
+        const bf16x8 k8 = ld8(kb + r * D);
+        const bf16x8 v8 = ld8(vb + r * D);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            sum[j] += (double)(float)k8[j];
+            mx[j] = fmaxf(mx[j], fabsf((float)v8[j]));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        red[0][rg][8 * cg + j] = sum[j];
+        red[1][rg][8 * cg + j] = mx[j];
+    }
     __syncthreads();
     for (int i = threadIdx.x; i < 2 * D; i += 256) {
         const int w = i / D, d = i % D;
