@@ -262,6 +262,8 @@ def probe_lib():
     lib.sta_probe_exp.restype = ctypes.c_int
     lib.sta_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.sta_probe_copy.restype = ctypes.c_int
+    lib.sta_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.sta_probe_mfma.restype = ctypes.c_int
     return lib
 
 
@@ -277,6 +279,39 @@ def calibration_copy(torch, x):
         raise RuntimeError("copy probe failed to launch")
     torch.cuda.synchronize()
     del y
+
+
+def mfma_launcher(torch, dev, blocks=4096, iters=1024):
+    """One launch of the matrix-core rate probe (v_mfma_f32_32x32x16_bf16 with
+    nothing else issued; 2 workgroups of 4 waves resident per CU, 8 rounds of
+    them) and the flop it executes."""
+    import ctypes
+    lib = probe_lib()
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        if lib.sta_probe_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters,
+                              ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("matrix-core rate probe failed to launch")
+    return launch, blocks * 4.0 * iters * 16 * 32 * 32 * 16 * 2
+
+
+def mfma_rate(torch, dev, reps=5):
+    """Sustained dense bf16 rate of the matrix instruction the attention
+    kernels use, on this board and clock, timed with HIP events (TFLOP/s)."""
+    launch, flop = mfma_launcher(torch, dev)
+    for _ in range(2):
+        launch()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return flop / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
 
 
 def exp_rate(torch, dev, blocks=2048, iters=1024, reps=5):
@@ -559,6 +594,7 @@ def main():
         ga = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
         gb = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
         calls["gemm_8192"] = lambda: torch.matmul(ga, gb)
+        calls["mfma_probe"] = mfma_launcher(torch, dev)[0]
         power = power_samples(torch, calls)
         del ga, gb
     scores = fwd_flop / (4.0 * D)
@@ -566,6 +602,9 @@ def main():
     exp_bound = {"exps_per_fwd": scores, "measured_exp_rate_per_s": round(rate, -6),
                  "exp_ms_at_that_rate": round(scores / rate * 1e3, 3),
                  "share_of_fwd_kernel": round(scores / rate * 1e3 / per["fwd"], 4)}
+    mrate = mfma_rate(torch, dev)
+    matrix_core = {"instr": "v_mfma_f32_32x32x16_bf16", "chain_rate_tflops": round(mrate, 1),
+                   "fwd_share_of_it": round(fwd_flop / (per["fwd"] * 1e-3) / 1e12 / mrate, 4)}
     tensor_bytes = B * H * S * D * 2
     reorder_gbs = 3 * 2 * tensor_bytes / (per["reorder_qkv"] * 1e-3) / 1e9 if "reorder_qkv" in per else None
     out = {
@@ -616,6 +655,11 @@ def main():
             # the forward's secondary bound: one hardware exponential per
             # counted score (the lazy-max rule redoes a fraction of a percent)
             "exp_bound": exp_bound,
+            # what the matrix cores alone sustain on this board (the probe
+            # issues nothing but the attention kernels' MFMA, on operands
+            # that change every instruction); its power and clock are in
+            # `power` under mfma_probe
+            "matrix_core_rate": matrix_core,
             # socket power and GFX clock while each call runs back to back
             # (after the timed steps; amdsmi sensors)
             "power": power,

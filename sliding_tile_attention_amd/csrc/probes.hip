@@ -14,6 +14,15 @@
 //    HBM traffic is known exactly (2 * 16 * n bytes).  The hardware traffic
 //    counters (FETCH_SIZE, WRITE_SIZE) of the attention kernels are scaled
 //    by what they read for this launch.
+//
+// 3. mfma_rate_kernel: the sustained rate of v_mfma_f32_32x32x16_bf16, the
+//    matrix instruction of the bf16 attention kernels, with nothing else
+//    issued.  Every wave runs `iters` rounds of 16 MFMAs over 4 independent
+//    accumulators; their operands rotate over 4 register sets of
+//    pseudo-random bf16 values, so that the operand data changes from one
+//    instruction to the next as it does in a real product (constant
+//    operands draw less power and would let the clock rise).  A launch
+//    executes blocks * 4 waves * iters * 16 MFMAs of 32*32*16*2 flop.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,6 +44,47 @@ __global__ __launch_bounds__(256) void exp_rate_kernel(float *__restrict__ out, 
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// a value in [-1, 1) from an integer (a 32-bit mixing function)
+__device__ inline float mix_unit(uint32_t x)
+{
+    x ^= x >> 16;
+    x *= 0x7feb352dU;
+    x ^= x >> 15;
+    x *= 0x846ca68bU;
+    x ^= x >> 16;
+    return (float)(x & 0xffff) * (2.0f / 65536.0f) - 1.0f;
+}
+
+__global__ __launch_bounds__(256, 2) void mfma_rate_kernel(float *__restrict__ out, int iters)
+{
+    const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+    bf16x8 a[4], b[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a[m][i] = (__bf16)mix_unit(t * 64u + m * 8u + i);
+            b[m][i] = (__bf16)mix_unit(t * 64u + 32u + m * 8u + i + 0x9e3779b9u);
+        }
+    f32x16 acc[4] = {};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(u + m) & 3], b[(u + 2 * m + 1) & 3], acc[m], 0, 0,
+                                                                 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s += acc[m][i];
+    out[t] = s;
+}
 
 // grid-stride copy: granule i of src to granule i of dst
 __global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
@@ -68,6 +118,16 @@ int sta_probe_copy(const void *src, void *dst, int64_t bytes, void *stream)
     const int64_t n = bytes / 16;
     hipLaunchKernelGGL(copy_probe_kernel, dim3(4096), dim3(256), 0, (hipStream_t)stream, (const u32x4 *)src,
                        (u32x4 *)dst, n);
+    return (int)hipGetLastError();
+}
+
+// Enqueues one matrix-core rate launch of `blocks` workgroups of 256
+// threads on `stream`; out holds blocks * 256 floats (device).  Returns 0, or
+// the HIP error code of the launch (1 for a non-positive size).
+int sta_probe_mfma(float *out, int blocks, int iters, void *stream)
+{
+    if (blocks <= 0 || iters < 0) return 1;
+    hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
     return (int)hipGetLastError();
 }
 

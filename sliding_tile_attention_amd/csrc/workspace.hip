@@ -1,7 +1,7 @@
 // Stream-ordered device workspace for kernels that need a temporary buffer
-// (every attention launch's work plan, the bf16 forward's transposed V
-// tiles, the quantized forward's codes, the window-shift producer's tile
-// means).
+// (every attention launch's work plan, with the key-tile order of the
+// dK/dV walk; the quantized forward's codes and scales; the window-shift
+// producer's tile means).
 //
 // Each device gets one memory pool of its own whose release threshold is
 // unlimited (memory freed on a stream goes back to the pool, not to the
