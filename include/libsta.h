@@ -271,7 +271,9 @@ sta_status sta_fwd(const void *q, const void *k, const void *v, void *o, float *
  * caller-owned device workspace of B*H*N floats.  bf16: the dK/dV and dQ
  * stages take their work plan from the stream-ordered workspace
  * (Conventions); with dK/dV it also orders each list set's key tiles by the
- * length of their transposed lists (grids of at most 4096 tiles).
+ * length of their transposed lists (grids of at most 4096 tiles), and the
+ * same workspace holds B*H*N more floats, -lse*log2(e) of every row, which a
+ * pass before the dK/dV kernel writes.
  * Source: the pages' system adapts a pre-trained DiT by full-parameter
  * training through the local attention operator ("MegaSlide-DiT",
  * abstract), which needs these gradients.

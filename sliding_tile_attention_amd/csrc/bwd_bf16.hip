@@ -9,7 +9,9 @@
 // P enters the products rounded to bf16; dK/dV also form dS from that
 // rounded P (dQ from the fp32 one).
 // Three kernels, no atomics, deterministic:
-//   1. bwd_pre: Delta_i = <dO_i, O_i> (fp32), one pass over O and dO.
+//   1. bwd_pre: Delta_i = <dO_i, O_i> (fp32), one pass over O and dO; and
+//      for dK/dV, lse_log2: -lse_i log2(e) of every row, so that their loop
+//      forms each exponent with one multiply-add.
 //   2. dq: query-stationary, walks each query tile's key-tile list (same
 //      schedule as the forward) and accumulates dQ in registers.
 //   3. dkdv: key-stationary, walks each key tile's TRANSPOSED list (the query
@@ -67,6 +69,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16 *__restrict__
     if (row < rows && part == 0) delta[row] = s;
 }
 
+
+// -lse * log2(e) of every row (the base-2 exponent offset of dK/dV's P).
+__global__ __launch_bounds__(256) void lse_log2_kernel(const float *__restrict__ lse, float *__restrict__ out,
+                                                       int64_t rows)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < rows) out[i] = -lse[i] * 1.4426950408889634f;
+}
 
 // ---------------------------------------------------------------------------
 // 2. dQ (query-stationary).
@@ -237,15 +247,15 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
 template <int D, int NW, int BQ, int NBUF, bool RASTER>
 __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
-    const __bf16 *__restrict__ dO, const float *__restrict__ LSE, const float *__restrict__ Delta,
+    const __bf16 *__restrict__ dO, const float *__restrict__ NLSE2, const float *__restrict__ Delta,
     __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, const int32_t *__restrict__ q_idx,
     const int32_t *__restrict__ q_cnt, int max_q, int IH, Geo g, int rblocks, const int *__restrict__ split, float scale_log2,
     float scale)
 {
     constexpr int THREADS = NW * 64, M = NW * 32, KS = D / 16, SB = BQ / 32, DB = D / 32;
     constexpr int BLK = BQ * D;
-    constexpr int SROWS = BQ > 64 ? BQ : 64;        // LSE / Delta slots (one 64-lane dword copy each)
-    constexpr int STAGE = 2 * BLK + 2 * SROWS * 2;  // Q, dO (bf16) + LSE, Delta (fp32 as 2 bf16 slots each)
+    constexpr int SROWS = BQ > 64 ? BQ : 64;        // -lse log2(e) / Delta slots (one 64-lane dword copy each)
+    constexpr int STAGE = 2 * BLK + 2 * SROWS * 2;  // Q, dO (bf16) + -lse log2(e), Delta (fp32 as 2 bf16 slots each)
     static_assert(BQ <= 64 && BQ % 32 == 0, "query block of 32 or 64 rows");
     __shared__ __attribute__((aligned(1024))) __bf16 slot0[STAGE], slot1[STAGE], slot2[NBUF > 2 ? STAGE : 1];
     auto stage = [&](auto bc) -> __bf16 * {
@@ -332,8 +342,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
             rc.copy(Q + base + row0 * D, valid, stage(bc), wave);
             rc.copy(dO + base + row0 * D, valid, stage(bc) + BLK, wave);
         }
-        if (wave == 0) {                            // LSE and Delta of the block's rows (zero past the end)
-            const auto rl = make_rsrc(LSE + sbase + row0, valid * 4);
+        if (wave == 0) {                            // -lse log2(e) and Delta of the block's rows (zero past the end)
+            const auto rl = make_rsrc(NLSE2 + sbase + row0, valid * 4);
             const auto rd = make_rsrc(Delta + sbase + row0, valid * 4);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void *)(stage(bc) + 2 * BLK),
                                                      4, lo, 0, 0, 0);
@@ -378,8 +388,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
                 bf16x8 pv;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float lse = i < 4 ? l0[i] : l1[i - 4];
-                    pv[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc[8 * kk + i], scale_log2, -lse * 1.4426950408889634f));
+                    const float nl2 = i < 4 ? l0[i] : l1[i - 4];
+                    pv[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc[8 * kk + i], scale_log2, nl2));
                 }
                 pf[kk] = pv;
             }
@@ -391,11 +401,15 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
             for (int kk = 0; kk < 2; ++kk) {
                 const int qr = sb * 32 + 16 * kk + 8 * grp;
                 const f32x4 d0 = *(const f32x4 *)(Dl + qr), d1 = *(const f32x4 *)(Dl + qr + 4);
+                // the rounded P as fp32, taken from its packed bf16 pairs
+                // (one shift or mask each)
+                const u32x4 pw = __builtin_bit_cast(u32x4, pf[kk]);
                 bf16x8 dv8;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float dl = i < 4 ? d0[i] : d1[i - 4];
-                    dv8[i] = (__bf16)((float)pf[kk][i] * (acc[8 * kk + i] - dl));
+                    const float p = __uint_as_float((i & 1) ? (pw[i >> 1] & 0xffff0000u) : (pw[i >> 1] << 16));
+                    dv8[i] = (__bf16)(p * (acc[8 * kk + i] - dl));
                 }
                 dsf[kk] = dv8;
             }
@@ -478,11 +492,14 @@ static sta_status run_bwd(const void *q, const void *k, const void *v, const voi
     // listed tile pairs, counted from either list)
     void *ws = nullptr;
     const int *split = nullptr;
-    // (with dK/dV, the key tiles in order of their transposed-list lengths)
+    // (with dK/dV, the key tiles in order of their transposed-list lengths,
+    // and after the plan, at a 256-byte boundary, -lse log2(e) of every row)
+    float *nlse2 = nullptr;
     if (parts & (STA_BWD_DKDV | STA_BWD_DQ)) {
         const bool kv = parts & STA_BWD_DKDV;
-        if ((st = workspace_alloc(&ws, plan_bytes(idx.num_heads, (int64_t)B * H, kv ? &g : nullptr), s)) != STA_OK)
-            return st;
+        const size_t plan = (plan_bytes(idx.num_heads, (int64_t)B * H, kv ? &g : nullptr) + 255) & ~(size_t)255;
+        if ((st = workspace_alloc(&ws, plan + (kv ? (size_t)rows * 4 : 0), s)) != STA_OK) return st;
+        if (kv) nlse2 = (float *)((char *)ws + plan);
         if ((st = plan_work(g, idx.kv_cnt, idx.num_heads, (int64_t)B * H, rblocks, blocks, ws, s, &split,
                             kv ? idx.q_cnt : nullptr)) != STA_OK) {
             (void)workspace_free(ws, s);      // the launch error is the one reported
@@ -499,13 +516,15 @@ static sta_status run_bwd(const void *q, const void *k, const void *v, const voi
         if ((st = check_launch()) != STA_OK) return done(st);
     }
     if (parts & STA_BWD_DKDV) {
+        hipLaunchKernelGGL(lse_log2_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, lse, nlse2, rows);
+        if ((st = check_launch()) != STA_OK) return done(st);
         if (g.raster)
             hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ, STA_BWD_NBUF, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, s, Q, K,
-                               V, dO, lse, (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q,
+                               V, dO, (const float *)nlse2, (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q,
                                idx.num_heads, g, rblocks, split, scale_log2, scale);
         else
             hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ, STA_BWD_NBUF, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, s, Q, K,
-                               V, dO, lse, (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q,
+                               V, dO, (const float *)nlse2, (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q,
                                idx.num_heads, g, rblocks, split, scale_log2, scale);
         if ((st = check_launch()) != STA_OK) return done(st);
     }
