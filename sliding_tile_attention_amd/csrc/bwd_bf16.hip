@@ -10,8 +10,11 @@
 // rounded P (dQ from the fp32 one).
 // Three kernels, no atomics, deterministic:
 //   1. bwd_pre: Delta_i = <dO_i, O_i> (fp32), one pass over O and dO; and
-//      for dK/dV, lse_log2: -lse_i log2(e) of every row, so that their loop
-//      forms each exponent with one multiply-add.
+//      for dK/dV, lse_log2: -lse_i log2(e) and -Delta_i of every row, so
+//      that their loop forms each exponent with one multiply-add and starts
+//      the dP product from -Delta.
+// Both dP products accumulate onto -Delta (the MFMA chain's initial value),
+// so dS = P * (that sum) needs no subtraction.
 //   2. dq: query-stationary, walks each query tile's key-tile list (same
 //      schedule as the forward) and accumulates dQ in registers.
 //   3. dkdv: key-stationary, walks each key tile's TRANSPOSED list (the query
@@ -70,12 +73,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const __bf16 *__restrict__
 }
 
 
-// -lse * log2(e) of every row (the base-2 exponent offset of dK/dV's P).
-__global__ __launch_bounds__(256) void lse_log2_kernel(const float *__restrict__ lse, float *__restrict__ out,
+// -lse * log2(e) of every row (the base-2 exponent offset of dK/dV's P) and
+// -Delta (the initial value of its dP product).
+__global__ __launch_bounds__(256) void lse_log2_kernel(const float *__restrict__ lse, const float *__restrict__ delta,
+                                                       float *__restrict__ nlse2, float *__restrict__ ndelta,
                                                        int64_t rows)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < rows) out[i] = -lse[i] * 1.4426950408889634f;
+    if (i < rows) {
+        nlse2[i] = -lse[i] * 1.4426950408889634f;
+        ndelta[i] = -delta[i];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -128,7 +136,13 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
         of[ks] = ld8(dO + base + grow * D + ks * 16 + grp * 8);
     }
     const float nlse2 = -LSE[(int64_t)bh * g.S + grow] * 1.4426950408889634f;
-    const float dlt = Delta[(int64_t)bh * g.S + grow];
+    // -Delta of the lane's row in every register: the dP^T chain's start
+    f32x16 ndl;
+    {
+        const float nd = -Delta[(int64_t)bh * g.S + grow];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ndl[r] = nd;
+    }
     // Q, dO, LSE, Delta complete before the first copy (later waits leave
     // copies in flight, which would otherwise guard every use of them).
     wait_vmem<0>();
@@ -186,13 +200,16 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) { s[kb][r] = 0.f; dp[kb][r] = 0.f; }
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+            dp[kb] = ndl;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 s[kb] = mfma32(ld8(Ks + kb * 32 * D + (kbase ^ (16 * ks))), qf[ks], s[kb]);
                 dp[kb] = mfma32(ld8(Vs + kb * 32 * D + (kbase ^ (16 * ks))), of[ks], dp[kb]);
             }
         }
+        // issue order: two (K, V) row-read pairs ahead of the MFMA pairs
+        sched_chain<2, 2 * KB * KS, 2, 2, 1>();
         bf16x8 dsf[KB][2];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -203,7 +220,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
                 for (int i = 0; i < 8; ++i) {
                     const int r = 8 * hf + i;
                     const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, nlse2));
-                    v[i] = (__bf16)(p * (dp[kb][r] - dlt));
+                    v[i] = (__bf16)(p * dp[kb][r]);
                 }
                 dsf[kb][hf] = v;
             }
@@ -217,6 +234,8 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
                     acc[db] = mfma32(cat8(ld_tr4(kp + (tbase[0] ^ (32 * db))), ld_tr4(kp + (tbase[1] ^ (32 * db)))),
                                      dsf[kb][kk], acc[db]);
                 }
+        // the K^T fragments (two transposing reads each) two ahead
+        sched_chain<2, DB * KB * 2, 1, 2, 1>();
     };
 
     static_for<0, NBUF - 1>([&](auto bc) {
@@ -247,15 +266,15 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
 template <int D, int NW, int BQ, int NBUF, bool RASTER>
 __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
     const __bf16 *__restrict__ Q, const __bf16 *__restrict__ K, const __bf16 *__restrict__ V,
-    const __bf16 *__restrict__ dO, const float *__restrict__ NLSE2, const float *__restrict__ Delta,
+    const __bf16 *__restrict__ dO, const float *__restrict__ NLSE2, const float *__restrict__ NDelta,
     __bf16 *__restrict__ dK, __bf16 *__restrict__ dV, const int32_t *__restrict__ q_idx,
     const int32_t *__restrict__ q_cnt, int max_q, int IH, Geo g, int rblocks, const int *__restrict__ split, float scale_log2,
     float scale)
 {
     constexpr int THREADS = NW * 64, M = NW * 32, KS = D / 16, SB = BQ / 32, DB = D / 32;
     constexpr int BLK = BQ * D;
-    constexpr int SROWS = BQ > 64 ? BQ : 64;        // -lse log2(e) / Delta slots (one 64-lane dword copy each)
-    constexpr int STAGE = 2 * BLK + 2 * SROWS * 2;  // Q, dO (bf16) + -lse log2(e), Delta (fp32 as 2 bf16 slots each)
+    constexpr int SROWS = BQ > 64 ? BQ : 64;        // -lse log2(e) / -Delta slots (one 64-lane dword copy each)
+    constexpr int STAGE = 2 * BLK + 2 * SROWS * 2;  // Q, dO (bf16) + -lse log2(e), -Delta (fp32 as 2 bf16 slots each)
     static_assert(BQ <= 64 && BQ % 32 == 0, "query block of 32 or 64 rows");
     __shared__ __attribute__((aligned(1024))) __bf16 slot0[STAGE], slot1[STAGE], slot2[NBUF > 2 ? STAGE : 1];
     auto stage = [&](auto bc) -> __bf16 * {
@@ -342,9 +361,9 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
             rc.copy(Q + base + row0 * D, valid, stage(bc), wave);
             rc.copy(dO + base + row0 * D, valid, stage(bc) + BLK, wave);
         }
-        if (wave == 0) {                            // -lse log2(e) and Delta of the block's rows (zero past the end)
+        if (wave == 0) {                            // -lse log2(e) and -Delta of the block's rows (zero past the end)
             const auto rl = make_rsrc(NLSE2 + sbase + row0, valid * 4);
-            const auto rd = make_rsrc(Delta + sbase + row0, valid * 4);
+            const auto rd = make_rsrc(NDelta + sbase + row0, valid * 4);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void *)(stage(bc) + 2 * BLK),
                                                      4, lo, 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -371,9 +390,10 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) {
-            // S, then P (rounded to bf16: the dV operand), then dP and
-            // dS = P (dP - Delta) from the same rounded P, so that S and dP
-            // are never live together.
+            // S, then P (rounded to bf16: the dV operand), then dP - Delta
+            // (the chain starts from the rows' -Delta) and dS = P (dP -
+            // Delta) from the same rounded P, so that S and dP are never
+            // live together.
             // Registers 8kk..8kk+7 hold query rows sb*32 + 16kk + 8grp + 0..7.
             f32x16 acc;
 #pragma unroll
@@ -394,22 +414,31 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
                 pf[kk] = pv;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc = mfma32(ld8(Os + sb * 32 * D + (kb_ ^ (16 * ks))), vf[ks], acc);
-#pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const int qr = sb * 32 + 16 * kk + 8 * grp;
                 const f32x4 d0 = *(const f32x4 *)(Dl + qr), d1 = *(const f32x4 *)(Dl + qr + 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[8 * kk + i] = d0[i];
+                    acc[8 * kk + 4 + i] = d1[i];
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc = mfma32(ld8(Os + sb * 32 * D + (kb_ ^ (16 * ks))), vf[ks], acc);
+            // issue order of the S and dP chains: the Q and dO row reads
+            // four fragments ahead of the MFMAs (each MFMA otherwise waits
+            // for its own read)
+            sched_chain<4, 2 * KS, 1, 1>();
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
                 // the rounded P as fp32, taken from its packed bf16 pairs
                 // (one shift or mask each)
                 const u32x4 pw = __builtin_bit_cast(u32x4, pf[kk]);
                 bf16x8 dv8;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float dl = i < 4 ? d0[i] : d1[i - 4];
                     const float p = __uint_as_float((i & 1) ? (pw[i >> 1] & 0xffff0000u) : (pw[i >> 1] << 16));
-                    dv8[i] = (__bf16)(p * (acc[8 * kk + i] - dl));
+                    dv8[i] = (__bf16)(p * acc[8 * kk + i]);
                 }
                 dsf[kk] = dv8;
             }
@@ -493,13 +522,18 @@ static sta_status run_bwd(const void *q, const void *k, const void *v, const voi
     void *ws = nullptr;
     const int *split = nullptr;
     // (with dK/dV, the key tiles in order of their transposed-list lengths,
-    // and after the plan, at a 256-byte boundary, -lse log2(e) of every row)
-    float *nlse2 = nullptr;
+    // and after the plan, at 256-byte boundaries, -lse log2(e) and -Delta of
+    // every row)
+    float *nlse2 = nullptr, *ndelta = nullptr;
     if (parts & (STA_BWD_DKDV | STA_BWD_DQ)) {
         const bool kv = parts & STA_BWD_DKDV;
         const size_t plan = (plan_bytes(idx.num_heads, (int64_t)B * H, kv ? &g : nullptr) + 255) & ~(size_t)255;
-        if ((st = workspace_alloc(&ws, plan + (kv ? (size_t)rows * 4 : 0), s)) != STA_OK) return st;
-        if (kv) nlse2 = (float *)((char *)ws + plan);
+        const size_t row_bytes = ((size_t)rows * 4 + 255) & ~(size_t)255;
+        if ((st = workspace_alloc(&ws, plan + (kv ? 2 * row_bytes : 0), s)) != STA_OK) return st;
+        if (kv) {
+            nlse2 = (float *)((char *)ws + plan);
+            ndelta = (float *)((char *)ws + plan + row_bytes);
+        }
         if ((st = plan_work(g, idx.kv_cnt, idx.num_heads, (int64_t)B * H, rblocks, blocks, ws, s, &split,
                             kv ? idx.q_cnt : nullptr)) != STA_OK) {
             (void)workspace_free(ws, s);      // the launch error is the one reported
@@ -516,15 +550,16 @@ static sta_status run_bwd(const void *q, const void *k, const void *v, const voi
         if ((st = check_launch()) != STA_OK) return done(st);
     }
     if (parts & STA_BWD_DKDV) {
-        hipLaunchKernelGGL(lse_log2_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, lse, nlse2, rows);
+        hipLaunchKernelGGL(lse_log2_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, lse,
+                           (const float *)delta, nlse2, ndelta, rows);
         if ((st = check_launch()) != STA_OK) return done(st);
         if (g.raster)
             hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ, STA_BWD_NBUF, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, s, Q, K,
-                               V, dO, (const float *)nlse2, (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q,
+                               V, dO, (const float *)nlse2, (const float *)ndelta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q,
                                idx.num_heads, g, rblocks, split, scale_log2, scale);
         else
             hipLaunchKernelGGL((dkdv_kernel<D, NW, BQ, STA_BWD_NBUF, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, s, Q, K,
-                               V, dO, (const float *)nlse2, (const float *)delta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q,
+                               V, dO, (const float *)nlse2, (const float *)ndelta, (__bf16 *)dk, (__bf16 *)dv, idx.q_idx, idx.q_cnt, idx.max_q,
                                idx.num_heads, g, rblocks, split, scale_log2, scale);
         if ((st = check_launch()) != STA_OK) return done(st);
     }

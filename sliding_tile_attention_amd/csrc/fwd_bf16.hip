@@ -57,6 +57,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
 {
     constexpr int THREADS = NW * 64, M = NW * 32, KS = D / 16, KB = BN / 32, DB = D / 32;
     constexpr int BLK = BN * D, STAGE = 2 * BLK;
+    constexpr int SREAD = 3, VREAD = 2;              // LDS operand reads kept ahead of the MFMAs
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
     // one array per ring slot: the compiler then sees that LDS reads of one
     // slot never alias the copies in flight into another
@@ -165,6 +166,10 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) s[kb] = mfma32(ld8(Ks + kb * 32 * D + (kbase ^ (16 * ks))), qf[ks], s[kb]);
         }
+        // Issue order of the S^T chain: the LDS reads of K run SREAD
+        // fragments ahead of the MFMAs (left to itself the compiler keeps
+        // one or two, and each MFMA then waits for its own read).
+        sched_chain<SREAD, KB * KS, 1, 1>();
         if (valid < BN) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -225,6 +230,8 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
                     acc[db] = mfma32(cat8(ld_tr4(vp + (tbase[0] ^ (32 * db))), ld_tr4(vp + (tbase[1] ^ (32 * db)))),
                                      pf[kb][kk], acc[db]);
                 }
+        // PV: the V^T fragments (two transposing reads each) VREAD ahead
+        sched_chain<VREAD, DB * KB * 2, 1, 2, 1>();
     };
 
     static_for<0, NBUF - 1>([&](auto bc) {
