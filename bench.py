@@ -264,6 +264,8 @@ def probe_lib():
     lib.sta_probe_copy.restype = ctypes.c_int
     lib.sta_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.sta_probe_mfma.restype = ctypes.c_int
+    lib.sta_probe_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.sta_probe_lds.restype = ctypes.c_int
     return lib
 
 
@@ -312,6 +314,28 @@ def mfma_rate(torch, dev, reps=5):
     e1.record(stream)
     torch.cuda.synchronize()
     return flop / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
+
+
+def lds_rate(torch, dev, blocks=2048, iters=1024, reps=5):
+    """Rate of plain conflict-free 16-byte LDS reads on this GPU (TB/s), the
+    row reads that feed the attention kernels' MFMAs."""
+    import ctypes
+    lib = probe_lib()
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    launch = lambda: lib.sta_probe_lds(ctypes.c_void_p(out.data_ptr()), blocks, iters,
+                                       ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(2):
+        if launch() != 0:
+            raise RuntimeError("LDS-rate probe failed to launch")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return blocks * 256.0 * iters * 16 * 16 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
 
 
 def exp_rate(torch, dev, blocks=2048, iters=1024, reps=5):
@@ -605,6 +629,11 @@ def main():
     mrate = mfma_rate(torch, dev)
     matrix_core = {"instr": "v_mfma_f32_32x32x16_bf16", "chain_rate_tflops": round(mrate, 1),
                    "fwd_share_of_it": round(fwd_flop / (per["fwd"] * 1e-3) / 1e12 / mrate, 4)}
+    # every bf16 attention kernel reads one 1 KB operand fragment from LDS
+    # per 32x32x16 MFMA it executes (32768 flop): LDS bytes = executed flop / 32
+    executed = {"fwd": fwd_flop, "bwd_dkdv": 2.0 * fwd_flop, "bwd_dq": 1.5 * fwd_flop}
+    lds = {"probe_ds_read_b128_tbs": round(lds_rate(torch, dev), 1),
+           "kernels_tbs": {n: round(f / 32.0 / (per[n] * 1e-3) / 1e12, 1) for n, f in executed.items() if n in per}}
     tensor_bytes = B * H * S * D * 2
     reorder_gbs = 3 * 2 * tensor_bytes / (per["reorder_qkv"] * 1e-3) / 1e9 if "reorder_qkv" in per else None
     out = {
@@ -660,6 +689,10 @@ def main():
             # that change every instruction); its power and clock are in
             # `power` under mfma_probe
             "matrix_core_rate": matrix_core,
+            # LDS operand reads of the attention kernels against a plain
+            # stream of the same reads (the LDS port is not their limit
+            # while the first stays well below the second)
+            "lds_read": lds,
             # socket power and GFX clock while each call runs back to back
             # (after the timed steps; amdsmi sensors)
             "power": power,

@@ -23,6 +23,14 @@
 //    instruction to the next as it does in a real product (constant
 //    operands draw less power and would let the clock rise).  A launch
 //    executes blocks * 4 waves * iters * 16 MFMAs of 32*32*16*2 flop.
+//
+// 4. lds_rate_kernel: the rate of plain 16-byte LDS reads (ds_read_b128), the
+//    row reads the attention kernels feed their MFMAs with.  Each workgroup
+//    fills a 32 KB LDS tile, then every thread runs `iters` rounds of 16
+//    reads, consecutive lanes on consecutive 16-byte granules (no bank
+//    conflicts), the granule moving by one per round so that no read is
+//    loop-invariant; the XOR of what it read is written out.  A launch reads
+//    blocks * 256 * iters * 16 * 16 bytes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -95,6 +103,22 @@ __global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4 *__restrict
         __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+__global__ __launch_bounds__(256) void lds_rate_kernel(uint32_t *__restrict__ out, int iters)
+{
+    constexpr int G = 2048;                          // 16-byte granules: 32 KB
+    __shared__ u32x4 tile[G];
+    for (int i = threadIdx.x; i < G; i += 256) tile[i] = (u32x4){(uint32_t)i, (uint32_t)i * 3u, ~(uint32_t)i, 7u};
+    __syncthreads();
+    u32x4 x = {0u, 0u, 0u, 0u};
+    int g = threadIdx.x;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) x ^= tile[(g + (G / 16) * k) & (G - 1)];   // 16 distinct granules
+        g = (g + 1) & (G - 1);
+    }
+    out[blockIdx.x * 256u + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
+}
+
 }  // namespace
 
 extern "C" {
@@ -118,6 +142,16 @@ int sta_probe_copy(const void *src, void *dst, int64_t bytes, void *stream)
     const int64_t n = bytes / 16;
     hipLaunchKernelGGL(copy_probe_kernel, dim3(4096), dim3(256), 0, (hipStream_t)stream, (const u32x4 *)src,
                        (u32x4 *)dst, n);
+    return (int)hipGetLastError();
+}
+
+// Enqueues one LDS read-rate launch of `blocks` workgroups of 256 threads
+// on `stream`; out holds blocks * 256 uint32 (device).  Returns 0, or the HIP
+// error code of the launch (1 for a non-positive size).
+int sta_probe_lds(uint32_t *out, int blocks, int iters, void *stream)
+{
+    if (blocks <= 0 || iters < 0) return 1;
+    hipLaunchKernelGGL(lds_rate_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
     return (int)hipGetLastError();
 }
 

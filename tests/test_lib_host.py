@@ -38,19 +38,21 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_measurement_probes_load_and_reject_bad_sizes():
-    """The benchmark's probe library (exponential rate, matrix-core rate, copy
-    calibration) loads beside libsta and rejects sizes before launching
-    anything."""
+    """The benchmark's probe library (exponential rate, matrix-core rate, LDS
+    read rate, copy calibration) loads beside libsta and rejects sizes before
+    launching anything."""
     path = os.path.join(os.path.dirname(sta.LIB_PATH), "libsta_probe.so")
     lib = ctypes.CDLL(path)
     lib.sta_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.sta_probe_exp.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.sta_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.sta_probe_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     assert lib.sta_probe_copy(None, None, 0, None) == 1
     assert lib.sta_probe_copy(None, None, 24, None) == 1       # not a multiple of 16
     assert lib.sta_probe_exp(None, 0, 16, None) == 1
     assert lib.sta_probe_mfma(None, 0, 16, None) == 1
     assert lib.sta_probe_mfma(None, 4, -1, None) == 1
+    assert lib.sta_probe_lds(None, 0, 16, None) == 1
 
 
 def test_status_strings_and_version():
