@@ -6,8 +6,8 @@
 // for Efficient Video Diffusion", abstract):
 //   P = exp(s - lse),  dP = dO V^T,  Delta = rowsum(dO o O),
 //   dS = P o (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
-// P enters the products rounded to bf16; dK/dV also form dS from that
-// rounded P (dQ from the fp32 one).
+// P enters the dV product rounded to bf16; both kernels form dS from the
+// fp32 P.
 // Three kernels, no atomics, deterministic:
 //   1. bwd_pre: Delta_i = <dO_i, O_i> (fp32), one pass over O and dO; and
 //      for dK/dV, lse_log2: -lse_i log2(e) and -Delta_i of every row, so
@@ -196,46 +196,62 @@ __global__ __launch_bounds__(NW * 64, 2) void dq_kernel(
         const __bf16 *Ks = stage(bufc);
         const __bf16 *Vs = Ks + BLK;
 
-        f32x16 s[KB], dp[KB];
+        static_assert(KB == 1, "one 32-key block per step");
+        // S^T and dP^T chains interleaved: pairs (K, V row fragments) read
+        // QD pairs ahead into a ring of registers; compiler fences keep
+        // that issue order (left to itself the compiler issued each pair of
+        // reads just before its MFMAs, which then waited for them).
+        constexpr int QD = 2;
+        f32x16 s0, dp0 = ndl;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int r = 0; r < 16; ++r) s0[r] = 0.f;
+        bf16x8 rk[QD], rv[QD];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-            dp[kb] = ndl;
+        for (int j = 0; j < QD; ++j) {
+            rk[j] = ld8(Ks + (kbase ^ (16 * j)));
+            rv[j] = ld8(Vs + (kbase ^ (16 * j)));
+        }
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s[kb] = mfma32(ld8(Ks + kb * 32 * D + (kbase ^ (16 * ks))), qf[ks], s[kb]);
-                dp[kb] = mfma32(ld8(Vs + kb * 32 * D + (kbase ^ (16 * ks))), of[ks], dp[kb]);
+        for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);
+            s0 = mfma32(rk[ks % QD], qf[ks], s0);
+            dp0 = mfma32(rv[ks % QD], of[ks], dp0);
+            if (ks + QD < KS) {
+                rk[ks % QD] = ld8(Ks + (kbase ^ (16 * (ks + QD))));
+                rv[ks % QD] = ld8(Vs + (kbase ^ (16 * (ks + QD))));
             }
         }
-        // issue order: two (K, V) row-read pairs ahead of the MFMA pairs
-        sched_chain<2, 2 * KB * KS, 2, 2, 1>();
-        bf16x8 dsf[KB][2];
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 dsf[2];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int hf = 0; hf < 2; ++hf) {
+            bf16x8 v;
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                bf16x8 v;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int r = 8 * hf + i;
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale_log2, nlse2));
-                    v[i] = (__bf16)(p * dp[kb][r]);
-                }
-                dsf[kb][hf] = v;
+            for (int i = 0; i < 8; ++i) {
+                const int r = 8 * hf + i;
+                const float p = __builtin_amdgcn_exp2f(fmaf(s0[r], scale_log2, nlse2));
+                v[i] = (__bf16)(p * dp0[r]);
             }
+            dsf[hf] = v;
+        }
+        // dQ^T += K^T dS^T: the K^T fragments (two transposing reads each)
+        // QT ahead
+        constexpr int QT = 3, NT = 2 * DB;
+        auto tfrag = [&](int j) -> bf16x8 {
+            const int db = j >> 1, kk = j & 1;
+            const __bf16 *kp = Ks + kk * 16 * D;
+            return cat8(ld_tr4(kp + (tbase[0] ^ (32 * db))), ld_tr4(kp + (tbase[1] ^ (32 * db))));
+        };
+        bf16x8 tr[QT];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int j = 0; j < QT; ++j) tr[j] = tfrag(j);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const __bf16 *kp = Ks + (kb * 32 + kk * 16) * D;
-                    acc[db] = mfma32(cat8(ld_tr4(kp + (tbase[0] ^ (32 * db))), ld_tr4(kp + (tbase[1] ^ (32 * db)))),
-                                     dsf[kb][kk], acc[db]);
-                }
-        // the K^T fragments (two transposing reads each) two ahead
-        sched_chain<2, DB * KB * 2, 1, 2, 1>();
+        for (int j = 0; j < NT; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            acc[j >> 1] = mfma32(tr[j % QT], dsf[j & 1], acc[j >> 1]);
+            if (j + QT < NT) tr[j % QT] = tfrag(j + QT);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     static_for<0, NBUF - 1>([&](auto bc) {
@@ -390,67 +406,80 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) {
-            // S, then P (rounded to bf16: the dV operand), then dP - Delta
-            // (the chain starts from the rows' -Delta) and dS = P (dP -
-            // Delta) from the same rounded P, so that S and dP are never
-            // live together.
             // Registers 8kk..8kk+7 hold query rows sb*32 + 16kk + 8grp + 0..7.
-            f32x16 acc;
+            // The S and dP chains as one run of 2*KS MFMAs whose A operands
+            // (Q, then dO row fragments) are read PD fragments ahead into a
+            // ring of registers; compiler fences keep that issue order (left
+            // to itself the compiler issued each read just before its MFMA,
+            // which then waited for it).  S and dP are live together (255
+            // VGPRs, no spills).
+            constexpr int PD = 3;
+            f32x16 acc, dpa;
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc = mfma32(ld8(Qs + sb * 32 * D + (kb_ ^ (16 * ks))), kf[ks], acc);
+            for (int kk = 0; kk < 2; ++kk) {           // the dP chain starts from -Delta
+                const int qr = sb * 32 + 16 * kk + 8 * grp;
+                const f32x4 d0 = *(const f32x4 *)(Dl + qr), d1 = *(const f32x4 *)(Dl + qr + 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dpa[8 * kk + i] = d0[i];
+                    dpa[8 * kk + 4 + i] = d1[i];
+                }
+            }
+            auto frag = [&](int j) -> bf16x8 {
+                return j < KS ? ld8(Qs + sb * 32 * D + (kb_ ^ (16 * j))) : ld8(Os + sb * 32 * D + (kb_ ^ (16 * (j - KS))));
+            };
+            bf16x8 ring[PD];
+#pragma unroll
+            for (int j = 0; j < PD; ++j) ring[j] = frag(j);
+#pragma unroll
+            for (int j = 0; j < 2 * KS; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (j < KS) acc = mfma32(ring[j % PD], kf[j], acc);
+                else dpa = mfma32(ring[j % PD], vf[j - KS], dpa);
+                if (j + PD < 2 * KS) ring[j % PD] = frag(j + PD);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // P (fp32 in place of S; bf16 for the dV product), dS = P (dP - Delta)
             bf16x8 pf[2], dsf[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const int qr = sb * 32 + 16 * kk + 8 * grp;
                 const f32x4 l0 = *(const f32x4 *)(Ls + qr), l1 = *(const f32x4 *)(Ls + qr + 4);
-                bf16x8 pv;
+                bf16x8 pv, dv8;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float nl2 = i < 4 ? l0[i] : l1[i - 4];
-                    pv[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc[8 * kk + i], scale_log2, nl2));
+                    const float p = __builtin_amdgcn_exp2f(fmaf(acc[8 * kk + i], scale_log2, nl2));
+                    pv[i] = (__bf16)p;
+                    dv8[i] = (__bf16)(p * dpa[8 * kk + i]);
                 }
                 pf[kk] = pv;
-            }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int qr = sb * 32 + 16 * kk + 8 * grp;
-                const f32x4 d0 = *(const f32x4 *)(Dl + qr), d1 = *(const f32x4 *)(Dl + qr + 4);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[8 * kk + i] = d0[i];
-                    acc[8 * kk + 4 + i] = d1[i];
-                }
-            }
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc = mfma32(ld8(Os + sb * 32 * D + (kb_ ^ (16 * ks))), vf[ks], acc);
-            // issue order of the S and dP chains: the Q and dO row reads
-            // four fragments ahead of the MFMAs (each MFMA otherwise waits
-            // for its own read)
-            sched_chain<4, 2 * KS, 1, 1>();
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                // the rounded P as fp32, taken from its packed bf16 pairs
-                // (one shift or mask each)
-                const u32x4 pw = __builtin_bit_cast(u32x4, pf[kk]);
-                bf16x8 dv8;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float p = __uint_as_float((i & 1) ? (pw[i >> 1] & 0xffff0000u) : (pw[i >> 1] << 16));
-                    dv8[i] = (__bf16)(p * acc[8 * kk + i]);
-                }
                 dsf[kk] = dv8;
             }
+            // dV += P^T dO, dK += dS^T Q: their B fragments (two transposing
+            // reads each) PT MFMAs ahead
+            constexpr int PT = 2, NT = 4 * DB;
+            auto tfrag = [&](int j) -> bf16x8 {
+                const int db = j >> 2, kk = (j >> 1) & 1;
+                const int off = (sb * 32 + kk * 16) * D;
+                const int t0 = tb0 ^ (32 * db), t1 = tb1 ^ (32 * db);
+                const __bf16 *src = (j & 1) ? Qs : Os;
+                return cat8(ld_tr4(src + off + t0), ld_tr4(src + off + t1));
+            };
+            bf16x8 tr[PT];
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+            for (int j = 0; j < PT; ++j) tr[j] = tfrag(j);
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const int off = (sb * 32 + kk * 16) * D;
-                    const int t0 = tb0 ^ (32 * db), t1 = tb1 ^ (32 * db);
-                    dv[db] = mfma32(pf[kk], cat8(ld_tr4(Os + off + t0), ld_tr4(Os + off + t1)), dv[db]);
-                    dk[db] = mfma32(dsf[kk], cat8(ld_tr4(Qs + off + t0), ld_tr4(Qs + off + t1)), dk[db]);
-                }
+            for (int j = 0; j < NT; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                const int db = j >> 2, kk = (j >> 1) & 1;
+                if (j & 1) dk[db] = mfma32(dsf[kk], tr[j % PT], dk[db]);
+                else dv[db] = mfma32(pf[kk], tr[j % PT], dv[db]);
+                if (j + PT < NT) tr[j % PT] = tfrag(j + PT);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 

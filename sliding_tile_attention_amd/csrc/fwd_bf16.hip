@@ -57,7 +57,6 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
 {
     constexpr int THREADS = NW * 64, M = NW * 32, KS = D / 16, KB = BN / 32, DB = D / 32;
     constexpr int BLK = BN * D, STAGE = 2 * BLK;
-    constexpr int SREAD = 3, VREAD = 2;              // LDS operand reads kept ahead of the MFMAs
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
     // one array per ring slot: the compiler then sees that LDS reads of one
     // slot never alias the copies in flight into another
@@ -158,18 +157,25 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         const __bf16 *Vs = Ks + BLK;
         const int valid = bvalid[BUF];
 
+        // S^T chain: the K row fragments read FD ahead into a ring of
+        // registers; compiler fences keep that issue order (left to itself
+        // the compiler issued each read just before its MFMA, which then
+        // waited for it)
+        static_assert(KB == 1, "one 32-key block per step");
+        constexpr int FD = 3;
         f32x16 s[KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int r = 0; r < 16; ++r) s[0][r] = 0.f;
+        bf16x8 rk[FD];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        for (int j = 0; j < FD; ++j) rk[j] = ld8(Ks + (kbase ^ (16 * j)));
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) s[kb] = mfma32(ld8(Ks + kb * 32 * D + (kbase ^ (16 * ks))), qf[ks], s[kb]);
+        for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);
+            s[0] = mfma32(rk[ks % FD], qf[ks], s[0]);
+            if (ks + FD < KS) rk[ks % FD] = ld8(Ks + (kbase ^ (16 * (ks + FD))));
         }
-        // Issue order of the S^T chain: the LDS reads of K run SREAD
-        // fragments ahead of the MFMAs (left to itself the compiler keeps
-        // one or two, and each MFMA then waits for its own read).
-        sched_chain<SREAD, KB * KS, 1, 1>();
+        __builtin_amdgcn_sched_barrier(0);
         if (valid < BN) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -220,18 +226,23 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
         }
         l_i += ls;
 
+        // PV: the V^T fragments (two transposing reads each) FV ahead
+        constexpr int FV = 3, NV = 2 * DB;
+        auto vfrag = [&](int j) -> bf16x8 {
+            const __bf16 *vp = Vs + (j & 1) * 16 * D;
+            const int db = j >> 1;
+            return cat8(ld_tr4(vp + (tbase[0] ^ (32 * db))), ld_tr4(vp + (tbase[1] ^ (32 * db))));
+        };
+        bf16x8 rv[FV];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int j = 0; j < FV; ++j) rv[j] = vfrag(j);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const __bf16 *vp = Vs + (kb * 32 + kk * 16) * D;
-                    acc[db] = mfma32(cat8(ld_tr4(vp + (tbase[0] ^ (32 * db))), ld_tr4(vp + (tbase[1] ^ (32 * db)))),
-                                     pf[kb][kk], acc[db]);
-                }
-        // PV: the V^T fragments (two transposing reads each) VREAD ahead
-        sched_chain<VREAD, DB * KB * 2, 1, 2, 1>();
+        for (int j = 0; j < NV; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
+            acc[j >> 1] = mfma32(rv[j % FV], pf[0][j & 1], acc[j >> 1]);
+            if (j + FV < NV) rv[j % FV] = vfrag(j + FV);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     static_for<0, NBUF - 1>([&](auto bc) {

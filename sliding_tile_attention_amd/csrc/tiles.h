@@ -110,26 +110,6 @@ __device__ inline void ring_wait(int blk, int nblk)
     barrier_nofence();
 }
 
-// Issue order for a run of N MFMAs fed by LDS reads (compiler scheduling
-// groups; no effect on the arithmetic): first AHEAD operands' reads (PER
-// read instructions each), then each MFMA (MPER at a time) followed by the
-// reads of the next operand, then the last AHEAD MFMAs.  Placed after the
-// code of the run, in the same basic block.  SYNC separates independent
-// orderings of one block.
-template <int AHEAD, int N, int MPER, int PER, int SYNC = 0>
-__device__ inline void sched_chain()
-{
-    static_assert(AHEAD >= 1 && AHEAD <= N && N % MPER == 0, "chain shape");
-    constexpr int kMfma = 0x008, kDsRead = 0x100;
-    __builtin_amdgcn_sched_group_barrier(kDsRead, AHEAD * PER, SYNC);
-#pragma unroll
-    for (int i = 0; i < N / MPER - AHEAD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kMfma, MPER, SYNC);
-        __builtin_amdgcn_sched_group_barrier(kDsRead, PER, SYNC);
-    }
-    __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD * MPER, SYNC);
-}
-
 template <int I, int N, typename F>
 __device__ inline void static_for(F &&f)
 {
