@@ -46,7 +46,8 @@
  *     variants, the quantized forward included) its work plan (how the
  *     work splits over the chip's XCDs: about 4*B*H + 12*I*(TT + 1) bytes
  *     for an index of I list sets and TT tiles and text pseudo-tiles), the
- *     quantized forward also codes and scales (see sta_fwd_ex), and
+ *     dK/dV stage of the backward also 8 bytes per row (see sta_bwd), the
+ *     quantized forward codes and scales (see sta_fwd_ex), and
  *     sta_window_shifts tile means.
  *     They take it stream-ordered: each stream the library is called on
  *     (up to 16 per device) keeps one cached buffer, as large as the
@@ -272,8 +273,9 @@ sta_status sta_fwd(const void *q, const void *k, const void *v, void *o, float *
  * stages take their work plan from the stream-ordered workspace
  * (Conventions); with dK/dV it also orders each list set's key tiles by the
  * length of their transposed lists (grids of at most 4096 tiles), and the
- * same workspace holds B*H*N more floats, -lse*log2(e) of every row, which a
- * pass before the dK/dV kernel writes.
+ * same workspace holds 2*B*H*N more floats, -lse*log2(e) and -Delta of
+ * every row, which a pass before the dK/dV kernel writes (Delta is read
+ * from delta_ws, so a call of the dK/dV stage alone needs it filled).
  * Source: the pages' system adapts a pre-trained DiT by full-parameter
  * training through the local attention operator ("MegaSlide-DiT",
  * abstract), which needs these gradients.
