@@ -431,6 +431,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
                 return j < KS ? ld8(Qs + sb * 32 * D + (kb_ ^ (16 * j))) : ld8(Os + sb * 32 * D + (kb_ ^ (16 * (j - KS))));
             };
             bf16x8 ring[PD];
+            __builtin_amdgcn_s_setprio(3);         // MFMA phase: issue ahead of the other wave's vector work
 #pragma unroll
             for (int j = 0; j < PD; ++j) ring[j] = frag(j);
 #pragma unroll
@@ -441,6 +442,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
                 if (j + PD < 2 * KS) ring[j % PD] = frag(j + PD);
             }
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
             // P (fp32 in place of S; bf16 for the dV product), dS = P (dP - Delta)
             bf16x8 pf[2], dsf[2];
 #pragma unroll
@@ -469,6 +471,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
                 return cat8(ld_tr4(src + off + t0), ld_tr4(src + off + t1));
             };
             bf16x8 tr[PT];
+            __builtin_amdgcn_s_setprio(3);
 #pragma unroll
             for (int j = 0; j < PT; ++j) tr[j] = tfrag(j);
 #pragma unroll
@@ -480,6 +483,7 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
                 if (j + PT < NT) tr[j % PT] = tfrag(j + PT);
             }
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
         }
     };
 

@@ -167,6 +167,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[0][r] = 0.f;
         bf16x8 rk[FD];
+        __builtin_amdgcn_s_setprio(3);             // MFMA phase: issue ahead of other waves' vector work
 #pragma unroll
         for (int j = 0; j < FD; ++j) rk[j] = ld8(Ks + (kbase ^ (16 * j)));
 #pragma unroll
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
             if (ks + FD < KS) rk[ks % FD] = ld8(Ks + (kbase ^ (16 * (ks + FD))));
         }
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         if (valid < BN) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -234,6 +236,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
             return cat8(ld_tr4(vp + (tbase[0] ^ (32 * db))), ld_tr4(vp + (tbase[1] ^ (32 * db))));
         };
         bf16x8 rv[FV];
+        __builtin_amdgcn_s_setprio(3);
 #pragma unroll
         for (int j = 0; j < FV; ++j) rv[j] = vfrag(j);
 #pragma unroll
@@ -243,6 +246,7 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
             if (j + FV < NV) rv[j % FV] = vfrag(j + FV);
         }
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     static_for<0, NBUF - 1>([&](auto bc) {
