@@ -299,3 +299,41 @@ def test_f32_window_options():
     rq, rk, rv = oracle.bwd(q, k, v, do, grid, tile, windows, off, border="truncate")
     for name, got, ref in (("O", o, ro), ("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
         assert_close(to_host(got), ref, "f32", name)
+
+
+def test_bwd_stages_called_separately():
+    """The backward stages as separate calls (Delta, then dK/dV and dQ in
+    either order, and dK/dV alone after a Delta call) give the same bits as
+    one call of all stages: dK/dV reads Delta from delta_ws through its
+    per-row pre-pass (-lse log2 e, -Delta), and each call takes and returns
+    its own workspace."""
+    import sliding_tile_attention_amd as sta
+    from tests.gpu_util import to_dev
+
+    grid, tile, D = (12, 16, 24), (6, 8, 8), 128
+    windows = [(3, 3, 3), (1, 3, 3), (3, 3, 5)]
+    say("bwd stages called separately " + str(grid))
+    geom = sta.Geometry(grid, tile)
+    idx = sta.StaIndex(geom, windows)
+    N = geom.tokens
+    q, k, v, do = (to_dev(x, "bf16") for x in tensors(1, len(windows), N, D, "bf16", 97, with_dout=True))
+    o, lse = sta.forward(q, k, v, geom, idx)
+    stream = torch.cuda.current_stream()
+
+    def run(stages):
+        dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+        delta = torch.full_like(lse, float("nan"))
+        for p in stages:
+            sta.sta_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, delta, 1, len(windows), D, sta.STA_BF16, D ** -0.5,
+                           geom, idx, p, 0, stream, sta.STA_LAYOUT_TILE)
+        torch.cuda.synchronize()
+        return dq, dk, dv
+
+    ref = run([sta.STA_BWD_ALL])
+    for stages in ([sta.STA_BWD_DELTA, sta.STA_BWD_DKDV, sta.STA_BWD_DQ],
+                   [sta.STA_BWD_DELTA, sta.STA_BWD_DQ, sta.STA_BWD_DKDV],
+                   [sta.STA_BWD_DELTA | sta.STA_BWD_DQ, sta.STA_BWD_DKDV]):
+        got = run(stages)
+        for a, b, nm in zip(got, ref, ("dQ", "dK", "dV")):
+            assert torch.equal(a, b), "%s differs for stages %s" % (nm, stages)
+    assert all(torch.isfinite(t.float()).all() for t in ref)
