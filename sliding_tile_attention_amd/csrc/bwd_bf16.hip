@@ -517,9 +517,10 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
 
 // ---------------------------------------------------------------------------
 
-// Tile shapes (overridable at compile time for tuning sweeps): waves per
-// workgroup, keys per block in dQ, query rows per block in dK/dV, LDS ring
-// depth.
+// Tile shapes: waves per workgroup, LDS ring depth, keys per block in dQ,
+// query rows per block in dK/dV.  The dQ operand rings walk one 32-key block
+// per step, so its key block stays 32 rows wide (the dQ step asserts it); the
+// others may be set at compile time for tuning sweeps.
 #ifndef STA_BWD_NW
 #define STA_BWD_NW 4
 #endif

@@ -280,8 +280,10 @@ __global__ __launch_bounds__(NW * 64, STA_FWD_MINB) void fwd_bf16_kernel(
     }
 }
 
-// Tile shape: waves per workgroup, keys per LDS block, ring slots.
-// Overridable at compile time for tuning sweeps.
+// Tile shape: waves per workgroup, keys per LDS block, ring slots.  The
+// operand rings of the step walk one 32-key block per step, so the key block
+// stays 32 rows wide (the step asserts it); the wave count and the LDS ring
+// depth may be set at compile time for tuning sweeps.
 #ifndef STA_FWD_NW
 #define STA_FWD_NW 4
 #endif
