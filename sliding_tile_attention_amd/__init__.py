@@ -403,8 +403,28 @@ def tile_reorder(x, geom, inverse=False, out=None, stream=None, n_text=0):
     between raster and tile order (the n_text text rows after the grid's
     tokens stay in place); returns a new tensor (or writes `out`)."""
     S = geom.tokens + n_text
-    assert x.is_contiguous() and x.shape[-2] == S
-    out = torch.empty_like(x) if out is None else out
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch tensor")
+    if x.dim() < 2 or x.shape[-2] != S:
+        raise ValueError("x must be [..., %d, C] (%d grid tokens + %d text rows), got shape %s" % (
+            S, geom.tokens, n_text, tuple(x.shape)))
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    else:
+        if not isinstance(out, torch.Tensor):
+            raise TypeError("out must be a torch tensor")
+        if out.shape != x.shape or out.dtype != x.dtype:
+            raise ValueError("out is %s %s, x is %s %s" % (out.dtype, tuple(out.shape), x.dtype, tuple(x.shape)))
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+        if out.device != x.device:
+            raise ValueError("out is on %s, x on %s" % (out.device, x.device))
+    if x.device.type != "cuda":
+        raise ValueError("libsta computes on a GPU: x is on %s" % x.device)
+    if x.numel() == 0:
+        return out
     row_bytes = x.shape[-1] * x.element_size()
     outer = x.numel() // (S * x.shape[-1])
     sta_tile_reorder_ex(x, out, outer, row_bytes, geom, inverse, n_text, stream)

@@ -235,6 +235,7 @@ static_assert(sizeof(sta_status) == 4 && sizeof(sta_dtype) == 4 && sizeof(sta_bo
                   sizeof(sta_bwd_part) == 4 && sizeof(sta_precision) == 4 && sizeof(sta_layout) == 4,
               "ABI enums are 32-bit");
 
+// Largest candidate count and search region of the window-shift producer.
 static const int64_t kMaxShiftCandidates = 4096;
 static const int64_t kMaxShiftRegion = 8192;
 
@@ -515,8 +516,6 @@ sta_status sta_bwd(const void *q, const void *k, const void *v, const void *o, c
     return sta_bwd_parts(q, k, v, o, lse, dout, dq, dk, dv, delta_ws, B, H, D, dtype, scale, g, idx,
                          STA_BWD_ALL, stream);
 }
-
-// Largest candidate count and search region of the window-shift producer.
 
 sta_status sta_window_shifts(const void *q, const void *k, int32_t B, int32_t H, int32_t D, sta_dtype dtype,
                              float scale, const sta_geom *g, const sta_dim3 *windows_host,

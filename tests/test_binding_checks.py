@@ -92,3 +92,16 @@ def test_attention_function_checks_like_forward():
     q, k, v = _qkv()
     _raises(ValueError, "GPU", sta.attention, q, k, v, GEOM, _index())
     _raises(TypeError, "k is torch.float32", sta.attention, q, k.float(), v, GEOM, _index())
+
+
+def test_tile_reorder_checks_input_and_out():
+    x = torch.zeros(B, H, S, D, dtype=torch.bfloat16)
+    _raises(ValueError, r"\[\.\.\., 384, C\]", sta.tile_reorder, x[:, :, :100], GEOM)
+    _raises(ValueError, "x must be contiguous", sta.tile_reorder,
+            torch.zeros(B, H, D, S, dtype=torch.bfloat16).transpose(2, 3), GEOM)
+    # an out smaller than x, of another dtype, or strided would be written past its end or misread
+    _raises(ValueError, "out is", sta.tile_reorder, x, GEOM, out=torch.zeros(B, 1, S, D, dtype=torch.bfloat16))
+    _raises(ValueError, "out is", sta.tile_reorder, x, GEOM, out=torch.zeros_like(x, dtype=torch.float32))
+    _raises(ValueError, "out must be contiguous", sta.tile_reorder, x, GEOM,
+            out=torch.zeros(B, H, D, S, dtype=torch.bfloat16).transpose(2, 3))
+    _raises(ValueError, "GPU", sta.tile_reorder, x, GEOM)
