@@ -266,6 +266,9 @@ def probe_lib():
     lib.sta_probe_mfma.restype = ctypes.c_int
     lib.sta_probe_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.sta_probe_lds.restype = ctypes.c_int
+    lib.sta_probe_block_copy.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.sta_probe_block_copy.restype = ctypes.c_int
     return lib
 
 
@@ -316,6 +319,96 @@ def mfma_rate(torch, dev, reps=5):
     return flop / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
 
 
+def probe_launchers(torch, dev):
+    """Launch functions of the single-unit probes, each with the units one
+    launch issues: the matrix instruction (flop), 16-byte LDS reads (bytes),
+    exponentials (count), and 16 KB key/value block copies into LDS (bytes)
+    from a 2 MB region that stays in L2 and from a 1 GB region that streams
+    from HBM (3072 workgroups of 4 waves, 512 blocks each)."""
+    import ctypes
+    lib = probe_lib()
+    stream = torch.cuda.current_stream()
+    sp = lambda: ctypes.c_void_p(stream.cuda_stream)
+    out = torch.empty(3072 * 256, dtype=torch.int32, device=dev)
+    bufs = {"l2_copy_probe": torch.zeros(128 * 16384, dtype=torch.uint8, device=dev),
+            "hbm_copy_probe": torch.zeros(65536 * 16384, dtype=torch.uint8, device=dev)}
+
+    def checked(name, rc):
+        if rc != 0:
+            raise RuntimeError("%s failed to launch" % name)
+
+    mfma, mfma_flop = mfma_launcher(torch, dev)
+    calls = {"mfma_probe": (mfma, mfma_flop, "flop"),
+             "lds_probe": (lambda: checked("LDS-rate probe", lib.sta_probe_lds(ctypes.c_void_p(out.data_ptr()), 2048,
+                                                                               1024, sp())),
+                           2048 * 256.0 * 1024 * 16 * 16, "byte"),
+             "exp_probe": (lambda: checked("exponential probe", lib.sta_probe_exp(ctypes.c_void_p(out.data_ptr()),
+                                                                                  2048, 1024, sp())),
+                           2048 * 256.0 * 1024 * 16, "exp")}
+    for name, buf in bufs.items():
+        calls[name] = (lambda buf=buf, name=name: checked(name, lib.sta_probe_block_copy(
+            ctypes.c_void_p(buf.data_ptr()), buf.numel(), 3072, 512, ctypes.c_void_p(out.data_ptr()), sp())),
+            3072 * 512 * 16384.0, "byte")
+    return calls, (out, bufs)
+
+
+def timed_rate(torch, fn, units, reps=5):
+    """units per second of fn (HIP events over `reps` launches)."""
+    for _ in range(2):
+        fn()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return units / (e0.elapsed_time(e1) / reps * 1e-3)
+
+
+def block_copy_bytes(lens, lists, counts, batch, row_bytes, rows_per_wg=128):
+    """Bytes an attention kernel copies from global memory into LDS in one
+    launch: each workgroup (4 waves of 32 rows) of a stationary tile copies
+    every block of the tiles in that tile's list, `row_bytes` per listed row
+    (K and V rows for the forward and dQ; Q, dO, and the two per-row floats
+    for dK/dV); lens[t] = rows of tile t, list sets shared by `batch` items."""
+    total = 0.0
+    for h in range(counts.shape[0]):
+        for t in range(counts.shape[1]):
+            total += np.ceil(lens[t] / rows_per_wg) * lens[lists[h, t, :counts[h, t]]].sum()
+    return total * batch * row_bytes
+
+
+def energy_model(power, probes, rates, kernels, per):
+    """Energy per unit of each probe above the idle board (J), and for each
+    attention kernel the power its units would draw at those energies
+    against the power measured under it.  Each probe's energy is taken at the
+    clock the board ran it at."""
+    idle = power["idle_socket_w"]
+    e = {n: (power[n]["socket_w"] - idle) / rates[n] for n in probes if power.get(n) and power[n]["socket_w"]}
+    if len(e) != len(probes):
+        return None
+    out = {"pj_per_unit_above_idle": {n: round(e[n] * 1e12, 3) for n in probes},
+           "unit": {n: probes[n][2] for n in probes},
+           "probe_rate_per_s": {n: float("%.4g" % rates[n]) for n in probes},
+           "probe_clock_mhz": {n: power[n]["gfx_mhz"] for n in probes}, "kernels": {}}
+    # HBM blocks also pass through L2 into LDS: their extra energy is the
+    # HBM probe's less the L2 probe's
+    price = {"mfma_flop": e["mfma_probe"], "lds_read_bytes": e["lds_probe"], "exps": e["exp_probe"],
+             "l2_to_lds_bytes": e["l2_copy_probe"], "hbm_bytes": e["hbm_copy_probe"] - e["l2_copy_probe"]}
+    for name, units in kernels.items():
+        if name not in per or not power.get(name) or power[name]["socket_w"] is None:
+            continue
+        t = per[name] * 1e-3
+        watts = {u: units[u] * price[u] / t for u in units if units[u] is not None}
+        out["kernels"][name] = {"units_per_launch": {u: float("%.4g" % v) for u, v in units.items() if v is not None},
+                                "model_w": {u: round(w, 1) for u, w in watts.items()},
+                                "model_total_w": round(sum(watts.values()), 1),
+                                "measured_w_above_idle": round(power[name]["socket_w"] - idle, 1)}
+    return out
+
+
 def lds_rate(torch, dev, blocks=2048, iters=1024, reps=5):
     """Rate of plain conflict-free 16-byte LDS reads on this GPU (TB/s), the
     row reads that feed the attention kernels' MFMAs."""
@@ -363,15 +456,17 @@ def exp_rate(torch, dev, blocks=2048, iters=1024, reps=5):
     return blocks * 256.0 * iters * 16 / (ms * 1e-3)
 
 
-def power_samples(torch, calls, seconds=2.0):
+def power_samples(torch, calls, seconds=2.5, settle=1.0):
     """Socket power and GFX clock while each call in `calls` (name -> fn)
     runs back to back for `seconds`, read through amdsmi (the driver's
     sensors; no GPU setting is touched).  The calls are enqueued in chunks of
     ~50 ms with the next chunk always queued, and the sensors are read only
     while a chunk is still running, so every sample sees the GPU busy with
-    that call.  Means of the samples after the first third (the clock
-    settles), with the board's power limit and an idle reading; None where
-    amdsmi is missing or fails."""
+    that call.  The power reading trails the load by up to about a second,
+    so each call's samples of its first `settle` seconds are dropped, and the
+    idle reading is the mean over half a second taken 1.5 s after the GPU
+    went idle.  Means, with the board's power limit; None where amdsmi is
+    missing or fails."""
     try:
         import amdsmi
         amdsmi.amdsmi_init()
@@ -386,9 +481,13 @@ def power_samples(torch, calls, seconds=2.0):
 
     try:
         torch.cuda.synchronize()
-        time.sleep(0.2)
-        idle_w, _, limit = read()
-        out = {"idle_socket_w": idle_w,
+        time.sleep(1.5)
+        idle = []
+        for _ in range(10):
+            idle.append(read())
+            time.sleep(0.05)
+        limit = idle[-1][2]
+        out = {"idle_socket_w": round(float(np.mean([g[0] for g in idle])), 1),
                "power_limit_w": float(limit) / 1e6 if isinstance(limit, (int, float)) else None}
         for name, fn in calls.items():
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -406,11 +505,11 @@ def power_samples(torch, calls, seconds=2.0):
                 queued.record()
                 if running is not None:
                     while not running.query():
-                        got.append(read()[:2])
+                        if time.time() - t0 >= settle:
+                            got.append(read()[:2])
                         time.sleep(0.005)
                 running = queued
             torch.cuda.synchronize()
-            got = got[len(got) // 3:]
             out[name] = {"socket_w": round(float(np.mean([g[0] for g in got])), 1) if got else None,
                          "gfx_mhz": round(float(np.mean([g[1] for g in got])), 1) if got else None,
                          "samples": len(got)}
@@ -618,7 +717,9 @@ def main():
         ga = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
         gb = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
         calls["gemm_8192"] = lambda: torch.matmul(ga, gb)
-        calls["mfma_probe"] = mfma_launcher(torch, dev)[0]
+        probes, probe_bufs = probe_launchers(torch, dev)
+        for name, (fn, _, _) in probes.items():
+            calls[name] = fn
         power = power_samples(torch, calls)
         del ga, gb
     scores = fwd_flop / (4.0 * D)
@@ -634,6 +735,26 @@ def main():
     executed = {"fwd": fwd_flop, "bwd_dkdv": 2.0 * fwd_flop, "bwd_dq": 1.5 * fwd_flop}
     lds = {"probe_ds_read_b128_tbs": round(lds_rate(torch, dev), 1),
            "kernels_tbs": {n: round(f / 32.0 / (per[n] * 1e-3) / 1e12, 1) for n, f in executed.items() if n in per}}
+    # energy per unit of each probe, and what the attention kernels' units
+    # would draw at those energies (video rows only: text rows take other
+    # walks; the quantized forward issues other instructions)
+    energy = None
+    if power is not None and nt == 0 and prec == sta.STA_PREC_DEFAULT:
+        rates = {n: timed_rate(torch, fn, u) for n, (fn, u, _) in probes.items()}
+        batch = B if idx.num_heads == H else 1
+        fwd_copy = block_copy_bytes(lens, kv_idx, kv_cnt, batch, 4 * D)
+        scores = fwd_flop / (4.0 * D)
+        hbm = lambda n: measured_traffic(n) if default_step else None
+        kernels = {"fwd": {"mfma_flop": fwd_flop, "lds_read_bytes": fwd_flop / 32.0, "l2_to_lds_bytes": fwd_copy,
+                           "hbm_bytes": hbm("fwd"), "exps": scores}}
+        if not fwd_only:
+            dkdv_copy = block_copy_bytes(lens, idx.q_idx.cpu().numpy(), idx.q_cnt.cpu().numpy(), batch, 4 * D + 8)
+            kernels["bwd_dkdv"] = {"mfma_flop": 2.0 * fwd_flop, "lds_read_bytes": 2.0 * fwd_flop / 32.0,
+                                   "l2_to_lds_bytes": dkdv_copy, "hbm_bytes": hbm("bwd_dkdv"), "exps": scores}
+            kernels["bwd_dq"] = {"mfma_flop": 1.5 * fwd_flop, "lds_read_bytes": 1.5 * fwd_flop / 32.0,
+                                 "l2_to_lds_bytes": fwd_copy, "hbm_bytes": hbm("bwd_dq"), "exps": scores}
+        energy = energy_model(power, probes, rates, kernels, per)
+    probes = probe_bufs = None                      # frees the probes' source regions
     tensor_bytes = B * H * S * D * 2
     reorder_gbs = 3 * 2 * tensor_bytes / (per["reorder_qkv"] * 1e-3) / 1e9 if "reorder_qkv" in per else None
     out = {
@@ -696,6 +817,10 @@ def main():
             # socket power and GFX clock while each call runs back to back
             # (after the timed steps; amdsmi sensors)
             "power": power,
+            # energy per unit from the probes above, and each kernel's units
+            # priced at them against its measured power (the rest of the
+            # vector work is not priced)
+            "energy": energy,
         },
         "roofline": roofline,
     }

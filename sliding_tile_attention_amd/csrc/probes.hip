@@ -31,8 +31,18 @@
 //    conflicts), the granule moving by one per round so that no read is
 //    loop-invariant; the XOR of what it read is written out.  A launch reads
 //    blocks * 256 * iters * 16 * 16 bytes.
+//
+// 5. block_copy_kernel: the attention kernels' key/value block copies with
+//    nothing else issued.  A workgroup of 4 waves moves 16 KB blocks (32 rows
+//    of K and V at D = 128) from global memory into a 2-slot LDS ring with
+//    16-byte buffer-to-LDS loads, waits for them and meets at a barrier, as
+//    the kernels do once per key block.  The blocks come in turn from a
+//    source region of `bytes` bytes: a few MB stay in L2, a large region
+//    streams from HBM.  A launch copies blocks * iters * 16 KB.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "mfma.h"
 
 namespace {
 
@@ -119,6 +129,27 @@ __global__ __launch_bounds__(256) void lds_rate_kernel(uint32_t *__restrict__ ou
     out[blockIdx.x * 256u + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
 }
 
+__global__ __launch_bounds__(256) void block_copy_kernel(const char *__restrict__ src, int region_blocks, int iters,
+                                                         int32_t *__restrict__ out)
+{
+    constexpr int BLOCK = 16384;
+    __shared__ __attribute__((aligned(1024))) char ring[2][BLOCK];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int off = (wave * 64 + lane) * 16;             // this lane's granule of each 4 KB quarter
+    int b = (int)(blockIdx.x % (unsigned)region_blocks);
+    for (int it = 0; it < iters; ++it) {
+        const auto rs = sta::make_rsrc(src + (int64_t)b * BLOCK, BLOCK);
+        char *dst = ring[it & 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sta::b2lds16(rs, off + i * 4096, dst + (i * 4 + wave) * 1024);
+        sta::wait_vmem<0>();
+        sta::barrier_nofence();
+        b = b + 1 == region_blocks ? 0 : b + 1;
+    }
+    __syncthreads();
+    out[blockIdx.x * 256u + tid] = ((const int32_t *)ring[0])[tid] ^ ((const int32_t *)ring[1])[tid];
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,6 +193,19 @@ int sta_probe_mfma(float *out, int blocks, int iters, void *stream)
 {
     if (blocks <= 0 || iters < 0) return 1;
     hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+    return (int)hipGetLastError();
+}
+
+// Enqueues one block-copy launch of `blocks` workgroups of 256 threads on
+// `stream`: each copies `iters` 16 KB blocks of the source region (device,
+// `bytes` a positive multiple of 16384, 16-byte aligned) into LDS; out holds
+// blocks * 256 int32 (device).  Returns 0, or the HIP error code of the
+// launch (1 for a bad size).
+int sta_probe_block_copy(const void *src, int64_t bytes, int blocks, int iters, int32_t *out, void *stream)
+{
+    if (bytes < 16384 || bytes % 16384 != 0 || bytes / 16384 > INT32_MAX || blocks <= 0 || iters < 1) return 1;
+    hipLaunchKernelGGL(block_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const char *)src, (int)(bytes / 16384), iters, out);
     return (int)hipGetLastError();
 }
 

@@ -119,3 +119,24 @@ def test_index_options_720p_shape():
     offsets = g.integers([-1, -2, -2], [1, 2, 2], endpoint=True, size=(H, 300, 3)).astype(np.int32)
     say("index options 720p")
     _check_index(c["grid"], c["tile"], windows_for("720p-shifted-perhead"), offsets, "truncate")
+
+
+def test_tile_reorder_wrapper_writes_out():
+    """The tensor-level wrapper: [..., N, C] rows permuted into a caller's out
+    tensor (returned), bit-exact against the oracle's permutation, and back."""
+    grid, tile = (8, 24, 40), (4, 8, 8)
+    say("tile_reorder wrapper %s %s" % (grid, tile))
+    geom = sta.Geometry(grid, tile)
+    N = int(np.prod(grid))
+    g = torch.Generator(device="cpu").manual_seed(11)
+    x_h = torch.randint(-2 ** 15, 2 ** 15, (2, 3, N, 64), dtype=torch.int16, generator=g).view(torch.bfloat16)
+    x = x_h.cuda()
+    out = torch.empty_like(x)
+    got = sta.tile_reorder(x, geom, out=out)
+    assert got is out
+    back = sta.tile_reorder(out, geom, inverse=True)
+    torch.cuda.synchronize()
+    expect = np.empty_like(x_h.view(torch.int16).numpy())
+    expect[:, :, oracle.perm(grid, tile), :] = x_h.view(torch.int16).numpy()
+    assert np.array_equal(out.cpu().view(torch.int16).numpy(), expect)
+    assert torch.equal(back.cpu().view(torch.int16), x_h.view(torch.int16))

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_measurement_probes_load_and_reject_bad_sizes():
     """The benchmark's probe library (exponential rate, matrix-core rate, LDS
-    read rate, copy calibration) loads beside libsta and rejects sizes before
+    read rate, copy calibration, block copies into LDS) loads beside libsta and rejects sizes before
     launching anything."""
     path = os.path.join(os.path.dirname(sta.LIB_PATH), "libsta_probe.so")
     lib = ctypes.CDLL(path)
@@ -53,6 +53,13 @@ def test_measurement_probes_load_and_reject_bad_sizes():
     assert lib.sta_probe_mfma(None, 0, 16, None) == 1
     assert lib.sta_probe_mfma(None, 4, -1, None) == 1
     assert lib.sta_probe_lds(None, 0, 16, None) == 1
+    lib.sta_probe_block_copy.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    assert lib.sta_probe_block_copy(None, 8192, 4, 16, None, None) == 1         # below one 16 KB block
+    assert lib.sta_probe_block_copy(None, 16384 + 16, 4, 16, None, None) == 1   # not whole blocks
+    assert lib.sta_probe_block_copy(None, 16384 << 31, 4, 16, None, None) == 1  # too many blocks
+    assert lib.sta_probe_block_copy(None, 16384, 0, 16, None, None) == 1
+    assert lib.sta_probe_block_copy(None, 16384, 4, 0, None, None) == 1
 
 
 def test_status_strings_and_version():
