@@ -22,6 +22,10 @@ SOURCES = ["api.hip", "workspace.hip", "reorder.hip", "index.hip", "attn_f32.hip
 HEADERS = ["common.h", "mfma.h", "tiles.h"]
 # Per-source extra compiler flags (none at present).
 EXTRA = {}
+# Compile-time variants of the kernels for measurements, e.g.
+#   STA_DEFINES="-DSTA_FWD_QG=2" python sliding_tile_attention_amd/build.py --force
+# (the forward with two row groups per wave); empty for the library as shipped.
+DEFINES = os.environ.get("STA_DEFINES", "").split()
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -39,9 +43,9 @@ def _compile(src, force):
     s = os.path.join(CSRC, src)
     o = os.path.join(OBJ, src.replace(".hip", ".o"))
     deps = [s] + [os.path.join(CSRC, h) for h in HEADERS] + [os.path.join(ROOT, "include", "libsta.h")]
-    if not force and os.path.exists(o) and os.path.getmtime(o) >= _newest(deps):
+    if not force and not DEFINES and os.path.exists(o) and os.path.getmtime(o) >= _newest(deps):
         return o
-    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", s, "-o", o]
+    cmd = [HIPCC] + FLAGS + DEFINES + EXTRA.get(src, []) + ["-c", s, "-o", o]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
