@@ -50,6 +50,11 @@ namespace sta {
 #ifndef STA_FWD_MINB
 #define STA_FWD_MINB 3
 #endif
+// With two row groups per wave: group 0's PV chain interleaved with group
+// 1's exponentials, each group reading the V^T fragments itself.
+#ifndef STA_FWD_SPLITPV
+#define STA_FWD_SPLITPV 0
+#endif
 
 struct NoRasterCopy {
     __device__ NoRasterCopy(int, const Geo &) {}
@@ -224,23 +229,23 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? STA_FWD_MINB : 2) void fwd_bf16_
         // true max is taken, O and l are rescaled, and the block is
         // recomputed.
         bf16x8 pf[QG][2];
-        static_for<0, QG>([&](auto qc) {
+        auto probs = [&](auto qc) {
             constexpr int q = decltype(qc)::value;
-            auto probs = [&]() {
-                const float mneg = -m_i[q];
-                float ls = 0.f;
+            const float mneg = -m_i[q];
+            float ls = 0.f;
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    bf16x8 v;
+            for (int hf = 0; hf < 2; ++hf) {
+                bf16x8 v;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        v[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[q][8 * hf + i], scale_log2, mneg));
-                    pf[q][hf] = v;
-                    ls = sum8(v, ls);
-                }
-                return ls;
-            };
-            float ls = probs();
+                for (int i = 0; i < 8; ++i)
+                    v[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[q][8 * hf + i], scale_log2, mneg));
+                pf[q][hf] = v;
+                ls = sum8(v, ls);
+            }
+            return ls;
+        };
+        auto settle = [&](auto qc, float ls) {
+            constexpr int q = decltype(qc)::value;
             if (__any(!(ls < 256.f))) {
                 float mx = -INFINITY;
 #pragma unroll
@@ -254,10 +259,10 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? STA_FWD_MINB : 2) void fwd_bf16_
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[q][db][r] *= alpha;
-                ls = probs();
+                ls = probs(qc);
             }
             l_i[q] += ls;
-        });
+        };
 
         // PV: the V^T fragments (two transposing reads each) FV ahead
         constexpr int FV = QG == 1 ? 3 : 2, NV = 2 * DB;
@@ -266,19 +271,69 @@ __global__ __launch_bounds__(NW * 64, QG == 1 ? STA_FWD_MINB : 2) void fwd_bf16_
             const int db = j >> 1;
             return cat8(ld_tr4(vp + (tb0 ^ (32 * db))), ld_tr4(vp + (tb1 ^ (32 * db))));
         };
-        bf16x8 rv[FV];
-        __builtin_amdgcn_s_setprio(3);
+        // one group's PV chain: fences keep the reads FV ahead of the MFMAs
+        auto pv_chain = [&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            bf16x8 rv[FV];
 #pragma unroll
-        for (int j = 0; j < FV; ++j) rv[j] = vfrag(j);
+            for (int j = 0; j < FV; ++j) rv[j] = vfrag(j);
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
+            for (int j = 0; j < NV; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+                acc[q][j >> 1] = mfma32(rv[j % FV], pf[q][j & 1], acc[q][j >> 1]);
+                if (j + FV < NV) rv[j % FV] = vfrag(j + FV);
+            }
             __builtin_amdgcn_sched_barrier(0);
+        };
+        using Q0 = std::integral_constant<int, 0>;
+        if constexpr (QG == 2 && STA_FWD_SPLITPV) {
+            // Group 0's PV chain runs while group 1's exponentials are formed
+            // (scheduling groups interleave one MFMA, the two reads of a later
+            // fragment and a few vector instructions), then group 1's chain
+            // reads the V^T fragments again: the K fragments still feed both
+            // groups, the V^T fragments one each.
+            using Q1 = std::integral_constant<int, 1>;
+            settle(Q0{}, probs(Q0{}));
+            __builtin_amdgcn_s_setprio(3);
+            float ls1;
+            {
+                bf16x8 rv = vfrag(0);
+                ls1 = probs(Q1{});
 #pragma unroll
-            for (int q = 0; q < QG; ++q) acc[q][j >> 1] = mfma32(rv[j % FV], pf[q][j & 1], acc[q][j >> 1]);
-            if (j + FV < NV) rv[j % FV] = vfrag(j + FV);
+                for (int j = 0; j < NV; ++j) {
+                    acc[0][j >> 1] = mfma32(rv, pf[0][j & 1], acc[0][j >> 1]);
+                    if (j + 1 < NV) rv = vfrag(j + 1);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // the first fragment's reads
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);    // six vector instructions
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);    // the next fragment's reads
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
+            settle(Q1{}, ls1);
+            __builtin_amdgcn_s_setprio(3);
+            pv_chain(Q1{});
+            __builtin_amdgcn_s_setprio(0);
+        } else {
+            static_for<0, QG>([&](auto qc) { settle(qc, probs(qc)); });
+            bf16x8 rv[FV];
+            __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+            for (int j = 0; j < FV; ++j) rv[j] = vfrag(j);
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q = 0; q < QG; ++q) acc[q][j >> 1] = mfma32(rv[j % FV], pf[q][j & 1], acc[q][j >> 1]);
+                if (j + FV < NV) rv[j % FV] = vfrag(j + FV);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_setprio(0);
     };
 
     static_for<0, NBUF - 1>([&](auto bc) {

@@ -31,16 +31,21 @@ struct RowCopy {
     // the swizzle repeats every 16 rows: when a copy spans a multiple of
     // that, copy i is copy 0 shifted by i*ROWS_PER_COPY rows
     static constexpr bool SHIFT = ROWS_PER_COPY % 16 == 0;
+    // with 16 granules per row, f(r + 8) = f(r) ^ 2: a copy 8 rows on reads
+    // the granule with bit 1 flipped, so the odd copies share one offset
+    static constexpr bool SHIFT8 = !SHIFT && GR == 16 && ROWS_PER_COPY == 8;
+    static constexpr int NOFF = SHIFT ? 1 : SHIFT8 ? 2 : COPIES;
     static_assert(ROWS * D % (THREADS * 8) == 0, "tile must split evenly");
-    int off[SHIFT ? 1 : COPIES];
+    int off[NOFF];
     __device__ explicit RowCopy(int tid)
     {
         const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-        for (int i = 0; i < (SHIFT ? 1 : COPIES); ++i) {
+        for (int i = 0; i < NOFF; ++i) {
             const int slot = (i * W + wave) * 64 + lane;
             const int r = slot / GR, pg = slot % GR;
             off[i] = (r * D + (pg ^ swz_u<GR>(r)) * 8) * 2;
+            if constexpr (SHIFT8) off[i] -= i * ROWS_PER_COPY * D * 2;   // the row shift goes to soffset
         }
     }
     // Asynchronous copy of `valid` rows from src into the LDS tile; rows
@@ -53,6 +58,8 @@ struct RowCopy {
         for (int i = 0; i < COPIES; ++i) {
             if constexpr (SHIFT)
                 b2lds16(rs, off[0], lds + (i * W + wave) * 512, i * ROWS_PER_COPY * D * 2);
+            else if constexpr (SHIFT8)
+                b2lds16(rs, off[i & 1], lds + (i * W + wave) * 512, i * ROWS_PER_COPY * D * 2);
             else
                 b2lds16(rs, off[i], lds + (i * W + wave) * 512);
         }
