@@ -12,7 +12,7 @@
 // those past any block end.
 //
 // Work decomposition
-//   workgroup = NW waves = M = NW*32 consecutive query rows of one query
+//   workgroup = NW waves = M = NW*32*QG consecutive query rows of one query
 //   tile of one (b, h); work items are ordered head-major and each of the 8
 //   XCDs takes one contiguous range of that order, cut at equal cost
 //   (schedule.hip), so that the workgroups sharing an XCD's L2 walk
