@@ -380,10 +380,21 @@ __global__ __launch_bounds__(NW * 64, 2) void dkdv_kernel(
         if (wave == 0) {                            // -lse log2(e) and -Delta of the block's rows (zero past the end)
             const auto rl = make_rsrc(NLSE2 + sbase + row0, valid * 4);
             const auto rd = make_rsrc(NDelta + sbase + row0, valid * 4);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void *)(stage(bc) + 2 * BLK),
-                                                     4, lo, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rd, (__attribute__((address_space(3))) void *)(stage(bc) + 2 * BLK + 2 * SROWS), 4, lo, 0, 0, 0);
+            if constexpr (NBUF > 2) {
+                // LDS addresses from the low 32 bits of the generic ones: the
+                // address-space cast's null check fails to compile here
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rl, (__attribute__((address_space(3))) void *)(uint32_t)(uintptr_t)(stage(bc) + 2 * BLK), 4, lo, 0,
+                    0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rd, (__attribute__((address_space(3))) void *)(uint32_t)(uintptr_t)(stage(bc) + 2 * BLK + 2 * SROWS),
+                    4, lo, 0, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rl, (__attribute__((address_space(3))) void *)(stage(bc) + 2 * BLK), 4, lo, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rd, (__attribute__((address_space(3))) void *)(stage(bc) + 2 * BLK + 2 * SROWS), 4, lo, 0, 0, 0);
+            }
         }
         walk_next<RASTER>(cw, lst, cnt, BQ, g);
     };
